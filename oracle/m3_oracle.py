@@ -1,0 +1,210 @@
+"""fp64 CPU oracle for the Mamba-3 SSM core.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this module.  The HIP library never calls it and shares no code with
+it.  Everything here is deliberately plain: a token-by-token loop in float64,
+vectorised only over the independent (batch, head) pairs.
+
+Sources (web pages on Mamba-3; cited by title and section):
+  [CH]  "Znakomstvo s Mamba-3 ..." (chernovdev.ru), sec. 1 "Exponential-
+        trapezoidal discretisation" -- the one displayed three-term recurrence;
+        sec. 2 "Complex-valued SSMs and the RoPE trick" -- cumulative
+        data-dependent rotations of B and C; sec. 3 "MIMO" -- B_t in R^{N x R},
+        x_t in R^{P x R}, the state update becomes a matrix product.
+  [PB]  "La dualita: Mamba-2 e Mamba-3" (book.paithon.it), sec. "State Space
+        Duality" -- scalar-times-identity transition, masked-attention form
+        Y = (M o C B^T) X; sec. "Mamba-3" -- the lambda family (lambda = 1 is
+        Euler / Mamba-2, lambda = 1/2 the trapezoid), complex SSM of size N/2 ==
+        real SSM of size N with 2x2 rotation blocks scaled by the decay, and
+        MIMO as a sum of R outer products on an unchanged state.
+
+Readings where the pages are silent (each listed in the design notes):
+  * beta_t uses step t's own lambda, Delta and decay; Delta multiplies B
+    explicitly (the displayed recurrence), not folded into B.
+  * Fresh start: h_{-1} = 0 and B_{-1} x_{-1} = 0.  Continuation passes the
+    carry (h, rotated B_{t-1}, x_{t-1}, cumulative angle).
+  * Rotation pairs are adjacent state entries (2j, 2j+1); the rotated input is
+    Btil = R(Phi)^T B with R(phi) = [[cos, -sin], [sin, cos]]; Phi is the
+    inclusive cumulative angle (Phi_t includes theta_t).  The carried B_{t-1}
+    keeps the rotation of its own step.  The returned state is the real state
+    in this rotated frame.
+  * y_t = h_t^T Ctil_t uses the state after the update; there is no D skip.
+  * MIMO ranks share Delta, lambda, the decay and the rotation; no 1/R factor.
+
+Parity: every function here is pinned by the not-gpu tests in
+tests/test_oracle_pins.py (closed forms, special cases, brute force, an
+independent complex-arithmetic recurrence, order of accuracy).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=F64)
+
+
+def rotate_pairs(v: np.ndarray, phi: np.ndarray) -> np.ndarray:
+    """Rotate adjacent pairs of the last axis of ``v`` by -phi.
+
+    v: [..., R, N];  phi: [..., N/2] (broadcast over R).  Returns R(phi)^T v
+    pairwise: out[2j] = cos*v[2j] + sin*v[2j+1], out[2j+1] = -sin*v[2j] +
+    cos*v[2j+1]  ([CH] sec. 2; [PB] sec. "Mamba-3", 2x2 rotation blocks).
+    """
+    c = np.cos(phi)[..., None, :]
+    s = np.sin(phi)[..., None, :]
+    v0 = v[..., 0::2]
+    v1 = v[..., 1::2]
+    out = np.empty(np.broadcast_shapes(v.shape), dtype=F64)
+    out[..., 0::2] = c * v0 + s * v1
+    out[..., 1::2] = -s * v0 + c * v1
+    return out
+
+
+def coefficients(dt, lam, A):
+    """alpha = exp(Delta A), beta = (1 - lambda) Delta alpha, gamma = lambda Delta
+    ([CH] sec. 1, displayed recurrence).  dt, lam: [..., H]; A: [H]."""
+    alpha = np.exp(dt * A)
+    beta = (1.0 - lam) * dt * alpha
+    gamma = lam * dt
+    return alpha, beta, gamma
+
+
+def ssm_step(h, Bp, xp, phi, x_t, B_t, C_t, dt_t, lam_t, A, theta_t):
+    """One token of the exponential-trapezoidal MIMO recurrence.
+
+    h: [Bt,H,N,P]; Bp: [Bt,H,R,N] (rotated B of the previous token);
+    xp: [Bt,H,R,P]; phi: [Bt,H,N/2] or None; x_t: [Bt,H,R,P];
+    B_t, C_t: [Bt,H,R,N]; dt_t, lam_t: [Bt,H]; A: [H]; theta_t: [Bt,H,N/2] or None.
+
+    h_t = alpha h_{t-1} + beta Btil_{t-1} x_{t-1}^T + gamma Btil_t x_t^T with
+    u = sum_r Btil[:, r] x[:, r]^T ([CH] sec. 1 and sec. 3; [PB] "Mamba-3");
+    Y_t = h_t^T Ctil_t.  Returns (y_t [Bt,H,R,P], h, Btil_t, x_t, phi).
+    """
+    alpha, beta, gamma = coefficients(dt_t, lam_t, A)
+    if theta_t is not None:
+        phi = phi + theta_t
+        Bt_r = rotate_pairs(B_t, phi)
+        Ct_r = rotate_pairs(C_t, phi)
+    else:
+        Bt_r, Ct_r = B_t, C_t
+    u_prev = np.einsum("bhrn,bhrp->bhnp", Bp, xp)
+    u_cur = np.einsum("bhrn,bhrp->bhnp", Bt_r, x_t)
+    h = (alpha[..., None, None] * h + beta[..., None, None] * u_prev
+         + gamma[..., None, None] * u_cur)
+    y_t = np.einsum("bhnp,bhrn->bhrp", h, Ct_r)
+    return y_t, h, Bt_r, x_t, phi
+
+
+def ssm_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
+                  xprev=None, phi0=None):
+    """Sequential fp64 oracle of the whole sequence (prefill semantics).
+
+    x [Bt,L,H,R,P]; B, C [Bt,L,H,R,N]; dt, lam [Bt,L,H]; A [H];
+    theta [Bt,L,H,N/2] or None; carry-in (all optional, zeros if None):
+    h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
+    Returns dict(y [Bt,L,H,R,P], h [Bt,H,N,P], Bprev_rot [Bt,H,R,N],
+    xprev [Bt,H,R,P], phi [Bt,H,N/2] or None), all float64.
+    """
+    x, B, C, dt, lam, A = map(_f64, (x, B, C, dt, lam, A))
+    theta = _f64(theta)
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    h = np.zeros((Bt, H, N, P)) if h0 is None else _f64(h0).copy()
+    Bp = np.zeros((Bt, H, R, N)) if Bprev_rot is None else _f64(Bprev_rot).copy()
+    xp = np.zeros((Bt, H, R, P)) if xprev is None else _f64(xprev).copy()
+    phi = None
+    if theta is not None:
+        phi = np.zeros((Bt, H, N // 2)) if phi0 is None else _f64(phi0).copy()
+    y = np.zeros((Bt, L, H, R, P))
+    for t in range(L):
+        th = None if theta is None else theta[:, t]
+        y[:, t], h, Bp, xp, phi = ssm_step(h, Bp, xp, phi, x[:, t], B[:, t], C[:, t],
+                                           dt[:, t], lam[:, t], A, th)
+    return dict(y=y, h=h, Bprev_rot=Bp, xprev=xp, phi=phi)
+
+
+def decode_reference(h, Bprev_rot, xprev, phi, x, B, C, dt, lam, A, theta=None):
+    """One decode step against a resident state: the same token update as the
+    prefill loop.  Shapes as in :func:`ssm_step` (no time axis).
+    Returns dict(y, h, Bprev_rot, xprev, phi)."""
+    y, h2, Bp, xp, ph = ssm_step(_f64(h), _f64(Bprev_rot), _f64(xprev), _f64(phi),
+                                 _f64(x), _f64(B), _f64(C), _f64(dt), _f64(lam),
+                                 _f64(A), _f64(theta))
+    return dict(y=y, h=h2, Bprev_rot=Bp, xprev=xp, phi=ph)
+
+
+def rope_angles_cumsum(theta, phi0=None):
+    """Inclusive cumulative angle Phi_t = Phi_{-1} + sum_{s<=t} theta_s along the
+    sequence axis ([CH] sec. 2: rotations aggregated over all time steps).
+    theta [Bt,L,H,J]; phi0 [Bt,H,J] or None."""
+    th = _f64(theta)
+    out = np.cumsum(th, axis=1)
+    if phi0 is not None:
+        out = out + _f64(phi0)[:, None]
+    return out
+
+
+def dual_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
+                   xprev=None, phi0=None):
+    """Materialised masked-attention (SSD dual) form, O(L^2) per (b, h).
+
+    [PB] sec. "State Space Duality": with a scalar-times-identity transition the
+    recurrence equals Y = (M o C B^T) X with a causal decay mask.  For the
+    three-term recurrence the mask follows by unrolling the recurrence (our
+    derivation): with Lambda_t = sum_{k<=t} Delta_k A,
+        M[t, j] = exp(Lambda_t - Lambda_j) * (gamma_j + (1 - lambda_{j+1}) Delta_{j+1})  (j < t)
+        M[t, t] = gamma_t,   M[t, j] = 0 (j > t),
+    broadcast over the R x R rank blocks, plus the carried-in state
+    H' = h0 + (1 - lambda_0) Delta_0 Btil_{-1} x_{-1}^T read out with decay
+    exp(Lambda_t - Lambda_{-1}).  Rotations as in :func:`rotate_pairs`.
+    Returns y [Bt,L,H,R,P] (float64).
+    """
+    x, B, C, dt, lam, A = map(_f64, (x, B, C, dt, lam, A))
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    if theta is not None:
+        phi = rope_angles_cumsum(theta, phi0)  # [Bt,L,H,N/2]
+        Bt_r = rotate_pairs(B, phi)
+        Ct_r = rotate_pairs(C, phi)
+    else:
+        Bt_r, Ct_r = B, C
+    logA = dt * A  # [Bt,L,H]
+    Lam = np.cumsum(logA, axis=1)
+    gamma = lam * dt
+    nxt = np.zeros_like(dt)
+    nxt[:, :-1] = (1.0 - lam[:, 1:]) * dt[:, 1:]
+    delta = gamma + nxt
+    y = np.zeros((Bt, L, H, R, P))
+    tri = np.tril(np.ones((L, L), dtype=bool), k=-1)
+    for b in range(Bt):
+        for hh in range(H):
+            lam_v = Lam[b, :, hh]
+            diff = lam_v[:, None] - lam_v[None, :]
+            M = np.where(tri, np.exp(np.where(tri, diff, 0.0)) * delta[b, None, :, hh], 0.0)
+            M[np.arange(L), np.arange(L)] = gamma[b, :, hh]
+            Cm = Ct_r[b, :, hh].reshape(L * R, N)
+            Bm = Bt_r[b, :, hh].reshape(L * R, N)
+            G = Cm @ Bm.T
+            Mb = np.kron(M, np.ones((R, R)))
+            Y = (Mb * G) @ x[b, :, hh].reshape(L * R, P)
+            Hin = np.zeros((N, P))
+            if h0 is not None:
+                Hin += _f64(h0)[b, hh]
+            if Bprev_rot is not None and xprev is not None:
+                Hin += (1.0 - lam[b, 0, hh]) * dt[b, 0, hh] * (
+                    _f64(Bprev_rot)[b, hh].T @ _f64(xprev)[b, hh])
+            dec = np.exp(lam_v)  # exp(Lambda_t - Lambda_{-1})
+            Y += (dec[:, None, None] * (Ct_r[b, :, hh] @ Hin)).reshape(L * R, P)
+            y[b, :, hh] = Y.reshape(L, R, P)
+    return y
+
+
+def rel_l2(a, b) -> float:
+    """Relative L2 error ||a - b|| / ||b|| in float64 (parity metric)."""
+    a = np.asarray(a, dtype=F64)
+    b = np.asarray(b, dtype=F64)
+    den = np.linalg.norm(b.ravel())
+    return float(np.linalg.norm((a - b).ravel()) / (den if den > 0 else 1.0))

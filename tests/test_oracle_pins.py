@@ -1,0 +1,309 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: a closed
+form, an independently written special-case recurrence (Mamba-2 / Euler, the
+complex-diagonal SSM), brute-force impulse responses, an order-of-accuracy
+law, rotation periodicity, linearity, and the carry convention.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import m3_oracle as orc
+from synth.inputs import Shape, make_inputs
+
+
+
+def _tiny(Bt=2, L=24, H=3, P=5, N=6, R=1, rope=False, seed=7, **kw):
+    return make_inputs(Shape(Bt, L, H, P, N, R, "f32", rope), seed, **kw)
+
+
+# ---------------------------------------------------------------- P-cf
+def test_closed_form_scalar_constant_inputs():
+    """N=P=R=1, theta=0, constant Delta, lambda, x=B=C=1:
+    h_0 = gamma and h_t = alpha^t gamma + (beta+gamma)(1-alpha^t)/(1-alpha)."""
+    L, dtv, lamv, Av = 50, 0.3, 0.7, -1.3
+    ones = np.ones((1, L, 1, 1, 1))
+    dt = np.full((1, L, 1), dtv)
+    lam = np.full((1, L, 1), lamv)
+    A = np.array([Av])
+    out = orc.ssm_reference(ones, ones, ones, dt, lam, A)
+    a = np.exp(dtv * Av)
+    beta = (1 - lamv) * dtv * a
+    gamma = lamv * dtv
+    t = np.arange(L)
+    h = a ** t * gamma + (beta + gamma) * (1 - a ** t) / (1 - a)
+    np.testing.assert_allclose(out["y"][0, :, 0, 0, 0], h, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(out["h"][0, 0, 0, 0], h[-1], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- P-E
+def _mamba2_loop(x, B, C, dt, A):
+    """Independently written exponential-Euler (Mamba-2) recurrence, one (b,h)
+    at a time with explicit loops: h = exp(dt A) h + dt B x^T; y = h^T C."""
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    y = np.zeros((Bt, L, H, R, P))
+    hs = np.zeros((Bt, H, N, P))
+    for b in range(Bt):
+        for hh in range(H):
+            h = np.zeros((N, P))
+            for t in range(L):
+                a = np.exp(dt[b, t, hh] * A[hh])
+                upd = np.zeros((N, P))
+                for r in range(R):
+                    upd += np.outer(B[b, t, hh, r], x[b, t, hh, r])
+                h = a * h + dt[b, t, hh] * upd
+                for r in range(R):
+                    y[b, t, hh, r] = C[b, t, hh, r] @ h
+            hs[b, hh] = h
+    return y, hs
+
+
+@pytest.mark.parametrize("R", [1, 3])
+def test_lambda_one_is_mamba2_euler(R):
+    d = _tiny(R=R, lam_const=1.0)
+    out = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"])
+    y2, h2 = _mamba2_loop(*(np.float64(d[k]) for k in ("x", "B", "C", "dt")), np.float64(d["A"]))
+    assert orc.rel_l2(out["y"], y2) <= 1e-12
+    assert orc.rel_l2(out["h"], h2) <= 1e-12
+
+
+# ---------------------------------------------------------------- P-D
+@pytest.mark.parametrize("R,rope,carry", [(1, False, False), (2, True, False), (1, True, True), (4, False, True)])
+def test_dual_form_equals_loop(R, rope, carry):
+    d = _tiny(L=40, R=R, rope=rope, h0=carry, carry=carry)
+    loop = orc.ssm_reference(**{k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta",
+                                                   "h0", "Bprev_rot", "xprev", "phi0")})
+    dual = orc.dual_reference(**{k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta",
+                                                    "h0", "Bprev_rot", "xprev", "phi0")})
+    assert orc.rel_l2(dual, loop["y"]) <= 1e-10
+
+
+def test_impulse_responses_equal_mask_times_gram():
+    """Brute force: the loop's response to unit impulses e_(j, r') equals the
+    transfer matrix T[(t,r),(j,r')] = M[t,j] * <Ctil_{t,r}, Btil_{j,r'}>."""
+    L, R, N = 12, 2, 4
+    d = _tiny(Bt=1, L=L, H=1, P=1, N=N, R=R, rope=True, seed=11)
+    T_imp = np.zeros((L * R, L * R))
+    for j in range(L):
+        for r in range(R):
+            x = np.zeros((1, L, 1, R, 1))
+            x[0, j, 0, r, 0] = 1.0
+            out = orc.ssm_reference(x, d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"])
+            T_imp[:, j * R + r] = out["y"][0, :, 0, :, 0].reshape(L * R)
+    # independent scalar loops over (t, j) for the mask and the gram
+    dt = np.float64(d["dt"][0, :, 0])
+    lam = np.float64(d["lam"][0, :, 0])
+    A = float(d["A"][0])
+    phi = np.cumsum(np.float64(d["theta"][0, :, 0]), axis=0)  # [L, N/2]
+
+    def rot(v, ang):
+        out = np.empty(N)
+        for q in range(N // 2):
+            c, s = np.cos(ang[q]), np.sin(ang[q])
+            out[2 * q] = c * v[2 * q] + s * v[2 * q + 1]
+            out[2 * q + 1] = -s * v[2 * q] + c * v[2 * q + 1]
+        return out
+
+    T = np.zeros((L * R, L * R))
+    for t in range(L):
+        for j in range(t + 1):
+            if j == t:
+                m = lam[t] * dt[t]
+            else:
+                decay = np.exp(A * dt[j + 1:t + 1].sum())
+                m = decay * (lam[j] * dt[j] + (1 - lam[j + 1]) * dt[j + 1])
+            for r in range(R):
+                for rr in range(R):
+                    c = rot(np.float64(d["C"][0, t, 0, r]), phi[t])
+                    b = rot(np.float64(d["B"][0, j, 0, rr]), phi[j])
+                    T[t * R + r, j * R + rr] = m * (c @ b)
+    assert np.max(np.abs(T_imp - T)) <= 1e-12 * max(1.0, np.max(np.abs(T)))
+
+
+# ---------------------------------------------------------------- P-C
+def test_rope_equals_complex_diagonal_recurrence():
+    """Complex state z in C^{N/2 x P}: z_t = alpha e^{i theta_t} (z_{t-1} +
+    (1-lambda)Delta b_{t-1} x_{t-1}^T) + lambda Delta b_t x_t^T, b = B_{2j} + i B_{2j+1};
+    y = Re(sum_j conj(c_j) z_j).  Must equal the RoPE loop, and the oracle's
+    returned state must equal e^{-i Phi} z pairwise."""
+    d = _tiny(L=30, R=2, N=8, rope=True, h0=False, carry=False, seed=3)
+    out = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"])
+    x, B, C, dt, lam, A, th = (np.float64(d[k]) for k in ("x", "B", "C", "dt", "lam", "A", "theta"))
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    bc = B[..., 0::2] + 1j * B[..., 1::2]
+    cc = C[..., 0::2] + 1j * C[..., 1::2]
+    y = np.zeros((Bt, L, H, R, P))
+    zfin = np.zeros((Bt, H, N // 2, P), dtype=complex)
+    for b in range(Bt):
+        for hh in range(H):
+            z = np.zeros((N // 2, P), dtype=complex)
+            for t in range(L):
+                a = np.exp(dt[b, t, hh] * A[hh]) * np.exp(1j * th[b, t, hh])  # [N/2]
+                prev = np.zeros((N // 2, P), dtype=complex)
+                if t > 0:
+                    prev = sum(np.outer(bc[b, t - 1, hh, r], x[b, t - 1, hh, r]) for r in range(R))
+                cur = sum(np.outer(bc[b, t, hh, r], x[b, t, hh, r]) for r in range(R))
+                z = a[:, None] * (z + (1 - lam[b, t, hh]) * dt[b, t, hh] * prev) \
+                    + lam[b, t, hh] * dt[b, t, hh] * cur
+                for r in range(R):
+                    y[b, t, hh, r] = np.real(np.conj(cc[b, t, hh, r]) @ z)
+            zfin[b, hh] = z
+    assert orc.rel_l2(out["y"], y) <= 1e-10
+    w = np.exp(-1j * out["phi"])[..., None] * zfin
+    h_c = np.empty((Bt, H, N, P))
+    h_c[:, :, 0::2] = w.real
+    h_c[:, :, 1::2] = w.imag
+    assert orc.rel_l2(out["h"], h_c) <= 1e-10
+
+
+# ---------------------------------------------------------------- P-S
+@pytest.mark.parametrize("rope,R", [(False, 1), (True, 2)])
+def test_split_resume_and_decode_chain(rope, R):
+    d = _tiny(L=33, R=R, rope=rope, h0=True, carry=True, seed=5)
+    keys = ("x", "B", "C", "dt", "lam", "theta")
+    whole = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"],
+                              d["h0"], d["Bprev_rot"], d["xprev"], d["phi0"])
+    rng = np.random.default_rng(1)
+    for k in sorted(set(rng.integers(1, 32, size=3).tolist())):
+        sl1 = {n: (None if d[n] is None else d[n][:, :k]) for n in keys}
+        sl2 = {n: (None if d[n] is None else d[n][:, k:]) for n in keys}
+        a = orc.ssm_reference(A=d["A"], h0=d["h0"], Bprev_rot=d["Bprev_rot"], xprev=d["xprev"],
+                              phi0=d["phi0"], **sl1)
+        b = orc.ssm_reference(A=d["A"], h0=a["h"], Bprev_rot=a["Bprev_rot"], xprev=a["xprev"],
+                              phi0=a["phi"], **sl2)
+        y = np.concatenate([a["y"], b["y"]], axis=1)
+        assert orc.rel_l2(y, whole["y"]) <= 1e-12
+        assert orc.rel_l2(b["h"], whole["h"]) <= 1e-12
+    # decode chained token by token
+    st = dict(h=d["h0"], Bprev_rot=d["Bprev_rot"], xprev=d["xprev"], phi=d["phi0"])
+    ys = []
+    for t in range(d["x"].shape[1]):
+        th = None if d["theta"] is None else d["theta"][:, t]
+        st = orc.decode_reference(st["h"], st["Bprev_rot"], st["xprev"], st["phi"],
+                                  d["x"][:, t], d["B"][:, t], d["C"][:, t], d["dt"][:, t],
+                                  d["lam"][:, t], d["A"], th)
+        ys.append(st["y"])
+    assert orc.rel_l2(np.stack(ys, axis=1), whole["y"]) <= 1e-12
+    assert orc.rel_l2(st["h"], whole["h"]) <= 1e-12
+
+
+# ---------------------------------------------------------------- P-ord
+@pytest.mark.parametrize("lamv,order", [(0.5, 2.0), (1.0, 1.0), (0.0, 1.0)])
+def test_order_of_accuracy(lamv, order):
+    """dh/ds = a h + u(s), u = sin(w s), h(0) = 0, exact
+    h(s) = Im[(e^{iws} - e^{as}) / (iw - a)].  The lambda-scheme with alpha inside
+    beta is second order at lambda = 1/2 and first order at lambda in {0, 1}."""
+    a, w, S = -1.5, 3.0, 2.0
+    exact = np.imag((np.exp(1j * w * S) - np.exp(a * S)) / (1j * w - a))
+    errs, hs = [], []
+    for n in (40, 80, 160, 320):
+        dtv = S / n
+        t = np.arange(n + 1)
+        u = np.sin(w * dtv * t)
+        x = u.reshape(1, n + 1, 1, 1, 1)
+        ones = np.ones_like(x)
+        out = orc.ssm_reference(x, ones, ones, np.full((1, n + 1, 1), dtv),
+                                np.full((1, n + 1, 1), lamv), np.array([a]))
+        errs.append(abs(out["y"][0, -1, 0, 0, 0] - exact))
+        hs.append(dtv)
+    slope = np.polyfit(np.log(hs), np.log(errs), 1)[0]
+    assert abs(slope - order) <= 0.2, slope
+
+
+# ---------------------------------------------------------------- P-rot
+@pytest.mark.parametrize("m", [2, 3, 5])
+def test_rotation_periodicity(m):
+    """A = 0 (no decay), theta = 2 pi / m, one impulse at t = 0: the readout
+    repeats every m steps; m = 2 flips the sign every step."""
+    L, N, P = 4 * m + 3, 4, 2
+    rng = np.random.default_rng(m)
+    x = np.zeros((1, L, 1, 1, P))
+    x[0, 0, 0, 0] = rng.standard_normal(P)
+    B = np.broadcast_to(rng.standard_normal(N), (1, L, 1, 1, N)).copy()
+    C = np.broadcast_to(rng.standard_normal(N), (1, L, 1, 1, N)).copy()
+    dt = np.full((1, L, 1), 0.4)
+    lam = np.full((1, L, 1), 0.6)
+    theta = np.full((1, L, 1, N // 2), 2 * np.pi / m)
+    y = orc.ssm_reference(x, B, C, dt, lam, np.array([0.0]), theta)["y"][0, :, 0, 0]
+    for t in range(1, L - m):
+        np.testing.assert_allclose(y[t + m], y[t], atol=1e-12)
+    if m == 2:
+        for t in range(1, L - 1):
+            np.testing.assert_allclose(y[t + 1], -y[t], atol=1e-12)
+
+
+# ---------------------------------------------------------------- P-mimo
+def test_mimo_is_sum_of_siso():
+    R = 3
+    d = _tiny(L=20, R=R, rope=True, seed=9)
+    out = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"])
+    h_sum = 0.0
+    for rp in range(R):
+        h_sum = h_sum + orc.ssm_reference(d["x"][..., rp:rp + 1, :], d["B"][..., rp:rp + 1, :],
+                                          d["C"][..., rp:rp + 1, :], d["dt"], d["lam"], d["A"],
+                                          d["theta"])["h"]
+    assert orc.rel_l2(out["h"], h_sum) <= 1e-12
+    for r in range(R):
+        y_r = 0.0
+        for rp in range(R):
+            y_r = y_r + orc.ssm_reference(d["x"][..., rp:rp + 1, :], d["B"][..., rp:rp + 1, :],
+                                          d["C"][..., r:r + 1, :], d["dt"], d["lam"], d["A"],
+                                          d["theta"])["y"][..., 0, :]
+        assert orc.rel_l2(out["y"][..., r, :], y_r) <= 1e-12
+
+
+# ---------------------------------------------------------------- P-lin
+def test_linearity_and_norms():
+    d = _tiny(L=18, R=2, rope=True, h0=True, seed=4)
+    x2 = np.random.default_rng(0).standard_normal(d["x"].shape)
+    f = lambda x, h0: orc.ssm_reference(x, d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"], h0)
+    y1 = f(d["x"], None)["y"]
+    y2 = f(x2, None)["y"]
+    y12 = f(d["x"] + 2.5 * x2, None)["y"]
+    assert orc.rel_l2(y12, y1 + 2.5 * y2) <= 1e-12
+    yh = f(np.zeros_like(x2), d["h0"])["y"]
+    yboth = f(d["x"], d["h0"])["y"]
+    assert orc.rel_l2(yboth, y1 + yh) <= 1e-12
+    v = np.random.default_rng(1).standard_normal((5, 3, 8))
+    ang = np.random.default_rng(2).standard_normal((5, 4)) * 10
+    rv = orc.rotate_pairs(v, ang)
+    np.testing.assert_allclose(rv[..., 0::2] ** 2 + rv[..., 1::2] ** 2,
+                               v[..., 0::2] ** 2 + v[..., 1::2] ** 2, rtol=1e-12)
+    z = _tiny(L=5, lam_const=0.0)
+    y0 = orc.ssm_reference(z["x"], z["B"], z["C"], z["dt"], z["lam"], z["A"])["y"][:, 0]
+    assert np.all(y0 == 0.0)
+
+
+def test_rope_angles_cumsum_brute_force():
+    rng = np.random.default_rng(3)
+    th = rng.standard_normal((2, 9, 3, 4))
+    p0 = rng.standard_normal((2, 3, 4))
+    out = orc.rope_angles_cumsum(th, p0)
+    for b in range(2):
+        for h in range(3):
+            for j in range(4):
+                acc = p0[b, h, j]
+                for t in range(9):
+                    acc += th[b, t, h, j]
+                    assert abs(out[b, t, h, j] - acc) <= 1e-13
+
+
+def test_oracle_golden_regression():
+    """Stored oracle outputs (written by tests/golden/make_golden.py, which calls
+    only the oracle) still reproduce: guards later edits of the oracle."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "oracle_tiny.json")
+    with open(path) as f:
+        g = json.load(f)
+    from synth.inputs import make_inputs as mk
+    s = Shape(**g["shape"])
+    d = mk(s, g["seed"], h0=True, carry=True)
+    out = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"],
+                            d["h0"], d["Bprev_rot"], d["xprev"], d["phi0"])
+    np.testing.assert_allclose(out["y"].ravel()[: len(g["y_head"])], g["y_head"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(out["h"].ravel()[: len(g["h_head"])], g["h_head"], rtol=1e-12, atol=1e-15)
