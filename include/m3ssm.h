@@ -1,0 +1,176 @@
+/*
+ * m3ssm.h -- C ABI of the Mamba-3 SSM core for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are web pages on Mamba-3, cited by title/section):
+ *   "Znakomstvo s Mamba-3" (chernovdev.ru), sec. 1, the displayed recurrence:
+ *       h_t = alpha_t h_{t-1} + beta_t B_{t-1} x_{t-1}^T + gamma_t B_t x_t^T,
+ *       alpha_t = exp(Delta_t A), beta_t = (1 - lambda_t) Delta_t alpha_t,
+ *       gamma_t = lambda_t Delta_t;
+ *   same page, sec. 2: complex dynamics as data-dependent cumulative RoPE on
+ *       B and C (angles aggregated over all time steps);
+ *   same page, sec. 3, and "La dualita: Mamba-2 e Mamba-3" (book.paithon.it),
+ *       sec. "Mamba-3": rank-R MIMO, B_t, C_t in R^{N x R}, x_t in R^{P x R},
+ *       the update is a sum of R outer products on an unchanged N x P state;
+ *   "La dualita", sec. "State Space Duality" / "Perche conviene": the chunked
+ *       evaluation (intra-chunk masked product, chunk states, inter-chunk
+ *       recurrence, readout of the previous state).
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *   - Rotation pairs are adjacent state entries (2j, 2j+1).  With the inclusive
+ *     cumulative angle Phi_t = Phi_{-1} + sum_{s<=t} theta_s, the kernels use
+ *     Btil = R(Phi)^T B and Ctil = R(Phi)^T C, R(phi) = [[cos,-sin],[sin,cos]].
+ *   - y_t[r] = h_t^T Ctil_t[r] (state after the update, no skip term).
+ *   - The carried previous-token term uses the previous token's rotated B.
+ *   - The state h is the real state in the rotated frame, fp32, [N][P] per head.
+ *
+ * Layouts: every tensor is dense row-major (C order), innermost dimension
+ * last, with the shapes given below.  Base pointers of x, B, C, y, xprev,
+ * xprev_out, h0, h_final, h, Bprev_rot, Bprev_rot_out must be 16-byte
+ * aligned; theta / phi pointers must be 16-byte aligned.
+ * All pointers are device pointers (hipMalloc'd or equivalent) unless noted.
+ * The caller owns every buffer; the library allocates nothing and keeps no
+ * state between calls, so calls on different streams are independent.
+ * `stream` is a hipStream_t (NULL = the null stream).  All calls are
+ * asynchronous with respect to the host; results are visible after the
+ * stream is synchronised.  Results are deterministic (no atomics).
+ *
+ * Errors: every entry point validates its arguments on the host before any
+ * launch and returns a negative m3_status without touching the GPU when they
+ * are invalid.  No exception crosses the ABI.
+ */
+#ifndef M3SSM_H
+#define M3SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum m3_status {
+  M3_OK = 0,
+  M3_ERR_INVALID_ARG = -1, /* null required pointer, bad size, misalignment  */
+  M3_ERR_UNSUPPORTED = -2, /* shape/dtype outside the compiled kernel tiles  */
+  M3_ERR_HIP = -3          /* a HIP launch or runtime error was reported     */
+} m3_status;
+
+typedef enum m3_dtype {
+  M3_F32 = 0,  /* IEEE float32 */
+  M3_BF16 = 1  /* bfloat16 stored as uint16 bit patterns */
+} m3_dtype;
+
+/*
+ * Prefill (chunked, whole sequence per (batch, head)).
+ *
+ *   x       [Bt, L, H, R, P]  in_dtype   inputs x_t (R columns of length P)
+ *   B, C    [Bt, L, H, R, N]  in_dtype   input / output projections
+ *   dt      [Bt, L, H]        float32    Delta_t (> 0, already positive)
+ *   lam     [Bt, L, H]        float32    lambda_t in [0, 1]
+ *   A       [H]               float32    per-head scalar A (< 0)
+ *   theta   [Bt, L, H, N/2]   float32    per-token rotation angles, or NULL
+ *                                        for the real-valued SSM (no RoPE)
+ *   Carry-in, each nullable (NULL = zeros, i.e. a fresh sequence):
+ *   h0        [Bt, H, N, P]   float32    state before the first token
+ *   Bprev_rot [Bt, H, R, N]   float32    rotated B of the token before
+ *   xprev     [Bt, H, R, P]   in_dtype   x of the token before
+ *   phi0      [Bt, H, N/2]    float32    cumulative angle before the first token
+ *   Outputs:
+ *   y         [Bt, L, H, R, P] in_dtype  required
+ *   h_final   [Bt, H, N, P]   float32    state after token L-1 (nullable)
+ *   Bprev_rot_out [Bt,H,R,N]  float32    rotated B_{L-1} (nullable)
+ *   xprev_out [Bt, H, R, P]   in_dtype   x_{L-1} (nullable)
+ *   phi_out   [Bt, H, N/2]    float32    Phi_{L-1} reduced modulo 2*pi into
+ *                                        [-pi, pi] (nullable; needs theta)
+ * Sizes: Bt, L, H >= 1; N, P in {16, 32, 64, 128}; R a power of two <= 64;
+ * chunk = tokens per chunk, 0 selects 64 / R (the only value supported:
+ * one chunk tile always holds 64 (token, rank) rows).
+ * Outputs must not alias inputs.  Passing the carry-out of one call as the
+ * carry-in of the next continues the sequence exactly.
+ */
+typedef struct m3_prefill_args {
+  int32_t Bt, L, H, P, N, R, chunk;
+  int32_t in_dtype; /* m3_dtype */
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* A;
+  const float* theta;
+  const float* h0;
+  const float* Bprev_rot;
+  const void* xprev;
+  const float* phi0;
+  void* y;
+  float* h_final;
+  float* Bprev_rot_out;
+  void* xprev_out;
+  float* phi_out;
+} m3_prefill_args;
+
+int m3_ssm_prefill(const m3_prefill_args* args, void* stream);
+
+/* Device scratch needed by m3_ssm_prefill: always 0 (the fused kernel keeps
+ * chunk states on chip).  Kept so callers can size a workspace generically. */
+size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args);
+
+/*
+ * One decode token against a resident state (the same token update as the
+ * prefill, "La dualita", sec. "Mamba-3": MIMO update on an unchanged state).
+ *
+ *   In/out (updated in place):
+ *   h         [Bt, H, N, P]   float32    state
+ *   phi       [Bt, H, N/2]    float32    cumulative angle (NULL iff theta NULL);
+ *                                        stored reduced modulo 2*pi
+ *   Bprev_rot [Bt, H, R, N]   float32    rotated B of the previous token
+ *   xprev     [Bt, H, R, P]   in_dtype   x of the previous token
+ *   In:
+ *   x [Bt,H,R,P], B, C [Bt,H,R,N] (in_dtype); dt, lam [Bt,H] float32;
+ *   A [H] float32; theta [Bt,H,N/2] float32 or NULL.
+ *   Out: y [Bt, H, R, P] in_dtype.
+ * Sizes: N, P in {16, 32, 64, 128}; R in 1..16.  A fresh sequence starts with
+ * h = 0 (or any state), Bprev_rot = 0, xprev = 0, phi = 0.
+ */
+typedef struct m3_decode_args {
+  int32_t Bt, H, P, N, R;
+  int32_t in_dtype; /* m3_dtype */
+  float* h;
+  float* phi;
+  float* Bprev_rot;
+  void* xprev;
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* A;
+  const float* theta;
+  void* y;
+} m3_decode_args;
+
+int m3_ssm_decode_step(const m3_decode_args* args, void* stream);
+
+/*
+ * Inclusive cumulative rotation angle ("Znakomstvo s Mamba-3", sec. 2: the
+ * rotations are aggregated over all time steps):
+ *   phi[b, t, h, j] = phi0[b, h, j] + sum_{s <= t} theta[b, s, h, j].
+ * theta, phi: [Bt, L, H, npairs] float32; phi0: [Bt, H, npairs] or NULL.
+ * H * npairs must be a multiple of 4.  phi is the plain fp32 running sum
+ * (no modular reduction).  phi must not alias theta.
+ */
+int m3_rope_angles_cumsum(const float* theta, const float* phi0, float* phi,
+                          int32_t Bt, int32_t L, int32_t H, int32_t npairs,
+                          void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* m3_status_string(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char* m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3SSM_H */

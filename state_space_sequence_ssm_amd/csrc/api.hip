@@ -1,0 +1,116 @@
+// C ABI of the Mamba-3 SSM core: host-side validation and dispatch.
+// Every check runs on the host before any HIP call, so invalid arguments are
+// rejected without a GPU (the contract of include/m3ssm.h).
+#include <stdint.h>
+
+#include "m3ssm.h"
+#include "m3ssm_internal.hpp"
+
+namespace {
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool tile_dim(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool al16(const void* p) { return p == nullptr || aligned(p, 16); }
+bool al4(const void* p) { return p == nullptr || aligned(p, 4); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? M3_OK : M3_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* m3_status_string(int status) {
+  switch (status) {
+    case M3_OK: return "ok";
+    case M3_ERR_INVALID_ARG: return "invalid argument";
+    case M3_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case M3_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* m3_version(void) { return "0.1.0"; }
+
+size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args) {
+  (void)args;
+  return 0;
+}
+
+int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
+  if (a == nullptr) return M3_ERR_INVALID_ARG;
+  if (a->Bt < 1 || a->L < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
+  if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
+  if (!a->x || !a->B || !a->C || !a->dt || !a->lam || !a->A || !a->y) return M3_ERR_INVALID_ARG;
+  if ((a->Bprev_rot == nullptr) != (a->xprev == nullptr)) return M3_ERR_INVALID_ARG;
+  if (a->theta == nullptr && (a->phi0 != nullptr || a->phi_out != nullptr)) return M3_ERR_INVALID_ARG;
+  if (a->theta != nullptr && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
+  if (!pow2(a->R) || a->R > 64) return M3_ERR_UNSUPPORTED;
+  if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
+  if (a->chunk != 0 && a->chunk != 64 / a->R) return M3_ERR_UNSUPPORTED;
+  const void* v16[] = {a->x, a->B, a->C, a->y, a->theta, a->h0, a->Bprev_rot, a->xprev,
+                       a->phi0, a->h_final, a->Bprev_rot_out, a->xprev_out, a->phi_out};
+  for (const void* p : v16)
+    if (!al16(p)) return M3_ERR_INVALID_ARG;
+  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A)) return M3_ERR_INVALID_ARG;
+  const double elems = double(a->Bt) * a->L * a->H * a->R * (a->N > a->P ? a->N : a->P);
+  if (elems > 4.0e18 || double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
+  const bool bf16 = a->in_dtype == M3_BF16;
+  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, a->theta != nullptr)
+                          : m3::prefill_lds_bytes_f32(a->N, a->P, a->theta != nullptr);
+  if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
+
+  m3::PrefillParams p{};
+  p.Bt = a->Bt; p.L = a->L; p.H = a->H; p.P = a->P; p.N = a->N; p.R = a->R;
+  int lg = 0;
+  while ((1 << lg) < a->R) ++lg;
+  p.log2R = lg;
+  p.bf16 = bf16;
+  p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.theta = a->theta;
+  p.h0 = a->h0; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev; p.phi0 = a->phi0;
+  p.y = a->y; p.h_final = a->h_final; p.Bprev_rot_out = a->Bprev_rot_out; p.xprev_out = a->xprev_out;
+  p.phi_out = a->phi_out;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(bf16 ? m3::launch_prefill_bf16(p, st) : m3::launch_prefill_f32(p, st));
+}
+
+int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
+  if (a == nullptr) return M3_ERR_INVALID_ARG;
+  if (a->Bt < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
+  if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
+  if (!a->h || !a->Bprev_rot || !a->xprev || !a->x || !a->B || !a->C || !a->dt || !a->lam || !a->A || !a->y)
+    return M3_ERR_INVALID_ARG;
+  if ((a->theta == nullptr) != (a->phi == nullptr)) return M3_ERR_INVALID_ARG;
+  if (a->theta != nullptr && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
+  if (a->R > 16) return M3_ERR_UNSUPPORTED;
+  if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
+  const void* v16[] = {a->h, a->Bprev_rot, a->xprev, a->x, a->B, a->C, a->y, a->phi, a->theta};
+  for (const void* p : v16)
+    if (!al16(p)) return M3_ERR_INVALID_ARG;
+  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A)) return M3_ERR_INVALID_ARG;
+  if (double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
+  m3::DecodeParams p{};
+  p.Bt = a->Bt; p.H = a->H; p.P = a->P; p.N = a->N; p.R = a->R;
+  p.bf16 = a->in_dtype == M3_BF16;
+  p.h = a->h; p.phi = a->phi; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev;
+  p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.theta = a->theta;
+  p.y = a->y;
+  return hip_status(m3::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int m3_rope_angles_cumsum(const float* theta, const float* phi0, float* phi, int32_t Bt, int32_t L,
+                          int32_t H, int32_t npairs, void* stream) {
+  if (theta == nullptr || phi == nullptr) return M3_ERR_INVALID_ARG;
+  if (Bt < 1 || L < 1 || H < 1 || npairs < 1) return M3_ERR_INVALID_ARG;
+  if ((int64_t(H) * npairs) % 4 != 0) return M3_ERR_UNSUPPORTED;
+  if (!al16(theta) || !al16(phi) || !al16(phi0)) return M3_ERR_INVALID_ARG;
+  if (theta == phi) return M3_ERR_INVALID_ARG;
+  const int64_t tiles = (int64_t(H) * npairs / 4 + 7) / 8;
+  if (tiles * Bt > 2147483647LL || double(Bt) * L * H * npairs > 4.0e18) return M3_ERR_INVALID_ARG;
+  m3::AnglesParams p{theta, phi0, phi, Bt, L, H, npairs};
+  return hip_status(m3::launch_angles(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Kernel parameter blocks and launcher entry points shared between the C-ABI
+// layer (api.hip) and the kernels.  Plain pointers and sizes only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+struct DecodeParams {
+  int Bt, H, P, N, R;
+  bool bf16;
+  float* h;
+  float* phi;
+  float* Bprev_rot;
+  void* xprev;
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* A;
+  const float* theta;
+  void* y;
+};
+
+struct PrefillParams {
+  int Bt, L, H, P, N, R;
+  int log2R;
+  bool bf16;
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* A;
+  const float* theta;
+  const float* h0;
+  const float* Bprev_rot;
+  const void* xprev;
+  const float* phi0;
+  void* y;
+  float* h_final;
+  float* Bprev_rot_out;
+  void* xprev_out;
+  float* phi_out;
+};
+
+struct AnglesParams {
+  const float* theta;
+  const float* phi0;
+  float* phi;
+  int Bt, L, H, J;  // J = number of angle pairs per head
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t s);
+hipError_t launch_angles(const AnglesParams& p, hipStream_t s);
+// LDS bytes the prefill kernel needs for (N, P, rope); 0 if not compiled.
+size_t prefill_lds_bytes_bf16(int N, int P, bool rope);
+size_t prefill_lds_bytes_f32(int N, int P, bool rope);
+
+}  // namespace m3

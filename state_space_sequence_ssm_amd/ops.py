@@ -1,0 +1,140 @@
+"""Thin torch binding of the C ABI: the same three entry points, marshalling
+device tensors into the argument structures.  Every step of the computation
+runs in the HIP kernels of libm3ssm.so; torch only provides device memory
+and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+
+class M3Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {_lib.status_string(code)} ({code})")
+        self.code = code
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.M3_BF16
+    if t.dtype == torch.float32:
+        return _lib.M3_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
+                   *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
+                   want_state=True, want_carry=False, chunk=0, stream=None):
+    """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
+    dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None; optional
+    carry-in h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
+    Output tensors are allocated when not given.  Returns a dict with y and,
+    as requested, h_final and the carry-out (Bprev_rot, xprev, phi)."""
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    f32 = torch.float32
+    if y is None:
+        y = torch.empty_like(x)
+    if want_state and h_final is None:
+        h_final = torch.empty((Bt, H, N, P), device=x.device, dtype=f32)
+    if want_carry:
+        if Bprev_rot_out is None:
+            Bprev_rot_out = torch.empty((Bt, H, R, N), device=x.device, dtype=f32)
+        if xprev_out is None:
+            xprev_out = torch.empty((Bt, H, R, P), device=x.device, dtype=x.dtype)
+        if theta is not None and phi_out is None:
+            phi_out = torch.empty((Bt, H, N // 2), device=x.device, dtype=f32)
+    a = _lib.PrefillArgs()
+    a.Bt, a.L, a.H, a.P, a.N, a.R, a.chunk = Bt, L, H, P, N, R, chunk
+    a.in_dtype = _dtype_code(x)
+    a.x = _ptr(x, x.dtype, (Bt, L, H, R, P), "x")
+    a.B = _ptr(B, x.dtype, (Bt, L, H, R, N), "B")
+    a.C = _ptr(C, x.dtype, (Bt, L, H, R, N), "C")
+    a.dt = _ptr(dt, f32, (Bt, L, H), "dt")
+    a.lam = _ptr(lam, f32, (Bt, L, H), "lam")
+    a.A = _ptr(A, f32, (H,), "A")
+    a.theta = _ptr(theta, f32, (Bt, L, H, N // 2), "theta")
+    a.h0 = _ptr(h0, f32, (Bt, H, N, P), "h0")
+    a.Bprev_rot = _ptr(Bprev_rot, f32, (Bt, H, R, N), "Bprev_rot")
+    a.xprev = _ptr(xprev, x.dtype, (Bt, H, R, P), "xprev")
+    a.phi0 = _ptr(phi0, f32, (Bt, H, N // 2), "phi0")
+    a.y = _ptr(y, x.dtype, (Bt, L, H, R, P), "y")
+    a.h_final = _ptr(h_final, f32, (Bt, H, N, P), "h_final")
+    a.Bprev_rot_out = _ptr(Bprev_rot_out, f32, (Bt, H, R, N), "Bprev_rot_out")
+    a.xprev_out = _ptr(xprev_out, x.dtype, (Bt, H, R, P), "xprev_out")
+    a.phi_out = _ptr(phi_out, f32, (Bt, H, N // 2), "phi_out")
+    rc = _lib.load().m3_ssm_prefill(ctypes.byref(a), _stream(stream))
+    if rc != _lib.M3_OK:
+        raise M3Error(rc, "m3_ssm_prefill")
+    return dict(y=y, h=h_final, Bprev_rot=Bprev_rot_out, xprev=xprev_out, phi=phi_out)
+
+
+def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None, *, y=None, stream=None):
+    """One decode token.  In/out (updated in place): h [Bt,H,N,P] fp32,
+    phi [Bt,H,N/2] fp32 (None iff theta None), Bprev_rot [Bt,H,R,N] fp32,
+    xprev [Bt,H,R,P].  Inputs x [Bt,H,R,P], B/C [Bt,H,R,N], dt/lam [Bt,H],
+    A [H], theta [Bt,H,N/2] or None.  Returns y [Bt,H,R,P]."""
+    Bt, H, R, P = x.shape
+    N = B.shape[-1]
+    f32 = torch.float32
+    if y is None:
+        y = torch.empty_like(x)
+    a = _lib.DecodeArgs()
+    a.Bt, a.H, a.P, a.N, a.R = Bt, H, P, N, R
+    a.in_dtype = _dtype_code(x)
+    a.h = _ptr(h, f32, (Bt, H, N, P), "h")
+    a.phi = _ptr(phi, f32, (Bt, H, N // 2), "phi")
+    a.Bprev_rot = _ptr(Bprev_rot, f32, (Bt, H, R, N), "Bprev_rot")
+    a.xprev = _ptr(xprev, x.dtype, (Bt, H, R, P), "xprev")
+    a.x = _ptr(x, x.dtype, (Bt, H, R, P), "x")
+    a.B = _ptr(B, x.dtype, (Bt, H, R, N), "B")
+    a.C = _ptr(C, x.dtype, (Bt, H, R, N), "C")
+    a.dt = _ptr(dt, f32, (Bt, H), "dt")
+    a.lam = _ptr(lam, f32, (Bt, H), "lam")
+    a.A = _ptr(A, f32, (H,), "A")
+    a.theta = _ptr(theta, f32, (Bt, H, N // 2), "theta")
+    a.y = _ptr(y, x.dtype, (Bt, H, R, P), "y")
+    rc = _lib.load().m3_ssm_decode_step(ctypes.byref(a), _stream(stream))
+    if rc != _lib.M3_OK:
+        raise M3Error(rc, "m3_ssm_decode_step")
+    return y
+
+
+def m3_rope_angles_cumsum(theta, phi0=None, *, phi=None, stream=None):
+    """Inclusive cumulative angles phi = phi0 + cumsum(theta, dim=1).
+    theta [Bt,L,H,J] fp32; phi0 [Bt,H,J] or None.  Returns phi [Bt,L,H,J]."""
+    Bt, L, H, J = theta.shape
+    if phi is None:
+        phi = torch.empty_like(theta)
+    pt = _ptr(theta, torch.float32, (Bt, L, H, J), "theta")
+    pp = _ptr(phi0, torch.float32, (Bt, H, J), "phi0")
+    po = _ptr(phi, torch.float32, (Bt, L, H, J), "phi")
+    rc = _lib.load().m3_rope_angles_cumsum(pt, pp, po, Bt, L, H, J, _stream(stream))
+    if rc != _lib.M3_OK:
+        raise M3Error(rc, "m3_rope_angles_cumsum")
+    return phi

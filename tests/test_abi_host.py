@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function the header declares, and rejects invalid arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_space_sequence_ssm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3ssm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libm3ssm.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(m3_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    lib = _lib.load()
+    decl = _declared_functions()
+    assert set(decl) == set(_lib.EXPORTS), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert _lib.status_string(0) == "ok"
+    assert lib.m3_version().decode().count(".") == 2
+
+
+def _good_prefill():
+    a = _lib.PrefillArgs()
+    a.Bt, a.L, a.H, a.P, a.N, a.R, a.chunk, a.in_dtype = 2, 100, 3, 64, 64, 1, 0, _lib.M3_BF16
+    base = 0x10000000
+    for i, f in enumerate(("x", "B", "C", "dt", "lam", "A", "y")):
+        setattr(a, f, base + 0x100000 * i)
+    return a
+
+
+def _rc_prefill(a):
+    return _lib.load().m3_ssm_prefill(ctypes.byref(a), None)
+
+
+def test_prefill_validation():
+    lib = _lib.load()
+    assert lib.m3_ssm_prefill(None, None) == _lib.M3_ERR_INVALID_ARG
+    cases = [
+        (lambda a: setattr(a, "x", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "y", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "L", 0), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "R", 0), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "R", 3), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "N", 48), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "P", 8), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "in_dtype", 7), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "chunk", 32), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "x", 0x10000008), _lib.M3_ERR_INVALID_ARG),  # misaligned
+        (lambda a: setattr(a, "Bprev_rot", 0x20000000), _lib.M3_ERR_INVALID_ARG),  # without xprev
+        (lambda a: setattr(a, "phi0", 0x20000000), _lib.M3_ERR_INVALID_ARG),  # angle without theta
+        (lambda a: setattr(a, "phi_out", 0x20000000), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "N", 128), setattr(a, "P", 128),
+                    setattr(a, "theta", 0x30000000)), _lib.M3_ERR_UNSUPPORTED),  # LDS too large
+    ]
+    for mutate, code in cases:
+        a = _good_prefill()
+        mutate(a)
+        assert _rc_prefill(a) == code
+    assert lib.m3_ssm_prefill_workspace_size(ctypes.byref(_good_prefill())) == 0
+
+
+def test_decode_validation():
+    lib = _lib.load()
+    assert lib.m3_ssm_decode_step(None, None) == _lib.M3_ERR_INVALID_ARG
+
+    def good():
+        a = _lib.DecodeArgs()
+        a.Bt, a.H, a.P, a.N, a.R, a.in_dtype = 4, 2, 64, 64, 4, _lib.M3_BF16
+        for i, f in enumerate(("h", "Bprev_rot", "xprev", "x", "B", "C", "dt", "lam", "A", "y")):
+            setattr(a, f, 0x10000000 + 0x100000 * i)
+        return a
+
+    cases = [
+        (lambda a: setattr(a, "h", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "theta", 0x30000000), _lib.M3_ERR_INVALID_ARG),  # theta without phi
+        (lambda a: setattr(a, "phi", 0x30000000), _lib.M3_ERR_INVALID_ARG),  # phi without theta
+        (lambda a: setattr(a, "R", 17), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "N", 24), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "Bt", 0), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "y", 0x10000004), _lib.M3_ERR_INVALID_ARG),
+    ]
+    for mutate, code in cases:
+        a = good()
+        mutate(a)
+        assert lib.m3_ssm_decode_step(ctypes.byref(a), None) == code
+
+
+def test_angles_validation():
+    f = _lib.load().m3_rope_angles_cumsum
+    assert f(None, None, 0x1000, 1, 1, 1, 4, None) == _lib.M3_ERR_INVALID_ARG
+    assert f(0x1000, None, 0x1000, 1, 1, 1, 4, None) == _lib.M3_ERR_INVALID_ARG  # aliasing
+    assert f(0x1000, None, 0x2000, 1, 0, 1, 4, None) == _lib.M3_ERR_INVALID_ARG
+    assert f(0x1000, None, 0x2000, 1, 5, 1, 3, None) == _lib.M3_ERR_UNSUPPORTED
+    assert f(0x1004, None, 0x2000, 1, 5, 1, 4, None) == _lib.M3_ERR_INVALID_ARG

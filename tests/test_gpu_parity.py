@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path through the C ABI vs the fp64 oracle on the same
+seeded inputs (relative L2 <= 2e-3 for fp32 inputs, <= 2e-2 for bf16 inputs,
+outputs and final states both checked)."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import m3_oracle as orc  # noqa: E402
+from synth.inputs import CONFIGS, SEED_BASE, Shape, make_decode_inputs, make_inputs  # noqa: E402
+from tests.gpu_util import TOL, angle_diff, dev, host, oracle_prefill, storage_dtype, to_device  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from state_space_sequence_ssm_amd import ops as o
+    return o
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run_prefill(ops, dd, s, carry=False, **kw):
+    return ops.m3_ssm_prefill(dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], dd["A"], dd["theta"],
+                              dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"),
+                              want_state=True, want_carry=carry, **kw)
+
+
+# ----------------------------------------------------------------- angles
+@pytest.mark.parametrize("shape", [(2, 1000, 3, 8), (1, 1, 1, 4), (3, 257, 5, 12), (8, 4096, 32, 32)])
+def test_angles_cumsum(ops, shape):
+    _say("angles", shape)
+    rng = np.random.default_rng(sum(shape))
+    th = (rng.standard_normal(shape) * 0.05).astype(np.float32)
+    p0 = rng.standard_normal((shape[0], shape[2], shape[3])).astype(np.float32)
+    out = host(ops.m3_rope_angles_cumsum(dev(th), dev(p0)))
+    ref = orc.rope_angles_cumsum(th, p0)
+    assert orc.rel_l2(out, ref) <= 1e-5
+    out0 = host(ops.m3_rope_angles_cumsum(dev(th)))
+    assert orc.rel_l2(out0, orc.rope_angles_cumsum(th)) <= 1e-5
+
+
+# ----------------------------------------------------------------- prefill, small
+SMALL = [
+    # Bt, L, H, P, N, R, dtype, rope, carry
+    (1, 256, 4, 16, 16, 1, "f32", False, False),
+    (2, 200, 3, 32, 16, 1, "f32", True, True),
+    (2, 150, 2, 64, 64, 2, "f32", True, True),
+    (2, 200, 3, 64, 128, 1, "bf16", False, False),
+    (2, 131, 2, 64, 64, 1, "bf16", True, True),
+    (2, 100, 2, 64, 64, 4, "bf16", True, True),
+    (1, 77, 3, 32, 32, 2, "bf16", True, False),
+    (1, 45, 2, 16, 32, 8, "bf16", True, True),
+    (1, 1, 2, 64, 64, 4, "bf16", True, True),
+    (1, 63, 2, 128, 64, 1, "bf16", False, True),
+    (1, 65, 1, 128, 128, 1, "bf16", True, False),
+    (1, 33, 2, 16, 16, 1, "bf16", True, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_small(ops, case):
+    Bt, L, H, P, N, R, dt_, rope, carry = case
+    s = Shape(Bt, L, H, P, N, R, dt_, rope)
+    _say("prefill small", case)
+    d = make_inputs(s, 1000 + L + N, h0=carry, carry=carry)
+    dd = to_device(d, s)
+    out = _run_prefill(ops, dd, s, carry=True)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(d)
+    tol = TOL[dt_]
+    ey = orc.rel_l2(host(out["y"]), ref["y"])
+    eh = orc.rel_l2(host(out["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= tol and eh <= tol
+    assert orc.rel_l2(host(out["Bprev_rot"]), ref["Bprev_rot"]) <= 1e-5
+    assert np.array_equal(host(out["xprev"]), ref["xprev"])
+    if rope:
+        assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-4
+
+
+def test_prefill_deterministic(ops):
+    s = Shape(2, 300, 4, 64, 64, 4, "bf16", True)
+    dd = to_device(make_inputs(s, 77), s)
+    a = _run_prefill(ops, dd, s)
+    b = _run_prefill(ops, dd, s)
+    torch.cuda.synchronize()
+    assert torch.equal(a["y"], b["y"]) and torch.equal(a["h"], b["h"])
+
+
+# ----------------------------------------------------------------- prefill, full configs
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_prefill_config_full_size(ops, cfg):
+    """Full configuration sizes on the GPU (the benchmarked launch); the oracle
+    checks a sample of (batch, head) units one by one."""
+    s = CONFIGS[cfg]
+    _say("prefill config", cfg, s)
+    d = make_inputs(s, SEED_BASE + cfg)
+    dd = to_device(d, s)
+    out = _run_prefill(ops, dd, s, carry=True)
+    torch.cuda.synchronize()
+    y = out["y"]
+    assert bool(torch.isfinite(y.float()).all())
+    sb = sorted({0, s.Bt - 1})
+    sh = sorted({0, s.H // 2, s.H - 1})
+    ref = oracle_prefill(d, sel_b=sb, sel_h=sh)
+    yg = host(y[sb][:, :, sh])
+    hg = host(out["h"][sb][:, sh])
+    ey, eh = orc.rel_l2(yg, ref["y"]), orc.rel_l2(hg, ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    tol = TOL[s.dtype]
+    assert ey <= tol and eh <= tol
+    if s.rope:
+        assert np.max(angle_diff(host(out["phi"][sb][:, sh]), ref["phi"])) <= 1e-3
+
+
+# ----------------------------------------------------------------- carry / split-resume
+@pytest.mark.parametrize("R,rope", [(1, False), (4, True)])
+def test_split_resume(ops, R, rope):
+    s = Shape(2, 300, 3, 64, 64, R, "bf16", rope)
+    d = make_inputs(s, 31 + R, h0=True, carry=True)
+    dd = to_device(d, s)
+    whole = _run_prefill(ops, dd, s, carry=True)
+    ref = oracle_prefill(d)
+    for k in (1, 64, 97):
+        _say("split-resume", R, rope, k)
+        first = {n: (None if dd[n] is None else dd[n][:, :k].contiguous()) for n in ("x", "B", "C", "dt", "lam", "theta")}
+        second = {n: (None if dd[n] is None else dd[n][:, k:].contiguous()) for n in ("x", "B", "C", "dt", "lam", "theta")}
+        a = ops.m3_ssm_prefill(first["x"], first["B"], first["C"], first["dt"], first["lam"], dd["A"], first["theta"],
+                               dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"], want_carry=True)
+        b = ops.m3_ssm_prefill(second["x"], second["B"], second["C"], second["dt"], second["lam"], dd["A"],
+                               second["theta"], a["h"], a["Bprev_rot"], a["xprev"], a["phi"], want_carry=True)
+        torch.cuda.synchronize()
+        y = np.concatenate([host(a["y"]), host(b["y"])], axis=1)
+        assert orc.rel_l2(y, ref["y"]) <= TOL["bf16"]
+        assert orc.rel_l2(host(b["h"]), ref["h"]) <= TOL["bf16"]
+        assert orc.rel_l2(y, host(whole["y"])) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------- decode
+def _decode_chain(ops, dd_state, steps, dec, R, dtype, rope):
+    ys = []
+    for t in range(steps):
+        y = ops.m3_ssm_decode_step(dd_state["h"], dd_state["phi"], dd_state["Bprev_rot"], dd_state["xprev"],
+                                   dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t], dec["A"],
+                                   dec["theta"][t] if rope else None)
+        ys.append(host(y))
+    torch.cuda.synchronize()
+    return np.stack(ys, axis=1)
+
+
+@pytest.mark.parametrize("case", [(3, 2, 64, 64, 4, "bf16", True, 40), (2, 3, 32, 16, 1, "f32", False, 25),
+                                  (2, 2, 128, 128, 16, "bf16", True, 6), (1, 2, 16, 32, 3, "f32", True, 10)])
+def test_decode_chain(ops, case):
+    Bt, H, P, N, R, dt_, rope, steps = case
+    _say("decode chain", case)
+    s = Shape(Bt, steps, H, P, N, R, dt_, rope)
+    d = make_inputs(s, 500 + steps, h0=True)
+    st = storage_dtype(s)
+    dec = {k: (None if d[k] is None else dev(np.moveaxis(d[k], 1, 0), st if k in ("x", "B", "C") else torch.float32))
+           for k in ("x", "B", "C", "dt", "lam", "theta")}
+    dec["A"] = dev(d["A"])
+    state = dict(h=dev(d["h0"]), phi=dev(np.zeros((Bt, H, N // 2))) if rope else None,
+                 Bprev_rot=dev(np.zeros((Bt, H, R, N))), xprev=dev(np.zeros((Bt, H, R, P)), st))
+    y = _decode_chain(ops, state, steps, dec, R, dt_, rope)
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"], d["h0"])
+    ey, eh = orc.rel_l2(y, ref["y"]), orc.rel_l2(host(state["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL[dt_] and eh <= TOL[dt_]
+    assert orc.rel_l2(host(state["Bprev_rot"]), ref["Bprev_rot"]) <= 1e-5
+    if rope:
+        assert np.max(angle_diff(host(state["phi"]), ref["phi"])) <= 1e-4
+
+
+def test_decode_config_full_size(ops):
+    """Decode workload at full size (B=256, H=32, N=P=64, R=4) for a few steps,
+    checked against the oracle on every (batch, head)."""
+    s = CONFIGS[4]
+    steps = 3
+    _say("decode config 4, steps", steps)
+    dd = make_decode_inputs(s, steps, SEED_BASE + 4)
+    st = storage_dtype(s)
+    dec = {k: dev(dd[k], st if k in ("x", "B", "C") else torch.float32) for k in ("x", "B", "C", "dt", "lam", "theta")}
+    dec["A"] = dev(dd["A"])
+    state = dict(h=dev(dd["h0"]), phi=dev(np.zeros((s.Bt, s.H, s.N // 2))),
+                 Bprev_rot=dev(np.zeros((s.Bt, s.H, s.R, s.N))), xprev=dev(np.zeros((s.Bt, s.H, s.R, s.P)), st))
+    y = _decode_chain(ops, state, steps, dec, s.R, s.dtype, True)
+    ref = dict(h=dd["h0"], Bprev_rot=np.zeros((s.Bt, s.H, s.R, s.N)), xprev=np.zeros((s.Bt, s.H, s.R, s.P)),
+               phi=np.zeros((s.Bt, s.H, s.N // 2)))
+    ys = []
+    for t in range(steps):
+        ref = orc.decode_reference(ref["h"], ref["Bprev_rot"], ref["xprev"], ref["phi"], dd["x"][t], dd["B"][t],
+                                   dd["C"][t], dd["dt"][t], dd["lam"][t], dd["A"], dd["theta"][t])
+        ys.append(ref["y"])
+    ey = orc.rel_l2(y, np.stack(ys, axis=1))
+    eh = orc.rel_l2(host(state["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+def test_prefill_then_decode(ops):
+    """Prefill tokens [0, k) then decode [k, L) equals the oracle on [0, L)."""
+    Bt, L, H, P, N, R, k = 2, 90, 2, 64, 64, 4, 70
+    s = Shape(Bt, L, H, P, N, R, "bf16", True)
+    d = make_inputs(s, 4242, h0=True, carry=True)
+    dd = to_device(d, s)
+    a = ops.m3_ssm_prefill(dd["x"][:, :k].contiguous(), dd["B"][:, :k].contiguous(), dd["C"][:, :k].contiguous(),
+                           dd["dt"][:, :k].contiguous(), dd["lam"][:, :k].contiguous(), dd["A"],
+                           dd["theta"][:, :k].contiguous(), dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"],
+                           want_carry=True)
+    state = dict(h=a["h"], phi=a["phi"], Bprev_rot=a["Bprev_rot"], xprev=a["xprev"])
+    dec = {n: dd[n][:, k:].transpose(0, 1).contiguous() for n in ("x", "B", "C", "dt", "lam", "theta")}
+    dec["A"] = dd["A"]
+    y2 = _decode_chain(ops, state, L - k, dec, R, "bf16", True)
+    ref = oracle_prefill(d)
+    y = np.concatenate([host(a["y"]), y2], axis=1)
+    assert orc.rel_l2(y, ref["y"]) <= TOL["bf16"]
+    assert orc.rel_l2(host(state["h"]), ref["h"]) <= TOL["bf16"]

@@ -307,3 +307,55 @@ def test_oracle_golden_regression():
                             d["h0"], d["Bprev_rot"], d["xprev"], d["phi0"])
     np.testing.assert_allclose(out["y"].ravel()[: len(g["y_head"])], g["y_head"], rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(out["h"].ravel()[: len(g["h_head"])], g["h_head"], rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- chunk algebra
+@pytest.mark.parametrize("R,Q,rope", [(1, 8, False), (2, 4, True), (4, 5, True)])
+def test_chunked_shifted_state_decomposition(R, Q, rope):
+    """The chunked form the GPU kernel evaluates, written out with numpy on the
+    CPU: per chunk, intra-chunk masked product, readout of the carried shifted
+    state H' = h_end + (1 - lambda_{end+1}) Delta_{end+1} u_end, and the
+    inter-chunk update H'_c = exp(Lambda_end) H'_{c-1} + sum_j w_j Btil_j x_j^T.
+    Must equal the sequential loop (pins the chunk decomposition)."""
+    d = _tiny(L=23, R=R, rope=rope, h0=True, carry=True, seed=12)
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"],
+                            d["h0"], d["Bprev_rot"], d["xprev"], d["phi0"])
+    x, B, C, dt, lam, A = (np.float64(d[k]) for k in ("x", "B", "C", "dt", "lam", "A"))
+    Bt, L, H, _, P = x.shape
+    N = B.shape[-1]
+    if rope:
+        phi = orc.rope_angles_cumsum(d["theta"], d["phi0"])
+        Br, Cr = orc.rotate_pairs(B, phi), orc.rotate_pairs(C, phi)
+    else:
+        Br, Cr = B, C
+    y = np.zeros_like(x)
+    hfin = np.zeros((Bt, H, N, P))
+    for b in range(Bt):
+        for hh in range(H):
+            Hs = np.float64(d["h0"][b, hh]) + (1 - lam[b, 0, hh]) * dt[b, 0, hh] * (
+                np.float64(d["Bprev_rot"][b, hh]).T @ np.float64(d["xprev"][b, hh]))
+            for s in range(0, L, Q):
+                e = min(s + Q, L)
+                lg = dt[b, s:e, hh] * A[hh]
+                Lam = np.cumsum(lg)
+                gam = lam[b, s:e, hh] * dt[b, s:e, hh]
+                nd = np.zeros(e - s)
+                nd[:-1] = (1 - lam[b, s + 1:e, hh]) * dt[b, s + 1:e, hh]
+                if e < L:
+                    nd[-1] = (1 - lam[b, e, hh]) * dt[b, e, hh]
+                dl = gam + nd
+                rows = (e - s) * R
+                tok = np.repeat(np.arange(e - s), R)
+                Cm = Cr[b, s:e, hh].reshape(rows, N)
+                Bm = Br[b, s:e, hh].reshape(rows, N)
+                Xm = x[b, s:e, hh].reshape(rows, P)
+                ti, tj = tok[:, None], tok[None, :]
+                M = np.where(tj < ti, np.exp(Lam[ti] - Lam[tj]) * dl[tj], 0.0)
+                M = np.where(tj == ti, gam[ti], M)
+                Y = (M * (Cm @ Bm.T)) @ Xm + np.exp(Lam[tok])[:, None] * (Cm @ Hs)
+                y[b, s:e, hh] = Y.reshape(e - s, R, P)
+                w = np.exp(Lam[-1] - Lam[tok]) * dl[tok]
+                Hs = np.exp(Lam[-1]) * Hs + Bm.T @ (w[:, None] * Xm)
+            hfin[b, hh] = Hs
+    assert orc.rel_l2(y, ref["y"]) <= 1e-12
+    assert orc.rel_l2(hfin, ref["h"]) <= 1e-12
