@@ -288,7 +288,7 @@ def main():
         tr = traffic_for("prefill_siso_real", 1)
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": head["hbm_frac"], "traffic": tr,
-                           "kernel": "m3::prefill_kernel<bf16_t,128,64>",
+                           "kernel": "m3::pc::prefill_pc_kernel<128,64>",
                            "algorithmic_bytes_per_launch": head["bytes"],
                            "mfma_tflops": head["tflops"], "mfma_frac": head["mfma_frac"]}
     elif "decode" in results:
@@ -303,7 +303,7 @@ def main():
         out["decode"] = dres
         out["decode_roofline"] = {"bound": "hbm", "achieved": dres["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": dres["hbm_frac"], "traffic": traffic_for("decode", 1),
-                                  "kernel": "m3::decode_step_kernel<bf16_t,64,64>"}
+                                  "kernel": "m3::decode_step_kernel<bf16_t,64,64,4>"}
     for k in ("siso_rope", "mimo_rope"):
         if k in results:
             out["prefill_" + k] = results[k]

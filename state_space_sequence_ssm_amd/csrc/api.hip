@@ -58,6 +58,14 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   const double elems = double(a->Bt) * a->L * a->H * a->R * (a->N > a->P ? a->N : a->P);
   if (elems > 4.0e18 || double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
   const bool bf16 = a->in_dtype == M3_BF16;
+  if (bf16) {
+    // the bf16 kernel is compiled for R <= 8 and addresses one batch item with
+    // 32-bit buffer offsets
+    if (a->R > 8) return M3_ERR_UNSUPPORTED;
+    const double item = double(a->L) * a->H * a->R * (a->N > a->P ? a->N : a->P) * 2.0;
+    const double itemTh = double(a->L) * a->H * (a->N / 2) * 4.0;
+    if (item > 2147483000.0 || itemTh > 2147483000.0) return M3_ERR_UNSUPPORTED;
+  }
   const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, a->theta != nullptr)
                           : m3::prefill_lds_bytes_f32(a->N, a->P, a->theta != nullptr);
   if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;

@@ -18,10 +18,12 @@
 namespace m3 {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecMaxR = 16;
 
-template <typename T, int N, int P>
+// RMAX bounds the rank held in registers (R <= RMAX); two variants keep the
+// common small-rank case at low register pressure.
+template <typename T, int N, int P, int RMAX>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p) {
+  constexpr int kDecMaxR = RMAX;
   constexpr int QP = P / 4;                  // float4 quads per state row
   constexpr int NQUAD = N * P / 4;           // quads in the state
   static_assert(kDecThreads % QP == 0, "quad column must be fixed per thread");
@@ -36,6 +38,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
   float* sRed = sXp + R * P;         // per-wave y partials   [4][R][P]
   float* sCS = sRed + 4 * R * P;     // cos/sin of new angle  [N]
   float* sPhi = sCS + N;             // new angle (wrapped)   [N/2]
+  float* sBr = sPhi + N / 2;         // raw B_t               [R][N]
+  float* sCr = sBr + R * N;          // raw C_t               [R][N]
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -48,6 +52,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
   T* xprev = static_cast<T*>(p.xprev) + vecP;
   float* Bprev = p.Bprev_rot + vecN;
   float* h = p.h + static_cast<size_t>(bh) * N * P;
+
+  // issue the state loads first so their latency overlaps the staging below
+  constexpr int kIters = (NQUAD + kDecThreads - 1) / kDecThreads;
+  f32x4 hv[kIters];
+#pragma unroll
+  for (int k = 0; k < kIters; ++k) {
+    const int q = tid + k * kDecThreads;
+    if (q < NQUAD) hv[k] = *reinterpret_cast<const f32x4*>(h + 4 * q);
+  }
 
   const float dt = p.dt[bh];
   const float lm = p.lam[bh];
@@ -72,14 +85,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
     sX[e] = load_scalar(x + e);
     sXp[e] = load_scalar(xprev + e);
   }
-  for (int e = tid; e < R * N; e += kDecThreads) sBp[e] = beta * Bprev[e];
+  for (int e = tid; e < R * N; e += kDecThreads) {
+    sBp[e] = beta * Bprev[e];
+    sBr[e] = load_scalar(Bin + e);
+    sCr[e] = load_scalar(Cin + e);
+  }
   __syncthreads();
   // rotate B_t, C_t pairwise; write carry-out Btil_t, x_t, Phi
   for (int e = tid; e < R * (N / 2); e += kDecThreads) {
     const int r = e / (N / 2);
     const int j = e % (N / 2);
-    float b0 = load_scalar(Bin + r * N + 2 * j), b1 = load_scalar(Bin + r * N + 2 * j + 1);
-    float c0 = load_scalar(Cin + r * N + 2 * j), c1 = load_scalar(Cin + r * N + 2 * j + 1);
+    float b0 = sBr[r * N + 2 * j], b1 = sBr[r * N + 2 * j + 1];
+    float c0 = sCr[r * N + 2 * j], c1 = sCr[r * N + 2 * j + 1];
     if (p.theta != nullptr) {
       const float c = sCS[2 * j], s = sCS[2 * j + 1];
       const float rb0 = c * b0 + s * b1, rb1 = -s * b0 + c * b1;
@@ -109,13 +126,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
 #pragma unroll
     for (int i = 0; i < 4; ++i) yacc[r][i] = 0.f;
 
-  constexpr int kIters = (NQUAD + kDecThreads - 1) / kDecThreads;
-  f32x4 hv[kIters];
-#pragma unroll
-  for (int k = 0; k < kIters; ++k) {
-    const int q = tid + k * kDecThreads;
-    if (q < NQUAD) hv[k] = *reinterpret_cast<const f32x4*>(h + 4 * q);
-  }
 #pragma unroll
   for (int k = 0; k < kIters; ++k) {
     const int q = tid + k * kDecThreads;
@@ -164,8 +174,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
 
 template <typename T, int N, int P>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  const size_t lds = sizeof(float) * (3 * p.R * N + 6 * p.R * P + N + N / 2);
-  hipLaunchKernelGGL((decode_step_kernel<T, N, P>), dim3(p.Bt * p.H), dim3(kDecThreads), lds, s, p);
+  const size_t lds = sizeof(float) * (5 * p.R * N + 6 * p.R * P + N + N / 2);
+  if (p.R <= 4)
+    hipLaunchKernelGGL((decode_step_kernel<T, N, P, 4>), dim3(p.Bt * p.H), dim3(kDecThreads), lds, s, p);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<T, N, P, 16>), dim3(p.Bt * p.H), dim3(kDecThreads), lds, s, p);
   return hipGetLastError();
 }
 

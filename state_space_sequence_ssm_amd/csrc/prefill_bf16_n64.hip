@@ -1,0 +1,6 @@
+// bf16 prefill instantiations for N = 64 (prefill_pc_impl.hpp).
+#include "prefill_pc_launch.hpp"
+
+namespace m3 {
+hipError_t launch_prefill_bf16_n64(const PrefillParams& p, hipStream_t s) { return pc::launch_n<64>(p, s); }
+}  // namespace m3

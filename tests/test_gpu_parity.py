@@ -62,7 +62,9 @@ SMALL = [
     (1, 45, 2, 16, 32, 8, "bf16", True, True),
     (1, 1, 2, 64, 64, 4, "bf16", True, True),
     (1, 63, 2, 128, 64, 1, "bf16", False, True),
-    (1, 65, 1, 128, 128, 1, "bf16", True, False),
+    (1, 65, 1, 64, 128, 1, "bf16", True, False),
+    (1, 40, 2, 128, 128, 1, "bf16", False, True),
+    (1, 70, 1, 128, 32, 2, "bf16", True, True),
     (1, 33, 2, 16, 16, 1, "bf16", True, True),
 ]
 
