@@ -1,5 +1,4 @@
-// Producer/consumer fused chunked prefill of the Mamba-3 SSM core, bf16 inputs
-// (gfx950, CDNA4).
+// Fused chunked prefill of the Mamba-3 SSM core, bf16 inputs (gfx950, CDNA4).
 //
 // Operation: the exponential-trapezoidal recurrence ("Znakomstvo s Mamba-3"
 // (chernovdev.ru), sec. 1, displayed recurrence) with cumulative RoPE on B and
@@ -15,40 +14,41 @@
 //   H'_new = exp(Lam_e) H'_prev + sum_j exp(Lam_e - Lam_j) delta_j Btil_j x_j^T,
 //   H'_{-1} = h0 + (1 - lambda_0) Delta_0 Btil_{-1} x_{-1}^T, h_final = H' at the end.
 //
-// MI355X design.  Written naively the kernel is issue-bound on the vector ALU
-// long before HBM (a wave64 VALU op occupies a SIMD16 for four cycles), so the
-// per-chunk VALU work is kept to a few hundred instructions per SIMD:
-//   * rank R (hence chunk length Q = 64/R) is a template parameter: token
-//     indices are shifts by constants and scans are DPP row operations;
-//   * loads and stores use buffer resources spanning one batch item, so the
-//     ragged tail and padded columns read as zero and stores past the end are
-//     dropped by the hardware range check (no per-element branches);
-//   * decays are exp2 of log2-scaled cumulative sums (one v_exp per element);
-//     rotations use the hardware sin/cos on angles kept within [-pi, pi] plus
-//     one chunk of growth;
-//   * off-diagonal mask tiles need no token comparisons.
-// One 512-thread workgroup owns one (batch, head).  Waves 0-3 are consumers,
-// waves 4-7 producers; one workgroup barrier per chunk hands a double-buffered
-// LDS operand slot from producers to consumers:
-//   iteration k: consumers compute chunk k from slot k%2; producers build slot
-//   (k+1)%2 from registers holding chunk k+1, issue the loads of chunk k+3 (two
-//   register sets in flight; one set, i.e. chunk k+2, at N = 128), and scan the
-//   decay scalars and angles of chunk k+2.
-// Producer wave w owns rows 16w..16w+15 of every chunk.  It loads them as
-// 16-byte pieces in the bf16 MFMA A-operand layout, rotates B and C pairwise in
-// fp32, stores them row-major for the consumers, and transposes B (scaled by
-// w_j = exp(Lam_e - Lam_j) delta_j) and X with MFMA products against an identity
-// operand: the 16x16 fp32 result of A x I holds per lane four consecutive rows
-// of one column, the k-contiguous operand the token contractions need.  These
-// pieces go to LDS in lane-linear order (no bank-conflicted transposes).
-// Consumer wave c owns p tiles c, c+4, ...: H' (N x 16 per p tile) lives in its
-// MFMA accumulators; it computes G^T = B C^T on its causal tiles, masks it in
-// registers and feeds it straight into Y^T += X^T S^T, reads the previous state
-// out of its own accumulators (Y^T += diag(exp Lam) H'^T C^T), stores y and
-// updates H'.  MFMA k index: a k-block of 32 holds, for lane group g, indices
-// {4g..4g+3} and {16+4g..16+4g+3}, matching the accumulator rows of two
-// adjacent 16-row tiles, so accumulators feed the next product unchanged.
+// MI355X design.  One 512-thread workgroup (8 wave64, two per SIMD) owns one
+// (batch, head) and walks its chunks of 64 (token, rank) rows with the N x P
+// state in MFMA accumulators.  Every wave has two jobs per chunk, and one
+// workgroup barrier per chunk hands a double-buffered LDS operand slot over:
+//   * staging (for chunk k+1 into slot (k+1)%2): wave w owns rows 16(w&3)..+15
+//     and half of their 16-byte pieces.  Its loads were issued two chunks ahead
+//     into registers, using buffer resources that span one batch item (the
+//     hardware range check zero-fills the ragged tail, so every wave issues the
+//     same loads every chunk and the wait counters stay exact).  B and C are
+//     rotated pairwise in fp32 (hardware sin/cos of the cumulative angle),
+//     rounded to bf16 and stored row-major; B (scaled by w_j = exp(Lam_e -
+//     Lam_j) delta_j) and X are transposed by MFMA products against an identity
+//     operand: the 16x16 fp32 result of A x I holds per lane four consecutive
+//     rows of one column, exactly the k-contiguous operand the token
+//     contractions need, and it is stored to LDS in lane-linear order (no
+//     bank-conflicted transposes).  The decay scan (log2 units, one wave64 DPP
+//     scan) and the angle scan (DPP segments of Q lanes, carry across chunks)
+//     of chunk k+2 run here too.
+//   * compute (chunk k from slot k%2): wave w owns p tiles (w&3) + 4u and the i
+//     tiles {0,3} (w < 4) or {1,2} (five Gram tiles each).  It computes
+//     G^T = B C^T on its causal tiles, masks it in registers (one exp2 per
+//     element, no comparisons off the diagonal) and feeds it straight into
+//     Y^T += X^T S^T, reads the previous state out of its own accumulators
+//     (Y^T += diag(exp Lam) H'^T C^T), stores y and updates
+//     H' = exp(Lam_e) H' + (w B)^T X (both waves of a p tile keep the state).
+// MFMA k index: a k-block of 32 holds, for lane group g, indices {4g..4g+3} and
+// {16+4g..16+4g+3}, matching the accumulator rows of two adjacent 16-row tiles,
+// so accumulators feed the next product without a trip through LDS.
+// Rank R (chunk length Q = 64/R) and RoPE are template parameters: token
+// indices are constant shifts, scans are DPP row operations and every tile is
+// straight-line code, which keeps the vector-ALU work per chunk small (a wave64
+// VALU op occupies a SIMD16 for four cycles).
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "m3ssm_internal.hpp"
 
@@ -57,8 +57,8 @@ namespace pc {
 
 constexpr int kRows = 64;
 constexpr int kThreads = 512;
-constexpr int kConsumers = 4;
-constexpr int kProducers = 4;
+constexpr int kWaves = kThreads / 64;
+constexpr int kPGroups = 4;  // p tiles are dealt round-robin over wave & 3
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr uint32_t kBad = 0x7FFFFFF0u;  // buffer offset past any valid range -> reads 0
 
@@ -110,6 +110,12 @@ __device__ __forceinline__ float seg_scan(float v) {
   return v;
 }
 
+// 16-byte pieces of one 16-row tile: B and C k-blocks of 32 columns (kind 0, 1)
+// and X k-blocks (kind 2), split between the two waves that share the rows.
+struct Piece {
+  int kind, kb;
+};
+
 template <int N, int P>
 struct PcLayout {
   static constexpr int NK = N < 32 ? 32 : N;  // n contraction length (zero padded)
@@ -117,11 +123,36 @@ struct PcLayout {
   static constexpr int NTH = N / 16;          // state n tiles
   static constexpr int NPT = P / 16;          // p tiles
   static constexpr int PKB = (P + 31) / 32;   // k blocks over p (X pieces)
-  static constexpr int UPT = (NPT + kConsumers - 1) / kConsumers;  // p tiles per consumer
-  static constexpr int UPW = 2 * NKB + PKB;   // producer pieces per chunk and wave
+  static constexpr int UPT = (NPT + kPGroups - 1) / kPGroups;  // p tiles per wave
   static constexpr int PN = NK + 8;           // bf16 pitch of B/C rows (16-byte pad)
   static constexpr int NG = N / 8;            // float4 groups of angles per token
-  static constexpr int TSL = (NG + 3) / 4;    // angle groups per producer lane (at Q = 64)
+  static constexpr int TSL = (NG + kWaves - 1) / kWaves;  // angle groups per lane (Q = 64)
+  static constexpr int PH = N / 2 + 4;        // padded angle-table row (spreads banks)
+  // piece ownership: B/C k-block kb -> half (2 kb / NKB); X k-block -> alternate
+  static constexpr int bc_half(int kb) { return NKB == 1 ? 0 : (2 * kb) / NKB; }
+  static constexpr int x_half(int kb) { return PKB == 1 ? (NKB == 1 ? 1 : 0) : (kb & 1); }
+  static constexpr int count(int h) {
+    int n = 0;
+    for (int kb = 0; kb < NKB; ++kb) n += bc_half(kb) == h ? 2 : 0;
+    for (int kb = 0; kb < PKB; ++kb) n += x_half(kb) == h ? 1 : 0;
+    return n;
+  }
+  static constexpr int UPH = count(0) > count(1) ? count(0) : count(1);  // pieces per wave
+  static constexpr Piece piece(int h, int s) {
+    int n = 0;
+    for (int kb = 0; kb < NKB; ++kb)
+      if (bc_half(kb) == h) {
+        if (n == s) return Piece{0, kb};
+        if (n + 1 == s) return Piece{1, kb};
+        n += 2;
+      }
+    for (int kb = 0; kb < PKB; ++kb)
+      if (x_half(kb) == h) {
+        if (n == s) return Piece{2, kb};
+        n += 1;
+      }
+    return Piece{-1, 0};
+  }
   // LDS (bytes)
   static constexpr size_t kSlotC = size_t(kRows) * PN * 2;
   static constexpr size_t kSlotBwT = size_t(NTH) * 4 * 64 * 8;  // [nt][m][half][lane] x 8 B
@@ -133,10 +164,11 @@ struct PcLayout {
   static constexpr size_t kSlot = oXT + kSlotXT;
   static constexpr size_t oSC = 2 * kSlot;                // [3][6][64] fp32 scalars
   static constexpr size_t kSC = 6 * 64 * 4;
-  static constexpr size_t oPhiC = oSC + 3 * kSC;          // [N/2] fp32 angle carry
-  static constexpr size_t oPhi = oPhiC + (N / 2) * 4;     // [2][64][N/2] fp32 angles
+  static constexpr size_t oS = oSC + 3 * kSC;             // [10][64] x 8 B masked S^T pieces
+  static constexpr size_t oPhiC = oS + 10 * 64 * 8;       // [N/2] fp32 angle carry
+  static constexpr size_t oPhi = oPhiC + (N / 2) * 4;     // [2][64][PH] fp32 angles
   static constexpr size_t kBytesReal = oPhi;
-  static constexpr size_t kBytesRope = oPhi + 2 * size_t(kRows) * (N / 2) * 4;
+  static constexpr size_t kBytesRope = oPhi + 2 * size_t(kRows) * PH * 4;
 };
 
 template <int N, int P, int LGR, bool ROPE>
@@ -144,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   using Lt = PcLayout<N, P>;
   constexpr int R = 1 << LGR;
   constexpr int Q = kRows >> LGR;  // tokens per chunk
-  constexpr int NKB = Lt::NKB, NTH = Lt::NTH, NPT = Lt::NPT, PKB = Lt::PKB, UPT = Lt::UPT;
-  constexpr int UPW = Lt::UPW, PN = Lt::PN, NG = Lt::NG, TSL = Lt::TSL;
+  constexpr int NKB = Lt::NKB, NTH = Lt::NTH, NPT = Lt::NPT, UPT = Lt::UPT;
+  constexpr int UPH = Lt::UPH, PN = Lt::PN, NG = Lt::NG, TSL = Lt::TSL, PH = Lt::PH;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -153,15 +185,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g = lane >> 4;
+  const int quad = wave & 3;             // row tile (staging) and p-tile group (compute)
+  const bool upper = (wave >> 2) & 1;    // piece half (staging) and i-tile pair (compute)
   const int bh = blockIdx.x;
   const int b = bh / p.H;
   const int hh = bh % p.H;
   const int L = p.L, H = p.H;
-  constexpr bool rope = ROPE;  // theta != nullptr
   const float A2 = p.A[hh] * kLog2e;  // decays in log2 units
   const int nch = (L + Q - 1) / Q;
-  const bool consumer = wave < kConsumers;
-  const int pw = wave - kConsumers;
 
   // per-batch-item buffer resources (the range check zero-fills t >= L)
   const size_t tokB = static_cast<size_t>(L) * H;  // (t, h) pairs per batch item
@@ -171,21 +202,19 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const rsrc_t rY = make_rsrc(static_cast<bf16_t*>(p.y) + b * tokB * R * P, uint32_t(tokB * R * P * 2));
   const rsrc_t rDt = make_rsrc(p.dt + b * tokB, uint32_t(tokB * 4));
   const rsrc_t rLam = make_rsrc(p.lam + b * tokB, uint32_t(tokB * 4));
-  const rsrc_t rTh = make_rsrc(rope ? p.theta + b * tokB * (N / 2) : p.dt, uint32_t(rope ? tokB * (N / 2) * 4 : 0));
+  const rsrc_t rTh = make_rsrc(ROPE ? p.theta + b * tokB * (N / 2) : p.dt, uint32_t(ROPE ? tokB * (N / 2) * 4 : 0));
 
-  auto slotC = [&](int s) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oC); };
-  auto slotB = [&](int s) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oB); };
-  auto slotBwT = [&](int s) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oBwT); };
-  auto slotXT = [&](int s) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oXT); };
-  auto sc = [&](int s) { return reinterpret_cast<float*>(smem + Lt::oSC + s * Lt::kSC); };
+  auto slotC = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oC); };
+  auto slotB = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oB); };
+  auto slotBwT = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oBwT); };
+  auto slotXT = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oXT); };
+  auto sc = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oSC + s * Lt::kSC); };
   float* phiC = reinterpret_cast<float*>(smem + Lt::oPhiC);
-  auto phiTab = [&](int s) { return reinterpret_cast<float*>(smem + Lt::oPhi) + s * kRows * (N / 2); };
+  auto phiTab = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oPhi) + s * kRows * PH; };
 
-  // ================================================================ producer
-  // Register sets of in-flight B/C/X loads (chunk c lives in set c % NSET): two
-  // when they fit next to the consumer's state, else one.
-  constexpr int NSET = UPW <= 6 ? 2 : 1;
-  u32x4 raw[NSET][UPW];
+  // ================================================================ staging state
+  // chunk c's pieces live in register set c % 2 (two chunks in flight)
+  u32x4 raw[2][UPH];
   f32x4 rawTh[2][ROPE ? TSL : 1];
   float rdt[2], rlam[2], rdtn[2], rlamn[2];
   bf16x8 Ilo, Ihi;  // identity selectors: column c <- k slot (g, e) with 8g + e == c (+16)
@@ -200,46 +229,44 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     Ilo = as_bf16x8(lo);
     Ihi = as_bf16x8(hi);
   }
-  // producer row of the chunk and its (token offset, rank)
-  const int prow = 16 * pw + l16;
+  const int prow = 16 * quad + l16;  // staging row of the chunk
   const int ptok = prow >> LGR;
   const int prank = prow & (R - 1);
 
-  // pieces: u < NKB -> B k-block u, u < 2 NKB -> C k-block u - NKB, else X k-block
-  auto issue_bcx = [&](int c, u32x4 (&dst)[UPW]) {
+  // Every wave issues the same loads every chunk (chunks past the end read
+  // zeros): with no load behind a branch the wait counters stay exact.
+  auto issue_bcx = [&](int c, u32x4 (&dst)[UPH], auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
     const uint32_t row = static_cast<uint32_t>(((c * Q + ptok) * H + hh) * R + prank);
 #pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-      const bool isX = u >= 2 * NKB;
-      const int kb = isX ? u - 2 * NKB : (u % NKB);
-      const int D = isX ? P : N;
-      const int col = 32 * kb + 8 * g;
-      const uint32_t off = col < D ? (row * D + col) * 2u : kBad;
-      dst[u] = bload16(isX ? rX : (u < NKB ? rB : rC), off);
+    for (int s = 0; s < UPH; ++s) {
+      const Piece pc = Lt::piece(h, s);
+      const int D = pc.kind == 2 ? P : N;
+      const int col = 32 * pc.kb + 8 * g;
+      const uint32_t off = (pc.kind >= 0 && col < D) ? (row * D + col) * 2u : kBad;
+      dst[s] = bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
     }
   };
-  auto issue_small = [&](int c, int set) {
-    if (pw == 0) {
-      const uint32_t off = lane < Q ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
-      rdt[set] = bloadf(rDt, off);
-      rlam[set] = bloadf(rLam, off);
-      const uint32_t offn = lane < Q ? off + H * 4u : kBad;
-      rdtn[set] = bloadf(rDt, offn);
-      rlamn[set] = bloadf(rLam, offn);
-    }
+  auto issue_small = [&](int c, int set) __attribute__((always_inline)) {
+    const uint32_t off = lane < Q ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
+    rdt[set] = bloadf(rDt, off);
+    rlam[set] = bloadf(rLam, off);
+    const uint32_t offn = lane < Q ? off + H * 4u : kBad;
+    rdtn[set] = bloadf(rDt, offn);
+    rlamn[set] = bloadf(rLam, offn);
     if constexpr (ROPE) {
       const int tl = lane % Q, pg = lane / Q;
 #pragma unroll
       for (int s = 0; s < TSL; ++s) {
-        const int q4 = (s * kProducers + pw) * R + pg;
-        const uint32_t off = q4 < NG ? (static_cast<uint32_t>((c * Q + tl) * H + hh) * (N / 2) + 4 * q4) * 4u : kBad;
-        rawTh[set][s] = bloadf4(rTh, off);
+        const int q4 = (s * kWaves + wave) * R + pg;
+        const uint32_t off4 = q4 < NG ? (static_cast<uint32_t>((c * Q + tl) * H + hh) * (N / 2) + 4 * q4) * 4u : kBad;
+        rawTh[set][s] = bloadf4(rTh, off4);
       }
     }
   };
   // decay scalars (log2 units) and cumulative angles of chunk c -> SC[c%3], Phi[c%2]
-  auto stage_small = [&](int c, int set) {
-    if (pw == 0) {
+  auto stage_small = [&](int c, int set) __attribute__((always_inline)) {
+    if (wave == 0) {
       float* S = sc(c % 3);
       const float lamc = seg_scan<64>(rdt[set] * A2);
       const float lamEnd = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lamc), Q - 1));
@@ -257,15 +284,15 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       float* tab = phiTab(c & 1);
 #pragma unroll
       for (int s = 0; s < TSL; ++s) {
-        const int q4 = (s * kProducers + pw) * R + pg;  // uniform within a Q-lane segment
-        if ((s * kProducers + pw) * R < NG) {
+        const int q4 = (s * kWaves + wave) * R + pg;  // uniform within a Q-lane segment
+        if ((s * kWaves + wave) * R < NG) {
           f32x4 v = rawTh[set][s];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = seg_scan<Q>(v[e]);
           if (q4 < NG) {
             const f32x4 cin = *reinterpret_cast<const f32x4*>(phiC + 4 * q4);
             const f32x4 a = v + cin;
-            *reinterpret_cast<f32x4*>(tab + tl * (N / 2) + 4 * q4) = a;
+            *reinterpret_cast<f32x4*>(tab + tl * PH + 4 * q4) = a;
             if (tl == Q - 1) {
               f32x4 w;
 #pragma unroll
@@ -277,105 +304,129 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     }
   };
-  // build operand slot c%2 from one register set
-  auto build_slot = [&](int c, const u32x4 (&src)[UPW]) {
-    const int s = c & 1;
-    const bool lastTok = (c * Q + ptok == L - 1);
+  // stage this wave's pieces of chunk c into operand slot c%2
+  auto build_slot = [&](int c, const u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    const int s2 = c & 1;
     const float* S = sc(c % 3);
-    f32x4 wj;  // w of the four rows (16pw + 4g + jj) this lane holds after a transpose
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) wj[jj] = S[3 * 64 + ((16 * pw + 4 * g + jj) >> LGR)];
-    uint16_t* sB = slotB(s);
-    uint16_t* sC = slotC(s);
-    u32x2* bwt = slotBwT(s);
-    u32x2* xt = slotXT(s);
+    uint16_t* sB = slotB(s2);
+    uint16_t* sC = slotC(s2);
+    u32x2* bwt = slotBwT(s2);
+    u32x2* xt = slotXT(s2);
     const float* tab = phiTab(c & 1);
-    const int m = pw >> 1, half = pw & 1;
+    const int m = quad >> 1, half = quad & 1;  // j tile `quad` -> k-block m, half of it
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < UPH; ++s) {
+      const Piece pc = Lt::piece(h, s);
+      if (pc.kind < 0) continue;
+      const u32x4 v = src[s];
+      const int col = 32 * pc.kb + 8 * g;
+      if (pc.kind == 2) {
+        const bf16x8 a = as_bf16x8(v);
+        if (2 * pc.kb < NPT) xt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
+        if (2 * pc.kb + 1 < NPT) xt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
+        continue;
+      }
+      u32x4 o = v;
+      if constexpr (ROPE) {
+        if (pc.kind == 0) {  // B comes first for a k-block; C reuses its sin/cos
+          const int q = (N >= 32 || 16 * pc.kb + 4 * g < N / 2) ? 16 * pc.kb + 4 * g : 0;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(tab + ptok * PH + q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sn[e] = __sinf(a[e]);
+            cs[e] = __cosf(a[e]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a0 = __uint_as_float(v[q] << 16), a1 = __uint_as_float(v[q] & 0xffff0000u);
+          o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
+        }
+      }
+      *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + prow * PN + col) = o;
+      if (pc.kind == 0) {
+        f32x4 wj;  // w of the rows 16 quad + 4g + jj this lane holds after the transpose
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) wj[jj] = S[3 * 64 + ((16 * quad + 4 * g + jj) >> LGR)];
+        const bf16x8 a = as_bf16x8(o);
+        if (2 * pc.kb < NTH) bwt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
+        if (2 * pc.kb + 1 < NTH) bwt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
+      }
+    }
+  };
+  // ================================================================ compute state
+  f32x4 acc[UPT][NTH];
+  constexpr bool kAllPt = NPT % kPGroups == 0;  // every wave owns UPT real p tiles
+  u32x2* sS = reinterpret_cast<u32x2*>(smem + Lt::oS);
+  // causal (j tile, i tile) pairs, numbered (0,0) (0,1) (1,1) (0,2) (1,2) (2,2)
+  // (0,3) (1,3) (2,3) (3,3); tile t is computed once, by wave t % 8
+  auto tile_id = [](int jt, int it) { return it * (it + 1) / 2 + jt; };
+  // phase A: masked Gram tile S^T(jt, it) = M o (B C^T)^T of chunk k -> LDS
+  auto gram_tile = [&](int k, auto JT, auto IT) __attribute__((always_inline)) {
+    constexpr int jt = decltype(JT)::value, it = decltype(IT)::value;
+    const int s2 = k & 1;
+    const float* S = sc(k % 3);
+    const uint16_t* sB = slotB(s2);
+    const uint16_t* sC = slotC(s2);
+    const int iRow = 16 * it + l16;
+    const int ti = iRow >> LGR;
+    const float lamI = S[ti], gamI = S[64 + ti];
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int col = 32 * kb + 8 * g;
-      float cs[4], sn[4];
-      if constexpr (ROPE) {
-        const int q = (N >= 32 || 16 * kb + 4 * g < N / 2) ? 16 * kb + 4 * g : 0;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(tab + ptok * (N / 2) + q);
+      const uint16_t* rb = sB + (16 * jt + l16) * PN + 32 * kb + 4 * g;
+      const uint16_t* rc = sC + iRow * PN + 32 * kb + 4 * g;
+      a = mma(cat8(*reinterpret_cast<const u32x2*>(rb), *reinterpret_cast<const u32x2*>(rb + 16)),
+              cat8(*reinterpret_cast<const u32x2*>(rc), *reinterpret_cast<const u32x2*>(rc + 16)), a);
+    }
+    // scalars are read and the decay evaluated on every lane, then selected:
+    // keeps the tile free of divergent control flow
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sn[e] = __sinf(a[e]);
-          cs[e] = __cosf(a[e]);
-        }
-      }
-#pragma unroll
-      for (int which = 0; which < 2; ++which) {  // 0: B, 1: C
-        const u32x4 v = src[which * NKB + kb];
-        u32x4 o = v;
-        float f[8];
-        if (ROPE || (which == 0 && lastTok)) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f[2 * q] = __uint_as_float(v[q] << 16);
-            f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
-          }
-          if constexpr (ROPE) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float a0 = f[2 * q], a1 = f[2 * q + 1];
-              f[2 * q] = cs[q] * a0 + sn[q] * a1;
-              f[2 * q + 1] = cs[q] * a1 - sn[q] * a0;
-              o[q] = pack_bf16x2(f[2 * q], f[2 * q + 1]);
-            }
-          }
-        }
-        *reinterpret_cast<u32x4*>((which ? sC : sB) + prow * PN + col) = o;
-        if (which == 0) {
-          if (lastTok && p.Bprev_rot_out != nullptr && col < N) {
-            float* dst = p.Bprev_rot_out + (static_cast<size_t>(bh) * R + prank) * N + col;
-            store4<float>(dst, f[0], f[1], f[2], f[3]);
-            store4<float>(dst + 4, f[4], f[5], f[6], f[7]);
-          }
-          const bf16x8 a = as_bf16x8(o);
-          if (2 * kb < NTH) bwt[(((2 * kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
-          if (2 * kb + 1 < NTH) bwt[(((2 * kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
-        }
+    for (int jj = 0; jj < 4; ++jj) {
+      const int tj = (16 * jt + 4 * g + jj) >> LGR;
+      const float mk = __builtin_amdgcn_exp2f(lamI - S[tj]) * S[2 * 64 + tj];
+      if constexpr (jt < it) {  // every token of tile jt precedes every token of tile it
+        a[jj] *= mk;
+      } else {
+        const float sel = tj < ti ? mk : gamI;
+        a[jj] *= tj <= ti ? sel : 0.f;
       }
     }
-#pragma unroll
-    for (int kb = 0; kb < PKB; ++kb) {
-      const u32x4 v = src[2 * NKB + kb];
-      const bf16x8 a = as_bf16x8(v);
-      if (2 * kb < NPT) xt[(((2 * kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
-      if (2 * kb + 1 < NPT) xt[(((2 * kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
-      const int col = 32 * kb + 8 * g;
-      if (lastTok && p.xprev_out != nullptr && col < P)
-        *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(p.xprev_out) + (static_cast<size_t>(bh) * R + prank) * P + col) = v;
+    sS[tile_id(jt, it) * 64 + lane] = pack4(a);
+  };
+  auto gram_tiles = [&](int k) __attribute__((always_inline)) {
+    using std::integral_constant;
+    switch (wave) {
+      case 0: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 0>{});
+              gram_tile(k, integral_constant<int, 2>{}, integral_constant<int, 3>{}); break;
+      case 1: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 1>{});
+              gram_tile(k, integral_constant<int, 3>{}, integral_constant<int, 3>{}); break;
+      case 2: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 1>{}); break;
+      case 3: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 2>{}); break;
+      case 4: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 2>{}); break;
+      case 5: gram_tile(k, integral_constant<int, 2>{}, integral_constant<int, 2>{}); break;
+      case 6: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 3>{}); break;
+      default: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 3>{}); break;
     }
   };
-  // one producer iteration; `bcx` holds chunk k+1 on entry and chunk k+1+NSET on exit
-  auto producer_iter = [&](int k, u32x4 (&bcx)[UPW], int sset) {
-    if (k + 1 < nch) build_slot(k + 1, bcx);
-    if (k + 1 + NSET < nch) issue_bcx(k + 1 + NSET, bcx);
-    if (k + 2 < nch) stage_small(k + 2, sset);
-    if (k + 4 < nch) issue_small(k + 4, sset);
-  };
-
-  // ================================================================ consumer
-  f32x4 acc[UPT][NTH];
-  const int cw = wave;
-  auto consumer_iter = [&](int k) {
-    const int s = k & 1;
+  // phase B: y of this wave's i tiles and p tiles, then the state update
+  auto compute_rest = [&](int k) __attribute__((always_inline)) {
+    const int s2 = k & 1;
     const float* S = sc(k % 3);
-    const uint16_t* sB = slotB(s);
-    const uint16_t* sC = slotC(s);
-    const u32x2* bwt = slotBwT(s);
-    const u32x2* xt = slotXT(s);
+    const uint16_t* sC = slotC(s2);
+    const u32x2* bwt = slotBwT(s2);
+    const u32x2* xt = slotXT(s2);
     const float cdec = S[5 * 64];
     bf16x8 xfr[UPT][2];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int pt = cw + kConsumers * u;
+      const int pt = quad + kPGroups * u;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        if (pt < NPT) xfr[u][m] = cat8(xt[((pt * 2 + m) * 2 + 0) * 64 + lane], xt[((pt * 2 + m) * 2 + 1) * 64 + lane]);
+        if (kAllPt || pt < NPT) xfr[u][m] = cat8(xt[((pt * 2 + m) * 2 + 0) * 64 + lane], xt[((pt * 2 + m) * 2 + 1) * 64 + lane]);
     }
     // H'^T operand pieces straight from the accumulators (state before chunk k)
     bf16x8 hfr[UPT][NKB];
@@ -388,71 +439,53 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         const u32x2 hi = (2 * kb + 1 < NTH) ? pack4(acc[u][2 * kb + 1 < NTH ? 2 * kb + 1 : 0]) : zero2;
         hfr[u][kb] = cat8(lo, hi);
       }
-#pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
+    auto do_it = [&](auto IT) __attribute__((always_inline)) {
+      constexpr int it = decltype(IT)::value;
       const int iRow = 16 * it + l16;
       const int ti = iRow >> LGR;
-      const float lamI = S[ti], gamI = S[64 + ti], decI = S[4 * 64 + ti];
-      bf16x8 cfr[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const uint16_t* rp = sC + iRow * PN + 32 * kb + 4 * g;
-        cfr[kb] = cat8(*reinterpret_cast<const u32x2*>(rp), *reinterpret_cast<const u32x2*>(rp + 16));
-      }
+      const float decI = S[4 * 64 + ti];
       f32x4 yacc[UPT];
 #pragma unroll
       for (int u = 0; u < UPT; ++u) yacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto gram = [&](int jt) -> f32x4 {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const uint16_t* rp = sB + (16 * jt + l16) * PN + 32 * kb + 4 * g;
-          a = mma(cat8(*reinterpret_cast<const u32x2*>(rp), *reinterpret_cast<const u32x2*>(rp + 16)), cfr[kb], a);
-        }
-        if (jt < it) {  // every token of tile jt precedes every token of tile it
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int tj = (16 * jt + 4 * g + jj) >> LGR;
-            a[jj] *= __builtin_amdgcn_exp2f(lamI - S[tj]) * S[2 * 64 + tj];
-          }
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int tj = (16 * jt + 4 * g + jj) >> LGR;
-            const float mk = __builtin_amdgcn_exp2f(lamI - S[tj]) * S[2 * 64 + tj];
-            a[jj] *= tj < ti ? mk : (tj == ti ? gamI : 0.f);
-          }
-        }
-        return a;
-      };
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (2 * m <= it) {
-          const f32x4 g0 = gram(2 * m);
-          const f32x4 g1 = (2 * m + 1 <= it) ? gram(2 * m + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
-          const bf16x8 sop = cat8(pack4(g0), pack4(g1));
+          constexpr u32x2 zero2 = {0u, 0u};
+          const u32x2 lo = sS[tile_id(2 * m, it) * 64 + lane];
+          const u32x2 hi = (2 * m + 1 <= it) ? sS[tile_id(2 * m + 1 <= it ? 2 * m + 1 : 0, it) * 64 + lane] : zero2;
+          const bf16x8 sop = cat8(lo, hi);
 #pragma unroll
           for (int u = 0; u < UPT; ++u)
-            if (cw + kConsumers * u < NPT) yacc[u] = mma(xfr[u][m], sop, yacc[u]);
+            if (kAllPt || quad + kPGroups * u < NPT) yacc[u] = mma(xfr[u][m], sop, yacc[u]);
         }
       }
       const uint32_t yrow = static_cast<uint32_t>(((k * Q + ti) * H + hh) * R + (iRow & (R - 1))) * P;
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
-        const int pt = cw + kConsumers * u;
-        if (pt < NPT) {
+        const int pt = quad + kPGroups * u;
+        if (kAllPt || pt < NPT) {
           f32x4 zz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) zz = mma(hfr[u][kb], cfr[kb], zz);
+          for (int kb = 0; kb < NKB; ++kb) {
+            const uint16_t* rc = sC + iRow * PN + 32 * kb + 4 * g;
+            zz = mma(hfr[u][kb], cat8(*reinterpret_cast<const u32x2*>(rc), *reinterpret_cast<const u32x2*>(rc + 16)), zz);
+          }
           const f32x4 yv = yacc[u] + decI * zz;
           bstore8(rY, (yrow + 16 * pt + 4 * g) * 2u, pack4(yv));  // rows past L are dropped
         }
       }
+    };
+    if (!upper) {
+      do_it(std::integral_constant<int, 0>{});
+      do_it(std::integral_constant<int, 3>{});
+    } else {
+      do_it(std::integral_constant<int, 1>{});
+      do_it(std::integral_constant<int, 2>{});
     }
     // H' = exp(Lam_e) H' + (w B)^T X
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      if (cw + kConsumers * u < NPT) {
+      if (kAllPt || quad + kPGroups * u < NPT) {
 #pragma unroll
         for (int nt = 0; nt < NTH; ++nt) {
           f32x4 a = acc[u][nt] * cdec;
@@ -467,22 +500,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   };
 
   // ================================================================ prologue
-  if (!consumer) {
-    if constexpr (ROPE)
-      for (int q = lane + 64 * pw; q < N / 2; q += 64 * kProducers)
-        phiC[q] = p.phi0 != nullptr ? p.phi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
-    issue_small(0, 0);
-    if (nch > 1) issue_small(1, 1);
-    issue_bcx(0, raw[0]);
-    if (NSET > 1 && nch > 1) issue_bcx(1, raw[NSET - 1]);
-  } else {
+  {
     // H'_{-1} = h0 + (1 - lambda_0) Delta_0 sum_r Bprev_rot[r] xprev[r]^T
     const size_t o0 = static_cast<size_t>(b) * L * H + hh;
     const float coef = (1.f - p.lam[o0]) * p.dt[o0];
     const bool hasCarry = p.Bprev_rot != nullptr && p.xprev != nullptr;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int pt = cw + kConsumers * u;
+      const int pt = quad + kPGroups * u;
 #pragma unroll
       for (int nt = 0; nt < NTH; ++nt) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -506,53 +531,101 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         acc[u][nt] = a;
       }
     }
+    if constexpr (ROPE)
+      for (int q = tid; q < N / 2; q += kThreads)
+        phiC[q] = p.phi0 != nullptr ? p.phi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
   }
-  __syncthreads();  // angle carry visible
-  if (!consumer) {
+  // retire the prologue's state and carry loads here, so no wait on them is
+  // left for the loop to repeat every chunk
+  __builtin_amdgcn_s_waitcnt(0);
+  auto prologue = [&](auto HALF) __attribute__((always_inline)) {
+    issue_small(0, 0);
+    issue_small(1, 1);
+    issue_bcx(0, raw[0], HALF);
+    issue_bcx(1, raw[1], HALF);
+    __syncthreads();  // angle carry visible
     stage_small(0, 0);
-    if (nch > 2) issue_small(2, 0);
-  }
-  __syncthreads();  // SC(0), Phi(0) visible
-  if (!consumer) {
-    build_slot(0, raw[0]);
-    if (nch > NSET) issue_bcx(NSET, raw[0]);
-    if (nch > 1) stage_small(1, 1);
-    if (nch > 3) issue_small(3, 1);
-  }
-  __syncthreads();  // slot 0, SC(1), Phi(1) visible
-
-  // ================================================================ chunk walk, unrolled by two so the
-  // register sets are indexed statically
-  for (int k = 0; k < nch; k += 2) {
-    if (consumer) consumer_iter(k);
-    else producer_iter(k, raw[1 % NSET], 0);
-    __syncthreads();
-    if (k + 1 < nch) {
-      if (consumer) consumer_iter(k + 1);
-      else producer_iter(k + 1, raw[0], 1);  // (k + 2) % NSET == 0
-      __syncthreads();
+    issue_small(2, 0);
+    __syncthreads();  // SC(0), Phi(0) visible
+    build_slot(0, raw[0], HALF);
+    issue_bcx(2, raw[0], HALF);
+    stage_small(1, 1);
+    issue_small(3, 1);
+    __syncthreads();  // slot 0, SC(1), Phi(1) visible
+  };
+  // chunk walk, unrolled by two so the register sets are indexed statically.
+  // Phase A: stage chunk k+1 (set `bcx` holds it), refill `bcx` with the loads
+  // of chunk k+3, scan decays and angles of chunk k+2, issue the small loads of
+  // chunk k+4, and compute the masked Gram tiles of chunk k; phase B: products,
+  // y and state of chunk k.
+  auto chunk = [&](int k, u32x4 (&bcx)[UPH], int sset, auto HALF) __attribute__((always_inline)) {
+    build_slot(k + 1, bcx, HALF);
+    issue_bcx(k + 3, bcx, HALF);  // registers free again: refill before the y stores queue up
+    stage_small(k + 2, sset);
+    issue_small(k + 4, sset);
+    gram_tiles(k);
+    __syncthreads();  // S pieces visible
+    compute_rest(k);
+    __syncthreads();  // slot k+1, SC(k+2), Phi(k+2) visible; slot k and S free
+  };
+  auto walk = [&](auto HALF) __attribute__((always_inline)) {
+    for (int k = 0; k < nch; k += 2) {
+      chunk(k, raw[1], 0, HALF);
+      if (k + 1 < nch) chunk(k + 1, raw[0], 1, HALF);
     }
+  };
+  if (!upper) {
+    prologue(std::integral_constant<int, 0>{});
+    walk(std::integral_constant<int, 0>{});
+  } else {
+    prologue(std::integral_constant<int, 1>{});
+    walk(std::integral_constant<int, 1>{});
   }
 
   // ================================================================ epilogue
-  if (consumer) {
-    if (p.h_final != nullptr) {
+  if (p.h_final != nullptr && !upper) {  // both waves of a p tile hold the same state
 #pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-        const int pt = cw + kConsumers * u;
-        if (pt < NPT) {
+    for (int u = 0; u < UPT; ++u) {
+      const int pt = quad + kPGroups * u;
+      if (pt < NPT) {
 #pragma unroll
-          for (int nt = 0; nt < NTH; ++nt)
+        for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-              p.h_final[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * nt + 4 * g + jj) * P + 16 * pt + l16] =
-                  acc[u][nt][jj];
-        }
+          for (int jj = 0; jj < 4; ++jj)
+            p.h_final[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * nt + 4 * g + jj) * P + 16 * pt + l16] =
+                acc[u][nt][jj];
       }
     }
-  } else if (ROPE && p.phi_out != nullptr) {
-    for (int q = lane + 64 * pw; q < N / 2; q += 64 * kProducers)
-      p.phi_out[static_cast<size_t>(bh) * (N / 2) + q] = phiC[q];
+  }
+  if constexpr (ROPE) {
+    if (p.phi_out != nullptr)
+      for (int q = tid; q < N / 2; q += kThreads) p.phi_out[static_cast<size_t>(bh) * (N / 2) + q] = phiC[q];
+  }
+  // carry-out of token L-1: rotated B (fp32) and x
+  {
+    const int t = L - 1;
+    if (p.Bprev_rot_out != nullptr) {
+      for (int e = tid; e < R * (N / 2); e += kThreads) {
+        const int r = e / (N / 2), q = e % (N / 2);
+        const bf16_t* src = static_cast<const bf16_t*>(p.B) + ((static_cast<size_t>(b) * L + t) * H + hh) * R * N + r * N;
+        float a0 = bf16_to_f32(src[2 * q].bits), a1 = bf16_to_f32(src[2 * q + 1].bits);
+        if constexpr (ROPE) {
+          // Phi_{L-1} is the final angle carry (reduced modulo 2 pi)
+          float sn, cs;
+          sincosf(phiC[q], &sn, &cs);
+          const float b0 = cs * a0 + sn * a1, b1 = cs * a1 - sn * a0;
+          a0 = b0;
+          a1 = b1;
+        }
+        float* dst = p.Bprev_rot_out + (static_cast<size_t>(bh) * R + r) * N + 2 * q;
+        dst[0] = a0;
+        dst[1] = a1;
+      }
+    }
+    if (p.xprev_out != nullptr)
+      for (int e = tid; e < R * P; e += kThreads)
+        static_cast<bf16_t*>(p.xprev_out)[static_cast<size_t>(bh) * R * P + e] =
+            static_cast<const bf16_t*>(p.x)[((static_cast<size_t>(b) * L + t) * H + hh) * R * P + e];
   }
 }
 
