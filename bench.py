@@ -14,7 +14,14 @@ omega ~ N(0,1) per token and pair; decode state ~ N(0, 0.1^2)) and are
 resident in HBM before timing starts.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S]
-                       [--no-cpu-baseline] [--only prefill|decode|all]
+                       [--no-cpu-baseline] [--only prefill|decode|all|pmc]
+       python bench.py --report-trace PREFIX          (rocprofv3 kernel trace -> markdown)
+       python bench.py --report-pmc FETCH_PREFIX WRITE_PREFIX   (HBM counters -> markdown)
+
+--only pmc runs the counter workload: a plain device copy of known size (the
+scale for FETCH_SIZE / WRITE_SIZE), then two launches of each prefill kernel
+and three decode steps, untimed.  PREFIX is the rocprofv3 output prefix
+(-d DIR -o NAME gives DIR/NAME).
 """
 from __future__ import annotations
 
@@ -42,6 +49,29 @@ def prefill_shapes():
         "siso_rope": (8, 4096, 32, 64, 64, 1, True),
         "mimo_rope": (4, 8192, 32, 64, 64, 4, True),
     }
+
+
+DECODE_SHAPE = (256, 32, 64, 64, 4)  # Bt, H, P, N, R
+COPY_BYTES = 1 << 30                 # plain copy used to scale the HBM counters
+
+
+def prefill_kernel_name(Bt, L, H, P, N, R, rope):
+    """Kernel symbol (as rocprofv3 prints it) that runs a bf16 prefill shape."""
+    return f"m3::pc::prefill_pc_kernel<{N}, {P}, {int(math.log2(R))}, {'true' if rope else 'false'}>"
+
+
+def decode_kernel_name(Bt, H, P, N, R):
+    return f"m3::decode_step_kernel<m3::bf16_t, {N}, {P}, {4 if R <= 4 else 16}>"
+
+
+def unit_kernels():
+    """(unit key, kernel symbol, launch grid in threads) of every timed launch."""
+    out = []
+    for name, (Bt, L, H, P, N, R, rope) in prefill_shapes().items():
+        out.append(("prefill_" + name, prefill_kernel_name(Bt, L, H, P, N, R, rope), Bt * H * 512))
+    Bt, H, P, N, R = DECODE_SHAPE
+    out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
+    return out
 
 
 def prefill_algo(Bt, L, H, P, N, R, rope):
@@ -167,7 +197,7 @@ def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
     return per_step, kern, ok
 
 
-def cpu_baseline(batch_items=2):
+def cpu_baseline(batch_items=6):
     """The fp64 oracle, as it stands, on a bounded sample of the headline
     prefill workload: `batch_items` sequences x all 32 heads x L 4096."""
     import dataclasses
@@ -205,19 +235,140 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key, launch_units):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counters, if they were taken on the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+
+
+def traffic_for(unit_key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, if it was taken on the current kernel sources (else None)."""
     try:
-        with open(path) as f:
-            t = json.load(f)
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
     except OSError:
         return None
-    e = t.get(kernel_key)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    tag = "traffic-json:"
+    if tag not in text:
         return None
-    return e.get("bytes_per_launch")
+    t = json.loads(text.split(tag, 1)[1].strip().splitlines()[0])
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    e = t.get("units", {}).get(unit_key)
+    return None if e is None else e["bytes_per_launch"]
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    return name.replace("void ", "").split("(")[0]
+
+
+def report_trace(prefix):
+    """Per-dispatch durations of the m3 kernels from a rocprofv3 kernel trace."""
+    import statistics
+    rows = _csv_rows(prefix + "_kernel_trace.csv")
+    grp, meta = {}, {}
+    for r in rows:
+        if "m3::" not in r["Kernel_Name"]:
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+        grp.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        meta[key] = (r["Workgroup_Size_X"], r["LDS_Block_Size"], r["VGPR_Count"], r["Accum_VGPR_Count"],
+                     r["SGPR_Count"], r["Scratch_Size"])
+    units = {(k, g): u for u, k, g in unit_kernels()}
+    lines = ["| unit | kernel | grid (threads) | block | calls | avg us | median us | min us | max us "
+             "| LDS B | arch VGPR | acc VGPR | SGPR | scratch |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, g), v in sorted(grp.items(), key=lambda kv: -sum(kv[1])):
+        wg, lds, vg, ag, sg, sc = meta[(k, g)]
+        lines.append(f"| {units.get((k, g), '-')} | `{k}` | {g} | {wg} | {len(v)} | {statistics.mean(v):.1f} "
+                     f"| {statistics.median(v):.1f} | {min(v):.1f} | {max(v):.1f} | {lds} | {vg} | {ag} | {sg} "
+                     f"| {sc} |")
+    try:
+        stats = _csv_rows(prefix + "_kernel_stats.csv")
+        lines += ["", "`--stats` summary (m3 kernels, all grids of one symbol merged):", "",
+                  "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in stats:
+            if "m3::" in r["Name"]:
+                lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} "
+                             f"| {int(r['MinNs']) / 1e3:.1f} | {int(r['MaxNs']) / 1e3:.1f} |")
+    except OSError:
+        pass
+    print("\n".join(lines))
+
+
+def report_pmc(fetch_prefix, write_prefix):
+    """HBM bytes per launch of each timed kernel: FETCH_SIZE and WRITE_SIZE (KiB
+    per dispatch), each scaled by what the same counter reads for the plain
+    copy of COPY_BYTES in the counter workload."""
+    def per_kernel(prefix, counter):
+        acc = {}
+        for r in _csv_rows(prefix + "_counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            acc.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
+        return acc
+
+    fetch = per_kernel(fetch_prefix, "FETCH_SIZE")
+    write = per_kernel(write_prefix, "WRITE_SIZE")
+
+    def copy_value(acc):
+        cands = [(k, v) for k, v in acc.items() if "neg_kernel" in k[0]]
+        k, v = max(cands, key=lambda kv: max(kv[1]))
+        return k[0], sum(v) / len(v)
+
+    cname, cf = copy_value(fetch)
+    _, cw = copy_value(write)
+    sf, sw = COPY_BYTES / cf, COPY_BYTES / cw
+    units = {}
+    lines = [f"Scale: a plain elementwise copy (negation) of {COPY_BYTES} B (`{cname}`) reads FETCH_SIZE = {cf:.4g} B and "
+             f"WRITE_SIZE = {cw:.4g} B, so the factors are {sf:.4f} (fetch) and {sw:.4f} (write).", "",
+             "| unit | kernel | dispatches | FETCH_SIZE B | WRITE_SIZE B | scaled HBM B per launch "
+             "| algorithmic B per launch | ratio |", "|---|---|---|---|---|---|---|---|"]
+    algo = {}
+    for name, shp in prefill_shapes().items():
+        algo["prefill_" + name] = prefill_algo(*shp)[0]
+    Bt, H, P, N, R = DECODE_SHAPE
+    algo["decode"] = decode_algo(Bt, H, P, N, R, True)[0]
+    for unit, k, g in unit_kernels():
+        fv, wv = fetch.get((k, g)), write.get((k, g))
+        if not fv or not wv:
+            continue
+        f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)
+        tot = f_avg * sf + w_avg * sw
+        units[unit] = {"bytes_per_launch": round(tot), "fetch_bytes": round(f_avg * sf),
+                       "write_bytes": round(w_avg * sw)}
+        lines.append(f"| {unit} | `{k}` | {len(fv)} | {f_avg:.4g} | {w_avg:.4g} | {tot:.4g} | {algo[unit]:.4g} "
+                     f"| {tot / algo[unit]:.3f} |")
+    lines += ["", "traffic-json: " + json.dumps({"source_hash": kernel_source_hash(), "units": units,
+                                                 "fetch_scale": sf, "write_scale": sw})]
+    print("\n".join(lines))
+
+
+def pmc_workload(torch, ops):
+    """Untimed launches for counter collection (see the module docstring)."""
+    # same-dtype copy_ becomes a DMA transfer, so the plain copy kernel is an
+    # elementwise negation: it reads COPY_BYTES and writes COPY_BYTES
+    a = torch.ones(COPY_BYTES // 4, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+    for i, (name, shp) in enumerate(prefill_shapes().items()):
+        inp = gen_prefill(torch, *shp, seed=20260100 + i)
+        time_prefill(torch, ops, inp, 2, 0)
+        del inp
+        torch.cuda.empty_cache()
+    Bt, H, P, N, R = DECODE_SHAPE
+    time_decode(torch, ops, Bt, H, P, N, R, 3, 1, seed=20260104)
+    torch.cuda.synchronize()
+    print("# counter workload done", file=sys.stderr, flush=True)
 
 
 def main():
@@ -227,8 +378,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "pmc"), default="all")
+    ap.add_argument("--report-trace", metavar="PREFIX")
+    ap.add_argument("--report-pmc", nargs=2, metavar=("FETCH_PREFIX", "WRITE_PREFIX"))
     args = ap.parse_args()
+    if args.report_trace:
+        report_trace(args.report_trace)
+        return
+    if args.report_pmc:
+        report_pmc(*args.report_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is "
               "not built: (batch, head) units shard with no exchange, see the design notes.", file=sys.stderr)
@@ -240,6 +399,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.only == "pmc":
+        pmc_workload(torch, ops)
+        return
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -258,6 +421,7 @@ def main():
                        gbs=byts / (launch_ms * 1e-3) / 1e9, tflops=flops / (launch_ms * 1e-3) / 1e12,
                        bytes=byts, flops=flops)
             res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
+            res["traffic"] = traffic_for("prefill_" + name)
             res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFS
             res["roofline_frac"] = max(byts / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFS * 1e12)) / (
                 launch_ms * 1e-3)
@@ -268,14 +432,15 @@ def main():
             del inp
             torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
-        Bt, H, P, N, R = 256, 32, 64, 64, 4
+        Bt, H, P, N, R = DECODE_SHAPE
         per_step, kern, ok = time_decode(torch, ops, Bt, H, P, N, R, args.decode_steps, 20, seed=20260104)
         byts, flops = decode_algo(Bt, H, P, N, R, True)
         results["decode"] = dict(
             workload=f"decode MIMO RoPE: Bt={Bt} H={H} P={P} N={N} R={R} bf16 inputs, fp32 state, "
                      f"{args.decode_steps} sequential steps",
             us_per_step=per_step * 1e3, kernel_us=kern * 1e3, gbs=byts / (kern * 1e-3) / 1e9,
-            hbm_frac=byts / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, bytes=byts, flops=flops, finite=ok)
+            hbm_frac=byts / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, bytes=byts, flops=flops, finite=ok,
+            traffic=traffic_for("decode"))
         print(f"# decode: {per_step * 1e3:.1f} us/step ({kern * 1e3:.1f} us kernel), "
               f"{results['decode']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
@@ -285,10 +450,10 @@ def main():
         out["unit"] = "tokens/s"
         out["ms_per_step"] = head["ms_per_step"]
         out["config"] = {"workload": head["workload"], "global_batch": 8, "seq_len": 4096}
-        tr = traffic_for("prefill_siso_real", 1)
+        tr = traffic_for("prefill_siso_real")
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": head["hbm_frac"], "traffic": tr,
-                           "kernel": "m3::pc::prefill_pc_kernel<128,64>",
+                           "kernel": prefill_kernel_name(*prefill_shapes()["siso_real"]),
                            "algorithmic_bytes_per_launch": head["bytes"],
                            "mfma_tflops": head["tflops"], "mfma_frac": head["mfma_frac"]}
     elif "decode" in results:
@@ -302,8 +467,8 @@ def main():
         dres = results["decode"]
         out["decode"] = dres
         out["decode_roofline"] = {"bound": "hbm", "achieved": dres["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": dres["hbm_frac"], "traffic": traffic_for("decode", 1),
-                                  "kernel": "m3::decode_step_kernel<bf16_t,64,64,4>"}
+                                  "frac": dres["hbm_frac"], "traffic": traffic_for("decode"),
+                                  "kernel": decode_kernel_name(*DECODE_SHAPE)}
     for k in ("siso_rope", "mimo_rope"):
         if k in results:
             out["prefill_" + k] = results[k]
