@@ -55,6 +55,11 @@ DECODE_SHAPE = (256, 32, 64, 64, 4)  # Bt, H, P, N, R
 COPY_BYTES = 1 << 30                 # plain copy used to scale the HBM counters
 
 
+def ANGLES_GRID(Bt, H, J):
+    """Threads launched by the angle scan: 256 per 32 (head, pair) columns per batch item."""
+    return Bt * ((H * J // 4 + 7) // 8) * 256
+
+
 def prefill_kernel_name(Bt, L, H, P, N, R, rope):
     """Kernel symbol (as rocprofv3 prints it) that runs a bf16 prefill shape."""
     return f"m3::pc::prefill_pc_kernel<{N}, {P}, {int(math.log2(R))}, {'true' if rope else 'false'}>"
@@ -71,6 +76,8 @@ def unit_kernels():
         out.append(("prefill_" + name, prefill_kernel_name(Bt, L, H, P, N, R, rope), Bt * H * 512))
     Bt, H, P, N, R = DECODE_SHAPE
     out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
+    Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
+    out.append(("angles", "m3::angles_cumsum_kernel", ANGLES_GRID(Bt, H, N // 2)))
     return out
 
 
@@ -150,6 +157,27 @@ def time_prefill(torch, ops, inp, steps, warmup):
     total_ms = start.elapsed_time(end)
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     return total_ms / steps, sum(launch_ms) / len(launch_ms), wall
+
+
+def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
+    """Mean per-launch duration (ms) of the cumulative-angle scan and its
+    algorithmic bytes (theta read once, phi written once, phi0 read once)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    theta = torch.randn((Bt, L, H, J), generator=g, device="cuda") * 0.05
+    phi0 = torch.randn((Bt, H, J), generator=g, device="cuda")
+    phi = torch.empty_like(theta)
+    for _ in range(warmup):
+        ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return ms, 2 * theta.numel() * 4 + phi0.numel() * 4
 
 
 def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
@@ -334,6 +362,8 @@ def report_pmc(fetch_prefix, write_prefix):
         algo["prefill_" + name] = prefill_algo(*shp)[0]
     Bt, H, P, N, R = DECODE_SHAPE
     algo["decode"] = decode_algo(Bt, H, P, N, R, True)[0]
+    Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
+    algo["angles"] = 2 * Bt * L * H * (N // 2) * 4 + Bt * H * (N // 2) * 4
     for unit, k, g in unit_kernels():
         fv, wv = fetch.get((k, g)), write.get((k, g))
         if not fv or not wv:
@@ -365,6 +395,8 @@ def pmc_workload(torch, ops):
         time_prefill(torch, ops, inp, 2, 0)
         del inp
         torch.cuda.empty_cache()
+    Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
+    time_angles(torch, ops, Bt, L, H, N // 2, 2, 0, seed=20260110)
     Bt, H, P, N, R = DECODE_SHAPE
     time_decode(torch, ops, Bt, H, P, N, R, 3, 1, seed=20260104)
     torch.cuda.synchronize()
@@ -431,6 +463,15 @@ def main():
                   f"{res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.2f}% MFMA)", file=sys.stderr, flush=True)
             del inp
             torch.cuda.empty_cache()
+    if args.only in ("all", "prefill"):
+        Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
+        ms, byts = time_angles(torch, ops, Bt, L, H, N // 2, args.steps, args.warmup, seed=20260110)
+        results["angles"] = dict(workload=f"cumulative angles: theta [{Bt},{L},{H},{N // 2}] fp32",
+                                 kernel_ms=ms, gbs=byts / (ms * 1e-3) / 1e9, bytes=byts,
+                                 hbm_frac=byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 traffic=traffic_for("angles"))
+        print(f"# {results['angles']['workload']}: {ms * 1e3:.1f} us, {results['angles']['gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
     if args.only in ("all", "decode"):
         Bt, H, P, N, R = DECODE_SHAPE
         per_step, kern, ok = time_decode(torch, ops, Bt, H, P, N, R, args.decode_steps, 20, seed=20260104)
@@ -472,6 +513,8 @@ def main():
     for k in ("siso_rope", "mimo_rope"):
         if k in results:
             out["prefill_" + k] = results[k]
+    if "angles" in results:
+        out["angles"] = results["angles"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
