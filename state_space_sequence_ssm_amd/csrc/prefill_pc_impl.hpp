@@ -167,8 +167,17 @@ struct PcLayout {
   static constexpr size_t oS = oSC + 3 * kSC;             // [10][64] x 8 B masked S^T pieces
   static constexpr size_t oPhiC = oS + 10 * 64 * 8;       // [N/2] fp32 angle carry
   static constexpr size_t oPhi = oPhiC + (N / 2) * 4;     // [2][64][PH] fp32 angles
-  static constexpr size_t kBytesReal = oPhi;
-  static constexpr size_t kBytesRope = oPhi + 2 * size_t(kRows) * PH * 4;
+  static constexpr size_t kBytesReal0 = oPhi;
+  static constexpr size_t kBytesRope0 = oPhi + 2 * size_t(kRows) * PH * 4;
+  // The two waves of a p tile split the state's n tiles when the exchange of
+  // readout partials fits: [wave][u][2][lane] x f32x4.
+  static constexpr size_t kLdsMax = 160 * 1024;
+  static constexpr size_t kExBytes = size_t(kWaves) * UPT * 2 * 64 * 16;
+  static constexpr size_t base(bool rope) { return rope ? kBytesRope0 : kBytesReal0; }
+  static constexpr bool split_n(bool rope) { return NTH >= 2 && base(rope) + kExBytes <= kLdsMax; }
+  static constexpr size_t oEx(bool rope) { return base(rope); }
+  static constexpr size_t kBytesReal = base(false) + (split_n(false) ? kExBytes : 0);
+  static constexpr size_t kBytesRope = base(true) + (split_n(true) ? kExBytes : 0);
 };
 
 template <int N, int P, int LGR, bool ROPE>
@@ -358,7 +367,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     }
   };
   // ================================================================ compute state
-  f32x4 acc[UPT][NTH];
+  // The state H' (N x P) lives in MFMA accumulators: wave (quad, upper) keeps p
+  // tiles quad + 4u and, when the pair splits n, n tiles [NTW upper, NTW upper + NTW).
+  constexpr bool kSplit = Lt::split_n(ROPE);
+  constexpr int NTW = kSplit ? NTH / 2 : NTH;  // n tiles kept per wave
+  constexpr int NKW = NTW >= 2 ? NTW / 2 : 1;  // k blocks of the readout over the kept n
+  f32x4 acc[UPT][NTW];
+  f32x4 zown[UPT][2];  // readout of this wave's two i tiles (own part), phase A -> B
+  f32x4* sEx = reinterpret_cast<f32x4*>(smem + Lt::oEx(ROPE));
   constexpr bool kAllPt = NPT % kPGroups == 0;  // every wave owns UPT real p tiles
   u32x2* sS = reinterpret_cast<u32x2*>(smem + Lt::oS);
   // causal (j tile, i tile) pairs, numbered (0,0) (0,1) (1,1) (0,2) (1,2) (2,2)
@@ -412,11 +428,51 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       default: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 3>{}); break;
     }
   };
+  // i tiles owned in phase B: {0, 3} (lower waves) and {1, 2} (upper waves)
+  auto own_tile = [](int h, int idx) { return h == 0 ? (idx == 0 ? 0 : 3) : (idx == 0 ? 1 : 2); };
+  // phase A: readout C^T H'_prev of chunk k from the kept part of the state.
+  // With the n split, every wave covers all four i tiles over its n tiles and
+  // hands the partner's two to LDS; otherwise it covers its own two over all n.
+  auto readout = [&](int k, auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    constexpr int nb = kSplit && h ? NTW : 0;  // first kept n tile
+    const uint16_t* sC = slotC(k & 1);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      if (!(kAllPt || quad + kPGroups * u < NPT)) continue;
+      bf16x8 hfr[NKW];
+#pragma unroll
+      for (int kw = 0; kw < NKW; ++kw) {
+        constexpr u32x2 zero2 = {0u, 0u};
+        if constexpr (NTW >= 2) {
+          hfr[kw] = cat8(pack4(acc[u][2 * kw]), pack4(acc[u][2 * kw + 1]));
+        } else {  // one kept n tile: the low or high half of k block 0
+          hfr[kw] = (nb & 1) ? cat8(zero2, pack4(acc[u][0])) : cat8(pack4(acc[u][0]), zero2);
+        }
+      }
+      constexpr int kb0 = NTW >= 2 ? nb / 2 : 0;
+      auto part = [&](int it) __attribute__((always_inline)) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kw = 0; kw < NKW; ++kw) {
+          const uint16_t* rc = sC + (16 * it + l16) * PN + 32 * (kb0 + kw) + 4 * g;
+          z = mma(hfr[kw], cat8(*reinterpret_cast<const u32x2*>(rc), *reinterpret_cast<const u32x2*>(rc + 16)), z);
+        }
+        return z;
+      };
+#pragma unroll
+      for (int idx = 0; idx < 2; ++idx) {
+        zown[u][idx] = part(own_tile(h, idx));
+        if constexpr (kSplit) sEx[((wave * UPT + u) * 2 + idx) * 64 + lane] = part(own_tile(1 - h, idx));
+      }
+    }
+  };
   // phase B: y of this wave's i tiles and p tiles, then the state update
-  auto compute_rest = [&](int k) __attribute__((always_inline)) {
+  auto compute_rest = [&](int k, auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    constexpr int nb = kSplit && h ? NTW : 0;
     const int s2 = k & 1;
     const float* S = sc(k % 3);
-    const uint16_t* sC = slotC(s2);
     const u32x2* bwt = slotBwT(s2);
     const u32x2* xt = slotXT(s2);
     const float cdec = S[5 * 64];
@@ -428,19 +484,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       for (int m = 0; m < 2; ++m)
         if (kAllPt || pt < NPT) xfr[u][m] = cat8(xt[((pt * 2 + m) * 2 + 0) * 64 + lane], xt[((pt * 2 + m) * 2 + 1) * 64 + lane]);
     }
-    // H'^T operand pieces straight from the accumulators (state before chunk k)
-    bf16x8 hfr[UPT][NKB];
-#pragma unroll
-    for (int u = 0; u < UPT; ++u)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        constexpr u32x2 zero2 = {0u, 0u};
-        const u32x2 lo = (2 * kb < NTH) ? pack4(acc[u][2 * kb < NTH ? 2 * kb : 0]) : zero2;
-        const u32x2 hi = (2 * kb + 1 < NTH) ? pack4(acc[u][2 * kb + 1 < NTH ? 2 * kb + 1 : 0]) : zero2;
-        hfr[u][kb] = cat8(lo, hi);
-      }
-    auto do_it = [&](auto IT) __attribute__((always_inline)) {
-      constexpr int it = decltype(IT)::value;
+    auto do_it = [&](auto IT, auto IDX) __attribute__((always_inline)) {
+      constexpr int it = decltype(IT)::value, idx = decltype(IDX)::value;
       const int iRow = 16 * it + l16;
       const int ti = iRow >> LGR;
       const float decI = S[4 * 64 + ti];
@@ -464,44 +509,39 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       for (int u = 0; u < UPT; ++u) {
         const int pt = quad + kPGroups * u;
         if (kAllPt || pt < NPT) {
-          f32x4 zz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const uint16_t* rc = sC + iRow * PN + 32 * kb + 4 * g;
-            zz = mma(hfr[u][kb], cat8(*reinterpret_cast<const u32x2*>(rc), *reinterpret_cast<const u32x2*>(rc + 16)), zz);
-          }
+          f32x4 zz = zown[u][idx];
+          if constexpr (kSplit) zz += sEx[(((wave ^ 4) * UPT + u) * 2 + idx) * 64 + lane];
           const f32x4 yv = yacc[u] + decI * zz;
           bstore8(rY, (yrow + 16 * pt + 4 * g) * 2u, pack4(yv));  // rows past L are dropped
         }
       }
     };
-    if (!upper) {
-      do_it(std::integral_constant<int, 0>{});
-      do_it(std::integral_constant<int, 3>{});
-    } else {
-      do_it(std::integral_constant<int, 1>{});
-      do_it(std::integral_constant<int, 2>{});
-    }
-    // H' = exp(Lam_e) H' + (w B)^T X
+    using std::integral_constant;
+    do_it(integral_constant<int, h == 0 ? 0 : 1>{}, integral_constant<int, 0>{});
+    do_it(integral_constant<int, h == 0 ? 3 : 2>{}, integral_constant<int, 1>{});
+    // H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (kAllPt || quad + kPGroups * u < NPT) {
 #pragma unroll
-        for (int nt = 0; nt < NTH; ++nt) {
-          f32x4 a = acc[u][nt] * cdec;
+        for (int i = 0; i < NTW; ++i) {
+          const int nt = nb + i;
+          f32x4 a = acc[u][i] * cdec;
 #pragma unroll
           for (int m = 0; m < 2; ++m)
             a = mma(cat8(bwt[((nt * 2 + m) * 2 + 0) * 64 + lane], bwt[((nt * 2 + m) * 2 + 1) * 64 + lane]),
                     xfr[u][m], a);
-          acc[u][nt] = a;
+          acc[u][i] = a;
         }
       }
     }
   };
 
   // ================================================================ prologue
-  {
-    // H'_{-1} = h0 + (1 - lambda_0) Delta_0 sum_r Bprev_rot[r] xprev[r]^T
+  // H'_{-1} = h0 + (1 - lambda_0) Delta_0 sum_r Bprev_rot[r] xprev[r]^T (kept tiles)
+  auto init_state = [&](auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    constexpr int nb = kSplit && h ? NTW : 0;
     const size_t o0 = static_cast<size_t>(b) * L * H + hh;
     const float coef = (1.f - p.lam[o0]) * p.dt[o0];
     const bool hasCarry = p.Bprev_rot != nullptr && p.xprev != nullptr;
@@ -509,7 +549,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     for (int u = 0; u < UPT; ++u) {
       const int pt = quad + kPGroups * u;
 #pragma unroll
-      for (int nt = 0; nt < NTH; ++nt) {
+      for (int i = 0; i < NTW; ++i) {
+        const int nt = nb + i;
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         if (pt < NPT) {
           const int pc = 16 * pt + l16;
@@ -528,13 +569,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
             a[jj] = v;
           }
         }
-        acc[u][nt] = a;
+        acc[u][i] = a;
       }
     }
-    if constexpr (ROPE)
-      for (int q = tid; q < N / 2; q += kThreads)
-        phiC[q] = p.phi0 != nullptr ? p.phi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
-  }
+  };
+  if (!upper)
+    init_state(std::integral_constant<int, 0>{});
+  else
+    init_state(std::integral_constant<int, 1>{});
+  if constexpr (ROPE)
+    for (int q = tid; q < N / 2; q += kThreads)
+      phiC[q] = p.phi0 != nullptr ? p.phi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
   // retire the prologue's state and carry loads here, so no wait on them is
   // left for the loop to repeat every chunk
   __builtin_amdgcn_s_waitcnt(0);
@@ -564,8 +609,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     stage_small(k + 2, sset);
     issue_small(k + 4, sset);
     gram_tiles(k);
-    __syncthreads();  // S pieces visible
-    compute_rest(k);
+    readout(k, HALF);
+    __syncthreads();  // S pieces and readout partials visible
+    compute_rest(k, HALF);
     __syncthreads();  // slot k+1, SC(k+2), Phi(k+2) visible; slot k and S free
   };
   auto walk = [&](auto HALF) __attribute__((always_inline)) {
@@ -583,19 +629,28 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   }
 
   // ================================================================ epilogue
-  if (p.h_final != nullptr && !upper) {  // both waves of a p tile hold the same state
+  // each wave writes its kept n tiles (both waves hold all of them without the split)
+  auto write_state = [&](auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    constexpr int nb = kSplit && h ? NTW : 0;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int pt = quad + kPGroups * u;
       if (pt < NPT) {
 #pragma unroll
-        for (int nt = 0; nt < NTH; ++nt)
+        for (int i = 0; i < NTW; ++i)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            p.h_final[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * nt + 4 * g + jj) * P + 16 * pt + l16] =
-                acc[u][nt][jj];
+            p.h_final[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * (nb + i) + 4 * g + jj) * P + 16 * pt + l16] =
+                acc[u][i][jj];
       }
     }
+  };
+  if (p.h_final != nullptr) {
+    if (!upper)
+      write_state(std::integral_constant<int, 0>{});
+    else if (kSplit)
+      write_state(std::integral_constant<int, 1>{});
   }
   if constexpr (ROPE) {
     if (p.phi_out != nullptr)
