@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // chunk c's pieces live in register set c % 2 (two chunks in flight)
   u32x4 raw[2][UPH];
   f32x4 rawTh[2][ROPE ? TSL : 1];
-  float rdt[2], rlam[2], rdtn[2], rlamn[2];
+  float rdt[2], rlam[2];
   bf16x8 Ilo, Ihi;  // identity selectors: column c <- k slot (g, e) with 8g + e == c (+16)
   {
     u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
@@ -257,12 +257,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     }
   };
   auto issue_small = [&](int c, int set) __attribute__((always_inline)) {
-    const uint32_t off = lane < Q ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
+    // Delta and lambda feed only the decay scan of wave 0.  The other waves
+    // issue the same instructions with an out-of-range offset: no memory
+    // request (one strided scalar per lane is one cache-line lookup per lane)
+    // and identical wait counts everywhere.
+    const uint32_t off = (wave == 0 && lane < Q) ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
     rdt[set] = bloadf(rDt, off);
     rlam[set] = bloadf(rLam, off);
-    const uint32_t offn = lane < Q ? off + H * 4u : kBad;
-    rdtn[set] = bloadf(rDt, offn);
-    rlamn[set] = bloadf(rLam, offn);
     if constexpr (ROPE) {
       const int tl = lane % Q, pg = lane / Q;
 #pragma unroll
@@ -279,8 +280,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       float* S = sc(c % 3);
       const float lamc = seg_scan<64>(rdt[set] * A2);
       const float lamEnd = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lamc), Q - 1));
+      // next token's Delta, lambda: lane t + 1, or token 0 of chunk c + 1 (the
+      // other register set; zeros past the end, i.e. Delta_L = 0) for t = Q - 1
+      const float dNext = __shfl_down(rdt[set], 1), lNext = __shfl_down(rlam[set], 1);
+      const float d0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rdt[set ^ 1]), 0));
+      const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rlam[set ^ 1]), 0));
       const float gam = rlam[set] * rdt[set];
-      const float del = gam + (1.f - rlamn[set]) * rdtn[set];
+      const float del = gam + (1.f - (lane == Q - 1 ? l0 : lNext)) * (lane == Q - 1 ? d0 : dNext);
       S[0 * 64 + lane] = lamc;
       S[1 * 64 + lane] = gam;
       S[2 * 64 + lane] = del;
