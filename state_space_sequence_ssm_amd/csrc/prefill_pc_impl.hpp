@@ -164,8 +164,9 @@ struct PcLayout {
   static constexpr size_t kSlot = oXT + kSlotXT;
   static constexpr size_t oSC = 2 * kSlot;                // [3][6][64] fp32 scalars
   static constexpr size_t kSC = 6 * 64 * 4;
-  static constexpr size_t oS = oSC + 3 * kSC;             // [10][64] x 8 B masked S^T pieces
-  static constexpr size_t oPhiC = oS + 10 * 64 * 8;       // [N/2] fp32 angle carry
+  static constexpr size_t kSBytes = 10 * 64 * 8;          // [10][64] x 8 B masked S^T pieces
+  static constexpr size_t oS = oSC + 3 * kSC;
+  static constexpr size_t oPhiC = oS + kSBytes;           // [N/2] fp32 angle carry
   static constexpr size_t oPhi = oPhiC + (N / 2) * 4;     // [2][64][PH] fp32 angles
   static constexpr size_t kBytesReal0 = oPhi;
   static constexpr size_t kBytesRope0 = oPhi + 2 * size_t(kRows) * PH * 4;
@@ -176,8 +177,13 @@ struct PcLayout {
   static constexpr size_t base(bool rope) { return rope ? kBytesRope0 : kBytesReal0; }
   static constexpr bool split_n(bool rope) { return NTH >= 2 && base(rope) + kExBytes <= kLdsMax; }
   static constexpr size_t oEx(bool rope) { return base(rope); }
-  static constexpr size_t kBytesReal = base(false) + (split_n(false) ? kExBytes : 0);
-  static constexpr size_t kBytesRope = base(true) + (split_n(true) ? kExBytes : 0);
+  static constexpr size_t used(bool rope) { return base(rope) + (split_n(rope) ? kExBytes : 0); }
+  // The Gram tiles of chunk k+1 are computed while chunk k finishes when a
+  // second S buffer fits.
+  static constexpr bool early_gram(bool rope) { return used(rope) + kSBytes <= kLdsMax; }
+  static constexpr size_t oS2(bool rope) { return used(rope); }
+  static constexpr size_t kBytesReal = used(false) + (early_gram(false) ? kSBytes : 0);
+  static constexpr size_t kBytesRope = used(true) + (early_gram(true) ? kSBytes : 0);
 };
 
 template <int N, int P, int LGR, bool ROPE>
@@ -224,7 +230,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // ================================================================ staging state
   // chunk c's pieces live in register set c % 2 (two chunks in flight)
   u32x4 raw[2][UPH];
-  f32x4 rawTh[2][ROPE ? TSL : 1];
+  // theta of one chunk as whole token rows: float4 unit e = token e / NG, group e % NG
+  constexpr int kThUnits = Q * NG;
+  constexpr int kThU = (kThUnits + kThreads - 1) / kThreads;
+  f32x4 rawTh[2][ROPE ? kThU : 1];
   float rdt[2], rlam[2];
   bf16x8 Ilo, Ihi;  // identity selectors: column c <- k slot (g, e) with 8g + e == c (+16)
   {
@@ -264,17 +273,18 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const uint32_t off = (wave == 0 && lane < Q) ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
     rdt[set] = bloadf(rDt, off);
     rlam[set] = bloadf(rLam, off);
-    if constexpr (ROPE) {
-      const int tl = lane % Q, pg = lane / Q;
+    if constexpr (ROPE) {  // consecutive lanes read consecutive 16 bytes of a token's row
 #pragma unroll
-      for (int s = 0; s < TSL; ++s) {
-        const int q4 = (s * kWaves + wave) * R + pg;
-        const uint32_t off4 = q4 < NG ? (static_cast<uint32_t>((c * Q + tl) * H + hh) * (N / 2) + 4 * q4) * 4u : kBad;
+      for (int s = 0; s < kThU; ++s) {
+        const int e = tid + s * kThreads;
+        const int tok = e / NG, grp = e % NG;
+        const uint32_t off4 =
+            e < kThUnits ? (static_cast<uint32_t>((c * Q + tok) * H + hh) * (N / 2) + 4 * grp) * 4u : kBad;
         rawTh[set][s] = bloadf4(rTh, off4);
       }
     }
   };
-  // decay scalars (log2 units) and cumulative angles of chunk c -> SC[c%3], Phi[c%2]
+  // decay scalars (log2 units) of chunk c -> SC[c%3]; raw theta -> Phi[c%2]
   auto stage_small = [&](int c, int set) __attribute__((always_inline)) {
     if (wave == 0) {
       float* S = sc(c % 3);
@@ -295,13 +305,27 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       if (lane == 0) S[5 * 64] = __builtin_amdgcn_exp2f(lamEnd);
     }
     if constexpr (ROPE) {
+      float* tab = phiTab(c & 1);
+#pragma unroll
+      for (int s = 0; s < kThU; ++s) {
+        const int e = tid + s * kThreads;
+        if (e < kThUnits) *reinterpret_cast<f32x4*>(tab + (e / NG) * PH + 4 * (e % NG)) = rawTh[set][s];
+      }
+    }
+  };
+  // cumulative angles of chunk c in place in Phi[c%2] (after a barrier since
+  // its raw theta was stored): lanes are tokens, a segment of Q lanes per
+  // group of four angles, carry across chunks in phiC
+  auto scan_angles = [&](int c) __attribute__((always_inline)) {
+    if constexpr (ROPE) {
       const int tl = lane % Q, pg = lane / Q;
       float* tab = phiTab(c & 1);
 #pragma unroll
       for (int s = 0; s < TSL; ++s) {
         const int q4 = (s * kWaves + wave) * R + pg;  // uniform within a Q-lane segment
         if ((s * kWaves + wave) * R < NG) {
-          f32x4 v = rawTh[set][s];
+          constexpr f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+          f32x4 v = q4 < NG ? *reinterpret_cast<const f32x4*>(tab + tl * PH + 4 * q4) : zero4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = seg_scan<Q>(v[e]);
           if (q4 < NG) {
@@ -382,7 +406,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   f32x4 zown[UPT][2];  // readout of this wave's two i tiles (own part), phase A -> B
   f32x4* sEx = reinterpret_cast<f32x4*>(smem + Lt::oEx(ROPE));
   constexpr bool kAllPt = NPT % kPGroups == 0;  // every wave owns UPT real p tiles
-  u32x2* sS = reinterpret_cast<u32x2*>(smem + Lt::oS);
+  constexpr bool kEarly = Lt::early_gram(ROPE);
+  // S pieces of chunk c (two buffers with the early Gram tiles)
+  auto sSb = [&](int c) __attribute__((always_inline)) {
+    return reinterpret_cast<u32x2*>(smem + ((kEarly && (c & 1)) ? Lt::oS2(ROPE) : Lt::oS));
+  };
   // causal (j tile, i tile) pairs, numbered (0,0) (0,1) (1,1) (0,2) (1,2) (2,2)
   // (0,3) (1,3) (2,3) (3,3); tile t is computed once, by wave t % 8
   auto tile_id = [](int jt, int it) { return it * (it + 1) / 2 + jt; };
@@ -417,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         a[jj] *= tj <= ti ? sel : 0.f;
       }
     }
-    sS[tile_id(jt, it) * 64 + lane] = pack4(a);
+    sSb(k)[tile_id(jt, it) * 64 + lane] = pack4(a);
   };
   auto gram_tiles = [&](int k) __attribute__((always_inline)) {
     using std::integral_constant;
@@ -481,6 +509,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const float* S = sc(k % 3);
     const u32x2* bwt = slotBwT(s2);
     const u32x2* xt = slotXT(s2);
+    const u32x2* sS = sSb(k);
     const float cdec = S[5 * 64];
     bf16x8 xfr[UPT][2];
 #pragma unroll
@@ -594,31 +623,39 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     issue_small(1, 1);
     issue_bcx(0, raw[0], HALF);
     issue_bcx(1, raw[1], HALF);
-    __syncthreads();  // angle carry visible
     stage_small(0, 0);
     issue_small(2, 0);
+    __syncthreads();  // angle carry, raw theta(0) visible
+    scan_angles(0);
     __syncthreads();  // SC(0), Phi(0) visible
     build_slot(0, raw[0], HALF);
     issue_bcx(2, raw[0], HALF);
     stage_small(1, 1);
     issue_small(3, 1);
-    __syncthreads();  // slot 0, SC(1), Phi(1) visible
+    __syncthreads();  // slot 0, raw theta(1) visible
+    scan_angles(1);
+    if constexpr (kEarly) gram_tiles(0);
+    __syncthreads();  // slot 0, S(0), SC(1), Phi(1) visible
   };
   // chunk walk, unrolled by two so the register sets are indexed statically.
   // Phase A: stage chunk k+1 (set `bcx` holds it), refill `bcx` with the loads
-  // of chunk k+3, scan decays and angles of chunk k+2, issue the small loads of
-  // chunk k+4, and compute the masked Gram tiles of chunk k; phase B: products,
-  // y and state of chunk k.
+  // of chunk k+3, scan the decays and store the raw angles of chunk k+2, issue
+  // the small loads of chunk k+4, and compute the readout partials of chunk k
+  // (and its masked Gram tiles when they are not computed early); phase B:
+  // scan the angles of chunk k+2, products, y and state of chunk k, then the
+  // Gram tiles of chunk k+1.
   auto chunk = [&](int k, u32x4 (&bcx)[UPH], int sset, auto HALF) __attribute__((always_inline)) {
     build_slot(k + 1, bcx, HALF);
     issue_bcx(k + 3, bcx, HALF);  // registers free again: refill before the y stores queue up
     stage_small(k + 2, sset);
     issue_small(k + 4, sset);
-    gram_tiles(k);
+    if constexpr (!kEarly) gram_tiles(k);
     readout(k, HALF);
-    __syncthreads();  // S pieces and readout partials visible
+    __syncthreads();  // S(k), readout partials, slot k+1, raw theta(k+2) visible
+    scan_angles(k + 2);
     compute_rest(k, HALF);
-    __syncthreads();  // slot k+1, SC(k+2), Phi(k+2) visible; slot k and S free
+    if constexpr (kEarly) gram_tiles(k + 1);  // overlaps the tail of chunk k
+    __syncthreads();  // S(k+1), SC(k+2), Phi(k+2) visible; slot k free
   };
   auto walk = [&](auto HALF) __attribute__((always_inline)) {
     for (int k = 0; k < nch; k += 2) {
