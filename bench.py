@@ -141,22 +141,21 @@ def time_prefill(torch, ops, inp, steps, warmup):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    # per-launch HIP events on the launch stream (torch's current stream)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # HIP events on the launch stream (torch's current stream) bracket `steps`
+    # back-to-back launches; the GPU is the bottleneck, so region / steps is
+    # the average launch duration (events between launches would add their
+    # own gaps to it)
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for e0, e1 in evs:
-        e0.record()
+    for _ in range(steps):
         run()
-        e1.record()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    return total_ms / steps, sum(launch_ms) / len(launch_ms), wall
+    ms = start.elapsed_time(end) / steps
+    return ms, ms, wall
 
 
 def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
@@ -170,13 +169,14 @@ def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
     for _ in range(warmup):
         ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for e0, e1 in evs:
-        e0.record()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
         ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)
-        e1.record()
+    e1.record()
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    ms = e0.elapsed_time(e1) / steps
     return ms, 2 * theta.numel() * 4 + phi0.numel() * 4
 
 
@@ -207,22 +207,14 @@ def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    # a few individually bracketed launches give the kernel-only duration
-    nk = min(50, steps)
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
     start.record()
     for i in range(steps):
-        if i < nk:
-            kev[i][0].record()
         step(warmup + i)
-        if i < nk:
-            kev[i][1].record()
     end.record()
     torch.cuda.synchronize()
-    per_step = start.elapsed_time(end) / steps
-    kern = sum(a.elapsed_time(b) for a, b in kev) / nk
+    per_step = start.elapsed_time(end) / steps  # back-to-back launches: the launch duration
     ok = bool(torch.isfinite(h).all())
-    return per_step, kern, ok
+    return per_step, per_step, ok
 
 
 def cpu_baseline(batch_items=6):
@@ -482,8 +474,8 @@ def main():
             us_per_step=per_step * 1e3, kernel_us=kern * 1e3, gbs=byts / (kern * 1e-3) / 1e9,
             hbm_frac=byts / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, bytes=byts, flops=flops, finite=ok,
             traffic=traffic_for("decode"))
-        print(f"# decode: {per_step * 1e3:.1f} us/step ({kern * 1e3:.1f} us kernel), "
-              f"{results['decode']['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        print(f"# decode: {per_step * 1e3:.1f} us/step, {results['decode']['gbs']:.0f} GB/s "
+              f"({100 * results['decode']['hbm_frac']:.1f}% HBM)", file=sys.stderr, flush=True)
 
     head = results.get("siso_real")
     if head is not None:

@@ -67,6 +67,16 @@ __device__ __forceinline__ float load_scalar<float>(const float* p) { return *p;
 template <>
 __device__ __forceinline__ float load_scalar<bf16_t>(const bf16_t* p) { return bf16_to_f32(p->bits); }
 
+// Same, with the nontemporal hint (data read once).
+template <typename T>
+__device__ __forceinline__ float load_scalar_nt(const T* p);
+template <>
+__device__ __forceinline__ float load_scalar_nt<float>(const float* p) { return __builtin_nontemporal_load(p); }
+template <>
+__device__ __forceinline__ float load_scalar_nt<bf16_t>(const bf16_t* p) {
+  return bf16_to_f32(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)));
+}
+
 template <typename T>
 __device__ __forceinline__ void store_scalar(T* p, float v);
 template <>

@@ -42,134 +42,183 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
   float* sCr = sBr + R * N;          // raw C_t               [R][N]
 
   const int tid = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int hh = bh % p.H;
-  const size_t vecN = static_cast<size_t>(bh) * R * N;
-  const size_t vecP = static_cast<size_t>(bh) * R * P;
-  const T* x = static_cast<const T*>(p.x) + vecP;
-  const T* Bin = static_cast<const T*>(p.B) + vecN;
-  const T* Cin = static_cast<const T*>(p.C) + vecN;
-  T* xprev = static_cast<T*>(p.xprev) + vecP;
-  float* Bprev = p.Bprev_rot + vecN;
-  float* h = p.h + static_cast<size_t>(bh) * N * P;
-
-  // issue the state loads first so their latency overlaps the staging below
-  constexpr int kIters = (NQUAD + kDecThreads - 1) / kDecThreads;
-  f32x4 hv[kIters];
-#pragma unroll
-  for (int k = 0; k < kIters; ++k) {
-    const int q = tid + k * kDecThreads;
-    if (q < NQUAD) hv[k] = *reinterpret_cast<const f32x4*>(h + 4 * q);
-  }
-
-  const float dt = p.dt[bh];
-  const float lm = p.lam[bh];
-  const float alpha = __expf(dt * p.A[hh]);
-  const float beta = (1.f - lm) * dt * alpha;
-  const float gamma = lm * dt;
-
-  // ---- angles: Phi <- wrap(Phi + theta); table of cos/sin per pair
-  if (p.theta != nullptr) {
-    for (int j = tid; j < N / 2; j += kDecThreads) {
-      float* phi = p.phi + static_cast<size_t>(bh) * (N / 2);
-      float a = wrap_angle(phi[j] + p.theta[static_cast<size_t>(bh) * (N / 2) + j]);
-      sPhi[j] = a;
-      float s, c;
-      sincosf(a, &s, &c);
-      sCS[2 * j] = c;
-      sCS[2 * j + 1] = s;
-    }
-  }
-  // ---- small vectors into LDS (read everything before any carry is overwritten)
-  for (int e = tid; e < R * P; e += kDecThreads) {
-    sX[e] = load_scalar(x + e);
-    sXp[e] = load_scalar(xprev + e);
-  }
-  for (int e = tid; e < R * N; e += kDecThreads) {
-    sBp[e] = beta * Bprev[e];
-    sBr[e] = load_scalar(Bin + e);
-    sCr[e] = load_scalar(Cin + e);
-  }
-  __syncthreads();
-  // rotate B_t, C_t pairwise; write carry-out Btil_t, x_t, Phi
-  for (int e = tid; e < R * (N / 2); e += kDecThreads) {
-    const int r = e / (N / 2);
-    const int j = e % (N / 2);
-    float b0 = sBr[r * N + 2 * j], b1 = sBr[r * N + 2 * j + 1];
-    float c0 = sCr[r * N + 2 * j], c1 = sCr[r * N + 2 * j + 1];
-    if (p.theta != nullptr) {
-      const float c = sCS[2 * j], s = sCS[2 * j + 1];
-      const float rb0 = c * b0 + s * b1, rb1 = -s * b0 + c * b1;
-      const float rc0 = c * c0 + s * c1, rc1 = -s * c0 + c * c1;
-      b0 = rb0; b1 = rb1; c0 = rc0; c1 = rc1;
-    }
-    Bprev[r * N + 2 * j] = b0;
-    Bprev[r * N + 2 * j + 1] = b1;
-    sBc[r * N + 2 * j] = gamma * b0;
-    sBc[r * N + 2 * j + 1] = gamma * b1;
-    sC[r * N + 2 * j] = c0;
-    sC[r * N + 2 * j + 1] = c1;
-  }
-  for (int e = tid; e < R * P; e += kDecThreads) store_scalar(xprev + e, sX[e]);
-  if (p.theta != nullptr) {
-    for (int j = tid; j < N / 2; j += kDecThreads) {
-      p.phi[static_cast<size_t>(bh) * (N / 2) + j] = sPhi[j];
-    }
-  }
-  __syncthreads();
-
-  // ---- state update, 16-byte coalesced: thread owns quad column c4, rows n
+  const int lane = tid & 63, wave = tid >> 6;
   const int c4 = tid % QP;
-  float yacc[kDecMaxR][4];
-#pragma unroll
-  for (int r = 0; r < kDecMaxR; ++r)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) yacc[r][i] = 0.f;
+  constexpr int KX = (RMAX * P + kDecThreads - 1) / kDecThreads;  // x elements per thread
+  constexpr int KB = (RMAX * N + kDecThreads - 1) / kDecThreads;  // B, C elements per thread
+  constexpr int kIters = (NQUAD + kDecThreads - 1) / kDecThreads;  // state quads per thread
 
+  // Everything one unit (batch, head) reads, held in registers from issue to use.
+  struct Unit {
+    float rx[KX], rxp[KX], rb[KB], rc[KB], rbp[KB], rth, rph;
+    f32x4 hv[kIters];
+  };
+  // The state and this token's inputs are touched once per step: they are
+  // loaded (and the state stored) with the nontemporal hint, which keeps them
+  // from displacing the carries in the caches (measured ~15% faster with
+  // fresh per-step inputs).
+  // Loads in the order they are consumed: the small per-token vectors first,
+  // then the state.  Wait counters retire loads in issue order, so staging the
+  // small vectors (and its barriers) overlaps the state fetch, and a later
+  // unit's loads never hold up an earlier one.  Indices are clamped rather
+  // than branched so the wait counts stay static.
+  auto fetch = [&](int bh, Unit& U) __attribute__((always_inline)) {
+    const size_t vecN = static_cast<size_t>(bh) * R * N;
+    const size_t vecP = static_cast<size_t>(bh) * R * P;
 #pragma unroll
-  for (int k = 0; k < kIters; ++k) {
-    const int q = tid + k * kDecThreads;
-    if (q < NQUAD) {
-      const int n = q / QP;
-      f32x4 v = hv[k] * alpha;
-      for (int r = 0; r < R; ++r) {
-        const float bp = sBp[r * N + n], bc = sBc[r * N + n];
-        const f32x4 xp4 = *reinterpret_cast<const f32x4*>(&sXp[r * P + 4 * c4]);
-        const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sX[r * P + 4 * c4]);
-        v += bp * xp4 + bc * x4;
+    for (int i = 0; i < KX; ++i) {
+      const int e = tid + i * kDecThreads;
+      const int ec = e < R * P ? e : 0;
+      U.rx[i] = load_scalar_nt(static_cast<const T*>(p.x) + vecP + ec);
+      U.rxp[i] = load_scalar(static_cast<const T*>(p.xprev) + vecP + ec);
+    }
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const int e = tid + i * kDecThreads;
+      const int ec = e < R * N ? e : 0;
+      U.rb[i] = load_scalar_nt(static_cast<const T*>(p.B) + vecN + ec);
+      U.rc[i] = load_scalar_nt(static_cast<const T*>(p.C) + vecN + ec);
+      U.rbp[i] = p.Bprev_rot[vecN + ec];
+    }
+    U.rth = 0.f;
+    U.rph = 0.f;
+    if (p.theta != nullptr) {
+      const int j = tid < N / 2 ? tid : 0;
+      U.rth = __builtin_nontemporal_load(p.theta + static_cast<size_t>(bh) * (N / 2) + j);
+      U.rph = p.phi[static_cast<size_t>(bh) * (N / 2) + j];
+    }
+    const float* h = p.h + static_cast<size_t>(bh) * N * P;
+#pragma unroll
+    for (int k = 0; k < kIters; ++k) {
+      const int q = tid + k * kDecThreads;
+      U.hv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(h + 4 * (q < NQUAD ? q : 0)));
+    }
+  };
+
+  auto process = [&](int bh, Unit& U) __attribute__((always_inline)) {
+    const int hh = bh % p.H;
+    const size_t vecN = static_cast<size_t>(bh) * R * N;
+    const size_t vecP = static_cast<size_t>(bh) * R * P;
+    T* xprev = static_cast<T*>(p.xprev) + vecP;
+    float* Bprev = p.Bprev_rot + vecN;
+    float* h = p.h + static_cast<size_t>(bh) * N * P;
+    const float dt = p.dt[bh];
+    const float lm = p.lam[bh];
+    const float alpha = __expf(dt * p.A[hh]);
+    const float beta = (1.f - lm) * dt * alpha;
+    const float gamma = lm * dt;
+
+    // ---- angles: Phi <- wrap(Phi + theta); table of cos/sin per pair
+    if (p.theta != nullptr && tid < N / 2) {
+      const float a = wrap_angle(U.rph + U.rth);
+      sPhi[tid] = a;
+      float sn, cs;
+      sincosf(a, &sn, &cs);
+      sCS[2 * tid] = cs;
+      sCS[2 * tid + 1] = sn;
+    }
+    // ---- small vectors into LDS (everything is read before any carry is overwritten)
+#pragma unroll
+    for (int i = 0; i < KX; ++i) {
+      const int e = tid + i * kDecThreads;
+      if (e < R * P) {
+        sX[e] = U.rx[i];
+        sXp[e] = U.rxp[i];
       }
-      *reinterpret_cast<f32x4*>(h + 4 * q) = v;
+    }
 #pragma unroll
-      for (int r = 0; r < kDecMaxR; ++r) {
-        if (r < R) {
-          const float c = sC[r * N + n];
+    for (int i = 0; i < KB; ++i) {
+      const int e = tid + i * kDecThreads;
+      if (e < R * N) {
+        sBp[e] = beta * U.rbp[i];
+        sBr[e] = U.rb[i];
+        sCr[e] = U.rc[i];
+      }
+    }
+    __syncthreads();
+    // rotate B_t, C_t pairwise; write carry-out Btil_t, x_t, Phi
+    for (int e = tid; e < R * (N / 2); e += kDecThreads) {
+      const int r = e / (N / 2);
+      const int j = e % (N / 2);
+      float b0 = sBr[r * N + 2 * j], b1 = sBr[r * N + 2 * j + 1];
+      float c0 = sCr[r * N + 2 * j], c1 = sCr[r * N + 2 * j + 1];
+      if (p.theta != nullptr) {
+        const float c = sCS[2 * j], sn = sCS[2 * j + 1];
+        const float rb0 = c * b0 + sn * b1, rb1 = -sn * b0 + c * b1;
+        const float rc0 = c * c0 + sn * c1, rc1 = -sn * c0 + c * c1;
+        b0 = rb0; b1 = rb1; c0 = rc0; c1 = rc1;
+      }
+      Bprev[r * N + 2 * j] = b0;
+      Bprev[r * N + 2 * j + 1] = b1;
+      sBc[r * N + 2 * j] = gamma * b0;
+      sBc[r * N + 2 * j + 1] = gamma * b1;
+      sC[r * N + 2 * j] = c0;
+      sC[r * N + 2 * j + 1] = c1;
+    }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) yacc[r][i] += c * v[i];
+    for (int i = 0; i < KX; ++i) {
+      const int e = tid + i * kDecThreads;
+      if (e < R * P) store_scalar(xprev + e, U.rx[i]);
+    }
+    if (p.theta != nullptr && tid < N / 2) p.phi[static_cast<size_t>(bh) * (N / 2) + tid] = sPhi[tid];
+    __syncthreads();
+
+    // ---- state update, 16-byte coalesced: thread owns quad column c4, rows n
+    float yacc[kDecMaxR][4];
+#pragma unroll
+    for (int r = 0; r < kDecMaxR; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yacc[r][i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kIters; ++k) {
+      const int q = tid + k * kDecThreads;
+      if (q < NQUAD) {
+        const int n = q / QP;
+        f32x4 v = U.hv[k] * alpha;
+        for (int r = 0; r < R; ++r) {
+          const float bp = sBp[r * N + n], bc = sBc[r * N + n];
+          const f32x4 xp4 = *reinterpret_cast<const f32x4*>(&sXp[r * P + 4 * c4]);
+          const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sX[r * P + 4 * c4]);
+          v += bp * xp4 + bc * x4;
+        }
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(h + 4 * q));
+#pragma unroll
+        for (int r = 0; r < kDecMaxR; ++r) {
+          if (r < R) {
+            const float c = sC[r * N + n];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[r][i] += c * v[i];
+          }
         }
       }
     }
-  }
-  // ---- y = h^T Ctil: reduce over the rows held by lanes sharing column c4
-  const int lane = tid & 63, wave = tid >> 6;
+    // ---- y = h^T Ctil: reduce over the rows held by lanes sharing column c4
 #pragma unroll
-  for (int r = 0; r < kDecMaxR; ++r) {
-    if (r < R) {
+    for (int r = 0; r < kDecMaxR; ++r) {
+      if (r < R) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = yacc[r][i];
-        for (int off = QP; off < 64; off <<= 1) v += __shfl_xor(v, off);
-        if (lane < QP) sRed[(wave * R + r) * P + 4 * lane + i] = v;
+        for (int i = 0; i < 4; ++i) {
+          float v = yacc[r][i];
+          for (int off = QP; off < 64; off <<= 1) v += __shfl_xor(v, off);
+          if (lane < QP) sRed[(wave * R + r) * P + 4 * lane + i] = v;
+        }
       }
     }
-  }
-  __syncthreads();
-  T* y = static_cast<T*>(p.y) + vecP;
-  for (int e = tid; e < R * P; e += kDecThreads) {
-    float s = 0.f;
+    __syncthreads();
+    T* y = static_cast<T*>(p.y) + vecP;
+    for (int e = tid; e < R * P; e += kDecThreads) {
+      float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) s += sRed[w * R * P + e];
-    store_scalar(y + e, s);
-  }
+      for (int w = 0; w < 4; ++w) s += sRed[w * R * P + e];
+      store_scalar(y + e, s);
+    }
+    // the next process() writes sRed only after two barriers, and the staged
+    // vectors read above before this barrier
+  };
+
+  Unit U;
+  fetch(blockIdx.x, U);
+  process(blockIdx.x, U);
 }
 
 template <typename T, int N, int P>
