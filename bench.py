@@ -138,24 +138,11 @@ def time_prefill(torch, ops, inp, steps, warmup):
         ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], inp["theta"],
                            y=y, h_final=hf)
 
-    for _ in range(warmup):
+    for _ in range(max(warmup, 1)):
         run()
     torch.cuda.synchronize()
-    # HIP events on the launch stream (torch's current stream) bracket `steps`
-    # back-to-back launches; the GPU is the bottleneck, so region / steps is
-    # the average launch duration (events between launches would add their
-    # own gaps to it)
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        run()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / steps
-    return ms, ms, wall
+    ms = replay_ms(torch, [run] * steps)
+    return ms, ms, None
 
 
 def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
@@ -169,15 +156,30 @@ def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
     for _ in range(warmup):
         ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = replay_ms(torch, [lambda: ops.m3_rope_angles_cumsum(theta, phi0, phi=phi)] * steps)
     return ms, 2 * theta.numel() * 4 + phi0.numel() * 4
+
+
+def replay_ms(torch, launches):
+    """Average duration of the launches (callables, in order) on the GPU: they
+    are captured once in a HIP graph, so no host work sits between kernels,
+    and the graph is replayed between two HIP events on the replay stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for launch in launches:
+                launch()
+        g.replay()  # untimed first replay
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / len(launches)
 
 
 def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
@@ -205,14 +207,8 @@ def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
     for t in range(warmup):
         step(t)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        step(warmup + i)
-    end.record()
-    torch.cuda.synchronize()
-    per_step = start.elapsed_time(end) / steps  # back-to-back launches: the launch duration
+    # the whole sequence of steps (each with its own token's inputs) is one graph
+    per_step = replay_ms(torch, [(lambda t=t: step(t)) for t in range(warmup, warmup + steps)])
     ok = bool(torch.isfinite(h).all())
     return per_step, per_step, ok
 

@@ -253,17 +253,18 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 
   // Every wave issues the same loads every chunk (chunks past the end read
   // zeros): with no load behind a branch the wait counters stay exact.
-  auto issue_bcx = [&](int c, u32x4 (&dst)[UPH], auto HALF) __attribute__((always_inline)) {
+  auto load_piece = [&](int c, int s, auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     const uint32_t row = static_cast<uint32_t>(((c * Q + ptok) * H + hh) * R + prank);
+    const Piece pc = Lt::piece(h, s);
+    const int D = pc.kind == 2 ? P : N;
+    const int col = 32 * pc.kb + 8 * g;
+    const uint32_t off = (pc.kind >= 0 && col < D) ? (row * D + col) * 2u : kBad;
+    return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
+  };
+  auto issue_bcx = [&](int c, u32x4 (&dst)[UPH], auto HALF) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < UPH; ++s) {
-      const Piece pc = Lt::piece(h, s);
-      const int D = pc.kind == 2 ? P : N;
-      const int col = 32 * pc.kb + 8 * g;
-      const uint32_t off = (pc.kind >= 0 && col < D) ? (row * D + col) * 2u : kBad;
-      dst[s] = bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
-    }
+    for (int s = 0; s < UPH; ++s) dst[s] = load_piece(c, s, HALF);
   };
   auto issue_small = [&](int c, int set) __attribute__((always_inline)) {
     // Delta and lambda feed only the decay scan of wave 0.  The other waves
@@ -343,8 +344,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     }
   };
-  // stage this wave's pieces of chunk c into operand slot c%2
-  auto build_slot = [&](int c, const u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
+  // stage this wave's pieces of chunk c into operand slot c%2; each register
+  // is refilled with the same piece of chunk c+2 as soon as it is consumed,
+  // which spreads the load issue over the staging work
+  auto build_slot = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     const int s2 = c & 1;
     const float* S = sc(c % 3);
@@ -359,13 +362,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 #pragma unroll
     for (int s = 0; s < UPH; ++s) {
       const Piece pc = Lt::piece(h, s);
-      if (pc.kind < 0) continue;
+      if (pc.kind < 0) {  // padding slot of the smaller half: keep the load count uniform
+        src[s] = load_piece(c + 2, s, HALF);
+        continue;
+      }
       const u32x4 v = src[s];
       const int col = 32 * pc.kb + 8 * g;
       if (pc.kind == 2) {
         const bf16x8 a = as_bf16x8(v);
         if (2 * pc.kb < NPT) xt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
         if (2 * pc.kb + 1 < NPT) xt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
+        src[s] = load_piece(c + 2, s, HALF);
         continue;
       }
       u32x4 o = v;
@@ -394,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if (2 * pc.kb < NTH) bwt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
         if (2 * pc.kb + 1 < NTH) bwt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
       }
+      src[s] = load_piece(c + 2, s, HALF);
     }
   };
   // ================================================================ compute state
@@ -628,8 +636,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     __syncthreads();  // angle carry, raw theta(0) visible
     scan_angles(0);
     __syncthreads();  // SC(0), Phi(0) visible
-    build_slot(0, raw[0], HALF);
-    issue_bcx(2, raw[0], HALF);
+    build_slot(0, raw[0], HALF);  // and issues chunk 2 into raw[0]
     stage_small(1, 1);
     issue_small(3, 1);
     __syncthreads();  // slot 0, raw theta(1) visible
@@ -645,8 +652,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // scan the angles of chunk k+2, products, y and state of chunk k, then the
   // Gram tiles of chunk k+1.
   auto chunk = [&](int k, u32x4 (&bcx)[UPH], int sset, auto HALF) __attribute__((always_inline)) {
-    build_slot(k + 1, bcx, HALF);
-    issue_bcx(k + 3, bcx, HALF);  // registers free again: refill before the y stores queue up
+    build_slot(k + 1, bcx, HALF);  // and issues chunk k+3 into bcx
     stage_small(k + 2, sset);
     issue_small(k + 4, sset);
     if constexpr (!kEarly) gram_tiles(k);
