@@ -160,10 +160,15 @@ def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
     return ms, 2 * theta.numel() * 4 + phi0.numel() * 4
 
 
+WARM_S = 0.06  # sustained untimed work before timing: the clocks ramp for ~25 ms
+
+
 def replay_ms(torch, launches):
     """Average duration of the launches (callables, in order) on the GPU: they
     are captured once in a HIP graph, so no host work sits between kernels,
-    and the graph is replayed between two HIP events on the replay stream."""
+    replayed untimed until WARM_S of sustained work has passed (the GPU clocks
+    ramp up under load), then replayed once between two HIP events on the
+    replay stream."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
@@ -171,8 +176,12 @@ def replay_ms(torch, launches):
         with torch.cuda.graph(g, stream=s):
             for launch in launches:
                 launch()
-        g.replay()  # untimed first replay
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:  # untimed replays
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARM_S:
+                break
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(s)

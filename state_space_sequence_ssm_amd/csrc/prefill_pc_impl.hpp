@@ -124,7 +124,10 @@ struct PcLayout {
   static constexpr int NPT = P / 16;          // p tiles
   static constexpr int PKB = (P + 31) / 32;   // k blocks over p (X pieces)
   static constexpr int UPT = (NPT + kPGroups - 1) / kPGroups;  // p tiles per wave
-  static constexpr int PN = NK + 8;           // bf16 pitch of B/C rows (16-byte pad)
+  // bf16 pitch of B/C rows: NK + 4 puts a row 2 (mod 32) dwords after the
+  // previous one, so the 16 rows of an 8-byte-per-lane fragment read fall on
+  // 16 distinct bank pairs (rows are then only 8-byte aligned)
+  static constexpr int PN = NK + 4;
   static constexpr int NG = N / 8;            // float4 groups of angles per token
   static constexpr int TSL = (NG + kWaves - 1) / kWaves;  // angle groups per lane (Q = 64)
   static constexpr int PH = N / 2 + 4;        // padded angle-table row (spreads banks)
@@ -392,7 +395,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
         }
       }
-      *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + prow * PN + col) = o;
+      u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + prow * PN + col);
+      dstRow[0] = u32x2{o[0], o[1]};
+      dstRow[1] = u32x2{o[2], o[3]};
       if (pc.kind == 0) {
         f32x4 wj;  // w of the rows 16 quad + 4g + jj this lane holds after the transpose
 #pragma unroll
