@@ -265,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const uint32_t off = (pc.kind >= 0 && col < D) ? (row * D + col) * 2u : kBad;
     return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
   };
+  constexpr bool kLateRefill = ROPE && LGR == 0;
   auto issue_bcx = [&](int c, u32x4 (&dst)[UPH], auto HALF) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < UPH; ++s) dst[s] = load_piece(c, s, HALF);
@@ -349,9 +350,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   };
   // stage this wave's pieces of chunk c into operand slot c%2; each register
   // is refilled with the same piece of chunk c+2 as soon as it is consumed,
-  // which spreads the load issue over the staging work
+  // which spreads the load issue over the staging work.  With RoPE at R = 1
+  // the upper waves refill in the second phase instead (measured faster
+  // there: their loads then do not queue behind the lower waves').
   auto build_slot = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
+    constexpr bool kRefill = !(kLateRefill && h == 1);
     const int s2 = c & 1;
     const float* S = sc(c % 3);
     uint16_t* sB = slotB(s2);
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     for (int s = 0; s < UPH; ++s) {
       const Piece pc = Lt::piece(h, s);
       if (pc.kind < 0) {  // padding slot of the smaller half: keep the load count uniform
-        src[s] = load_piece(c + 2, s, HALF);
+        if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
         continue;
       }
       const u32x4 v = src[s];
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         const bf16x8 a = as_bf16x8(v);
         if (2 * pc.kb < NPT) xt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
         if (2 * pc.kb + 1 < NPT) xt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
-        src[s] = load_piece(c + 2, s, HALF);
+        if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
         continue;
       }
       u32x4 o = v;
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if (2 * pc.kb < NTH) bwt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
         if (2 * pc.kb + 1 < NTH) bwt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
       }
-      src[s] = load_piece(c + 2, s, HALF);
+      if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
     }
   };
   // ================================================================ compute state
@@ -642,6 +646,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     scan_angles(0);
     __syncthreads();  // SC(0), Phi(0) visible
     build_slot(0, raw[0], HALF);  // and issues chunk 2 into raw[0]
+    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(2, raw[0], HALF);
     stage_small(1, 1);
     issue_small(3, 1);
     __syncthreads();  // slot 0, raw theta(1) visible
@@ -665,6 +670,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     __syncthreads();  // S(k), readout partials, slot k+1, raw theta(k+2) visible
     scan_angles(k + 2);
     compute_rest(k, HALF);
+    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 3, bcx, HALF);
     if constexpr (kEarly) gram_tiles(k + 1);  // overlaps the tail of chunk k
     __syncthreads();  // S(k+1), SC(k+2), Phi(k+2) visible; slot k free
   };
