@@ -134,9 +134,13 @@ def time_prefill(torch, ops, inp, steps, warmup):
     N = inp["B"].shape[-1]
     hf = torch.empty((Bt, H, N, P), device="cuda", dtype=torch.float32)
 
+    # the optional workspace (sequence split when the units leave compute units idle)
+    nws = ops.prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=inp["x"].dtype, rope=inp["theta"] is not None)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else False
+
     def run():
         ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], inp["theta"],
-                           y=y, h_final=hf)
+                           y=y, h_final=hf, workspace=ws)
 
     for _ in range(max(warmup, 1)):
         run()

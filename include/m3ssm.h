@@ -28,8 +28,9 @@
  * xprev_out, h0, h_final, h, Bprev_rot, Bprev_rot_out must be 16-byte
  * aligned; theta / phi pointers must be 16-byte aligned.
  * All pointers are device pointers (hipMalloc'd or equivalent) unless noted.
- * The caller owns every buffer; the library allocates nothing and keeps no
- * state between calls, so calls on different streams are independent.
+ * The caller owns every buffer, including the optional prefill workspace; the
+ * library allocates nothing and keeps no state between calls, so calls on
+ * different streams are independent (given separate workspaces).
  * `stream` is a hipStream_t (NULL = the null stream).  All calls are
  * asynchronous with respect to the host; results are visible after the
  * stream is synchronised.  Results are deterministic (no atomics).
@@ -90,6 +91,9 @@ typedef enum m3_dtype {
  * one chunk tile always holds 64 (token, rank) rows).
  * Outputs must not alias inputs.  Passing the carry-out of one call as the
  * carry-in of the next continues the sequence exactly.
+ * workspace: optional, see m3_ssm_prefill_workspace_size; a non-NULL
+ * workspace smaller than that size (or not 256-byte aligned) is
+ * M3_ERR_INVALID_ARG.
  */
 typedef struct m3_prefill_args {
   int32_t Bt, L, H, P, N, R, chunk;
@@ -110,12 +114,28 @@ typedef struct m3_prefill_args {
   float* Bprev_rot_out;
   void* xprev_out;
   float* phi_out;
+  void* workspace;        /* device scratch of workspace_bytes (256-byte aligned), or NULL */
+  size_t workspace_bytes;
 } m3_prefill_args;
 
 int m3_ssm_prefill(const m3_prefill_args* args, void* stream);
 
-/* Device scratch needed by m3_ssm_prefill: always 0 (the fused kernel keeps
- * chunk states on chip).  Kept so callers can size a workspace generically. */
+/* Device scratch that lets m3_ssm_prefill use more of the GPU; 0 when it
+ * would not (fp32 inputs, or at least half as many (batch, head) units as the
+ * device has compute units, or sequences shorter than 8 chunks).
+ *   With fewer units than that, a bf16 prefill given a workspace of this size
+ * first walks the first half of every sequence for its state only (the
+ * chunked evaluation of "La dualita: Mamba-2 e Mamba-3", sec. "Perche
+ * conviene", needs only the state to hand over), then computes both halves at
+ * once, the second one starting from that state -- the same carry that
+ * continues a sequence across calls.  Results agree with the unsplit call to
+ * rounding (the handed-over carry is exact fp32, where the unsplit walk
+ * passes the pending term through bf16).  With workspace == NULL the call
+ * runs unsplit.
+ * The workspace holds the state and carry in the middle of each sequence
+ * (Bt*H*(4NP + 4RN + 2RP + 2N) bytes, rounded); it is overwritten by every
+ * call, so concurrent calls need their own.  Depends only on the shape
+ * fields (and the current device), not on pointers. */
 size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args);
 
 /*

@@ -18,6 +18,55 @@ bool al4(const void* p) { return p == nullptr || aligned(p, 4); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? M3_OK : M3_ERR_HIP; }
 
+// Compute units of the current device (cached per device; 256, the MI355X
+// count, when no device can be queried).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = 256;
+    }
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// Sequence split of the bf16 prefill: with fewer (batch, head) units than
+// half the compute units, a state-only walk over the first half of every
+// sequence hands its end state to the second half, and both halves then run
+// at once (twice the workgroups).  Workspace: the state and carry in the
+// middle of each sequence.
+constexpr int kMinSegChunks = 4;  // both halves keep at least this many chunks
+struct SplitPlan {
+  bool on = false;
+  int segLen = 0;
+  size_t oH = 0, oB = 0, oX = 0, oPhi = 0, bytes = 0;
+};
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+SplitPlan split_plan(const m3_prefill_args* a) {
+  SplitPlan s;
+  if (a->in_dtype != M3_BF16 || a->R < 1 || a->R > 8) return s;
+  const int Q = 64 / a->R;
+  const long units = long(a->Bt) * a->H;
+  if (2 * units > device_cus() || a->L < 2 * kMinSegChunks * Q) return s;
+  const size_t u = size_t(units);
+  s.on = true;
+  s.segLen = (((a->L + 1) / 2 + Q - 1) / Q) * Q;
+  s.oH = 0;
+  s.oB = up256(s.oH + u * a->N * a->P * 4);
+  s.oX = up256(s.oB + u * a->R * a->N * 4);
+  s.oPhi = up256(s.oX + u * a->R * a->P * 2);
+  s.bytes = up256(s.oPhi + (a->theta != nullptr ? u * (a->N / 2) * 4 : 0));
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -35,8 +84,9 @@ const char* m3_status_string(int status) {
 const char* m3_version(void) { return "0.1.0"; }
 
 size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args) {
-  (void)args;
-  return 0;
+  if (args == nullptr) return 0;
+  const SplitPlan s = split_plan(args);
+  return s.on ? s.bytes : 0;
 }
 
 int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
@@ -80,8 +130,40 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   p.h0 = a->h0; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev; p.phi0 = a->phi0;
   p.y = a->y; p.h_final = a->h_final; p.Bprev_rot_out = a->Bprev_rot_out; p.xprev_out = a->xprev_out;
   p.phi_out = a->phi_out;
+  p.Lfull = a->L;
+  p.nseg = 1;
+  p.segLen = a->L;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(bf16 ? m3::launch_prefill_bf16(p, st) : m3::launch_prefill_f32(p, st));
+  if (!bf16) return hip_status(m3::launch_prefill_f32(p, st));
+
+  const SplitPlan sp = split_plan(a);
+  if (!sp.on || a->workspace == nullptr) return hip_status(m3::launch_prefill_bf16(p, false, st));
+  if (a->workspace_bytes < sp.bytes || !aligned(a->workspace, 256)) return M3_ERR_INVALID_ARG;
+  unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+  float* hMid = reinterpret_cast<float*>(ws + sp.oH);
+  float* bMid = reinterpret_cast<float*>(ws + sp.oB);
+  void* xMid = ws + sp.oX;
+  float* phiMid = a->theta != nullptr ? reinterpret_cast<float*>(ws + sp.oPhi) : nullptr;
+  // 1) state and carry after the first segLen tokens (carry-in of the call)
+  m3::PrefillParams pa = p;
+  pa.L = sp.segLen;
+  pa.segLen = sp.segLen;
+  pa.y = nullptr;
+  pa.h_final = hMid;
+  pa.Bprev_rot_out = bMid;
+  pa.xprev_out = xMid;
+  pa.phi_out = phiMid;
+  hipError_t e = m3::launch_prefill_bf16(pa, true, st);
+  if (e != hipSuccess) return hip_status(e);
+  // 2) both segments at once; the second starts from that carry
+  m3::PrefillParams pb = p;
+  pb.nseg = 2;
+  pb.segLen = sp.segLen;
+  pb.h_mid = hMid;
+  pb.Bprev_mid = bMid;
+  pb.xprev_mid = xMid;
+  pb.phi_mid = phiMid;
+  return hip_status(m3::launch_prefill_bf16(pb, false, st));
 }
 
 int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {

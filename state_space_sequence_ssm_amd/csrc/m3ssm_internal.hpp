@@ -43,6 +43,17 @@ struct PrefillParams {
   float* Bprev_rot_out;
   void* xprev_out;
   float* phi_out;
+  // Sequence segments (bf16 path).  Tokens of batch item b start at
+  // b * Lfull; this launch covers tokens [0, L) of each item, cut into nseg
+  // segments of segLen tokens (the last one takes the rest), one workgroup per
+  // (segment, batch, head).  Segment 0 takes the carry-in above; segment s > 0
+  // takes the *_mid carry (the state after the previous segment).  Only the
+  // last segment writes h_final and the carry-out.
+  int Lfull, nseg, segLen;
+  const float* h_mid;
+  const float* Bprev_mid;
+  const void* xprev_mid;
+  const float* phi_mid;
 };
 
 struct AnglesParams {
@@ -53,7 +64,8 @@ struct AnglesParams {
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
-hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t s);
+// state_only: the walk that produces the state and carry only (no y)
+hipError_t launch_prefill_bf16(const PrefillParams& p, bool state_only, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t s);
 hipError_t launch_angles(const AnglesParams& p, hipStream_t s);
 // LDS bytes the prefill kernel needs for (N, P, rope); 0 if not compiled.

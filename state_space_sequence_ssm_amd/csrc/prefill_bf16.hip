@@ -4,17 +4,17 @@
 
 namespace m3 {
 
-hipError_t launch_prefill_bf16_n16(const PrefillParams& p, hipStream_t s);
-hipError_t launch_prefill_bf16_n32(const PrefillParams& p, hipStream_t s);
-hipError_t launch_prefill_bf16_n64(const PrefillParams& p, hipStream_t s);
-hipError_t launch_prefill_bf16_n128(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_bf16_n16(const PrefillParams& p, bool state_only, hipStream_t s);
+hipError_t launch_prefill_bf16_n32(const PrefillParams& p, bool state_only, hipStream_t s);
+hipError_t launch_prefill_bf16_n64(const PrefillParams& p, bool state_only, hipStream_t s);
+hipError_t launch_prefill_bf16_n128(const PrefillParams& p, bool state_only, hipStream_t s);
 
-hipError_t launch_prefill_bf16(const PrefillParams& p, hipStream_t s) {
+hipError_t launch_prefill_bf16(const PrefillParams& p, bool state_only, hipStream_t s) {
   switch (p.N) {
-    case 16: return launch_prefill_bf16_n16(p, s);
-    case 32: return launch_prefill_bf16_n32(p, s);
-    case 64: return launch_prefill_bf16_n64(p, s);
-    case 128: return launch_prefill_bf16_n128(p, s);
+    case 16: return launch_prefill_bf16_n16(p, state_only, s);
+    case 32: return launch_prefill_bf16_n32(p, state_only, s);
+    case 64: return launch_prefill_bf16_n64(p, state_only, s);
+    case 128: return launch_prefill_bf16_n128(p, state_only, s);
   }
   return hipErrorInvalidValue;
 }

@@ -2,5 +2,7 @@
 #include "prefill_pc_launch.hpp"
 
 namespace m3 {
-hipError_t launch_prefill_bf16_n64(const PrefillParams& p, hipStream_t s) { return pc::launch_n<64>(p, s); }
+hipError_t launch_prefill_bf16_n64(const PrefillParams& p, bool state_only, hipStream_t s) {
+  return pc::launch_n<64>(p, state_only, s);
+}
 }  // namespace m3

@@ -189,7 +189,11 @@ struct PcLayout {
   static constexpr size_t kBytesRope = used(true) + (early_gram(true) ? kSBytes : 0);
 };
 
-template <int N, int P, int LGR, bool ROPE>
+// SO (state only): the walk keeps only what the state needs -- no C, no Gram
+// tiles, no readout, no y -- and ends with h_final and the carry-out.  It
+// produces the state in the middle of a sequence so that the second half can
+// run at the same time as the first.
+template <int N, int P, int LGR, bool ROPE, bool SO = false>
 __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   using Lt = PcLayout<N, P>;
   constexpr int R = 1 << LGR;
@@ -205,22 +209,35 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const int g = lane >> 4;
   const int quad = wave & 3;             // row tile (staging) and p-tile group (compute)
   const bool upper = (wave >> 2) & 1;    // piece half (staging) and i-tile pair (compute)
-  const int bh = blockIdx.x;
+  const int units = p.Bt * p.H;
+  const int seg = blockIdx.x / units;
+  const int bh = blockIdx.x % units;
   const int b = bh / p.H;
   const int hh = bh % p.H;
-  const int L = p.L, H = p.H;
+  const int H = p.H;
+  const int t0 = seg * p.segLen;                                // first token of the segment
+  const int L = seg == p.nseg - 1 ? p.L - t0 : p.segLen;       // tokens of the segment
+  const bool lastSeg = seg == p.nseg - 1;
   const float A2 = p.A[hh] * kLog2e;  // decays in log2 units
   const int nch = (L + Q - 1) / Q;
+  // carry-in of this segment
+  const float* cH0 = seg == 0 ? p.h0 : p.h_mid;
+  const float* cBprev = seg == 0 ? p.Bprev_rot : p.Bprev_mid;
+  const void* cXprev = seg == 0 ? p.xprev : p.xprev_mid;
+  const float* cPhi0 = seg == 0 ? p.phi0 : p.phi_mid;
 
-  // per-batch-item buffer resources (the range check zero-fills t >= L)
-  const size_t tokB = static_cast<size_t>(L) * H;  // (t, h) pairs per batch item
-  const rsrc_t rX = make_rsrc(static_cast<const bf16_t*>(p.x) + b * tokB * R * P, uint32_t(tokB * R * P * 2));
-  const rsrc_t rB = make_rsrc(static_cast<const bf16_t*>(p.B) + b * tokB * R * N, uint32_t(tokB * R * N * 2));
-  const rsrc_t rC = make_rsrc(static_cast<const bf16_t*>(p.C) + b * tokB * R * N, uint32_t(tokB * R * N * 2));
-  const rsrc_t rY = make_rsrc(static_cast<bf16_t*>(p.y) + b * tokB * R * P, uint32_t(tokB * R * P * 2));
-  const rsrc_t rDt = make_rsrc(p.dt + b * tokB, uint32_t(tokB * 4));
-  const rsrc_t rLam = make_rsrc(p.lam + b * tokB, uint32_t(tokB * 4));
-  const rsrc_t rTh = make_rsrc(ROPE ? p.theta + b * tokB * (N / 2) : p.dt, uint32_t(ROPE ? tokB * (N / 2) * 4 : 0));
+  // buffer resources spanning the segment of one batch item: the range check
+  // zero-fills tokens past its end (Delta = 0 there: the segment ends like a
+  // sequence, and its successor adds the pending term through its carry-in)
+  const size_t tok0 = static_cast<size_t>(b) * p.Lfull + t0;  // first (t, h) row / H
+  const size_t tokB = static_cast<size_t>(L) * H;              // (t, h) pairs of the segment
+  const rsrc_t rX = make_rsrc(static_cast<const bf16_t*>(p.x) + tok0 * H * R * P, uint32_t(tokB * R * P * 2));
+  const rsrc_t rB = make_rsrc(static_cast<const bf16_t*>(p.B) + tok0 * H * R * N, uint32_t(tokB * R * N * 2));
+  const rsrc_t rC = make_rsrc(static_cast<const bf16_t*>(p.C) + tok0 * H * R * N, uint32_t(SO ? 0 : tokB * R * N * 2));
+  const rsrc_t rY = make_rsrc(SO ? p.x : static_cast<bf16_t*>(p.y) + tok0 * H * R * P, uint32_t(SO ? 0 : tokB * R * P * 2));
+  const rsrc_t rDt = make_rsrc(p.dt + tok0 * H, uint32_t(tokB * 4));
+  const rsrc_t rLam = make_rsrc(p.lam + tok0 * H, uint32_t(tokB * 4));
+  const rsrc_t rTh = make_rsrc(ROPE ? p.theta + tok0 * H * (N / 2) : p.dt, uint32_t(ROPE ? tokB * (N / 2) * 4 : 0));
 
   auto slotC = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oC); };
   auto slotB = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oB); };
@@ -262,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const Piece pc = Lt::piece(h, s);
     const int D = pc.kind == 2 ? P : N;
     const int col = 32 * pc.kb + 8 * g;
-    const uint32_t off = (pc.kind >= 0 && col < D) ? (row * D + col) * 2u : kBad;
+    const uint32_t off = (pc.kind >= 0 && !(SO && pc.kind == 1) && col < D) ? (row * D + col) * 2u : kBad;
     return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
   };
   constexpr bool kLateRefill = ROPE && LGR == 0;
@@ -382,6 +399,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
         continue;
       }
+      if (SO && pc.kind == 1) {  // C is not needed for the state
+        if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
+        continue;
+      }
       u32x4 o = v;
       if constexpr (ROPE) {
         if (pc.kind == 0) {  // B comes first for a k-block; C reuses its sin/cos
@@ -399,9 +420,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
         }
       }
-      u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + prow * PN + col);
-      dstRow[0] = u32x2{o[0], o[1]};
-      dstRow[1] = u32x2{o[2], o[3]};
+      if constexpr (!SO) {  // row-major B and C feed the Gram tiles and the readout
+        u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + prow * PN + col);
+        dstRow[0] = u32x2{o[0], o[1]};
+        dstRow[1] = u32x2{o[2], o[3]};
+      }
       if (pc.kind == 0) {
         f32x4 wj;  // w of the rows 16 quad + 4g + jj this lane holds after the transpose
 #pragma unroll
@@ -465,6 +488,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     sSb(k)[tile_id(jt, it) * 64 + lane] = pack4(a);
   };
   auto gram_tiles = [&](int k) __attribute__((always_inline)) {
+    if constexpr (SO) return;
     using std::integral_constant;
     switch (wave) {
       case 0: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 0>{});
@@ -485,6 +509,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // With the n split, every wave covers all four i tiles over its n tiles and
   // hands the partner's two to LDS; otherwise it covers its own two over all n.
   auto readout = [&](int k, auto HALF) __attribute__((always_inline)) {
+    if constexpr (SO) return;
     constexpr int h = decltype(HALF)::value;
     constexpr int nb = kSplit && h ? NTW : 0;  // first kept n tile
     const uint16_t* sC = slotC(k & 1);
@@ -569,8 +594,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     };
     using std::integral_constant;
-    do_it(integral_constant<int, h == 0 ? 0 : 1>{}, integral_constant<int, 0>{});
-    do_it(integral_constant<int, h == 0 ? 3 : 2>{}, integral_constant<int, 1>{});
+    if constexpr (!SO) {
+      do_it(integral_constant<int, h == 0 ? 0 : 1>{}, integral_constant<int, 0>{});
+      do_it(integral_constant<int, h == 0 ? 3 : 2>{}, integral_constant<int, 1>{});
+    }
     // H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -594,9 +621,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   auto init_state = [&](auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     constexpr int nb = kSplit && h ? NTW : 0;
-    const size_t o0 = static_cast<size_t>(b) * L * H + hh;
+    const size_t o0 = tok0 * H + hh;
     const float coef = (1.f - p.lam[o0]) * p.dt[o0];
-    const bool hasCarry = p.Bprev_rot != nullptr && p.xprev != nullptr;
+    const bool hasCarry = cBprev != nullptr && cXprev != nullptr;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int pt = quad + kPGroups * u;
@@ -609,13 +636,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int n = 16 * nt + 4 * g + jj;
-            float v = p.h0 != nullptr ? p.h0[static_cast<size_t>(bh) * N * P + static_cast<size_t>(n) * P + pc] : 0.f;
+            float v = cH0 != nullptr ? cH0[static_cast<size_t>(bh) * N * P + static_cast<size_t>(n) * P + pc] : 0.f;
             if (hasCarry) {
               float uu = 0.f;
 #pragma unroll
               for (int rr = 0; rr < R; ++rr)
-                uu += p.Bprev_rot[(static_cast<size_t>(bh) * R + rr) * N + n] *
-                      bf16_to_f32(static_cast<const bf16_t*>(p.xprev)[(static_cast<size_t>(bh) * R + rr) * P + pc].bits);
+                uu += cBprev[(static_cast<size_t>(bh) * R + rr) * N + n] *
+                      bf16_to_f32(static_cast<const bf16_t*>(cXprev)[(static_cast<size_t>(bh) * R + rr) * P + pc].bits);
               v += coef * uu;
             }
             a[jj] = v;
@@ -631,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     init_state(std::integral_constant<int, 1>{});
   if constexpr (ROPE)
     for (int q = tid; q < N / 2; q += kThreads)
-      phiC[q] = p.phi0 != nullptr ? p.phi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
+      phiC[q] = cPhi0 != nullptr ? cPhi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
   // retire the prologue's state and carry loads here, so no wait on them is
   // left for the loop to repeat every chunk
   __builtin_amdgcn_s_waitcnt(0);
@@ -706,6 +733,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     }
   };
+  if (!lastSeg) return;
   if (p.h_final != nullptr) {
     if (!upper)
       write_state(std::integral_constant<int, 0>{});
@@ -722,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if (p.Bprev_rot_out != nullptr) {
       for (int e = tid; e < R * (N / 2); e += kThreads) {
         const int r = e / (N / 2), q = e % (N / 2);
-        const bf16_t* src = static_cast<const bf16_t*>(p.B) + ((static_cast<size_t>(b) * L + t) * H + hh) * R * N + r * N;
+        const bf16_t* src = static_cast<const bf16_t*>(p.B) + ((tok0 + t) * H + hh) * R * N + r * N;
         float a0 = bf16_to_f32(src[2 * q].bits), a1 = bf16_to_f32(src[2 * q + 1].bits);
         if constexpr (ROPE) {
           // Phi_{L-1} is the final angle carry (reduced modulo 2 pi)
@@ -740,7 +768,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if (p.xprev_out != nullptr)
       for (int e = tid; e < R * P; e += kThreads)
         static_cast<bf16_t*>(p.xprev_out)[static_cast<size_t>(bh) * R * P + e] =
-            static_cast<const bf16_t*>(p.x)[((static_cast<size_t>(b) * L + t) * H + hh) * R * P + e];
+            static_cast<const bf16_t*>(p.x)[((tok0 + t) * H + hh) * R * P + e];
   }
 }
 

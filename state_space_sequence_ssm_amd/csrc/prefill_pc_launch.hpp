@@ -6,46 +6,52 @@
 namespace m3 {
 namespace pc {
 
-template <int N, int P, int LGR, bool ROPE>
+// one workgroup per (segment, batch, head)
+template <int N, int P, int LGR, bool ROPE, bool SO>
 hipError_t launch(const PrefillParams& p, hipStream_t s) {
   using Lt = PcLayout<N, P>;
   const size_t lds = ROPE ? Lt::kBytesRope : Lt::kBytesReal;
   static size_t attr_bytes = 64 * 1024;  // dynamic LDS this kernel has been cleared for
   if (lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<N, P, LGR, ROPE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<N, P, LGR, ROPE, SO>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
-  hipLaunchKernelGGL((prefill_pc_kernel<N, P, LGR, ROPE>), dim3(p.Bt * p.H), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((prefill_pc_kernel<N, P, LGR, ROPE, SO>), dim3(p.Bt * p.H * p.nseg), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 
-template <int N, int P, bool ROPE>
+template <int N, int P, bool ROPE, bool SO>
 hipError_t launch_r(const PrefillParams& p, hipStream_t s) {
   switch (p.log2R) {
-    case 0: return launch<N, P, 0, ROPE>(p, s);
-    case 1: return launch<N, P, 1, ROPE>(p, s);
-    case 2: return launch<N, P, 2, ROPE>(p, s);
-    case 3: return launch<N, P, 3, ROPE>(p, s);
+    case 0: return launch<N, P, 0, ROPE, SO>(p, s);
+    case 1: return launch<N, P, 1, ROPE, SO>(p, s);
+    case 2: return launch<N, P, 2, ROPE, SO>(p, s);
+    case 3: return launch<N, P, 3, ROPE, SO>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int N, int P>
+template <int N, int P, bool SO>
 hipError_t launch_rr(const PrefillParams& p, hipStream_t s) {
-  return p.theta != nullptr ? launch_r<N, P, true>(p, s) : launch_r<N, P, false>(p, s);
+  return p.theta != nullptr ? launch_r<N, P, true, SO>(p, s) : launch_r<N, P, false, SO>(p, s);
+}
+
+template <int N, bool SO>
+hipError_t launch_p(const PrefillParams& p, hipStream_t s) {
+  switch (p.P) {
+    case 16: return launch_rr<N, 16, SO>(p, s);
+    case 32: return launch_rr<N, 32, SO>(p, s);
+    case 64: return launch_rr<N, 64, SO>(p, s);
+    case 128: return launch_rr<N, 128, SO>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int N>
-hipError_t launch_n(const PrefillParams& p, hipStream_t s) {
-  switch (p.P) {
-    case 16: return launch_rr<N, 16>(p, s);
-    case 32: return launch_rr<N, 32>(p, s);
-    case 64: return launch_rr<N, 64>(p, s);
-    case 128: return launch_rr<N, 128>(p, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_n(const PrefillParams& p, bool state_only, hipStream_t s) {
+  return state_only ? launch_p<N, true>(p, s) : launch_p<N, false>(p, s);
 }
 
 }  // namespace pc

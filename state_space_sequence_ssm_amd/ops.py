@@ -49,12 +49,15 @@ def _stream(stream) -> int:
 
 def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
                    *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
-                   want_state=True, want_carry=False, chunk=0, stream=None):
+                   want_state=True, want_carry=False, chunk=0, workspace=None, stream=None):
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
     dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None; optional
     carry-in h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
-    Output tensors are allocated when not given.  Returns a dict with y and,
-    as requested, h_final and the carry-out (Bprev_rot, xprev, phi)."""
+    Output tensors are allocated when not given.  workspace: a uint8 device
+    tensor of at least prefill_workspace_bytes(...) bytes, None to allocate one
+    when the library asks for it, or False to run without (unsplit).  Returns
+    a dict with y and, as requested, h_final and the carry-out (Bprev_rot,
+    xprev, phi)."""
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
     f32 = torch.float32
@@ -88,10 +91,27 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a.Bprev_rot_out = _ptr(Bprev_rot_out, f32, (Bt, H, R, N), "Bprev_rot_out")
     a.xprev_out = _ptr(xprev_out, x.dtype, (Bt, H, R, P), "xprev_out")
     a.phi_out = _ptr(phi_out, f32, (Bt, H, N // 2), "phi_out")
-    rc = _lib.load().m3_ssm_prefill(ctypes.byref(a), _stream(stream))
+    lib = _lib.load()
+    if workspace is not False:
+        need = lib.m3_ssm_prefill_workspace_size(ctypes.byref(a))
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            a.workspace = _ptr(workspace, torch.uint8, None, "workspace")
+            a.workspace_bytes = workspace.numel()
+    rc = lib.m3_ssm_prefill(ctypes.byref(a), _stream(stream))
     if rc != _lib.M3_OK:
         raise M3Error(rc, "m3_ssm_prefill")
     return dict(y=y, h=h_final, Bprev_rot=Bprev_rot_out, xprev=xprev_out, phi=phi_out)
+
+
+def prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=torch.bfloat16, rope=False):
+    """Bytes of the optional prefill workspace for this shape (0: none used)."""
+    a = _lib.PrefillArgs()
+    a.Bt, a.L, a.H, a.P, a.N, a.R = Bt, L, H, P, N, R
+    a.in_dtype = _lib.M3_BF16 if dtype == torch.bfloat16 else _lib.M3_F32
+    a.theta = 1 if rope else None  # only NULL-ness is read
+    return _lib.load().m3_ssm_prefill_workspace_size(ctypes.byref(a))
 
 
 def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None, *, y=None, stream=None):

@@ -73,6 +73,45 @@ def test_prefill_validation():
     assert lib.m3_ssm_prefill_workspace_size(ctypes.byref(_good_prefill())) == 0
 
 
+def _up256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("Bt,H,L,N,P,R,rope,split", [
+    (1, 32, 4096, 64, 64, 4, True, True),     # 32 units: the sequences are split in two
+    (4, 32, 8192, 64, 64, 4, True, True),     # 128 units fill 256 compute units when split
+    (8, 32, 4096, 128, 64, 1, False, False),  # 256 units already fill the device
+    (1, 2, 511, 64, 64, 1, False, False),     # shorter than 8 chunks
+    (1, 2, 512, 64, 64, 1, False, True),
+    (1, 2, 128, 32, 16, 4, False, True),      # chunks of 16 tokens at R = 4
+])
+def test_prefill_workspace_size(Bt, H, L, N, P, R, rope, split):
+    """The split needs the state and carry in the middle of each sequence; the
+    size rule assumes the 256 compute units of MI355X (the host here has no GPU)."""
+    lib = _lib.load()
+    a = _good_prefill()
+    a.Bt, a.H, a.L, a.N, a.P, a.R = Bt, H, L, N, P, R
+    a.theta = 0x30000000 if rope else None
+    got = lib.m3_ssm_prefill_workspace_size(ctypes.byref(a))
+    u = Bt * H
+    want = _up256(u * N * P * 4) + _up256(u * R * N * 4) + _up256(u * R * P * 2) + _up256(u * (N // 2) * 4 if rope else 0)
+    assert got == (want if split else 0)
+    a.in_dtype = _lib.M3_F32
+    assert lib.m3_ssm_prefill_workspace_size(ctypes.byref(a)) == 0  # fp32 runs unsplit
+    assert lib.m3_ssm_prefill_workspace_size(None) == 0
+
+
+def test_prefill_workspace_validation():
+    a = _good_prefill()
+    a.Bt, a.H, a.L, a.R = 1, 2, 1024, 1
+    need = _lib.load().m3_ssm_prefill_workspace_size(ctypes.byref(a))
+    assert need > 0
+    a.workspace, a.workspace_bytes = 0x40000000, need - 1  # too small
+    assert _rc_prefill(a) == _lib.M3_ERR_INVALID_ARG
+    a.workspace, a.workspace_bytes = 0x40000010, need  # not 256-byte aligned
+    assert _rc_prefill(a) == _lib.M3_ERR_INVALID_ARG
+
+
 def test_decode_validation():
     lib = _lib.load()
     assert lib.m3_ssm_decode_step(None, None) == _lib.M3_ERR_INVALID_ARG

@@ -125,6 +125,44 @@ def test_prefill_config_full_size(ops, cfg):
         assert np.max(angle_diff(host(out["phi"][sb][:, sh]), ref["phi"])) <= 1e-3
 
 
+# ----------------------------------------------------------------- sequence split
+SPLIT = [
+    # Bt, L, H, P, N, R, rope, carry  (few units: the library halves each sequence)
+    (1, 600, 2, 64, 64, 1, True, True),
+    (2, 257, 3, 64, 64, 4, True, True),
+    (1, 700, 1, 64, 128, 1, False, False),
+    (1, 200, 2, 32, 32, 8, True, True),
+    (1, 1000, 1, 128, 128, 1, False, True),
+    (3, 300, 2, 16, 16, 2, True, False),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_split(ops, case):
+    """The split path (state-only walk of the first half, then both halves at
+    once) against the oracle and against the unsplit call."""
+    Bt, L, H, P, N, R, rope, carry = case
+    s = Shape(Bt, L, H, P, N, R, "bf16", rope)
+    assert ops.prefill_workspace_bytes(Bt, L, H, P, N, R, rope=rope) > 0, "case must take the split path"
+    _say("prefill split", case)
+    d = make_inputs(s, 3000 + L + N, h0=carry, carry=carry)
+    dd = to_device(d, s)
+    out = _run_prefill(ops, dd, s, carry=True)
+    one = _run_prefill(ops, dd, s, carry=True, workspace=False)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(d)
+    ey = orc.rel_l2(host(out["y"]), ref["y"])
+    eh = orc.rel_l2(host(out["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert orc.rel_l2(host(out["y"]), host(one["y"])) <= 5e-3
+    assert orc.rel_l2(host(out["h"]), host(one["h"])) <= 5e-3
+    assert orc.rel_l2(host(out["Bprev_rot"]), ref["Bprev_rot"]) <= 1e-5
+    assert np.array_equal(host(out["xprev"]), ref["xprev"])
+    if rope:
+        assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-4
+
+
 # ----------------------------------------------------------------- carry / split-resume
 @pytest.mark.parametrize("R,rope", [(1, False), (4, True)])
 def test_split_resume(ops, R, rope):
