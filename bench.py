@@ -60,9 +60,17 @@ def ANGLES_GRID(Bt, H, J):
     return Bt * ((H * J // 4 + 7) // 8) * 256
 
 
-def prefill_kernel_name(Bt, L, H, P, N, R, rope):
+def prefill_kernel_name(Bt, L, H, P, N, R, rope, state_only=False):
     """Kernel symbol (as rocprofv3 prints it) that runs a bf16 prefill shape."""
-    return f"m3::pc::prefill_pc_kernel<{N}, {P}, {int(math.log2(R))}, {'true' if rope else 'false'}>"
+    return (f"m3::pc::prefill_pc_kernel<{N}, {P}, {int(math.log2(R))}, {'true' if rope else 'false'}, "
+            f"{'true' if state_only else 'false'}>")
+
+
+def prefill_split(Bt, L, H, P, N, R, rope, cus=256):
+    """Whether the library splits the sequences of this bf16 shape in two (the
+    rule of m3_ssm_prefill_workspace_size): fewer than half as many units as
+    compute units and at least 8 chunks."""
+    return 2 * Bt * H <= cus and L >= 8 * (64 // R)
 
 
 def decode_kernel_name(Bt, H, P, N, R):
@@ -70,10 +78,17 @@ def decode_kernel_name(Bt, H, P, N, R):
 
 
 def unit_kernels():
-    """(unit key, kernel symbol, launch grid in threads) of every timed launch."""
+    """(unit key, kernel symbol, launch grid in threads) of every timed launch;
+    a split prefill is two launches of one unit (state-only walk, then both
+    halves)."""
     out = []
-    for name, (Bt, L, H, P, N, R, rope) in prefill_shapes().items():
-        out.append(("prefill_" + name, prefill_kernel_name(Bt, L, H, P, N, R, rope), Bt * H * 512))
+    for name, shp in prefill_shapes().items():
+        Bt, L, H, P, N, R, rope = shp
+        if prefill_split(*shp):
+            out.append(("prefill_" + name, prefill_kernel_name(*shp, state_only=True), Bt * H * 512))
+            out.append(("prefill_" + name, prefill_kernel_name(*shp), 2 * Bt * H * 512))
+        else:
+            out.append(("prefill_" + name, prefill_kernel_name(*shp), Bt * H * 512))
     Bt, H, P, N, R = DECODE_SHAPE
     out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
@@ -371,10 +386,16 @@ def report_pmc(fetch_prefix, write_prefix):
             continue
         f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)
         tot = f_avg * sf + w_avg * sw
-        units[unit] = {"bytes_per_launch": round(tot), "fetch_bytes": round(f_avg * sf),
-                       "write_bytes": round(w_avg * sw)}
+        e = units.setdefault(unit, {"bytes_per_launch": 0, "fetch_bytes": 0, "write_bytes": 0})
+        e["bytes_per_launch"] += round(tot)  # per call of the entry point (all its launches)
+        e["fetch_bytes"] += round(f_avg * sf)
+        e["write_bytes"] += round(w_avg * sw)
         lines.append(f"| {unit} | `{k}` | {len(fv)} | {f_avg:.4g} | {w_avg:.4g} | {tot:.4g} | {algo[unit]:.4g} "
                      f"| {tot / algo[unit]:.3f} |")
+    lines += ["", "Per call of the entry point (a split prefill is two launches):", "",
+              "| unit | HBM bytes per call | algorithmic bytes | ratio |", "|---|---|---|---|"]
+    for unit, e in units.items():
+        lines.append(f"| {unit} | {e['bytes_per_launch']:.4g} | {algo[unit]:.4g} | {e['bytes_per_launch'] / algo[unit]:.3f} |")
     lines += ["", "traffic-json: " + json.dumps({"source_hash": kernel_source_hash(), "units": units,
                                                  "fetch_scale": sf, "write_scale": sw})]
     print("\n".join(lines))
@@ -496,6 +517,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": head["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": head["hbm_frac"], "traffic": tr,
                            "kernel": prefill_kernel_name(*prefill_shapes()["siso_real"]),
+                           "split": prefill_split(*prefill_shapes()["siso_real"]),
                            "algorithmic_bytes_per_launch": head["bytes"],
                            "mfma_tflops": head["tflops"], "mfma_frac": head["mfma_frac"]}
     elif "decode" in results:
