@@ -15,30 +15,32 @@
 //   H'_{-1} = h0 + (1 - lambda_0) Delta_0 Btil_{-1} x_{-1}^T, h_final = H' at the end.
 //
 // MI355X design.  One 512-thread workgroup (8 wave64, two per SIMD) owns one
-// (batch, head) and walks its chunks of 64 (token, rank) rows with the N x P
-// state in MFMA accumulators.  Every wave has two jobs per chunk, and one
-// workgroup barrier per chunk hands a double-buffered LDS operand slot over:
-//   * staging (for chunk k+1 into slot (k+1)%2): wave w owns rows 16(w&3)..+15
-//     and half of their 16-byte pieces.  Its loads were issued two chunks ahead
-//     into registers, using buffer resources that span one batch item (the
-//     hardware range check zero-fills the ragged tail, so every wave issues the
-//     same loads every chunk and the wait counters stay exact).  B and C are
+// (segment, batch, head) and walks its chunks of 64 (token, rank) rows with the
+// N x P state in MFMA accumulators.  Wave w has a row tile / p-tile group
+// quad = w & 3 and a half upper = w >> 2.  Two workgroup barriers per chunk hand
+// a double-buffered LDS operand slot over:
+//   * phase A -- staging of chunk k+1 into slot (k+1)%2: wave w owns rows
+//     16 quad..+15 and half of their 16-byte pieces, loaded one chunk ahead into
+//     registers through buffer resources that span the segment of one batch
+//     item (the range check zero-fills the ragged tail, so every wave issues the
+//     same loads every chunk and the wait counters stay static).  B and C are
 //     rotated pairwise in fp32 (hardware sin/cos of the cumulative angle),
 //     rounded to bf16 and stored row-major; B (scaled by w_j = exp(Lam_e -
 //     Lam_j) delta_j) and X are transposed by MFMA products against an identity
 //     operand: the 16x16 fp32 result of A x I holds per lane four consecutive
 //     rows of one column, exactly the k-contiguous operand the token
-//     contractions need, and it is stored to LDS in lane-linear order (no
-//     bank-conflicted transposes).  The decay scan (log2 units, one wave64 DPP
-//     scan) and the angle scan (DPP segments of Q lanes, carry across chunks)
-//     of chunk k+2 run here too.
-//   * compute (chunk k from slot k%2): wave w owns p tiles (w&3) + 4u and the i
-//     tiles {0,3} (w < 4) or {1,2} (five Gram tiles each).  It computes
-//     G^T = B C^T on its causal tiles, masks it in registers (one exp2 per
-//     element, no comparisons off the diagonal) and feeds it straight into
-//     Y^T += X^T S^T, reads the previous state out of its own accumulators
-//     (Y^T += diag(exp Lam) H'^T C^T), stores y and updates
-//     H' = exp(Lam_e) H' + (w B)^T X (both waves of a p tile keep the state).
+//     contractions need, stored to LDS in lane order.  Wave 0 scans the decays
+//     of chunk k+2 (log2 units, one DPP wave scan); the raw angles of chunk k+2
+//     go to the angle table.  Every wave then computes the readout partials
+//     C^T H'_prev of chunk k from the state it keeps.
+//   * phase B -- products of chunk k from slot k%2: the angle scan of chunk k+2
+//     (DPP segments of Q lanes, carry across chunks), Y^T += X^T S^T for the
+//     wave's p tiles quad + 4u and i tiles {0,3} (lower) or {1,2} (upper) from
+//     the masked Gram tiles, the readout (own and partner's partials), the y
+//     stores and H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles (the two
+//     waves of a p tile split the n tiles when the readout exchange fits);
+//     then the 10 causal Gram tiles G^T = B C^T of chunk k+1, masked in
+//     registers (one exp2 per element, no comparisons off the diagonal).
 // MFMA k index: a k-block of 32 holds, for lane group g, indices {4g..4g+3} and
 // {16+4g..16+4g+3}, matching the accumulator rows of two adjacent 16-row tiles,
 // so accumulators feed the next product without a trip through LDS.
@@ -249,7 +251,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 
   // ================================================================ staging state
   // chunk c's pieces live in register set c % 2 (two chunks in flight)
-  u32x4 raw[2][UPH];
+  // Piece registers: loads run kSets chunks ahead.  One chunk (~3 us) covers
+  // the memory latency; two sets kept ~1300 cache-line requests in flight per
+  // CU and stalled the load issue of the later waves (measured 2-5% slower).
+  constexpr int kSets = 1;
+  u32x4 raw[kSets][UPH];
   // theta of one chunk as whole token rows: float4 unit e = token e / NG, group e % NG
   constexpr int kThUnits = Q * NG;
   constexpr int kThU = (kThUnits + kThreads - 1) / kThreads;
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     for (int s = 0; s < UPH; ++s) {
       const Piece pc = Lt::piece(h, s);
       if (pc.kind < 0) {  // padding slot of the smaller half: keep the load count uniform
-        if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
+        if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
       const u32x4 v = src[s];
@@ -396,11 +402,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         const bf16x8 a = as_bf16x8(v);
         if (2 * pc.kb < NPT) xt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
         if (2 * pc.kb + 1 < NPT) xt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
-        if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
+        if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
       if (SO && pc.kind == 1) {  // C is not needed for the state
-        if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
+        if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
       u32x4 o = v;
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if (2 * pc.kb < NTH) bwt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
         if (2 * pc.kb + 1 < NTH) bwt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
       }
-      if constexpr (kRefill) src[s] = load_piece(c + 2, s, HALF);
+      if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
     }
   };
   // ================================================================ compute state
@@ -666,14 +672,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     issue_small(0, 0);
     issue_small(1, 1);
     issue_bcx(0, raw[0], HALF);
-    issue_bcx(1, raw[1], HALF);
+    if constexpr (kSets == 2) issue_bcx(1, raw[kSets - 1], HALF);
     stage_small(0, 0);
     issue_small(2, 0);
     __syncthreads();  // angle carry, raw theta(0) visible
     scan_angles(0);
     __syncthreads();  // SC(0), Phi(0) visible
-    build_slot(0, raw[0], HALF);  // and issues chunk 2 into raw[0]
-    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(2, raw[0], HALF);
+    build_slot(0, raw[0], HALF);  // and issues chunk kSets into raw[0]
+    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(kSets, raw[0], HALF);
     stage_small(1, 1);
     issue_small(3, 1);
     __syncthreads();  // slot 0, raw theta(1) visible
@@ -681,15 +687,15 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if constexpr (kEarly) gram_tiles(0);
     __syncthreads();  // slot 0, S(0), SC(1), Phi(1) visible
   };
-  // chunk walk, unrolled by two so the register sets are indexed statically.
-  // Phase A: stage chunk k+1 (set `bcx` holds it), refill `bcx` with the loads
-  // of chunk k+3, scan the decays and store the raw angles of chunk k+2, issue
-  // the small loads of chunk k+4, and compute the readout partials of chunk k
+  // chunk walk, unrolled by two so the small-load register sets are indexed
+  // statically.  Phase A: stage chunk k+1 (`bcx` holds it), refill `bcx` with
+  // the loads of chunk k+2, scan the decays and store the raw angles of chunk
+  // k+2, issue the small loads of chunk k+4, and compute the readout partials of chunk k
   // (and its masked Gram tiles when they are not computed early); phase B:
   // scan the angles of chunk k+2, products, y and state of chunk k, then the
   // Gram tiles of chunk k+1.
   auto chunk = [&](int k, u32x4 (&bcx)[UPH], int sset, auto HALF) __attribute__((always_inline)) {
-    build_slot(k + 1, bcx, HALF);  // and issues chunk k+3 into bcx
+    build_slot(k + 1, bcx, HALF);  // and issues chunk k+1+kSets into bcx
     stage_small(k + 2, sset);
     issue_small(k + 4, sset);
     if constexpr (!kEarly) gram_tiles(k);
@@ -697,13 +703,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     __syncthreads();  // S(k), readout partials, slot k+1, raw theta(k+2) visible
     scan_angles(k + 2);
     compute_rest(k, HALF);
-    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 3, bcx, HALF);
+    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 1 + kSets, bcx, HALF);
     if constexpr (kEarly) gram_tiles(k + 1);  // overlaps the tail of chunk k
     __syncthreads();  // S(k+1), SC(k+2), Phi(k+2) visible; slot k free
   };
   auto walk = [&](auto HALF) __attribute__((always_inline)) {
     for (int k = 0; k < nch; k += 2) {
-      chunk(k, raw[1], 0, HALF);
+      chunk(k, raw[kSets - 1], 0, HALF);
       if (k + 1 < nch) chunk(k + 1, raw[0], 1, HALF);
     }
   };
