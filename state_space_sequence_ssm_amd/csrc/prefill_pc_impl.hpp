@@ -90,6 +90,9 @@ __device__ __forceinline__ f32x4 bloadf4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
 template <int CTRL, int ROWMASK, bool BOUND>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF, BOUND));
@@ -187,8 +190,14 @@ struct PcLayout {
   // second S buffer fits.
   static constexpr bool early_gram(bool rope) { return used(rope) + kSBytes <= kLdsMax; }
   static constexpr size_t oS2(bool rope) { return used(rope); }
-  static constexpr size_t kBytesReal = used(false) + (early_gram(false) ? kSBytes : 0);
-  static constexpr size_t kBytesRope = used(true) + (early_gram(true) ? kSBytes : 0);
+  static constexpr size_t used2(bool rope) { return used(rope) + (early_gram(rope) ? kSBytes : 0); }
+  // y of one chunk staged as [64][PY] bf16 so that it leaves in whole rows
+  static constexpr int PY = P + 8;
+  static constexpr size_t kYBytes = size_t(kRows) * PY * 2;
+  static constexpr bool stage_y(bool rope) { return used2(rope) + kYBytes <= kLdsMax; }
+  static constexpr size_t oY(bool rope) { return used2(rope); }
+  static constexpr size_t kBytesReal = used2(false) + (stage_y(false) ? kYBytes : 0);
+  static constexpr size_t kBytesRope = used2(true) + (stage_y(true) ? kYBytes : 0);
 };
 
 // SO (state only): the walk keeps only what the state needs -- no C, no Gram
@@ -247,6 +256,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   auto slotXT = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oXT); };
   auto sc = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oSC + s * Lt::kSC); };
   float* phiC = reinterpret_cast<float*>(smem + Lt::oPhiC);
+  // y leaves through LDS in whole rows at R = 1 (fewer, full-line stores:
+  // measured ~2% faster); at R > 1 the direct fragment stores are faster
+  constexpr bool kStageY = !SO && LGR == 0 && Lt::stage_y(ROPE);
+  u32x2* sY = reinterpret_cast<u32x2*>(smem + Lt::oY(ROPE));  // [64][PY/4] 8-byte units
   auto phiTab = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oPhi) + s * kRows * PH; };
 
   // ================================================================ staging state
@@ -595,7 +608,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           f32x4 zz = zown[u][idx];
           if constexpr (kSplit) zz += sEx[(((wave ^ 4) * UPT + u) * 2 + idx) * 64 + lane];
           const f32x4 yv = yacc[u] + decI * zz;
-          bstore8(rY, (yrow + 16 * pt + 4 * g) * 2u, pack4(yv));  // rows past L are dropped
+          if constexpr (kStageY)
+            sY[iRow * (Lt::PY / 4) + 4 * pt + g] = pack4(yv);
+          else
+            bstore8(rY, (yrow + 16 * pt + 4 * g) * 2u, pack4(yv));  // rows past L are dropped
         }
       }
     };
@@ -619,6 +635,26 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           acc[u][i] = a;
         }
       }
+    }
+  };
+
+  // staged y of chunk c -> HBM in whole rows, 16 bytes per lane; every thread
+  // issues the same number of stores (rows past the end, or c < 0, are dropped)
+  auto flush_y = [&](int c) __attribute__((always_inline)) {
+    constexpr int kUnits = kRows * P / 8;
+    constexpr int kIter = (kUnits + kThreads - 1) / kThreads;
+#pragma unroll
+    for (int it = 0; it < kIter; ++it) {
+      const int e = tid + it * kThreads;
+      const int eu = e < kUnits ? e : e - kUnits;
+      const int r = eu / (P / 8), c8 = eu % (P / 8);
+      const u32x2* src = sY + r * (Lt::PY / 4) + 2 * c8;
+      const u32x2 lo = src[0], hi = src[1];
+      const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+      const uint32_t off = (c >= 0 && e < kUnits)
+                               ? (static_cast<uint32_t>(((c * Q + (r >> LGR)) * H + hh) * R + (r & (R - 1))) * P + 8 * c8) * 2u
+                               : kBad;
+      bstore16(rY, off, v);
     }
   };
 
@@ -695,6 +731,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // scan the angles of chunk k+2, products, y and state of chunk k, then the
   // Gram tiles of chunk k+1.
   auto chunk = [&](int k, u32x4 (&bcx)[UPH], int sset, auto HALF) __attribute__((always_inline)) {
+    if constexpr (kStageY) flush_y(k - 1);
     build_slot(k + 1, bcx, HALF);  // and issues chunk k+1+kSets into bcx
     stage_small(k + 2, sset);
     issue_small(k + 4, sset);
@@ -722,6 +759,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   }
 
   // ================================================================ epilogue
+  if constexpr (kStageY) flush_y(nch - 1);  // the walk ended on a barrier
   // each wave writes its kept n tiles (both waves hold all of them without the split)
   auto write_state = [&](auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
