@@ -115,11 +115,17 @@ __device__ __forceinline__ float seg_scan(float v) {
   return v;
 }
 
-// 16-byte pieces of one 16-row tile: B and C k-blocks of 32 columns (kind 0, 1)
-// and X k-blocks (kind 2), split between the two waves that share the rows.
+// One staging load instruction: instruction i of the unit (16 rows x column
+// block cb of B, C or X: kind 0, 1, 2).  Lanes read whole 128-byte lines, 8
+// lanes per row (64-byte rows when the block is narrower), so each load asks
+// for full lines; half-line loads kept the vector L1 from accepting addresses
+// ~40% of the time.
 struct Piece {
-  int kind, kb;
+  int kind, cb, i;
 };
+// MFMA-layout staging (used at R > 1): a load is 16 rows x 32 columns (k block
+// cb) in the bf16 A-operand layout (lane (g, l16): row l16, 8 columns at 8 g),
+// which the identity transposes take straight from registers.
 
 template <int N, int P>
 struct PcLayout {
@@ -136,31 +142,68 @@ struct PcLayout {
   static constexpr int NG = N / 8;            // float4 groups of angles per token
   static constexpr int TSL = (NG + kWaves - 1) / kWaves;  // angle groups per lane (Q = 64)
   static constexpr int PH = N / 2 + 4;        // padded angle-table row (spreads banks)
-  // piece ownership: B/C k-block kb -> half (2 kb / NKB); X k-block -> alternate
-  static constexpr int bc_half(int kb) { return NKB == 1 ? 0 : (2 * kb) / NKB; }
-  static constexpr int x_half(int kb) { return PKB == 1 ? (NKB == 1 ? 1 : 0) : (kb & 1); }
+  // staging units: 16-byte chunks per row per load, loads per unit, blocks
+  static constexpr int cpr(int D) { return D >= 64 ? 8 : 4; }
+  static constexpr int ipu(int D) { return D >= 64 ? 2 : 1; }
+  static constexpr int ncb(int D) { return D >= 64 ? D / 64 : 1; }
+  static constexpr int NCBN = ncb(N), NCBP = ncb(P);
+  // unit ownership between the two waves of a row tile: B and C blocks by
+  // halves of n; X blocks alternate (all to the upper wave when B and C have a
+  // single block, all to the lower one when X has a single block)
+  static constexpr int bc_half(int cb) { return NCBN == 1 ? 0 : (2 * cb) / NCBN; }
+  static constexpr int x_half(int cb) { return NCBN == 1 ? 1 : (NCBP == 1 ? 0 : (cb & 1)); }
   static constexpr int count(int h) {
     int n = 0;
-    for (int kb = 0; kb < NKB; ++kb) n += bc_half(kb) == h ? 2 : 0;
-    for (int kb = 0; kb < PKB; ++kb) n += x_half(kb) == h ? 1 : 0;
+    for (int cb = 0; cb < NCBN; ++cb) n += bc_half(cb) == h ? 2 * ipu(N) : 0;
+    for (int cb = 0; cb < NCBP; ++cb) n += x_half(cb) == h ? ipu(P) : 0;
     return n;
   }
-  static constexpr int UPH = count(0) > count(1) ? count(0) : count(1);  // pieces per wave
-  static constexpr Piece piece(int h, int s) {
+  static constexpr int UPH_FL = count(0) > count(1) ? count(0) : count(1);  // loads per wave
+  // load s of half h; B(cb, i) directly precedes C(cb, i), which reuses its sin/cos
+  static constexpr Piece piece_fl(int h, int s) {
+    int n = 0;
+    for (int cb = 0; cb < NCBN; ++cb)
+      if (bc_half(cb) == h)
+        for (int i = 0; i < ipu(N); ++i) {
+          if (n == s) return Piece{0, cb, i};
+          if (n + 1 == s) return Piece{1, cb, i};
+          n += 2;
+        }
+    for (int cb = 0; cb < NCBP; ++cb)
+      if (x_half(cb) == h)
+        for (int i = 0; i < ipu(P); ++i) {
+          if (n == s) return Piece{2, cb, i};
+          n += 1;
+        }
+    return Piece{-1, 0, 0};
+  }
+  // MFMA-layout pieces: B/C k block kb -> half (2 kb / NKB); X k block -> alternate
+  static constexpr int mf_bc_half(int kb) { return NKB == 1 ? 0 : (2 * kb) / NKB; }
+  static constexpr int mf_x_half(int kb) { return PKB == 1 ? (NKB == 1 ? 1 : 0) : (kb & 1); }
+  static constexpr int mf_count(int h) {
+    int n = 0;
+    for (int kb = 0; kb < NKB; ++kb) n += mf_bc_half(kb) == h ? 2 : 0;
+    for (int kb = 0; kb < PKB; ++kb) n += mf_x_half(kb) == h ? 1 : 0;
+    return n;
+  }
+  static constexpr int UPH_MF = mf_count(0) > mf_count(1) ? mf_count(0) : mf_count(1);
+  static constexpr Piece piece_mf(int h, int s) {
     int n = 0;
     for (int kb = 0; kb < NKB; ++kb)
-      if (bc_half(kb) == h) {
-        if (n == s) return Piece{0, kb};
-        if (n + 1 == s) return Piece{1, kb};
+      if (mf_bc_half(kb) == h) {
+        if (n == s) return Piece{0, kb, 0};
+        if (n + 1 == s) return Piece{1, kb, 0};
         n += 2;
       }
     for (int kb = 0; kb < PKB; ++kb)
-      if (x_half(kb) == h) {
-        if (n == s) return Piece{2, kb};
+      if (mf_x_half(kb) == h) {
+        if (n == s) return Piece{2, kb, 0};
         n += 1;
       }
-    return Piece{-1, 0};
+    return Piece{-1, 0, 0};
   }
+  static constexpr int uph(bool fl) { return fl ? UPH_FL : UPH_MF; }
+  static constexpr Piece piece(bool fl, int h, int s) { return fl ? piece_fl(h, s) : piece_mf(h, s); }
   // LDS (bytes)
   static constexpr size_t kSlotC = size_t(kRows) * PN * 2;
   static constexpr size_t kSlotBwT = size_t(NTH) * 4 * 64 * 8;  // [nt][m][half][lane] x 8 B
@@ -210,7 +253,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   constexpr int R = 1 << LGR;
   constexpr int Q = kRows >> LGR;  // tokens per chunk
   constexpr int NKB = Lt::NKB, NTH = Lt::NTH, NPT = Lt::NPT, UPT = Lt::UPT;
-  constexpr int UPH = Lt::UPH, PN = Lt::PN, NG = Lt::NG, TSL = Lt::TSL, PH = Lt::PH;
+  // whole-line staging at R = 1 (the loads there are address-bound), MFMA-layout
+  // staging at R > 1 (short chunks: the LDS round trip before the transposes
+  // costs more than the full lines save; measured 18% slower at R = 4)
+  constexpr bool kFL = LGR == 0;
+  constexpr int UPH = Lt::uph(kFL), PN = Lt::PN, NG = Lt::NG, TSL = Lt::TSL, PH = Lt::PH;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -286,19 +333,30 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     Ilo = as_bf16x8(lo);
     Ihi = as_bf16x8(hi);
   }
-  const int prow = 16 * quad + l16;  // staging row of the chunk
-  const int ptok = prow >> LGR;
-  const int prank = prow & (R - 1);
 
   // Every wave issues the same loads every chunk (chunks past the end read
   // zeros): with no load behind a branch the wait counters stay exact.
+  // row (within the chunk) and column of this lane's 16 bytes in load s
+  auto piece_rc = [&](const Piece pc, int& row, int& col) __attribute__((always_inline)) {
+    if constexpr (kFL) {
+      const int D = pc.kind == 2 ? P : N;
+      const int cpr = Lt::cpr(D);
+      row = 16 * quad + (64 / cpr) * pc.i + lane / cpr;
+      col = 64 * pc.cb + 8 * (lane % cpr);
+    } else {
+      row = 16 * quad + l16;
+      col = 32 * pc.cb + 8 * g;
+    }
+  };
   auto load_piece = [&](int c, int s, auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
-    const uint32_t row = static_cast<uint32_t>(((c * Q + ptok) * H + hh) * R + prank);
-    const Piece pc = Lt::piece(h, s);
+    const Piece pc = Lt::piece(kFL, h, s);
+    if (pc.kind < 0 || (SO && pc.kind == 1)) return u32x4{0u, 0u, 0u, 0u};  // no load (unrolled away)
     const int D = pc.kind == 2 ? P : N;
-    const int col = 32 * pc.kb + 8 * g;
-    const uint32_t off = (pc.kind >= 0 && !(SO && pc.kind == 1) && col < D) ? (row * D + col) * 2u : kBad;
+    int row, col;
+    piece_rc(pc, row, col);
+    const uint32_t grow = static_cast<uint32_t>(((c * Q + (row >> LGR)) * H + hh) * R + (row & (R - 1)));
+    const uint32_t off = col < D ? (grow * D + col) * 2u : kBad;
     return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
   };
   constexpr bool kLateRefill = ROPE && LGR == 0;
@@ -389,7 +447,99 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // which spreads the load issue over the staging work.  With RoPE at R = 1
   // the upper waves refill in the second phase instead (measured faster
   // there: their loads then do not queue behind the lower waves').
-  auto build_slot = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
+  auto build_slot_fl = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    constexpr bool kRefill = !(kLateRefill && h == 1);
+    const int s2 = c & 1;
+    const float* S = sc(c % 3);
+    uint16_t* sB = slotB(s2);
+    uint16_t* sC = slotC(s2);
+    u32x2* bwt = slotBwT(s2);
+    u32x2* xt = slotXT(s2);
+    // raw X rows of this row tile are parked in the tile's own X^T fragment
+    // region ([p tile][16 rows][16 columns] bf16) until they are transposed
+    unsigned char* xtile = reinterpret_cast<unsigned char*>(xt);
+    const float* tab = phiTab(c & 1);
+    const int m = quad >> 1, half = quad & 1;  // j tile `quad` -> k-block m, half of it
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+    // 1) rotate and store: B, C row-major in the slot, X rows parked
+#pragma unroll
+    for (int s = 0; s < UPH; ++s) {
+      const Piece pc = Lt::piece(kFL, h, s);
+      if (pc.kind < 0 || (SO && pc.kind == 1)) continue;  // unrolled away
+      const u32x4 v = src[s];
+      int row, col;
+      piece_rc(pc, row, col);
+      if (pc.kind == 2) {
+        if (col < P) {
+          const int pt = col >> 4;
+          *reinterpret_cast<u32x4*>(xtile + (((pt * 2 + m) * 2 + half) * 64) * 8 + (row & 15) * 32 + (col & 15) * 2) = v;
+        }
+      } else {
+        u32x4 o = v;
+        if constexpr (ROPE) {
+          if (pc.kind == 0) {  // B precedes C of the same rows and columns: C reuses sin/cos
+            const int q = col < N ? (col >> 1) : 0;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(tab + (row >> LGR) * PH + q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sn[e] = __sinf(a[e]);
+              cs[e] = __cosf(a[e]);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float a0 = __uint_as_float(v[q] << 16), a1 = __uint_as_float(v[q] & 0xffff0000u);
+            o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
+          }
+        }
+        // row-major B and C feed the Gram tiles and the readout; B also the transposes
+        u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + row * PN + col);
+        dstRow[0] = u32x2{o[0], o[1]};
+        dstRow[1] = u32x2{o[2], o[3]};
+      }
+      if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
+    }
+    // 2) transposes by MFMA against the identity, from this wave's own rows read
+    // back in the A-operand layout (row l16, 8 columns at 32 kb + 8 g)
+    f32x4 wj;  // w of the rows 16 quad + 4g + jj this lane holds after the transpose
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wj[jj] = S[3 * 64 + ((16 * quad + 4 * g + jj) >> LGR)];
+#pragma unroll
+    for (int cb = 0; cb < Lt::NCBN; ++cb) {
+      if (Lt::bc_half(cb) != h) continue;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int kb = 2 * cb + kk;
+        if (32 * kb >= Lt::NK) continue;
+        const uint16_t* rb = sB + (16 * quad + l16) * PN + 32 * kb + 8 * g;
+        const bf16x8 a = cat8(*reinterpret_cast<const u32x2*>(rb), *reinterpret_cast<const u32x2*>(rb + 4));
+        if (2 * kb < NTH) bwt[(((2 * kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
+        if (2 * kb + 1 < NTH) bwt[(((2 * kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
+      }
+    }
+    constexpr int PKB = Lt::PKB;
+    bf16x8 xa[PKB];  // every parked X fragment is read before any X^T fragment overwrites it
+#pragma unroll
+    for (int kb = 0; kb < PKB; ++kb) {
+      const bool mine = Lt::x_half(Lt::NCBP == 1 ? 0 : kb >> 1) == h;
+      const int col = 32 * kb + 8 * g;
+      const int pt = col >> 4;
+      const u32x4 t = (mine && col < P)
+                          ? *reinterpret_cast<const u32x4*>(xtile + (((pt * 2 + m) * 2 + half) * 64) * 8 + l16 * 32 + (col & 15) * 2)
+                          : u32x4{0u, 0u, 0u, 0u};
+      xa[kb] = as_bf16x8(t);
+    }
+#pragma unroll
+    for (int kb = 0; kb < PKB; ++kb) {
+      const bool mine = Lt::x_half(Lt::NCBP == 1 ? 0 : kb >> 1) == h;
+      if (!mine) continue;
+      if (2 * kb < NPT) xt[(((2 * kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(xa[kb], Ilo, z));
+      if (2 * kb + 1 < NPT) xt[(((2 * kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(xa[kb], Ihi, z));
+    }
+  };
+  auto build_slot_mf = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     constexpr bool kRefill = !(kLateRefill && h == 1);
     const int s2 = c & 1;
@@ -404,17 +554,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < UPH; ++s) {
-      const Piece pc = Lt::piece(h, s);
+      const Piece pc = Lt::piece(kFL, h, s);
       if (pc.kind < 0) {  // padding slot of the smaller half: keep the load count uniform
         if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
       const u32x4 v = src[s];
-      const int col = 32 * pc.kb + 8 * g;
+      const int col = 32 * pc.cb + 8 * g;
       if (pc.kind == 2) {
         const bf16x8 a = as_bf16x8(v);
-        if (2 * pc.kb < NPT) xt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
-        if (2 * pc.kb + 1 < NPT) xt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
+        if (2 * pc.cb < NPT) xt[(((2 * pc.cb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
+        if (2 * pc.cb + 1 < NPT) xt[(((2 * pc.cb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
         if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
@@ -425,8 +575,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       u32x4 o = v;
       if constexpr (ROPE) {
         if (pc.kind == 0) {  // B comes first for a k-block; C reuses its sin/cos
-          const int q = (N >= 32 || 16 * pc.kb + 4 * g < N / 2) ? 16 * pc.kb + 4 * g : 0;
-          const f32x4 a = *reinterpret_cast<const f32x4*>(tab + ptok * PH + q);
+          const int q = (N >= 32 || 16 * pc.cb + 4 * g < N / 2) ? 16 * pc.cb + 4 * g : 0;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(tab + ((16 * quad + l16) >> LGR) * PH + q);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             sn[e] = __sinf(a[e]);
@@ -440,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         }
       }
       if constexpr (!SO) {  // row-major B and C feed the Gram tiles and the readout
-        u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + prow * PN + col);
+        u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + (16 * quad + l16) * PN + col);
         dstRow[0] = u32x2{o[0], o[1]};
         dstRow[1] = u32x2{o[2], o[3]};
       }
@@ -449,11 +599,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) wj[jj] = S[3 * 64 + ((16 * quad + 4 * g + jj) >> LGR)];
         const bf16x8 a = as_bf16x8(o);
-        if (2 * pc.kb < NTH) bwt[(((2 * pc.kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
-        if (2 * pc.kb + 1 < NTH) bwt[(((2 * pc.kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
+        if (2 * pc.cb < NTH) bwt[(((2 * pc.cb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
+        if (2 * pc.cb + 1 < NTH) bwt[(((2 * pc.cb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
       }
       if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
     }
+  };
+  auto build_slot = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
+    if constexpr (kFL)
+      build_slot_fl(c, src, HALF);
+    else
+      build_slot_mf(c, src, HALF);
   };
   // ================================================================ compute state
   // The state H' (N x P) lives in MFMA accumulators: wave (quad, upper) keeps p
