@@ -457,10 +457,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     u32x2* bwt = slotBwT(s2);
     u32x2* xt = slotXT(s2);
     // raw X rows of this row tile are parked in the tile's own X^T fragment
-    // region ([p tile][16 rows][16 columns] bf16) until they are transposed
+    // region (one 512-byte piece per p tile: 16 rows x 16 columns bf16) until
+    // they are transposed; the 16-byte slot is swizzled with the p tile and
+    // the row so that the 8 lanes of a row write, and 8 rows read, distinct banks
     unsigned char* xtile = reinterpret_cast<unsigned char*>(xt);
     const float* tab = phiTab(c & 1);
     const int m = quad >> 1, half = quad & 1;  // j tile `quad` -> k-block m, half of it
+    auto park = [&](int row, int col) __attribute__((always_inline)) {
+      const int pt = col >> 4;
+      const int slot = 2 * (row ^ (pt & 3)) + (((col >> 3) & 1) ^ ((row >> 2) & 1));
+      return xtile + (((pt * 2 + m) * 2 + half) * 64) * 8 + slot * 16;
+    };
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
     // 1) rotate and store: B, C row-major in the slot, X rows parked
@@ -472,10 +479,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       int row, col;
       piece_rc(pc, row, col);
       if (pc.kind == 2) {
-        if (col < P) {
-          const int pt = col >> 4;
-          *reinterpret_cast<u32x4*>(xtile + (((pt * 2 + m) * 2 + half) * 64) * 8 + (row & 15) * 32 + (col & 15) * 2) = v;
-        }
+        if (col < P) *reinterpret_cast<u32x4*>(park(row & 15, col)) = v;
       } else {
         u32x4 o = v;
         if constexpr (ROPE) {
@@ -525,10 +529,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     for (int kb = 0; kb < PKB; ++kb) {
       const bool mine = Lt::x_half(Lt::NCBP == 1 ? 0 : kb >> 1) == h;
       const int col = 32 * kb + 8 * g;
-      const int pt = col >> 4;
-      const u32x4 t = (mine && col < P)
-                          ? *reinterpret_cast<const u32x4*>(xtile + (((pt * 2 + m) * 2 + half) * 64) * 8 + l16 * 32 + (col & 15) * 2)
-                          : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 t = (mine && col < P) ? *reinterpret_cast<const u32x4*>(park(l16, col)) : u32x4{0u, 0u, 0u, 0u};
       xa[kb] = as_bf16x8(t);
     }
 #pragma unroll
