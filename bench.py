@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -270,12 +271,16 @@ def cpu_baseline(batch_items=6):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments and whitespace are dropped, so
+    that a change of wording leaves the profiled figures valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "state_space_sequence_ssm_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            h.update(f.encode() + b"\0" + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

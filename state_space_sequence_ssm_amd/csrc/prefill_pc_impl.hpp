@@ -19,17 +19,21 @@
 // N x P state in MFMA accumulators.  Wave w has a row tile / p-tile group
 // quad = w & 3 and a half upper = w >> 2.  Two workgroup barriers per chunk hand
 // a double-buffered LDS operand slot over:
-//   * phase A -- staging of chunk k+1 into slot (k+1)%2: wave w owns rows
-//     16 quad..+15 and half of their 16-byte pieces, loaded one chunk ahead into
-//     registers through buffer resources that span the segment of one batch
-//     item (the range check zero-fills the ragged tail, so every wave issues the
-//     same loads every chunk and the wait counters stay static).  B and C are
-//     rotated pairwise in fp32 (hardware sin/cos of the cumulative angle),
-//     rounded to bf16 and stored row-major; B (scaled by w_j = exp(Lam_e -
-//     Lam_j) delta_j) and X are transposed by MFMA products against an identity
-//     operand: the 16x16 fp32 result of A x I holds per lane four consecutive
-//     rows of one column, exactly the k-contiguous operand the token
-//     contractions need, stored to LDS in lane order.  Wave 0 scans the decays
+//   * phase A -- staging of chunk k+1 into slot (k+1)%2: the two waves of row
+//     tile quad own rows 16 quad..+15 and split their loads (whole 128-byte
+//     lines, 8 lanes per row, at R = 1; 16-byte pieces in the MFMA operand
+//     layout at R > 1), issued one chunk ahead into registers through buffer
+//     resources that span the segment of one batch item (the range check
+//     zero-fills the ragged tail, so every wave issues the same loads every
+//     chunk and the wait counters stay static).  B and C are rotated pairwise
+//     in fp32 (hardware sin/cos of the cumulative angle), rounded to bf16 and
+//     stored row-major; B (scaled by w_j = exp(Lam_e - Lam_j) delta_j) and X
+//     are transposed by MFMA products against an identity operand: the 16x16
+//     fp32 result of A x I holds per lane four consecutive rows of one column,
+//     exactly the k-contiguous operand the token contractions need, stored to
+//     LDS in lane order.  At R = 1 the operands of the transposes are read back
+//     from LDS (B from its row-major copy, X from raw rows parked, swizzled, in
+//     its own fragment region); at R > 1 they come straight from registers.  Wave 0 scans the decays
 //     of chunk k+2 (log2 units, one DPP wave scan); the raw angles of chunk k+2
 //     go to the angle table.  Every wave then computes the readout partials
 //     C^T H'_prev of chunk k from the state it keeps.
@@ -37,7 +41,8 @@
 //     (DPP segments of Q lanes, carry across chunks), Y^T += X^T S^T for the
 //     wave's p tiles quad + 4u and i tiles {0,3} (lower) or {1,2} (upper) from
 //     the masked Gram tiles, the readout (own and partner's partials), the y
-//     stores and H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles (the two
+//     stores (at R = 1 into an LDS tile that leaves as whole rows during the
+//     next chunk) and H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles (the two
 //     waves of a p tile split the n tiles when the readout exchange fits);
 //     then the 10 causal Gram tiles G^T = B C^T of chunk k+1, masked in
 //     registers (one exp2 per element, no comparisons off the diagonal).
