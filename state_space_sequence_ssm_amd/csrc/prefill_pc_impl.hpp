@@ -27,25 +27,25 @@
 //     zero-fills the ragged tail, so every wave issues the same loads every
 //     chunk and the wait counters stay static).  B and C are rotated pairwise
 //     in fp32 (hardware sin/cos of the cumulative angle), rounded to bf16 and
-//     stored row-major; B (scaled by w_j = exp(Lam_e - Lam_j) delta_j) and X
-//     are transposed by MFMA products against an identity operand: the 16x16
-//     fp32 result of A x I holds per lane four consecutive rows of one column,
-//     exactly the k-contiguous operand the token contractions need, stored to
-//     LDS in lane order.  At R = 1 the operands of the transposes are read back
-//     from LDS (B from its row-major copy, X from raw rows parked, swizzled, in
-//     its own fragment region); at R > 1 they come straight from registers.  Wave 0 scans the decays
-//     of chunk k+2 (log2 units, one DPP wave scan); the raw angles of chunk k+2
-//     go to the angle table.  Every wave then computes the readout partials
-//     C^T H'_prev of chunk k from the state it keeps.
+//     stored row-major with X, in tiles whose 8-byte units are XOR-swizzled by
+//     row.  Wave 0 scans the decays of chunk k+2 (log2 units, one DPP wave
+//     scan); the raw angles of chunk k+2 go to the angle table.  Every wave
+//     then computes the readout partials C^T H'_prev of chunk k from the state
+//     it keeps.
 //   * phase B -- products of chunk k from slot k%2: the angle scan of chunk k+2
 //     (DPP segments of Q lanes, carry across chunks), Y^T += X^T S^T for the
 //     wave's p tiles quad + 4u and i tiles {0,3} (lower) or {1,2} (upper) from
 //     the masked Gram tiles, the readout (own and partner's partials), the y
 //     stores (at R = 1 into an LDS tile that leaves as whole rows during the
-//     next chunk) and H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles (the two
-//     waves of a p tile split the n tiles when the readout exchange fits);
-//     then the 10 causal Gram tiles G^T = B C^T of chunk k+1, masked in
-//     registers (one exp2 per element, no comparisons off the diagonal).
+//     next chunk) and H' = exp(Lam_e) H' + B^T (w X) on the kept n tiles (the
+//     two waves of a p tile split the n tiles when the readout exchange
+//     fits); then the 10 causal Gram tiles G^T = B C^T of chunk k+1, masked in
+//     registers (one exp2 per element, no comparisons off the diagonal), and
+//     the X^T fragments of chunk k+1.
+// The token contractions need token-contiguous operands: X^T and B^T come
+// straight from the row-major tiles through the gfx950 transposing LDS read,
+// and w_j = exp(Lam_e - Lam_j) delta_j is applied to the X^T fragments in
+// registers, so no transposed copy is ever stored.
 // MFMA k index: a k-block of 32 holds, for lane group g, indices {4g..4g+3} and
 // {16+4g..16+4g+3}, matching the accumulator rows of two adjacent 16-row tiles,
 // so accumulators feed the next product without a trip through LDS.
@@ -92,6 +92,61 @@ __device__ __forceinline__ float bloadf(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ f32x4 bloadf4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  In each group of 16
+// lanes, lane 4e + q reads 4 bf16 at its own address; afterwards lane i holds
+// element i % 4 of lanes 4e + i / 4, e = 0..3.  With lane 4e + q pointing at
+// columns c0 + 4q..+3 of row r_e of a row-major matrix, lane i receives column
+// c0 + i of rows r_0..r_3: four k values of an MFMA operand column.
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) tr4_t* lds_tr4_ptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p)));
+}
+// Row-major bf16 tiles of D columns (D = 32, 64 or 128) keep their 8-byte
+// units XOR-swizzled by row.  Measured on gfx950: an 8-byte read (plain or
+// transposing) is served 32 lanes at a time from 64 four-byte banks, a
+// 16-byte store 8 lanes at a time on 32 banks.  With r0..r3 the low row bits,
+// the swizzle puts r0 ^ r3 (r1 ^ r3 at D = 32) in unit bit 1 and the next row
+// bits above it, so that all four access shapes used here are conflict-free:
+// 16 rows x 2 units (MFMA operand fragments), 8 aligned rows x 4 units
+// (transposing reads), 8 rows x 1 16-byte unit (stores in the MFMA layout) and
+// 8 lanes along one row (stores of whole-line pieces).  Row bits that the row
+// length already spreads over the banks are left out.
+template <int D>
+__device__ __forceinline__ int swz_unit(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  if constexpr (D >= 128)
+    return ((r0 ^ r3) << 1) | (r1 << 2) | (r2 << 3) | (r0 << 4);
+  else if constexpr (D == 64)
+    return ((r0 ^ r3) << 1) | (r1 << 2) | (r2 << 3);
+  else
+    return ((r1 ^ r3) << 1) | (r2 << 2);
+}
+// element offset of (r, c); c is a multiple of 4 (8 when 16 bytes are accessed)
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * D + ((((c >> 2) ^ swz_unit<D>(r))) << 2);
+}
+// A uniform LDS element offset the compiler cannot relate to other offsets.
+// Reads from two bases a constant distance apart are otherwise fused into one
+// ds_read2_b64, which the LDS serves at half the rate of two single 8-byte
+// reads (16 lanes per cycle on 32 banks instead of 32 lanes on 64 banks).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+// w-scaled copy of an MFMA operand: slots 0-3 by w0, slots 4-7 by w1 (one
+// rounding of the product to bf16)
+__device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 w0, f32x4 w1) {
+  const u32x4 v = __builtin_bit_cast(u32x4, x);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float wa = q < 2 ? w0[2 * q] : w1[2 * q - 4], wb = q < 2 ? w0[2 * q + 1] : w1[2 * q - 3];
+    o[q] = pack_bf16x2(wa * __uint_as_float(v[q] << 16), wb * __uint_as_float(v[q] & 0xffff0000u));
+  }
+  return as_bf16x8(o);
+}
 __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
@@ -129,21 +184,17 @@ struct Piece {
   int kind, cb, i;
 };
 // MFMA-layout staging (used at R > 1): a load is 16 rows x 32 columns (k block
-// cb) in the bf16 A-operand layout (lane (g, l16): row l16, 8 columns at 8 g),
-// which the identity transposes take straight from registers.
+// cb), lane (g, l16) reading row l16, 8 columns at 8 g.
 
 template <int N, int P>
 struct PcLayout {
   static constexpr int NK = N < 32 ? 32 : N;  // n contraction length (zero padded)
+  static constexpr int PK = P < 32 ? 32 : P;  // X row length (columns past P unused)
   static constexpr int NKB = NK / 32;         // k blocks over n
   static constexpr int NTH = N / 16;          // state n tiles
   static constexpr int NPT = P / 16;          // p tiles
   static constexpr int PKB = (P + 31) / 32;   // k blocks over p (X pieces)
   static constexpr int UPT = (NPT + kPGroups - 1) / kPGroups;  // p tiles per wave
-  // bf16 pitch of B/C rows: NK + 4 puts a row 2 (mod 32) dwords after the
-  // previous one, so the 16 rows of an 8-byte-per-lane fragment read fall on
-  // 16 distinct bank pairs (rows are then only 8-byte aligned)
-  static constexpr int PN = NK + 4;
   static constexpr int NG = N / 8;            // float4 groups of angles per token
   static constexpr int TSL = (NG + kWaves - 1) / kWaves;  // angle groups per lane (Q = 64)
   static constexpr int PH = N / 2 + 4;        // padded angle-table row (spreads banks)
@@ -210,14 +261,14 @@ struct PcLayout {
   static constexpr int uph(bool fl) { return fl ? UPH_FL : UPH_MF; }
   static constexpr Piece piece(bool fl, int h, int s) { return fl ? piece_fl(h, s) : piece_mf(h, s); }
   // LDS (bytes)
-  static constexpr size_t kSlotC = size_t(kRows) * PN * 2;
-  static constexpr size_t kSlotBwT = size_t(NTH) * 4 * 64 * 8;  // [nt][m][half][lane] x 8 B
-  static constexpr size_t kSlotXT = size_t(NPT) * 4 * 64 * 8;   // [pt][m][half][lane] x 8 B
+  // slot: C, B (NK columns) and X (PK columns), row-major and swizzled; B and
+  // X are also read transposed, which replaces any transposed copy
+  static constexpr size_t kSlotC = size_t(kRows) * NK * 2;
+  static constexpr size_t kSlotX = size_t(kRows) * PK * 2;
   static constexpr size_t oC = 0;
   static constexpr size_t oB = oC + kSlotC;
-  static constexpr size_t oBwT = oB + kSlotC;
-  static constexpr size_t oXT = oBwT + kSlotBwT;
-  static constexpr size_t kSlot = oXT + kSlotXT;
+  static constexpr size_t oX = oB + kSlotC;
+  static constexpr size_t kSlot = oX + kSlotX;
   static constexpr size_t oSC = 2 * kSlot;                // [3][6][64] fp32 scalars
   static constexpr size_t kSC = 6 * 64 * 4;
   static constexpr size_t kSBytes = 10 * 64 * 8;          // [10][64] x 8 B masked S^T pieces
@@ -258,11 +309,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   constexpr int R = 1 << LGR;
   constexpr int Q = kRows >> LGR;  // tokens per chunk
   constexpr int NKB = Lt::NKB, NTH = Lt::NTH, NPT = Lt::NPT, UPT = Lt::UPT;
-  // whole-line staging at R = 1 (the loads there are address-bound), MFMA-layout
-  // staging at R > 1 (short chunks: the LDS round trip before the transposes
-  // costs more than the full lines save; measured 18% slower at R = 4)
+  // whole-line staging at R = 1 (the loads there are address-bound),
+  // MFMA-layout staging at R > 1 (measured 5% faster at R = 4)
   constexpr bool kFL = LGR == 0;
-  constexpr int UPH = Lt::uph(kFL), PN = Lt::PN, NG = Lt::NG, TSL = Lt::TSL, PH = Lt::PH;
+  constexpr int UPH = Lt::uph(kFL), NG = Lt::NG, TSL = Lt::TSL, PH = Lt::PH;
+  constexpr int NK = Lt::NK, PK = Lt::PK;
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -304,8 +355,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 
   auto slotC = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oC); };
   auto slotB = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oB); };
-  auto slotBwT = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oBwT); };
-  auto slotXT = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<u32x2*>(smem + s * Lt::kSlot + Lt::oXT); };
+  auto slotX = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oX); };
   auto sc = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oSC + s * Lt::kSC); };
   float* phiC = reinterpret_cast<float*>(smem + Lt::oPhiC);
   // y leaves through LDS in whole rows at R = 1 (fewer, full-line stores:
@@ -326,19 +376,6 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   constexpr int kThU = (kThUnits + kThreads - 1) / kThreads;
   f32x4 rawTh[2][ROPE ? kThU : 1];
   float rdt[2], rlam[2];
-  bf16x8 Ilo, Ihi;  // identity selectors: column c <- k slot (g, e) with 8g + e == c (+16)
-  {
-    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t one = 0x3F80u << (16 * (e & 1));
-      if (8 * g + e == l16) lo[e >> 1] |= one;
-      if (8 * g + e == 16 + l16) hi[e >> 1] |= one;
-    }
-    Ilo = as_bf16x8(lo);
-    Ihi = as_bf16x8(hi);
-  }
-
   // Every wave issues the same loads every chunk (chunks past the end read
   // zeros): with no load behind a branch the wait counters stay exact.
   // row (within the chunk) and column of this lane's 16 bytes in load s
@@ -364,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const uint32_t off = col < D ? (grow * D + col) * 2u : kBad;
     return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
   };
-  constexpr bool kLateRefill = ROPE && LGR == 0;
+  constexpr bool kLateRefill = LGR == 0;
   auto issue_bcx = [&](int c, u32x4 (&dst)[UPH], auto HALF) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < UPH; ++s) dst[s] = load_piece(c, s, HALF);
@@ -447,35 +484,23 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     }
   };
+  // raw X row piece (8 columns) -> X rows
+  auto store_x = [&](int s2, int row, int col, u32x4 v) __attribute__((always_inline)) {
+    if (col < P) *reinterpret_cast<u32x4*>(slotX(s2) + swz<PK>(row, col)) = v;
+  };
   // stage this wave's pieces of chunk c into operand slot c%2; each register
-  // is refilled with the same piece of chunk c+2 as soon as it is consumed,
-  // which spreads the load issue over the staging work.  With RoPE at R = 1
-  // the upper waves refill in the second phase instead (measured faster
-  // there: their loads then do not queue behind the lower waves').
+  // is refilled with the same piece of chunk c+1 as soon as it is consumed,
+  // which spreads the load issue over the staging work.  At R = 1 the upper
+  // waves refill in the second phase instead: the loads of a chunk then do not
+  // all queue at its start (measured 3-5% faster).
   auto build_slot_fl = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     constexpr bool kRefill = !(kLateRefill && h == 1);
     const int s2 = c & 1;
-    const float* S = sc(c % 3);
     uint16_t* sB = slotB(s2);
     uint16_t* sC = slotC(s2);
-    u32x2* bwt = slotBwT(s2);
-    u32x2* xt = slotXT(s2);
-    // raw X rows of this row tile are parked in the tile's own X^T fragment
-    // region (one 512-byte piece per p tile: 16 rows x 16 columns bf16) until
-    // they are transposed; the 16-byte slot is swizzled with the p tile and
-    // the row so that the 8 lanes of a row write, and 8 rows read, distinct banks
-    unsigned char* xtile = reinterpret_cast<unsigned char*>(xt);
     const float* tab = phiTab(c & 1);
-    const int m = quad >> 1, half = quad & 1;  // j tile `quad` -> k-block m, half of it
-    auto park = [&](int row, int col) __attribute__((always_inline)) {
-      const int pt = col >> 4;
-      const int slot = 2 * (row ^ (pt & 3)) + (((col >> 3) & 1) ^ ((row >> 2) & 1));
-      return xtile + (((pt * 2 + m) * 2 + half) * 64) * 8 + slot * 16;
-    };
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-    // 1) rotate and store: B, C row-major in the slot, X rows parked
 #pragma unroll
     for (int s = 0; s < UPH; ++s) {
       const Piece pc = Lt::piece(kFL, h, s);
@@ -484,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       int row, col;
       piece_rc(pc, row, col);
       if (pc.kind == 2) {
-        if (col < P) *reinterpret_cast<u32x4*>(park(row & 15, col)) = v;
+        store_x(s2, row, col, v);
       } else {
         u32x4 o = v;
         if constexpr (ROPE) {
@@ -503,60 +528,19 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
             o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
           }
         }
-        // row-major B and C feed the Gram tiles and the readout; B also the transposes
-        u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + row * PN + col);
-        dstRow[0] = u32x2{o[0], o[1]};
-        dstRow[1] = u32x2{o[2], o[3]};
+        // B and C feed the Gram tiles and the readout, B also the state
+        *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(row, col)) = o;
       }
       if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
-    }
-    // 2) transposes by MFMA against the identity, from this wave's own rows read
-    // back in the A-operand layout (row l16, 8 columns at 32 kb + 8 g)
-    f32x4 wj;  // w of the rows 16 quad + 4g + jj this lane holds after the transpose
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) wj[jj] = S[3 * 64 + ((16 * quad + 4 * g + jj) >> LGR)];
-#pragma unroll
-    for (int cb = 0; cb < Lt::NCBN; ++cb) {
-      if (Lt::bc_half(cb) != h) continue;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int kb = 2 * cb + kk;
-        if (32 * kb >= Lt::NK) continue;
-        const uint16_t* rb = sB + (16 * quad + l16) * PN + 32 * kb + 8 * g;
-        const bf16x8 a = cat8(*reinterpret_cast<const u32x2*>(rb), *reinterpret_cast<const u32x2*>(rb + 4));
-        if (2 * kb < NTH) bwt[(((2 * kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
-        if (2 * kb + 1 < NTH) bwt[(((2 * kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
-      }
-    }
-    constexpr int PKB = Lt::PKB;
-    bf16x8 xa[PKB];  // every parked X fragment is read before any X^T fragment overwrites it
-#pragma unroll
-    for (int kb = 0; kb < PKB; ++kb) {
-      const bool mine = Lt::x_half(Lt::NCBP == 1 ? 0 : kb >> 1) == h;
-      const int col = 32 * kb + 8 * g;
-      const u32x4 t = (mine && col < P) ? *reinterpret_cast<const u32x4*>(park(l16, col)) : u32x4{0u, 0u, 0u, 0u};
-      xa[kb] = as_bf16x8(t);
-    }
-#pragma unroll
-    for (int kb = 0; kb < PKB; ++kb) {
-      const bool mine = Lt::x_half(Lt::NCBP == 1 ? 0 : kb >> 1) == h;
-      if (!mine) continue;
-      if (2 * kb < NPT) xt[(((2 * kb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(xa[kb], Ilo, z));
-      if (2 * kb + 1 < NPT) xt[(((2 * kb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(xa[kb], Ihi, z));
     }
   };
   auto build_slot_mf = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     constexpr bool kRefill = !(kLateRefill && h == 1);
     const int s2 = c & 1;
-    const float* S = sc(c % 3);
     uint16_t* sB = slotB(s2);
     uint16_t* sC = slotC(s2);
-    u32x2* bwt = slotBwT(s2);
-    u32x2* xt = slotXT(s2);
     const float* tab = phiTab(c & 1);
-    const int m = quad >> 1, half = quad & 1;  // j tile `quad` -> k-block m, half of it
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < UPH; ++s) {
@@ -568,9 +552,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       const u32x4 v = src[s];
       const int col = 32 * pc.cb + 8 * g;
       if (pc.kind == 2) {
-        const bf16x8 a = as_bf16x8(v);
-        if (2 * pc.cb < NPT) xt[(((2 * pc.cb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z));
-        if (2 * pc.cb + 1 < NPT) xt[(((2 * pc.cb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z));
+        store_x(s2, 16 * quad + l16, col, v);
         if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
@@ -595,19 +577,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
         }
       }
-      if constexpr (!SO) {  // row-major B and C feed the Gram tiles and the readout
-        u32x2* dstRow = reinterpret_cast<u32x2*>((pc.kind == 1 ? sC : sB) + (16 * quad + l16) * PN + col);
-        dstRow[0] = u32x2{o[0], o[1]};
-        dstRow[1] = u32x2{o[2], o[3]};
-      }
-      if (pc.kind == 0) {
-        f32x4 wj;  // w of the rows 16 quad + 4g + jj this lane holds after the transpose
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) wj[jj] = S[3 * 64 + ((16 * quad + 4 * g + jj) >> LGR)];
-        const bf16x8 a = as_bf16x8(o);
-        if (2 * pc.cb < NTH) bwt[(((2 * pc.cb) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ilo, z) * wj);
-        if (2 * pc.cb + 1 < NTH) bwt[(((2 * pc.cb + 1) * 2 + m) * 2 + half) * 64 + lane] = pack4(mma(a, Ihi, z) * wj);
-      }
+      // B and C feed the Gram tiles and the readout, B also the state
+      *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(16 * quad + l16, col)) = o;
       if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
     }
   };
@@ -640,18 +611,20 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     constexpr int jt = decltype(JT)::value, it = decltype(IT)::value;
     const int s2 = k & 1;
     const float* S = sc(k % 3);
-    const uint16_t* sB = slotB(s2);
-    const uint16_t* sC = slotC(s2);
+    const uint16_t* tB = slotB(s2) + opaque(16 * jt * NK);
+    const uint16_t* tC = slotC(s2) + opaque(16 * it * NK);
     const int iRow = 16 * it + l16;
     const int ti = iRow >> LGR;
     const float lamI = S[ti], gamI = S[64 + ti];
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const uint16_t* rb = sB + (16 * jt + l16) * PN + 32 * kb + 4 * g;
-      const uint16_t* rc = sC + iRow * PN + 32 * kb + 4 * g;
-      a = mma(cat8(*reinterpret_cast<const u32x2*>(rb), *reinterpret_cast<const u32x2*>(rb + 16)),
-              cat8(*reinterpret_cast<const u32x2*>(rc), *reinterpret_cast<const u32x2*>(rc + 16)), a);
+      const int col = 32 * kb + 4 * g;  // rows of a row tile share their swizzle with l16
+      a = mma(cat8(*reinterpret_cast<const u32x2*>(tB + swz<NK>(l16, col)),
+                   *reinterpret_cast<const u32x2*>(tB + swz<NK>(l16, col + 16))),
+              cat8(*reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col)),
+                   *reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col + 16))),
+              a);
     }
     // scalars are read and the decay evaluated on every lane, then selected:
     // keeps the tile free of divergent control flow
@@ -712,8 +685,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kw = 0; kw < NKW; ++kw) {
-          const uint16_t* rc = sC + (16 * it + l16) * PN + 32 * (kb0 + kw) + 4 * g;
-          z = mma(hfr[kw], cat8(*reinterpret_cast<const u32x2*>(rc), *reinterpret_cast<const u32x2*>(rc + 16)), z);
+          const uint16_t* tC = sC + opaque(16 * it * NK);
+          const int col = 32 * (kb0 + kw) + 4 * g;
+          z = mma(hfr[kw], cat8(*reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col)),
+                                *reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col + 16))),
+                  z);
         }
         return z;
       };
@@ -724,24 +700,35 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     }
   };
+  // transposed reads: slot e of k block m holds row 32 m + 4g + e (+16 in
+  // the upper four slots), the order of the masked Gram pieces; this lane
+  // points at row 32 m + 4g + l16 / 4, columns 4 (l16 % 4) + 0..3
+  const int rT = 4 * g + (l16 >> 2), c4 = 4 * (l16 & 3);
+  // X^T of p tile quad + 4u, k block m, of the next chunk to compute: read once
+  // its slot is visible, a phase before it is used
+  bf16x8 xnext[UPT][2];
+  auto load_x = [&](int c) __attribute__((always_inline)) {
+    const uint16_t* sX = slotX(c & 1);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int pt = quad + kPGroups * u;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        if (kAllPt || pt < NPT)
+          xnext[u][m] = cat8(lds_read_tr(sX + swz<PK>(32 * m + rT, 16 * pt + c4)),
+                             lds_read_tr(sX + swz<PK>(32 * m + 16 + rT, 16 * pt + c4)));
+    }
+  };
   // phase B: y of this wave's i tiles and p tiles, then the state update
   auto compute_rest = [&](int k, auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     constexpr int nb = kSplit && h ? NTW : 0;
     const int s2 = k & 1;
     const float* S = sc(k % 3);
-    const u32x2* bwt = slotBwT(s2);
-    const u32x2* xt = slotXT(s2);
+    const uint16_t* sB = slotB(s2);
     const u32x2* sS = sSb(k);
     const float cdec = S[5 * 64];
-    bf16x8 xfr[UPT][2];
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int pt = quad + kPGroups * u;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        if (kAllPt || pt < NPT) xfr[u][m] = cat8(xt[((pt * 2 + m) * 2 + 0) * 64 + lane], xt[((pt * 2 + m) * 2 + 1) * 64 + lane]);
-    }
+    auto& xfr = xnext;  // X^T of chunk k, read during chunk k - 1
     auto do_it = [&](auto IT, auto IDX) __attribute__((always_inline)) {
       constexpr int it = decltype(IT)::value, idx = decltype(IDX)::value;
       const int iRow = 16 * it + l16;
@@ -754,8 +741,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       for (int m = 0; m < 2; ++m) {
         if (2 * m <= it) {
           constexpr u32x2 zero2 = {0u, 0u};
-          const u32x2 lo = sS[tile_id(2 * m, it) * 64 + lane];
-          const u32x2 hi = (2 * m + 1 <= it) ? sS[tile_id(2 * m + 1 <= it ? 2 * m + 1 : 0, it) * 64 + lane] : zero2;
+          const u32x2 lo = sS[opaque(tile_id(2 * m, it) * 64) + lane];
+          const u32x2 hi = (2 * m + 1 <= it) ? sS[opaque(tile_id(2 * m + 1 <= it ? 2 * m + 1 : 0, it) * 64) + lane] : zero2;
           const bf16x8 sop = cat8(lo, hi);
 #pragma unroll
           for (int u = 0; u < UPT; ++u)
@@ -782,18 +769,31 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       do_it(integral_constant<int, h == 0 ? 0 : 1>{}, integral_constant<int, 0>{});
       do_it(integral_constant<int, h == 0 ? 3 : 2>{}, integral_constant<int, 1>{});
     }
-    // H' = exp(Lam_e) H' + (w B)^T X on the kept n tiles
+    // H' = exp(Lam_e) H' + B^T (w X) on the kept n tiles, w_j = exp(Lam_e -
+    // Lam_j) delta_j applied to the X fragments of the rows this lane holds
+    f32x4 wrow[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wrow[m][hh][e] = S[3 * 64 + ((32 * m + 16 * hh + 4 * g + e) >> LGR)];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      if (kAllPt || quad + kPGroups * u < NPT) {
+      const int pt = quad + kPGroups * u;
+      if (kAllPt || pt < NPT) {
+        bf16x8 wfr[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) wfr[m] = scale8(xfr[u][m], wrow[m][0], wrow[m][1]);
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
           const int nt = nb + i;
           f32x4 a = acc[u][i] * cdec;
 #pragma unroll
           for (int m = 0; m < 2; ++m)
-            a = mma(cat8(bwt[((nt * 2 + m) * 2 + 0) * 64 + lane], bwt[((nt * 2 + m) * 2 + 1) * 64 + lane]),
-                    xfr[u][m], a);
+            a = mma(cat8(lds_read_tr(sB + swz<NK>(32 * m + rT, 16 * nt + c4)),
+                         lds_read_tr(sB + swz<NK>(32 * m + 16 + rT, 16 * nt + c4))),
+                    wfr[m], a);
           acc[u][i] = a;
         }
       }
@@ -884,6 +884,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     scan_angles(1);
     if constexpr (kEarly) gram_tiles(0);
     __syncthreads();  // slot 0, S(0), SC(1), Phi(1) visible
+    load_x(0);
   };
   // chunk walk, unrolled by two so the small-load register sets are indexed
   // statically.  Phase A: stage chunk k+1 (`bcx` holds it), refill `bcx` with
@@ -902,6 +903,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     __syncthreads();  // S(k), readout partials, slot k+1, raw theta(k+2) visible
     scan_angles(k + 2);
     compute_rest(k, HALF);
+    load_x(k + 1);  // slot k+1 is visible since the first barrier
     if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 1 + kSets, bcx, HALF);
     if constexpr (kEarly) gram_tiles(k + 1);  // overlaps the tail of chunk k
     __syncthreads();  // S(k+1), SC(k+2), Phi(k+2) visible; slot k free
