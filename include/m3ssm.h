@@ -85,8 +85,7 @@ typedef enum m3_dtype {
  *                                        [-pi, pi] (nullable; needs theta)
  * Sizes: Bt, L, H >= 1; N, P in {16, 32, 64, 128}; R a power of two <= 64;
  * combinations whose chunk tiles exceed the 160 KB LDS of a CU return
- * M3_ERR_UNSUPPORTED (bf16 with RoPE at N = P = 128; fp32 with RoPE at
- * N = 128, and fp32 at N = P = 128);
+ * M3_ERR_UNSUPPORTED (fp32 with RoPE at N = 128, and fp32 at N = P = 128);
  * chunk = tokens per chunk, 0 selects 64 / R (the only value supported:
  * one chunk tile always holds 64 (token, rank) rows).
  * Outputs must not alias inputs.  Passing the carry-out of one call as the

@@ -63,8 +63,6 @@ def test_prefill_validation():
         (lambda a: setattr(a, "phi_out", 0x20000000), _lib.M3_ERR_INVALID_ARG),
         (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "N", 128), setattr(a, "P", 128),
                     setattr(a, "theta", 0x30000000)), _lib.M3_ERR_UNSUPPORTED),  # LDS too large
-        (lambda a: (setattr(a, "N", 128), setattr(a, "P", 128), setattr(a, "theta", 0x30000000)),
-         _lib.M3_ERR_UNSUPPORTED),  # bf16 RoPE tiles at N = P = 128 exceed the LDS
     ]
     for mutate, code in cases:
         a = _good_prefill()

@@ -66,6 +66,8 @@ SMALL = [
     (1, 40, 2, 128, 128, 1, "bf16", False, True),
     (1, 70, 1, 128, 32, 2, "bf16", True, True),
     (1, 33, 2, 16, 16, 1, "bf16", True, True),
+    (1, 90, 2, 128, 128, 1, "bf16", True, True),
+    (1, 50, 1, 128, 128, 4, "bf16", True, False),
 ]
 
 
