@@ -607,25 +607,33 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // (0,3) (1,3) (2,3) (3,3); tile t is computed once, by wave t % 8
   auto tile_id = [](int jt, int it) { return it * (it + 1) / 2 + jt; };
   // phase A: masked Gram tile S^T(jt, it) = M o (B C^T)^T of chunk k -> LDS
-  auto gram_tile = [&](int k, auto JT, auto IT) __attribute__((always_inline)) {
+  // The operand fragments of a tile are all read before its products start:
+  // the scheduler barrier keeps the compiler from interleaving each k block's
+  // reads with its product, which made a chain of LDS round trips.
+  auto gram_fetch = [&](int k, auto JT, auto IT, bf16x8 (&fb)[NKB], bf16x8 (&fc)[NKB]) __attribute__((always_inline)) {
     constexpr int jt = decltype(JT)::value, it = decltype(IT)::value;
-    const int s2 = k & 1;
-    const float* S = sc(k % 3);
-    const uint16_t* tB = slotB(s2) + opaque(16 * jt * NK);
-    const uint16_t* tC = slotC(s2) + opaque(16 * it * NK);
-    const int iRow = 16 * it + l16;
-    const int ti = iRow >> LGR;
-    const float lamI = S[ti], gamI = S[64 + ti];
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* tB = slotB(k & 1) + opaque(16 * jt * NK);
+    const uint16_t* tC = slotC(k & 1) + opaque(16 * it * NK);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int col = 32 * kb + 4 * g;  // rows of a row tile share their swizzle with l16
-      a = mma(cat8(*reinterpret_cast<const u32x2*>(tB + swz<NK>(l16, col)),
-                   *reinterpret_cast<const u32x2*>(tB + swz<NK>(l16, col + 16))),
-              cat8(*reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col)),
-                   *reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col + 16))),
-              a);
+      fb[kb] = cat8(*reinterpret_cast<const u32x2*>(tB + swz<NK>(l16, col)),
+                    *reinterpret_cast<const u32x2*>(tB + swz<NK>(l16, col + 16)));
+      fc[kb] = cat8(*reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col)),
+                    *reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col + 16)));
     }
+  };
+  auto gram_mma = [&](const bf16x8 (&fb)[NKB], const bf16x8 (&fc)[NKB]) __attribute__((always_inline)) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) a = mma(fb[kb], fc[kb], a);
+    return a;
+  };
+  auto gram_store = [&](int k, auto JT, auto IT, f32x4 a) __attribute__((always_inline)) {
+    constexpr int jt = decltype(JT)::value, it = decltype(IT)::value;
+    const float* S = sc(k % 3);
+    const int ti = (16 * it + l16) >> LGR;
+    const float lamI = S[ti], gamI = S[64 + ti];
     // scalars are read and the decay evaluated on every lane, then selected:
     // keeps the tile free of divergent control flow
 #pragma unroll
@@ -641,20 +649,38 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     }
     sSb(k)[tile_id(jt, it) * 64 + lane] = pack4(a);
   };
+  auto gram_one = [&](int k, auto JT, auto IT) __attribute__((always_inline)) {
+    bf16x8 fb[NKB], fc[NKB];
+    gram_fetch(k, JT, IT, fb, fc);
+    __builtin_amdgcn_sched_barrier(0);
+    gram_store(k, JT, IT, gram_mma(fb, fc));
+  };
+  // two tiles: the second tile's reads are issued behind the first tile's
+  // products and overlap its masking
+  auto gram_two = [&](int k, auto JT, auto IT, auto JT2, auto IT2) __attribute__((always_inline)) {
+    bf16x8 fb[NKB], fc[NKB], fb2[NKB], fc2[NKB];
+    gram_fetch(k, JT, IT, fb, fc);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4 a = gram_mma(fb, fc);
+    gram_fetch(k, JT2, IT2, fb2, fc2);
+    __builtin_amdgcn_sched_barrier(0);
+    gram_store(k, JT, IT, a);
+    gram_store(k, JT2, IT2, gram_mma(fb2, fc2));
+  };
   auto gram_tiles = [&](int k) __attribute__((always_inline)) {
     if constexpr (SO) return;
     using std::integral_constant;
     switch (wave) {
-      case 0: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 0>{});
-              gram_tile(k, integral_constant<int, 2>{}, integral_constant<int, 3>{}); break;
-      case 1: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 1>{});
-              gram_tile(k, integral_constant<int, 3>{}, integral_constant<int, 3>{}); break;
-      case 2: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 1>{}); break;
-      case 3: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 2>{}); break;
-      case 4: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 2>{}); break;
-      case 5: gram_tile(k, integral_constant<int, 2>{}, integral_constant<int, 2>{}); break;
-      case 6: gram_tile(k, integral_constant<int, 0>{}, integral_constant<int, 3>{}); break;
-      default: gram_tile(k, integral_constant<int, 1>{}, integral_constant<int, 3>{}); break;
+      case 0: gram_two(k, integral_constant<int, 0>{}, integral_constant<int, 0>{},
+                       integral_constant<int, 2>{}, integral_constant<int, 3>{}); break;
+      case 1: gram_two(k, integral_constant<int, 0>{}, integral_constant<int, 1>{},
+                       integral_constant<int, 3>{}, integral_constant<int, 3>{}); break;
+      case 2: gram_one(k, integral_constant<int, 1>{}, integral_constant<int, 1>{}); break;
+      case 3: gram_one(k, integral_constant<int, 0>{}, integral_constant<int, 2>{}); break;
+      case 4: gram_one(k, integral_constant<int, 1>{}, integral_constant<int, 2>{}); break;
+      case 5: gram_one(k, integral_constant<int, 2>{}, integral_constant<int, 2>{}); break;
+      case 6: gram_one(k, integral_constant<int, 0>{}, integral_constant<int, 3>{}); break;
+      default: gram_one(k, integral_constant<int, 1>{}, integral_constant<int, 3>{}); break;
     }
   };
   // i tiles owned in phase B: {0, 3} (lower waves) and {1, 2} (upper waves)
@@ -681,22 +707,30 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         }
       }
       constexpr int kb0 = NTW >= 2 ? nb / 2 : 0;
-      auto part = [&](int it) __attribute__((always_inline)) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      // all C fragments first (own i tiles, then the partner's), then the products
+      constexpr int NI = kSplit ? 4 : 2;
+      bf16x8 cf[NI][NKW];
+#pragma unroll
+      for (int q = 0; q < NI; ++q) {
+        const int it = q < 2 ? own_tile(h, q) : own_tile(1 - h, q - 2);
+        const uint16_t* tC = sC + opaque(16 * it * NK);
 #pragma unroll
         for (int kw = 0; kw < NKW; ++kw) {
-          const uint16_t* tC = sC + opaque(16 * it * NK);
           const int col = 32 * (kb0 + kw) + 4 * g;
-          z = mma(hfr[kw], cat8(*reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col)),
-                                *reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col + 16))),
-                  z);
+          cf[q][kw] = cat8(*reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col)),
+                           *reinterpret_cast<const u32x2*>(tC + swz<NK>(l16, col + 16)));
         }
-        return z;
-      };
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int idx = 0; idx < 2; ++idx) {
-        zown[u][idx] = part(own_tile(h, idx));
-        if constexpr (kSplit) sEx[((wave * UPT + u) * 2 + idx) * 64 + lane] = part(own_tile(1 - h, idx));
+      for (int q = 0; q < NI; ++q) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kw = 0; kw < NKW; ++kw) z = mma(hfr[kw], cf[q][kw], z);
+        if (q < 2)
+          zown[u][q] = z;
+        else
+          sEx[((wave * UPT + u) * 2 + (q - 2)) * 64 + lane] = z;
       }
     }
   };
@@ -729,6 +763,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const u32x2* sS = sSb(k);
     const float cdec = S[5 * 64];
     auto& xfr = xnext;  // X^T of chunk k, read during chunk k - 1
+    // B^T fragments of the state update are read first; the y products run
+    // while they land
+    bf16x8 btr[NTW][2];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        btr[i][m] = cat8(lds_read_tr(sB + swz<NK>(32 * m + rT, 16 * (nb + i) + c4)),
+                         lds_read_tr(sB + swz<NK>(32 * m + 16 + rT, 16 * (nb + i) + c4)));
+    __builtin_amdgcn_sched_barrier(0);
     auto do_it = [&](auto IT, auto IDX) __attribute__((always_inline)) {
       constexpr int it = decltype(IT)::value, idx = decltype(IDX)::value;
       const int iRow = 16 * it + l16;
@@ -790,10 +834,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           const int nt = nb + i;
           f32x4 a = acc[u][i] * cdec;
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-            a = mma(cat8(lds_read_tr(sB + swz<NK>(32 * m + rT, 16 * nt + c4)),
-                         lds_read_tr(sB + swz<NK>(32 * m + 16 + rT, 16 * nt + c4))),
-                    wfr[m], a);
+          for (int m = 0; m < 2; ++m) a = mma(btr[i][m], wfr[m], a);
           acc[u][i] = a;
         }
       }
