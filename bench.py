@@ -31,6 +31,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -162,7 +163,29 @@ def time_prefill(torch, ops, inp, steps, warmup):
         run()
     torch.cuda.synchronize()
     ms = replay_ms(torch, [run] * steps)
-    return ms, ms, None
+    return ms, ms, flushed_ms(torch, run)
+
+
+FLUSH_BYTES = 1 << 30  # four times the 256 MB Infinity Cache
+FLUSHED_RUNS = 9
+
+
+def flushed_ms(torch, run):
+    """Median duration of single launches, each after a 1 GiB read that
+    evicts the Infinity Cache, timed by HIP events on the launch stream.  The
+    eviction reads rather than writes: a written buffer leaves dirty lines
+    whose write-back to HBM overlaps the timed launch."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    acc = torch.zeros((), dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(FLUSHED_RUNS)]
+    for e0, e1 in ev:
+        acc += buf.sum()
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    del buf
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
 
 
 def time_angles(torch, ops, Bt, L, H, J, steps, warmup, seed):
@@ -472,13 +495,13 @@ def main():
             Bt, L, H, P, N, R, rope = shp
             inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260100 + i)
             torch.cuda.synchronize()
-            ms, launch_ms, wall = time_prefill(torch, ops, inp, args.steps, args.warmup)
+            ms, launch_ms, flushed = time_prefill(torch, ops, inp, args.steps, args.warmup)
             byts, flops = prefill_algo(*shp)
             res = dict(workload=f"prefill {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
                                 f"{'RoPE' if rope else 'real'} bf16 chunk {Q_ROWS // R}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, kernel_ms=launch_ms,
                        gbs=byts / (launch_ms * 1e-3) / 1e9, tflops=flops / (launch_ms * 1e-3) / 1e12,
-                       bytes=byts, flops=flops)
+                       bytes=byts, flops=flops, flushed_ms=flushed)
             res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
             res["traffic"] = traffic_for("prefill_" + name)
             res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFS
@@ -487,7 +510,8 @@ def main():
             results[name] = res
             print(f"# {res['workload']}: {ms:.3f} ms/step, {res['tokens_per_s']:.3e} tok/s, "
                   f"{res['gbs']:.0f} GB/s ({100 * res['hbm_frac']:.1f}% HBM), "
-                  f"{res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.2f}% MFMA)", file=sys.stderr, flush=True)
+                  f"{res['tflops']:.1f} TFLOP/s ({100 * res['mfma_frac']:.2f}% MFMA); "
+                  f"{flushed:.3f} ms per launch after an Infinity Cache eviction", file=sys.stderr, flush=True)
             del inp
             torch.cuda.empty_cache()
     if args.only in ("all", "prefill"):
@@ -524,7 +548,8 @@ def main():
                            "kernel": prefill_kernel_name(*prefill_shapes()["siso_real"]),
                            "split": prefill_split(*prefill_shapes()["siso_real"]),
                            "algorithmic_bytes_per_launch": head["bytes"],
-                           "mfma_tflops": head["tflops"], "mfma_frac": head["mfma_frac"]}
+                           "mfma_tflops": head["tflops"], "mfma_frac": head["mfma_frac"],
+                           "ms_after_cache_eviction": head["flushed_ms"]}
     elif "decode" in results:
         dres = results["decode"]
         out["value"] = dres["us_per_step"]
