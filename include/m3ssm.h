@@ -127,12 +127,15 @@ int m3_ssm_prefill(const m3_prefill_args* args, void* stream);
  * chunked evaluation of "La dualita: Mamba-2 e Mamba-3", sec. "Perche
  * conviene", needs only the state to hand over), then computes both halves at
  * once, the second one starting from that state -- the same carry that
- * continues a sequence across calls.  Results agree with the unsplit call to
- * rounding (the handed-over carry is exact fp32, where the unsplit walk
- * passes the pending term through bf16).  With workspace == NULL the call
- * runs unsplit.
- * The workspace holds the state and carry in the middle of each sequence
- * (Bt*H*(4NP + 4RN + 2RP + 2N) bytes, rounded); it is overwritten by every
+ * continues a sequence across calls.  When the first half has at least 8
+ * chunks, its state walk itself runs as two parts at once, the second from a
+ * zero state and zero angle, and a small kernel joins them (the recurrence is
+ * linear in the state and the rotations compose).  Results agree with the
+ * unsplit call to rounding (the handed-over carry is exact fp32, where the
+ * unsplit walk passes the pending term through bf16).  With workspace == NULL
+ * the call runs unsplit.
+ * The workspace holds the state and carry of two segments
+ * (Bt*H*2*(4NP + 4RN + 2RP + 2N) bytes, rounded); it is overwritten by every
  * call, so concurrent calls need their own.  Depends only on the shape
  * fields (and the current device), not on pointers. */
 size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args);

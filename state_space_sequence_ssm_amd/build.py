@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libm3ssm.so")
-SOURCES = ["api.hip", "angles.hip", "decode.hip", "prefill_bf16.hip", "prefill_bf16_n16.hip",
+SOURCES = ["api.hip", "angles.hip", "decode.hip", "split.hip", "prefill_bf16.hip", "prefill_bf16_n16.hip",
            "prefill_bf16_n32.hip", "prefill_bf16_n64.hip", "prefill_bf16_n128.hip", "prefill_f32.hip"]
 ARCH = "gfx950"
 

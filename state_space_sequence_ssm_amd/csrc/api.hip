@@ -46,7 +46,8 @@ int device_cus() {
 constexpr int kMinSegChunks = 4;  // both halves keep at least this many chunks
 struct SplitPlan {
   bool on = false;
-  int segLen = 0;
+  int segLen = 0;  // tokens of the first half
+  int segA = 0;    // > 0: the first half's state-only walk runs as two parts of segA and the rest
   size_t oH = 0, oB = 0, oX = 0, oPhi = 0, bytes = 0;
 };
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -59,11 +60,13 @@ SplitPlan split_plan(const m3_prefill_args* a) {
   const size_t u = size_t(units);
   s.on = true;
   s.segLen = (((a->L + 1) / 2 + Q - 1) / Q) * Q;
+  if (s.segLen >= 2 * kMinSegChunks * Q) s.segA = (((s.segLen + 1) / 2 + Q - 1) / Q) * Q;
+  // state and carry of two segments: [2][units][...] each
   s.oH = 0;
-  s.oB = up256(s.oH + u * a->N * a->P * 4);
-  s.oX = up256(s.oB + u * a->R * a->N * 4);
-  s.oPhi = up256(s.oX + u * a->R * a->P * 2);
-  s.bytes = up256(s.oPhi + (a->theta != nullptr ? u * (a->N / 2) * 4 : 0));
+  s.oB = up256(s.oH + 2 * u * a->N * a->P * 4);
+  s.oX = up256(s.oB + 2 * u * a->R * a->N * 4);
+  s.oPhi = up256(s.oX + 2 * u * a->R * a->P * 2);
+  s.bytes = up256(s.oPhi + (a->theta != nullptr ? 2 * u * (a->N / 2) * 4 : 0));
   return s;
 }
 
@@ -140,9 +143,10 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   if (!sp.on || a->workspace == nullptr) return hip_status(m3::launch_prefill_bf16(p, false, st));
   if (a->workspace_bytes < sp.bytes || !aligned(a->workspace, 256)) return M3_ERR_INVALID_ARG;
   unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+  const size_t u = size_t(a->Bt) * a->H;
   float* hMid = reinterpret_cast<float*>(ws + sp.oH);
   float* bMid = reinterpret_cast<float*>(ws + sp.oB);
-  void* xMid = ws + sp.oX;
+  unsigned char* xMid = ws + sp.oX;
   float* phiMid = a->theta != nullptr ? reinterpret_cast<float*>(ws + sp.oPhi) : nullptr;
   // 1) state and carry after the first segLen tokens (carry-in of the call)
   m3::PrefillParams pa = p;
@@ -153,16 +157,43 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   pa.Bprev_rot_out = bMid;
   pa.xprev_out = xMid;
   pa.phi_out = phiMid;
+  if (sp.segA > 0) {
+    // as two parts at once, the second from a zero start, then joined
+    pa.nseg = 2;
+    pa.segLen = sp.segA;
+    pa.outAll = 1;
+  }
   hipError_t e = m3::launch_prefill_bf16(pa, true, st);
   if (e != hipSuccess) return hip_status(e);
-  // 2) both segments at once; the second starts from that carry
+  const float* hCarry = hMid;
+  const float* bCarry = bMid;
+  const void* xCarry = xMid;
+  const float* phiCarry = phiMid;
+  if (sp.segA > 0) {
+    m3::CombineParams c{};
+    c.Bt = a->Bt; c.H = a->H; c.N = a->N; c.P = a->P; c.R = a->R; c.Lfull = a->L;
+    c.t1 = sp.segA;
+    c.t2 = sp.segLen;
+    c.dt = a->dt; c.lam = a->lam; c.A = a->A;
+    c.h = hMid;
+    c.Bprev = bMid;
+    c.x0 = xMid;
+    c.phi = phiMid;
+    e = m3::launch_split_combine(c, st);
+    if (e != hipSuccess) return hip_status(e);
+    // joined state in part 0's slot; B, x and angle carries of part 1
+    bCarry = bMid + u * a->R * a->N;
+    xCarry = xMid + u * a->R * a->P * 2;
+    phiCarry = phiMid != nullptr ? phiMid + u * (a->N / 2) : nullptr;
+  }
+  // 2) both halves at once; the second starts from that carry
   m3::PrefillParams pb = p;
   pb.nseg = 2;
   pb.segLen = sp.segLen;
-  pb.h_mid = hMid;
-  pb.Bprev_mid = bMid;
-  pb.xprev_mid = xMid;
-  pb.phi_mid = phiMid;
+  pb.h_mid = hCarry;
+  pb.Bprev_mid = bCarry;
+  pb.xprev_mid = xCarry;
+  pb.phi_mid = phiCarry;
   return hip_status(m3::launch_prefill_bf16(pb, false, st));
 }
 

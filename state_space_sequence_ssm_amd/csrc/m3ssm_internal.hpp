@@ -50,6 +50,9 @@ struct PrefillParams {
   // takes the *_mid carry (the state after the previous segment).  Only the
   // last segment writes h_final and the carry-out.
   int Lfull, nseg, segLen;
+  // outAll: every segment writes its end state and carry-out, segment s at
+  // offset s x (the size of one such output)
+  int outAll;
   const float* h_mid;
   const float* Bprev_mid;
   const void* xprev_mid;
@@ -68,6 +71,20 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillParams& p, bool state_only, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t s);
 hipError_t launch_angles(const AnglesParams& p, hipStream_t s);
+// Joins the end states of two consecutive segments into the state after the
+// second (see split.hip): in place in the workspace buffers.
+struct CombineParams {
+  int Bt, H, N, P, R, Lfull;
+  int t1, t2;  // the second segment covers tokens [t1, t2) of each batch item
+  const float* dt;
+  const float* lam;
+  const float* A;
+  float* h;        // [2][Bt*H][N][P]: segment 0 end state -> joined state
+  float* Bprev;    // [2][Bt*H][R][N]: segment 1's (relative frame) -> rotated in place
+  const void* x0;  // [Bt*H][R][P] bf16: segment 0's last x
+  float* phi;      // [2][Bt*H][N/2] or null: segment 1's relative angle -> absolute
+};
+hipError_t launch_split_combine(const CombineParams& c, hipStream_t s);
 // LDS bytes the prefill kernel needs for (N, P, rope); 0 if not compiled.
 size_t prefill_lds_bytes_bf16(int N, int P, bool rope);
 size_t prefill_lds_bytes_f32(int N, int P, bool rope);

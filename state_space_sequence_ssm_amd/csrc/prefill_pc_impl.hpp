@@ -965,6 +965,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 
   // ================================================================ epilogue
   if constexpr (kStageY) flush_y(nch - 1);  // the walk ended on a barrier
+  if (!lastSeg && !p.outAll) return;
+  // with outAll, segment s writes at offset s x (one output's size)
+  const size_t so = p.outAll ? static_cast<size_t>(seg) : 0;
+  const size_t uAll = static_cast<size_t>(units);
+  float* const hOut = p.h_final != nullptr ? p.h_final + so * uAll * N * P : nullptr;
+  float* const phiOut = p.phi_out != nullptr ? p.phi_out + so * uAll * (N / 2) : nullptr;
+  float* const bOut = p.Bprev_rot_out != nullptr ? p.Bprev_rot_out + so * uAll * R * N : nullptr;
+  bf16_t* const xOut = p.xprev_out != nullptr ? static_cast<bf16_t*>(p.xprev_out) + so * uAll * R * P : nullptr;
   // each wave writes its kept n tiles (both waves hold all of them without the split)
   auto write_state = [&](auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
@@ -977,26 +985,25 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         for (int i = 0; i < NTW; ++i)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            p.h_final[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * (nb + i) + 4 * g + jj) * P + 16 * pt + l16] =
+            hOut[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * (nb + i) + 4 * g + jj) * P + 16 * pt + l16] =
                 acc[u][i][jj];
       }
     }
   };
-  if (!lastSeg) return;
-  if (p.h_final != nullptr) {
+  if (hOut != nullptr) {
     if (!upper)
       write_state(std::integral_constant<int, 0>{});
     else if (kSplit)
       write_state(std::integral_constant<int, 1>{});
   }
   if constexpr (ROPE) {
-    if (p.phi_out != nullptr)
-      for (int q = tid; q < N / 2; q += kThreads) p.phi_out[static_cast<size_t>(bh) * (N / 2) + q] = phiC[q];
+    if (phiOut != nullptr)
+      for (int q = tid; q < N / 2; q += kThreads) phiOut[static_cast<size_t>(bh) * (N / 2) + q] = phiC[q];
   }
   // carry-out of token L-1: rotated B (fp32) and x
   {
     const int t = L - 1;
-    if (p.Bprev_rot_out != nullptr) {
+    if (bOut != nullptr) {
       for (int e = tid; e < R * (N / 2); e += kThreads) {
         const int r = e / (N / 2), q = e % (N / 2);
         const bf16_t* src = static_cast<const bf16_t*>(p.B) + ((tok0 + t) * H + hh) * R * N + r * N;
@@ -1009,14 +1016,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           a0 = b0;
           a1 = b1;
         }
-        float* dst = p.Bprev_rot_out + (static_cast<size_t>(bh) * R + r) * N + 2 * q;
+        float* dst = bOut + (static_cast<size_t>(bh) * R + r) * N + 2 * q;
         dst[0] = a0;
         dst[1] = a1;
       }
     }
-    if (p.xprev_out != nullptr)
+    if (xOut != nullptr)
       for (int e = tid; e < R * P; e += kThreads)
-        static_cast<bf16_t*>(p.xprev_out)[static_cast<size_t>(bh) * R * P + e] =
+        xOut[static_cast<size_t>(bh) * R * P + e] =
             static_cast<const bf16_t*>(p.x)[((tok0 + t) * H + hh) * R * P + e];
   }
 }

@@ -92,7 +92,9 @@ def test_prefill_workspace_size(Bt, H, L, N, P, R, rope, split):
     a.theta = 0x30000000 if rope else None
     got = lib.m3_ssm_prefill_workspace_size(ctypes.byref(a))
     u = Bt * H
-    want = _up256(u * N * P * 4) + _up256(u * R * N * 4) + _up256(u * R * P * 2) + _up256(u * (N // 2) * 4 if rope else 0)
+    # state and carry of two segments
+    want = (_up256(2 * u * N * P * 4) + _up256(2 * u * R * N * 4) + _up256(2 * u * R * P * 2)
+            + _up256(2 * u * (N // 2) * 4 if rope else 0))
     assert got == (want if split else 0)
     a.in_dtype = _lib.M3_F32
     assert lib.m3_ssm_prefill_workspace_size(ctypes.byref(a)) == 0  # fp32 runs unsplit
