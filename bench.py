@@ -75,19 +75,34 @@ def prefill_split(Bt, L, H, P, N, R, rope, cus=256):
     return 2 * Bt * H <= cus and L >= 8 * (64 // R)
 
 
+def prefill_two_part(Bt, L, H, P, N, R, rope, cus=256):
+    """Whether a split also walks the first half's state in two parts at once
+    (the first half has at least 8 chunks)."""
+    Q = 64 // R
+    half = ((L + 1) // 2 + Q - 1) // Q * Q
+    return prefill_split(Bt, L, H, P, N, R, rope, cus) and half >= 8 * Q
+
+
+COMBINE_KERNEL = "m3::(anonymous namespace)::split_combine_kernel"
+
+
 def decode_kernel_name(Bt, H, P, N, R):
     return f"m3::decode_step_kernel<m3::bf16_t, {N}, {P}, {4 if R <= 4 else 16}>"
 
 
 def unit_kernels():
     """(unit key, kernel symbol, launch grid in threads) of every timed launch;
-    a split prefill is two launches of one unit (state-only walk, then both
-    halves)."""
+    a split prefill is several launches of one unit (the state-only walk of
+    the first half, in two parts joined by the combine kernel when it is long
+    enough, then both halves)."""
     out = []
     for name, shp in prefill_shapes().items():
         Bt, L, H, P, N, R, rope = shp
         if prefill_split(*shp):
-            out.append(("prefill_" + name, prefill_kernel_name(*shp, state_only=True), Bt * H * 512))
+            two = prefill_two_part(*shp)
+            out.append(("prefill_" + name, prefill_kernel_name(*shp, state_only=True), (2 if two else 1) * Bt * H * 512))
+            if two:
+                out.append(("prefill_" + name, COMBINE_KERNEL, Bt * H * 256))
             out.append(("prefill_" + name, prefill_kernel_name(*shp), 2 * Bt * H * 512))
         else:
             out.append(("prefill_" + name, prefill_kernel_name(*shp), Bt * H * 512))
@@ -420,7 +435,7 @@ def report_pmc(fetch_prefix, write_prefix):
         e["write_bytes"] += round(w_avg * sw)
         lines.append(f"| {unit} | `{k}` | {len(fv)} | {f_avg:.4g} | {w_avg:.4g} | {tot:.4g} | {algo[unit]:.4g} "
                      f"| {tot / algo[unit]:.3f} |")
-    lines += ["", "Per call of the entry point (a split prefill is two launches):", "",
+    lines += ["", "Per call of the entry point (a split prefill is several launches):", "",
               "| unit | HBM bytes per call | algorithmic bytes | ratio |", "|---|---|---|---|"]
     for unit, e in units.items():
         lines.append(f"| {unit} | {e['bytes_per_launch']:.4g} | {algo[unit]:.4g} | {e['bytes_per_launch'] / algo[unit]:.3f} |")
