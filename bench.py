@@ -102,7 +102,7 @@ def unit_kernels():
             two = prefill_two_part(*shp)
             out.append(("prefill_" + name, prefill_kernel_name(*shp, state_only=True), (2 if two else 1) * Bt * H * 512))
             if two:
-                out.append(("prefill_" + name, COMBINE_KERNEL, Bt * H * 256))
+                out.append(("prefill_" + name, COMBINE_KERNEL, Bt * H * 256))  # grid x; y = 8 parts
             out.append(("prefill_" + name, prefill_kernel_name(*shp), 2 * Bt * H * 512))
         else:
             out.append(("prefill_" + name, prefill_kernel_name(*shp), Bt * H * 512))
@@ -350,7 +350,17 @@ def _csv_rows(path):
 
 
 def _short(name):
-    return name.replace("void ", "").split("(")[0]
+    """Kernel symbol without its argument list (the last parenthesised group)."""
+    name = name.replace("void ", "")
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        if name[i] == ")":
+            depth += 1
+        elif name[i] == "(":
+            depth -= 1
+            if depth == 0:
+                return name[:i]
+    return name
 
 
 def report_trace(prefix):
@@ -423,8 +433,14 @@ def report_pmc(fetch_prefix, write_prefix):
     algo["decode"] = decode_algo(Bt, H, P, N, R, True)[0]
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
     algo["angles"] = 2 * Bt * L * H * (N // 2) * 4 + Bt * H * (N // 2) * 4
+    def find(acc, k, g):  # the counter file gives the total grid: 2-D launches match by name
+        if (k, g) in acc:
+            return acc[(k, g)]
+        hits = [v for (kk, _), v in acc.items() if kk == k]
+        return hits[0] if len(hits) == 1 else None
+
     for unit, k, g in unit_kernels():
-        fv, wv = fetch.get((k, g)), write.get((k, g))
+        fv, wv = find(fetch, k, g), find(write, k, g)
         if not fv or not wv:
             continue
         f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)

@@ -23,8 +23,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// grid (Bt*H, kParts): part y joins state rows [y N / kParts, (y+1) N / kParts);
+// part 0 also handles the B and angle carries
+constexpr int kParts = 8;
+
 __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c) {
   const int bh = blockIdx.x;
+  const int part = blockIdx.y;
   const int b = bh / c.H, hh = bh % c.H;
   const int tid = threadIdx.x;
   const size_t units = static_cast<size_t>(c.Bt) * c.H;
@@ -50,7 +55,8 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
   const float* B1 = c.Bprev + static_cast<size_t>(bh) * c.R * c.N;
   const bf16_t* x1 = static_cast<const bf16_t*>(c.x0) + static_cast<size_t>(bh) * c.R * c.P;
   // state: element (n, p), rows handled in pairs so the rotation stays local
-  for (int e = tid; e < J * c.P; e += kThreads) {
+  const int j0 = part * J / kParts, j1 = (part + 1) * J / kParts;
+  for (int e = j0 * c.P + tid; e < j1 * c.P; e += kThreads) {
     const int j = e / c.P, p = e % c.P;
     float cs = 1.f, sn = 0.f;
     if (c.phi != nullptr) sincosf(sPhi[j], &sn, &cs);
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
     h1[static_cast<size_t>(2 * j) * c.P + p] = v[0] + cs * r0 + sn * r1;
     h1[static_cast<size_t>(2 * j + 1) * c.P + p] = v[1] + cs * r1 - sn * r0;
   }
-  if (c.phi != nullptr) {
+  if (c.phi != nullptr && part == 0) {
     // second segment's B carry (relative frame) -> absolute; its angle carry
     float* B2 = c.Bprev + (units + bh) * c.R * c.N;
     for (int e = tid; e < c.R * J; e += kThreads) {
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
 
 hipError_t launch_split_combine(const CombineParams& c, hipStream_t s) {
   if (c.N / 2 > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(split_combine_kernel, dim3(c.Bt * c.H), dim3(kThreads), 0, s, c);
+  hipLaunchKernelGGL(split_combine_kernel, dim3(c.Bt * c.H, kParts), dim3(kThreads), 0, s, c);
   return hipGetLastError();
 }
 
