@@ -113,14 +113,15 @@ def unit_kernels():
     return out
 
 
-def prefill_algo(Bt, L, H, P, N, R, rope):
+def prefill_algo(Bt, L, H, P, N, R, rope, omega=False):
     """Algorithmic bytes (each input read once, each output written once) and
-    MFMA flops (chunked-scan count 2L[Q R^2 (N+P) + 2 R N P] per (b,h), Q = 64/R)."""
+    MFMA flops (chunked-scan count 2L[Q R^2 (N+P) + 2 R N P] per (b,h), Q = 64/R).
+    omega: the angles come as rates per token shared by the heads."""
     bf, f4 = 2, 4
     tok = Bt * L * H
     byts = tok * R * (P + 2 * N) * bf + tok * 2 * f4 + H * f4   # x, B, C, dt, lam, A
     if rope:
-        byts += tok * (N // 2) * f4                               # theta
+        byts += (Bt * L if omega else tok) * (N // 2) * f4        # omega or theta
     byts += tok * R * P * bf                                      # y
     byts += Bt * H * N * P * f4                                   # h_final
     Q = Q_ROWS // R
@@ -153,14 +154,14 @@ def gen_prefill(torch, Bt, L, H, P, N, R, rope, seed):
     dt = torch.nn.functional.softplus(torch.randn((Bt, L, H), generator=g, device=dev) - 4.0).contiguous()
     lam = torch.sigmoid(torch.randn((Bt, L, H), generator=g, device=dev)).contiguous()
     A = (-torch.exp(torch.rand((H,), generator=g, device=dev) * math.log(16.0))).contiguous()
-    theta = None
+    theta = om = None
     if rope:
         om = torch.randn((Bt, L, N // 2), generator=g, device=dev)
         theta = (dt[:, :, :, None] * om[:, :, None, :]).contiguous()
-    return dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta)
+    return dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta, omega=om)
 
 
-def time_prefill(torch, ops, inp, steps, warmup):
+def time_prefill(torch, ops, inp, steps, warmup, use_omega=False):
     y = torch.empty_like(inp["x"])
     Bt, L, H, R, P = inp["x"].shape
     N = inp["B"].shape[-1]
@@ -170,9 +171,11 @@ def time_prefill(torch, ops, inp, steps, warmup):
     nws = ops.prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=inp["x"].dtype, rope=inp["theta"] is not None)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else False
 
+    theta, omega = (None, inp["omega"]) if use_omega else (inp["theta"], None)
+
     def run():
-        ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], inp["theta"],
-                           y=y, h_final=hf, workspace=ws)
+        ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], theta,
+                           y=y, h_final=hf, workspace=ws, omega=omega)
 
     for _ in range(max(warmup, 1)):
         run()
@@ -522,14 +525,18 @@ def main():
            "data": "synthetic (seeded, device-generated, resident in HBM)"}
     results = {}
     if args.only in ("all", "prefill"):
-        for i, (name, shp) in enumerate(prefill_shapes().items()):
+        # the RoPE workloads also with their angles given as rates (theta = dt * omega on chip)
+        runs = [(name, shp, False) for name, shp in prefill_shapes().items()]
+        runs += [(name + "_omega", shp, True) for name, shp in prefill_shapes().items() if shp[-1]]
+        for i, (name, shp, use_omega) in enumerate(runs):
             Bt, L, H, P, N, R, rope = shp
             inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260100 + i)
             torch.cuda.synchronize()
-            ms, launch_ms, flushed = time_prefill(torch, ops, inp, args.steps, args.warmup)
-            byts, flops = prefill_algo(*shp)
+            ms, launch_ms, flushed = time_prefill(torch, ops, inp, args.steps, args.warmup, use_omega)
+            byts, flops = prefill_algo(*shp, omega=use_omega)
+            angles = "RoPE, angles from rates" if use_omega else ("RoPE" if rope else "real")
             res = dict(workload=f"prefill {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
-                                f"{'RoPE' if rope else 'real'} bf16 chunk {Q_ROWS // R}",
+                                f"{angles} bf16 chunk {Q_ROWS // R}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, kernel_ms=launch_ms,
                        gbs=byts / (launch_ms * 1e-3) / 1e9, tflops=flops / (launch_ms * 1e-3) / 1e12,
                        bytes=byts, flops=flops, flushed_ms=flushed)
@@ -594,7 +601,7 @@ def main():
         out["decode_roofline"] = {"bound": "hbm", "achieved": dres["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": dres["hbm_frac"], "traffic": traffic_for("decode"),
                                   "kernel": decode_kernel_name(*DECODE_SHAPE)}
-    for k in ("siso_rope", "mimo_rope"):
+    for k in ("siso_rope", "mimo_rope", "siso_rope_omega", "mimo_rope_omega"):
         if k in results:
             out["prefill_" + k] = results[k]
     if "angles" in results:

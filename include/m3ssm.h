@@ -71,6 +71,16 @@ typedef enum m3_dtype {
  *   A       [H]               float32    per-head scalar A (< 0)
  *   theta   [Bt, L, H, N/2]   float32    per-token rotation angles, or NULL
  *                                        for the real-valued SSM (no RoPE)
+ *   omega   [Bt, L, N/2]      float32    alternative to theta (bf16 inputs
+ *                                        only): rotation rates per token and
+ *                                        pair, shared by all heads; the angle
+ *                                        is then theta_t = Delta_t * omega_t
+ *                                        (the step times the rate, per head),
+ *                                        formed on chip, which saves reading
+ *                                        the per-head theta tensor.  Setting
+ *                                        both theta and omega is
+ *                                        M3_ERR_INVALID_ARG; omega with fp32
+ *                                        inputs is M3_ERR_UNSUPPORTED.
  *   Carry-in, each nullable (NULL = zeros, i.e. a fresh sequence):
  *   h0        [Bt, H, N, P]   float32    state before the first token
  *   Bprev_rot [Bt, H, R, N]   float32    rotated B of the token before
@@ -82,7 +92,8 @@ typedef enum m3_dtype {
  *   Bprev_rot_out [Bt,H,R,N]  float32    rotated B_{L-1} (nullable)
  *   xprev_out [Bt, H, R, P]   in_dtype   x_{L-1} (nullable)
  *   phi_out   [Bt, H, N/2]    float32    Phi_{L-1} reduced modulo 2*pi into
- *                                        [-pi, pi] (nullable; needs theta)
+ *                                        [-pi, pi] (nullable; needs theta or
+ *                                        omega)
  * Sizes: Bt, L, H >= 1; N, P in {16, 32, 64, 128}; R a power of two <= 64;
  * combinations whose chunk tiles exceed the 160 KB LDS of a CU return
  * M3_ERR_UNSUPPORTED (fp32 with RoPE at N = 128, and fp32 at N = P = 128);
@@ -115,6 +126,7 @@ typedef struct m3_prefill_args {
   float* phi_out;
   void* workspace;        /* device scratch of workspace_bytes (256-byte aligned), or NULL */
   size_t workspace_bytes;
+  const float* omega;     /* [Bt, L, N/2] angular rates, or NULL (see above) */
 } m3_prefill_args;
 
 int m3_ssm_prefill(const m3_prefill_args* args, void* stream);

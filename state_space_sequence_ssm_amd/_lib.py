@@ -29,7 +29,7 @@ class PrefillArgs(ctypes.Structure):
         ("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp), ("lam", _vp), ("A", _vp), ("theta", _vp),
         ("h0", _vp), ("Bprev_rot", _vp), ("xprev", _vp), ("phi0", _vp),
         ("y", _vp), ("h_final", _vp), ("Bprev_rot_out", _vp), ("xprev_out", _vp), ("phi_out", _vp),
-        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("omega", _vp),
     ]
 
 

@@ -66,7 +66,8 @@ SplitPlan split_plan(const m3_prefill_args* a) {
   s.oB = up256(s.oH + 2 * u * a->N * a->P * 4);
   s.oX = up256(s.oB + 2 * u * a->R * a->N * 4);
   s.oPhi = up256(s.oX + 2 * u * a->R * a->P * 2);
-  s.bytes = up256(s.oPhi + (a->theta != nullptr ? 2 * u * (a->N / 2) * 4 : 0));
+  const bool rope = a->theta != nullptr || a->omega != nullptr;
+  s.bytes = up256(s.oPhi + (rope ? 2 * u * (a->N / 2) * 4 : 0));
   return s;
 }
 
@@ -98,12 +99,15 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
   if (!a->x || !a->B || !a->C || !a->dt || !a->lam || !a->A || !a->y) return M3_ERR_INVALID_ARG;
   if ((a->Bprev_rot == nullptr) != (a->xprev == nullptr)) return M3_ERR_INVALID_ARG;
-  if (a->theta == nullptr && (a->phi0 != nullptr || a->phi_out != nullptr)) return M3_ERR_INVALID_ARG;
-  if (a->theta != nullptr && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
+  if (a->theta != nullptr && a->omega != nullptr) return M3_ERR_INVALID_ARG;  // one angle source
+  const bool rope = a->theta != nullptr || a->omega != nullptr;
+  if (!rope && (a->phi0 != nullptr || a->phi_out != nullptr)) return M3_ERR_INVALID_ARG;
+  if (rope && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
+  if (a->omega != nullptr && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
   if (!pow2(a->R) || a->R > 64) return M3_ERR_UNSUPPORTED;
   if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
   if (a->chunk != 0 && a->chunk != 64 / a->R) return M3_ERR_UNSUPPORTED;
-  const void* v16[] = {a->x, a->B, a->C, a->y, a->theta, a->h0, a->Bprev_rot, a->xprev,
+  const void* v16[] = {a->x, a->B, a->C, a->y, a->theta, a->omega, a->h0, a->Bprev_rot, a->xprev,
                        a->phi0, a->h_final, a->Bprev_rot_out, a->xprev_out, a->phi_out};
   for (const void* p : v16)
     if (!al16(p)) return M3_ERR_INVALID_ARG;
@@ -119,8 +123,8 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
     const double itemTh = double(a->L) * a->H * (a->N / 2) * 4.0;
     if (item > 2147483000.0 || itemTh > 2147483000.0) return M3_ERR_UNSUPPORTED;
   }
-  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, a->theta != nullptr)
-                          : m3::prefill_lds_bytes_f32(a->N, a->P, a->theta != nullptr);
+  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, rope)
+                          : m3::prefill_lds_bytes_f32(a->N, a->P, rope);
   if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
 
   m3::PrefillParams p{};
@@ -130,6 +134,7 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   p.log2R = lg;
   p.bf16 = bf16;
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.theta = a->theta;
+  p.omega = a->omega;
   p.h0 = a->h0; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev; p.phi0 = a->phi0;
   p.y = a->y; p.h_final = a->h_final; p.Bprev_rot_out = a->Bprev_rot_out; p.xprev_out = a->xprev_out;
   p.phi_out = a->phi_out;
@@ -147,7 +152,7 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   float* hMid = reinterpret_cast<float*>(ws + sp.oH);
   float* bMid = reinterpret_cast<float*>(ws + sp.oB);
   unsigned char* xMid = ws + sp.oX;
-  float* phiMid = a->theta != nullptr ? reinterpret_cast<float*>(ws + sp.oPhi) : nullptr;
+  float* phiMid = rope ? reinterpret_cast<float*>(ws + sp.oPhi) : nullptr;
   // 1) state and carry after the first segLen tokens (carry-in of the call)
   m3::PrefillParams pa = p;
   pa.L = sp.segLen;

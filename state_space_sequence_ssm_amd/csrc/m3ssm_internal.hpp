@@ -34,6 +34,9 @@ struct PrefillParams {
   const float* lam;
   const float* A;
   const float* theta;
+  // omega [Bt, L, N/2] (bf16 path): per-token angular rates shared by the
+  // heads; when set (theta is then null), theta = Delta * omega on chip
+  const float* omega;
   const float* h0;
   const float* Bprev_rot;
   const void* xprev;

@@ -269,8 +269,8 @@ struct PcLayout {
   static constexpr size_t oB = oC + kSlotC;
   static constexpr size_t oX = oB + kSlotC;
   static constexpr size_t kSlot = oX + kSlotX;
-  static constexpr size_t oSC = 2 * kSlot;                // [3][6][64] fp32 scalars
-  static constexpr size_t kSC = 6 * 64 * 4;
+  static constexpr size_t oSC = 2 * kSlot;                // [3][7][64] fp32 scalars
+  static constexpr size_t kSC = 7 * 64 * 4;
   static constexpr size_t kSBytes = 10 * 64 * 8;          // [10][64] x 8 B masked S^T pieces
   static constexpr size_t oS = oSC + 3 * kSC;
   static constexpr size_t oPhiC = oS + kSBytes;           // [N/2] fp32 angle carry
@@ -351,7 +351,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const rsrc_t rY = make_rsrc(SO ? p.x : static_cast<bf16_t*>(p.y) + tok0 * H * R * P, uint32_t(SO ? 0 : tokB * R * P * 2));
   const rsrc_t rDt = make_rsrc(p.dt + tok0 * H, uint32_t(tokB * 4));
   const rsrc_t rLam = make_rsrc(p.lam + tok0 * H, uint32_t(tokB * 4));
-  const rsrc_t rTh = make_rsrc(ROPE ? p.theta + tok0 * H * (N / 2) : p.dt, uint32_t(ROPE ? tokB * (N / 2) * 4 : 0));
+  // angles: theta [.., H, N/2] per (token, head), or omega [.., N/2] per token
+  // (shared by the heads; scaled by Delta in the angle scan)
+  const bool om = ROPE && p.omega != nullptr;
+  const int thTok = om ? N / 2 : H * (N / 2);  // floats per token
+  const int thHead = om ? 0 : hh * (N / 2);
+  const rsrc_t rTh = make_rsrc(!ROPE ? p.dt : (om ? p.omega + (static_cast<size_t>(b) * p.Lfull + t0) * (N / 2)
+                                                   : p.theta + tok0 * H * (N / 2)),
+                               uint32_t(ROPE ? static_cast<size_t>(L) * thTok * 4 : 0));
 
   auto slotC = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oC); };
   auto slotB = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<uint16_t*>(smem + s * Lt::kSlot + Lt::oB); };
@@ -420,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         const int e = tid + s * kThreads;
         const int tok = e / NG, grp = e % NG;
         const uint32_t off4 =
-            e < kThUnits ? (static_cast<uint32_t>((c * Q + tok) * H + hh) * (N / 2) + 4 * grp) * 4u : kBad;
+            e < kThUnits ? (static_cast<uint32_t>((c * Q + tok) * thTok + thHead) + 4 * grp) * 4u : kBad;
         rawTh[set][s] = bloadf4(rTh, off4);
       }
     }
@@ -444,6 +451,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       S[3 * 64 + lane] = __builtin_amdgcn_exp2f(lamEnd - lamc) * del;
       S[4 * 64 + lane] = __builtin_amdgcn_exp2f(lamc);
       if (lane == 0) S[5 * 64] = __builtin_amdgcn_exp2f(lamEnd);
+      S[6 * 64 + lane] = rdt[set];  // Delta, for angles given as rates
     }
     if constexpr (ROPE) {
       float* tab = phiTab(c & 1);
@@ -467,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if ((s * kWaves + wave) * R < NG) {
           constexpr f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
           f32x4 v = q4 < NG ? *reinterpret_cast<const f32x4*>(tab + tl * PH + 4 * q4) : zero4;
+          if (om) v *= sc(c % 3)[6 * 64 + tl];  // theta = Delta * omega
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = seg_scan<Q>(v[e]);
           if (q4 < NG) {

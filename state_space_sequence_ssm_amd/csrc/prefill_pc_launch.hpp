@@ -35,7 +35,8 @@ hipError_t launch_r(const PrefillParams& p, hipStream_t s) {
 
 template <int N, int P, bool SO>
 hipError_t launch_rr(const PrefillParams& p, hipStream_t s) {
-  return p.theta != nullptr ? launch_r<N, P, true, SO>(p, s) : launch_r<N, P, false, SO>(p, s);
+  const bool rope = p.theta != nullptr || p.omega != nullptr;
+  return rope ? launch_r<N, P, true, SO>(p, s) : launch_r<N, P, false, SO>(p, s);
 }
 
 template <int N, bool SO>

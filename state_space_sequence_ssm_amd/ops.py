@@ -49,9 +49,11 @@ def _stream(stream) -> int:
 
 def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
                    *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
-                   want_state=True, want_carry=False, chunk=0, workspace=None, stream=None):
+                   want_state=True, want_carry=False, chunk=0, workspace=None, omega=None, stream=None):
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
-    dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None; optional
+    dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None (or
+    instead omega [Bt,L,N/2] fp32: rates shared by the heads, theta = dt * omega
+    formed on chip, bf16 inputs only); optional
     carry-in h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
     Output tensors are allocated when not given.  workspace: a uint8 device
     tensor of at least prefill_workspace_bytes(...) bytes, None to allocate one
@@ -70,7 +72,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
             Bprev_rot_out = torch.empty((Bt, H, R, N), device=x.device, dtype=f32)
         if xprev_out is None:
             xprev_out = torch.empty((Bt, H, R, P), device=x.device, dtype=x.dtype)
-        if theta is not None and phi_out is None:
+        if (theta is not None or omega is not None) and phi_out is None:
             phi_out = torch.empty((Bt, H, N // 2), device=x.device, dtype=f32)
     a = _lib.PrefillArgs()
     a.Bt, a.L, a.H, a.P, a.N, a.R, a.chunk = Bt, L, H, P, N, R, chunk
@@ -82,6 +84,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a.lam = _ptr(lam, f32, (Bt, L, H), "lam")
     a.A = _ptr(A, f32, (H,), "A")
     a.theta = _ptr(theta, f32, (Bt, L, H, N // 2), "theta")
+    a.omega = _ptr(omega, f32, (Bt, L, N // 2), "omega")
     a.h0 = _ptr(h0, f32, (Bt, H, N, P), "h0")
     a.Bprev_rot = _ptr(Bprev_rot, f32, (Bt, H, R, N), "Bprev_rot")
     a.xprev = _ptr(xprev, x.dtype, (Bt, H, R, P), "xprev")

@@ -93,13 +93,14 @@ def make_inputs(s: Shape, seed: int, *, h0: bool = False, carry: bool = False,
     if lam_const is not None:
         lam = np.full_like(lam, np.float32(lam_const))
     A = (-np.exp(u_A * np.float32(np.log(16.0)))).astype(np.float32)
-    theta = None
+    theta = omega = None
     if s.rope:
         omega = _normal(rng, (s.Bt, s.L, s.N // 2))
         theta = (dt[:, :, :, None] * omega[:, :, None, :]).astype(np.float32)
         if theta_zero:
             theta = np.zeros_like(theta)
-    out = dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta,
+            omega = np.zeros_like(omega)
+    out = dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta, omega=omega,
                h0=None, Bprev_rot=None, xprev=None, phi0=None)
     if h0:
         out["h0"] = _normal(rng, (s.Bt, s.H, s.N, s.P), 0.1)

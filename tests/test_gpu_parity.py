@@ -92,6 +92,44 @@ def test_prefill_small(ops, case):
         assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-4
 
 
+# ----------------------------------------------------------------- angles from rates
+OMEGA = [
+    # Bt, L, H, P, N, R, carry  (bf16; theta = dt * omega formed on chip)
+    (2, 131, 3, 64, 64, 1, True),
+    (1, 100, 2, 64, 64, 4, True),
+    (1, 77, 2, 32, 128, 2, False),
+    (1, 45, 2, 16, 32, 8, True),
+    (1, 1500, 2, 64, 64, 1, True),  # split, first half in two parts
+]
+
+
+@pytest.mark.parametrize("case", OMEGA, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_omega(ops, case):
+    """Angles given as per-token rates shared by the heads: the same results as
+    the oracle on theta = dt * omega, and as the call that is given that theta."""
+    Bt, L, H, P, N, R, carry = case
+    s = Shape(Bt, L, H, P, N, R, "bf16", True)
+    _say("prefill omega", case)
+    d = make_inputs(s, 3000 + L + N, h0=carry, carry=carry)
+    dd = to_device(d, s)
+    kw = dict(want_state=True, want_carry=True)
+    args = (dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], dd["A"])
+    carry_in = (dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"))
+    out = ops.m3_ssm_prefill(*args, None, *carry_in, omega=dd["omega"], **kw)
+    ref_gpu = ops.m3_ssm_prefill(*args, dd["theta"], *carry_in, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(d)
+    ey = orc.rel_l2(host(out["y"]), ref["y"])
+    eh = orc.rel_l2(host(out["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-3
+    # against the theta call: the products dt * omega agree to fp32 rounding
+    assert orc.rel_l2(host(out["y"]), host(ref_gpu["y"])) <= 5e-3
+    assert orc.rel_l2(host(out["h"]), host(ref_gpu["h"])) <= 5e-3
+    assert np.max(angle_diff(host(out["phi"]), host(ref_gpu["phi"]))) <= 1e-4
+
+
 def test_prefill_deterministic(ops):
     s = Shape(2, 300, 4, 64, 64, 4, "bf16", True)
     dd = to_device(make_inputs(s, 77), s)
