@@ -65,7 +65,9 @@ def rotate_pairs(v: np.ndarray, phi: np.ndarray) -> np.ndarray:
 
 def coefficients(dt, lam, A):
     """alpha = exp(Delta A), beta = (1 - lambda) Delta alpha, gamma = lambda Delta
-    ([CH] sec. 1, displayed recurrence).  dt, lam: [..., H]; A: [H]."""
+    ([CH] sec. 1, displayed recurrence).  dt, lam: [..., H]; A: [H], or an A
+    per token of the same shape as dt ([PB] sec. "Mamba-3": the decay rate may
+    itself depend on the token)."""
     alpha = np.exp(dt * A)
     beta = (1.0 - lam) * dt * alpha
     gamma = lam * dt
@@ -102,8 +104,8 @@ def ssm_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
                   xprev=None, phi0=None):
     """Sequential fp64 oracle of the whole sequence (prefill semantics).
 
-    x [Bt,L,H,R,P]; B, C [Bt,L,H,R,N]; dt, lam [Bt,L,H]; A [H];
-    theta [Bt,L,H,N/2] or None; carry-in (all optional, zeros if None):
+    x [Bt,L,H,R,P]; B, C [Bt,L,H,R,N]; dt, lam [Bt,L,H]; A [H] or per token
+    [Bt,L,H]; theta [Bt,L,H,N/2] or None; carry-in (all optional, zeros if None):
     h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
     Returns dict(y [Bt,L,H,R,P], h [Bt,H,N,P], Bprev_rot [Bt,H,R,N],
     xprev [Bt,H,R,P], phi [Bt,H,N/2] or None), all float64.
@@ -121,15 +123,16 @@ def ssm_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
     y = np.zeros((Bt, L, H, R, P))
     for t in range(L):
         th = None if theta is None else theta[:, t]
+        A_t = A if A.ndim == 1 else A[:, t]
         y[:, t], h, Bp, xp, phi = ssm_step(h, Bp, xp, phi, x[:, t], B[:, t], C[:, t],
-                                           dt[:, t], lam[:, t], A, th)
+                                           dt[:, t], lam[:, t], A_t, th)
     return dict(y=y, h=h, Bprev_rot=Bp, xprev=xp, phi=phi)
 
 
 def decode_reference(h, Bprev_rot, xprev, phi, x, B, C, dt, lam, A, theta=None):
     """One decode step against a resident state: the same token update as the
-    prefill loop.  Shapes as in :func:`ssm_step` (no time axis).
-    Returns dict(y, h, Bprev_rot, xprev, phi)."""
+    prefill loop.  Shapes as in :func:`ssm_step` (no time axis); A is [H] or
+    one per (batch, head) [Bt,H].  Returns dict(y, h, Bprev_rot, xprev, phi)."""
     y, h2, Bp, xp, ph = ssm_step(_f64(h), _f64(Bprev_rot), _f64(xprev), _f64(phi),
                                  _f64(x), _f64(B), _f64(C), _f64(dt), _f64(lam),
                                  _f64(A), _f64(theta))
@@ -154,7 +157,7 @@ def dual_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
     [PB] sec. "State Space Duality": with a scalar-times-identity transition the
     recurrence equals Y = (M o C B^T) X with a causal decay mask.  For the
     three-term recurrence the mask follows by unrolling the recurrence (our
-    derivation): with Lambda_t = sum_{k<=t} Delta_k A,
+    derivation): with Lambda_t = sum_{k<=t} Delta_k A_k (A [H], or [Bt,L,H] per token),
         M[t, j] = exp(Lambda_t - Lambda_j) * (gamma_j + (1 - lambda_{j+1}) Delta_{j+1})  (j < t)
         M[t, t] = gamma_t,   M[t, j] = 0 (j > t),
     broadcast over the R x R rank blocks, plus the carried-in state

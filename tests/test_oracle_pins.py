@@ -191,6 +191,76 @@ def test_split_resume_and_decode_chain(rope, R):
     assert orc.rel_l2(st["h"], whole["h"]) <= 1e-12
 
 
+# ---------------------------------------------------------------- per-token A
+def _A_tok(d, seed=3):
+    """A per token in [-16, -1], drawn like the per-head A."""
+    Bt, L, H = d["dt"].shape
+    u = np.random.default_rng(seed).random((Bt, L, H))
+    return -np.exp(u * np.log(16.0))
+
+
+def test_per_token_A_constant_in_time_is_the_per_head_A():
+    d = _tiny(L=30, R=2, rope=True, h0=True, carry=True, seed=21)
+    Bt, L, H = d["dt"].shape
+    A_tok = np.broadcast_to(np.float64(d["A"])[None, None, :], (Bt, L, H)).copy()
+    args = {k: d[k] for k in ("x", "B", "C", "dt", "lam", "theta", "h0", "Bprev_rot", "xprev", "phi0")}
+    a = orc.ssm_reference(A=d["A"], **args)
+    b = orc.ssm_reference(A=A_tok, **args)
+    for k in ("y", "h", "Bprev_rot", "phi"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_per_token_A_impulse_responses():
+    """Brute force with a decay rate per token: the loop's response to unit
+    impulses equals scalar loops over (t, j) for the mask (decay the product of
+    exp(Delta_s A_s) over j < s <= t) times the Gram entries."""
+    L, R, N = 10, 2, 4
+    d = _tiny(Bt=1, L=L, H=1, P=1, N=N, R=R, rope=False, seed=17)
+    A_tok = _A_tok(d)
+    T_imp = np.zeros((L * R, L * R))
+    for j in range(L):
+        for r in range(R):
+            x = np.zeros((1, L, 1, R, 1))
+            x[0, j, 0, r, 0] = 1.0
+            out = orc.ssm_reference(x, d["B"], d["C"], d["dt"], d["lam"], A_tok)
+            T_imp[:, j * R + r] = out["y"][0, :, 0, :, 0].reshape(L * R)
+    dt = np.float64(d["dt"][0, :, 0])
+    lam = np.float64(d["lam"][0, :, 0])
+    a = A_tok[0, :, 0]
+    T = np.zeros((L * R, L * R))
+    for t in range(L):
+        for j in range(t + 1):
+            if j == t:
+                m = lam[t] * dt[t]
+            else:
+                decay = 1.0
+                for s_ in range(j + 1, t + 1):
+                    decay *= np.exp(dt[s_] * a[s_])
+                m = decay * (lam[j] * dt[j] + (1 - lam[j + 1]) * dt[j + 1])
+            for r in range(R):
+                for rr in range(R):
+                    T[t * R + r, j * R + rr] = m * (np.float64(d["C"][0, t, 0, r]) @ np.float64(d["B"][0, j, 0, rr]))
+    assert np.max(np.abs(T_imp - T)) <= 1e-12 * max(1.0, np.max(np.abs(T)))
+
+
+@pytest.mark.parametrize("R,rope", [(1, False), (2, True)])
+def test_per_token_A_dual_form_and_decode_chain(R, rope):
+    d = _tiny(L=35, R=R, rope=rope, h0=True, carry=True, seed=23)
+    A_tok = _A_tok(d, seed=5)
+    args = {k: d[k] for k in ("x", "B", "C", "dt", "lam", "theta", "h0", "Bprev_rot", "xprev", "phi0")}
+    loop = orc.ssm_reference(A=A_tok, **args)
+    assert orc.rel_l2(orc.dual_reference(A=A_tok, **args), loop["y"]) <= 1e-10
+    st = dict(h=d["h0"], Bprev_rot=d["Bprev_rot"], xprev=d["xprev"], phi=d["phi0"])
+    ys = []
+    for t in range(d["x"].shape[1]):
+        th = None if d["theta"] is None else d["theta"][:, t]
+        st = orc.decode_reference(st["h"], st["Bprev_rot"], st["xprev"], st["phi"], d["x"][:, t], d["B"][:, t],
+                                  d["C"][:, t], d["dt"][:, t], d["lam"][:, t], A_tok[:, t], th)
+        ys.append(st["y"])
+    assert orc.rel_l2(np.stack(ys, axis=1), loop["y"]) <= 1e-12
+    assert orc.rel_l2(st["h"], loop["h"]) <= 1e-12
+
+
 # ---------------------------------------------------------------- P-ord
 @pytest.mark.parametrize("lamv,order", [(0.5, 2.0), (1.0, 1.0), (0.0, 1.0)])
 def test_order_of_accuracy(lamv, order):
