@@ -113,13 +113,14 @@ def unit_kernels():
     return out
 
 
-def prefill_algo(Bt, L, H, P, N, R, rope, omega=False):
+def prefill_algo(Bt, L, H, P, N, R, rope, omega=False, a_tok=False):
     """Algorithmic bytes (each input read once, each output written once) and
     MFMA flops (chunked-scan count 2L[Q R^2 (N+P) + 2 R N P] per (b,h), Q = 64/R).
-    omega: the angles come as rates per token shared by the heads."""
+    omega: the angles come as rates per token shared by the heads; a_tok: A is
+    given per token."""
     bf, f4 = 2, 4
     tok = Bt * L * H
-    byts = tok * R * (P + 2 * N) * bf + tok * 2 * f4 + H * f4   # x, B, C, dt, lam, A
+    byts = tok * R * (P + 2 * N) * bf + tok * 2 * f4 + (tok if a_tok else H) * f4   # x, B, C, dt, lam, A
     if rope:
         byts += (Bt * L if omega else tok) * (N // 2) * f4        # omega or theta
     byts += tok * R * P * bf                                      # y
@@ -158,10 +159,11 @@ def gen_prefill(torch, Bt, L, H, P, N, R, rope, seed):
     if rope:
         om = torch.randn((Bt, L, N // 2), generator=g, device=dev)
         theta = (dt[:, :, :, None] * om[:, :, None, :]).contiguous()
-    return dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta, omega=om)
+    a_tok = (-torch.exp(torch.rand((Bt, L, H), generator=g, device=dev) * math.log(16.0))).contiguous()
+    return dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta, omega=om, A_tok=a_tok)
 
 
-def time_prefill(torch, ops, inp, steps, warmup, use_omega=False):
+def time_prefill(torch, ops, inp, steps, warmup, mode=""):
     y = torch.empty_like(inp["x"])
     Bt, L, H, R, P = inp["x"].shape
     N = inp["B"].shape[-1]
@@ -171,11 +173,12 @@ def time_prefill(torch, ops, inp, steps, warmup, use_omega=False):
     nws = ops.prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=inp["x"].dtype, rope=inp["theta"] is not None)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else False
 
-    theta, omega = (None, inp["omega"]) if use_omega else (inp["theta"], None)
+    theta, omega = (None, inp["omega"]) if mode == "omega" else (inp["theta"], None)
+    A, a_tok = (None, inp["A_tok"]) if mode == "atok" else (inp["A"], None)
 
     def run():
-        ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], theta,
-                           y=y, h_final=hf, workspace=ws, omega=omega)
+        ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], A, theta,
+                           y=y, h_final=hf, workspace=ws, omega=omega, A_tok=a_tok)
 
     for _ in range(max(warmup, 1)):
         run()
@@ -525,16 +528,20 @@ def main():
            "data": "synthetic (seeded, device-generated, resident in HBM)"}
     results = {}
     if args.only in ("all", "prefill"):
-        # the RoPE workloads also with their angles given as rates (theta = dt * omega on chip)
-        runs = [(name, shp, False) for name, shp in prefill_shapes().items()]
-        runs += [(name + "_omega", shp, True) for name, shp in prefill_shapes().items() if shp[-1]]
-        for i, (name, shp, use_omega) in enumerate(runs):
+        # the RoPE workloads also with their angles given as rates (theta = dt * omega on
+        # chip), and the headline workload with A given per token
+        runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
+        runs += [(name + "_omega", shp, "omega") for name, shp in prefill_shapes().items() if shp[-1]]
+        runs += [("siso_real_atok", prefill_shapes()["siso_real"], "atok")]
+        for i, (name, shp, mode) in enumerate(runs):
             Bt, L, H, P, N, R, rope = shp
             inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260100 + i)
             torch.cuda.synchronize()
-            ms, launch_ms, flushed = time_prefill(torch, ops, inp, args.steps, args.warmup, use_omega)
-            byts, flops = prefill_algo(*shp, omega=use_omega)
-            angles = "RoPE, angles from rates" if use_omega else ("RoPE" if rope else "real")
+            ms, launch_ms, flushed = time_prefill(torch, ops, inp, args.steps, args.warmup, mode)
+            byts, flops = prefill_algo(*shp, omega=mode == "omega", a_tok=mode == "atok")
+            angles = "RoPE, angles from rates" if mode == "omega" else ("RoPE" if rope else "real")
+            if mode == "atok":
+                angles += ", A per token"
             res = dict(workload=f"prefill {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
                                 f"{angles} bf16 chunk {Q_ROWS // R}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, kernel_ms=launch_ms,
@@ -601,7 +608,7 @@ def main():
         out["decode_roofline"] = {"bound": "hbm", "achieved": dres["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": dres["hbm_frac"], "traffic": traffic_for("decode"),
                                   "kernel": decode_kernel_name(*DECODE_SHAPE)}
-    for k in ("siso_rope", "mimo_rope", "siso_rope_omega", "mimo_rope_omega"):
+    for k in ("siso_rope", "mimo_rope", "siso_rope_omega", "mimo_rope_omega", "siso_real_atok"):
         if k in results:
             out["prefill_" + k] = results[k]
     if "angles" in results:

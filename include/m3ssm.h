@@ -68,7 +68,12 @@ typedef enum m3_dtype {
  *   B, C    [Bt, L, H, R, N]  in_dtype   input / output projections
  *   dt      [Bt, L, H]        float32    Delta_t (> 0, already positive)
  *   lam     [Bt, L, H]        float32    lambda_t in [0, 1]
- *   A       [H]               float32    per-head scalar A (< 0)
+ *   A       [H]               float32    per-head scalar A (< 0); may be NULL
+ *                                        when A_tok is given
+ *   A_tok   [Bt, L, H]        float32    A per token (< 0), or NULL: the decay
+ *                                        rate itself depending on the token
+ *                                        ("La dualita", sec. "Mamba-3");
+ *                                        alpha_t = exp(Delta_t A_tok_t)
  *   theta   [Bt, L, H, N/2]   float32    per-token rotation angles, or NULL
  *                                        for the real-valued SSM (no RoPE)
  *   omega   [Bt, L, N/2]      float32    alternative to theta (bf16 inputs
@@ -127,6 +132,7 @@ typedef struct m3_prefill_args {
   void* workspace;        /* device scratch of workspace_bytes (256-byte aligned), or NULL */
   size_t workspace_bytes;
   const float* omega;     /* [Bt, L, N/2] angular rates, or NULL (see above) */
+  const float* A_tok;     /* [Bt, L, H] A per token, or NULL (see above) */
 } m3_prefill_args;
 
 int m3_ssm_prefill(const m3_prefill_args* args, void* stream);
@@ -164,7 +170,8 @@ size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args);
  *   xprev     [Bt, H, R, P]   in_dtype   x of the previous token
  *   In:
  *   x [Bt,H,R,P], B, C [Bt,H,R,N] (in_dtype); dt, lam [Bt,H] float32;
- *   A [H] float32; theta [Bt,H,N/2] float32 or NULL.
+ *   A [H] float32, or A_tok [Bt,H] float32 (A per (batch, head) for this
+ *   token; then A may be NULL); theta [Bt,H,N/2] float32 or NULL.
  *   Out: y [Bt, H, R, P] in_dtype.
  * Sizes: N, P in {16, 32, 64, 128}; R in 1..16.  A fresh sequence starts with
  * h = 0 (or any state), Bprev_rot = 0, xprev = 0, phi = 0.
@@ -184,6 +191,7 @@ typedef struct m3_decode_args {
   const float* A;
   const float* theta;
   void* y;
+  const float* A_tok; /* [Bt, H] A of this token, or NULL */
 } m3_decode_args;
 
 int m3_ssm_decode_step(const m3_decode_args* args, void* stream);

@@ -29,7 +29,7 @@ class PrefillArgs(ctypes.Structure):
         ("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp), ("lam", _vp), ("A", _vp), ("theta", _vp),
         ("h0", _vp), ("Bprev_rot", _vp), ("xprev", _vp), ("phi0", _vp),
         ("y", _vp), ("h_final", _vp), ("Bprev_rot_out", _vp), ("xprev_out", _vp), ("phi_out", _vp),
-        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("omega", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("omega", _vp), ("A_tok", _vp),
     ]
 
 
@@ -38,7 +38,7 @@ class DecodeArgs(ctypes.Structure):
         ("Bt", _i32), ("H", _i32), ("P", _i32), ("N", _i32), ("R", _i32), ("in_dtype", _i32),
         ("h", _vp), ("phi", _vp), ("Bprev_rot", _vp), ("xprev", _vp),
         ("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp), ("lam", _vp), ("A", _vp), ("theta", _vp),
-        ("y", _vp),
+        ("y", _vp), ("A_tok", _vp),
     ]
 
 

@@ -97,7 +97,7 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   if (a == nullptr) return M3_ERR_INVALID_ARG;
   if (a->Bt < 1 || a->L < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
   if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
-  if (!a->x || !a->B || !a->C || !a->dt || !a->lam || !a->A || !a->y) return M3_ERR_INVALID_ARG;
+  if (!a->x || !a->B || !a->C || !a->dt || !a->lam || (!a->A && !a->A_tok) || !a->y) return M3_ERR_INVALID_ARG;
   if ((a->Bprev_rot == nullptr) != (a->xprev == nullptr)) return M3_ERR_INVALID_ARG;
   if (a->theta != nullptr && a->omega != nullptr) return M3_ERR_INVALID_ARG;  // one angle source
   const bool rope = a->theta != nullptr || a->omega != nullptr;
@@ -111,7 +111,7 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
                        a->phi0, a->h_final, a->Bprev_rot_out, a->xprev_out, a->phi_out};
   for (const void* p : v16)
     if (!al16(p)) return M3_ERR_INVALID_ARG;
-  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A)) return M3_ERR_INVALID_ARG;
+  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A) || !al4(a->A_tok)) return M3_ERR_INVALID_ARG;
   const double elems = double(a->Bt) * a->L * a->H * a->R * (a->N > a->P ? a->N : a->P);
   if (elems > 4.0e18 || double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
   const bool bf16 = a->in_dtype == M3_BF16;
@@ -135,6 +135,7 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   p.bf16 = bf16;
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.theta = a->theta;
   p.omega = a->omega;
+  p.A_tok = a->A_tok;
   p.h0 = a->h0; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev; p.phi0 = a->phi0;
   p.y = a->y; p.h_final = a->h_final; p.Bprev_rot_out = a->Bprev_rot_out; p.xprev_out = a->xprev_out;
   p.phi_out = a->phi_out;
@@ -179,7 +180,7 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
     c.Bt = a->Bt; c.H = a->H; c.N = a->N; c.P = a->P; c.R = a->R; c.Lfull = a->L;
     c.t1 = sp.segA;
     c.t2 = sp.segLen;
-    c.dt = a->dt; c.lam = a->lam; c.A = a->A;
+    c.dt = a->dt; c.lam = a->lam; c.A = a->A; c.A_tok = a->A_tok;
     c.h = hMid;
     c.Bprev = bMid;
     c.x0 = xMid;
@@ -206,7 +207,8 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   if (a == nullptr) return M3_ERR_INVALID_ARG;
   if (a->Bt < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
   if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
-  if (!a->h || !a->Bprev_rot || !a->xprev || !a->x || !a->B || !a->C || !a->dt || !a->lam || !a->A || !a->y)
+  if (!a->h || !a->Bprev_rot || !a->xprev || !a->x || !a->B || !a->C || !a->dt || !a->lam || (!a->A && !a->A_tok) ||
+      !a->y)
     return M3_ERR_INVALID_ARG;
   if ((a->theta == nullptr) != (a->phi == nullptr)) return M3_ERR_INVALID_ARG;
   if (a->theta != nullptr && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
@@ -215,7 +217,7 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   const void* v16[] = {a->h, a->Bprev_rot, a->xprev, a->x, a->B, a->C, a->y, a->phi, a->theta};
   for (const void* p : v16)
     if (!al16(p)) return M3_ERR_INVALID_ARG;
-  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A)) return M3_ERR_INVALID_ARG;
+  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A) || !al4(a->A_tok)) return M3_ERR_INVALID_ARG;
   if (double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
   m3::DecodeParams p{};
   p.Bt = a->Bt; p.H = a->H; p.P = a->P; p.N = a->N; p.R = a->R;
@@ -223,6 +225,7 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   p.h = a->h; p.phi = a->phi; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev;
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.theta = a->theta;
   p.y = a->y;
+  p.A_tok = a->A_tok;
   return hip_status(m3::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 

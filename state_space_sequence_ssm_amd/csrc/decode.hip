@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
     float* h = p.h + static_cast<size_t>(bh) * N * P;
     const float dt = p.dt[bh];
     const float lm = p.lam[bh];
-    const float alpha = __expf(dt * p.A[hh]);
+    const float alpha = __expf(dt * (p.A_tok != nullptr ? p.A_tok[bh] : p.A[hh]));
     const float beta = (1.f - lm) * dt * alpha;
     const float gamma = lm * dt;
 

@@ -21,6 +21,7 @@ struct DecodeParams {
   const float* A;
   const float* theta;
   void* y;
+  const float* A_tok;  // [Bt, H] A of this token, or null (then A [H])
 };
 
 struct PrefillParams {
@@ -37,6 +38,8 @@ struct PrefillParams {
   // omega [Bt, L, N/2] (bf16 path): per-token angular rates shared by the
   // heads; when set (theta is then null), theta = Delta * omega on chip
   const float* omega;
+  // A_tok [Bt, L, H]: A per token, or null (then A [H] for every token)
+  const float* A_tok;
   const float* h0;
   const float* Bprev_rot;
   const void* xprev;
@@ -82,6 +85,7 @@ struct CombineParams {
   const float* dt;
   const float* lam;
   const float* A;
+  const float* A_tok;  // [Bt, L, H] or null
   float* h;        // [2][Bt*H][N][P]: segment 0 end state -> joined state
   float* Bprev;    // [2][Bt*H][R][N]: segment 1's (relative frame) -> rotated in place
   const void* x0;  // [Bt*H][R][P] bf16: segment 0's last x

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int L = p.L, H = p.H, R = p.R, lgR = p.log2R;
   const int Q = kRows >> lgR;  // tokens per chunk
   const bool rope = p.theta != nullptr;
-  const float Ah = p.A[hh];
+  const float Ah = p.A_tok != nullptr ? 0.f : p.A[hh];
   const int nch = (L + Q - 1) / Q;
 
   const T* xg = static_cast<const T*>(p.x);
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // ------------------------------------------------------------ prefetch state
   u32x4 raw[Lt::JS][4];
   f32x4 rawTh[Lt::TS];
-  float rdt = 0.f, rlam = 0.f, rdtn = 0.f, rlamn = 0.f;
+  float rdt = 0.f, rlam = 0.f, rdtn = 0.f, rlamn = 0.f, rA = 0.f;
 
   auto issue_loads = [&](int c) {
     const int s0 = c * Q;
@@ -213,10 +213,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     if (wave == 0) {
       const int t = s0 + lane;
       rdt = rlam = rdtn = rlamn = 0.f;
+      rA = Ah;
       if (lane < Q && t < L) {
         const size_t o = (static_cast<size_t>(b) * L + t) * H + hh;
         rdt = p.dt[o];
         rlam = p.lam[o];
+        if (p.A_tok != nullptr) rA = p.A_tok[o];
         if (t + 1 < L) {
           rdtn = p.dt[o + H];
           rlamn = p.lam[o + H];
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // stage A: per-token scalars (wave 0) and raw angles into LDS
   auto stage_scalars = [&]() {
     if (wave == 0) {
-      const float v = rdt * Ah;
+      const float v = rdt * rA;
       const float lamc = wave_inclusive_scan(v, 64);
       const float lamEnd = __shfl(lamc, Q - 1, 64);
       const float gam = rlam * rdt;

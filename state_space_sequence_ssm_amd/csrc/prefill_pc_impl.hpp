@@ -332,7 +332,6 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const int t0 = seg * p.segLen;                                // first token of the segment
   const int L = seg == p.nseg - 1 ? p.L - t0 : p.segLen;       // tokens of the segment
   const bool lastSeg = seg == p.nseg - 1;
-  const float A2 = p.A[hh] * kLog2e;  // decays in log2 units
   const int nch = (L + Q - 1) / Q;
   // carry-in of this segment
   const float* cH0 = seg == 0 ? p.h0 : p.h_mid;
@@ -351,6 +350,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const rsrc_t rY = make_rsrc(SO ? p.x : static_cast<bf16_t*>(p.y) + tok0 * H * R * P, uint32_t(SO ? 0 : tokB * R * P * 2));
   const rsrc_t rDt = make_rsrc(p.dt + tok0 * H, uint32_t(tokB * 4));
   const rsrc_t rLam = make_rsrc(p.lam + tok0 * H, uint32_t(tokB * 4));
+  // A per token (null: the head's A for every token)
+  const bool aTok = p.A_tok != nullptr;
+  const rsrc_t rAtok = make_rsrc(aTok ? p.A_tok + tok0 * H : p.dt, uint32_t(aTok ? tokB * 4 : 0));
+  const float A2 = aTok ? 0.f : p.A[hh] * kLog2e;  // decays in log2 units
   // angles: theta [.., H, N/2] per (token, head), or omega [.., N/2] per token
   // (shared by the heads; scaled by Delta in the angle scan)
   const bool om = ROPE && p.omega != nullptr;
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   constexpr int kThUnits = Q * NG;
   constexpr int kThU = (kThUnits + kThreads - 1) / kThreads;
   f32x4 rawTh[2][ROPE ? kThU : 1];
-  float rdt[2], rlam[2];
+  float rdt[2], rlam[2], rAt[2] = {0.f, 0.f};
   // Every wave issues the same loads every chunk (chunks past the end read
   // zeros): with no load behind a branch the wait counters stay exact.
   // row (within the chunk) and column of this lane's 16 bytes in load s
@@ -421,6 +424,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const uint32_t off = (wave == 0 && lane < Q) ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
     rdt[set] = bloadf(rDt, off);
     rlam[set] = bloadf(rLam, off);
+    if (aTok) rAt[set] = bloadf(rAtok, off);  // uniform branch: no load without A_tok
     if constexpr (ROPE) {  // consecutive lanes read consecutive 16 bytes of a token's row
 #pragma unroll
       for (int s = 0; s < kThU; ++s) {
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   auto stage_small = [&](int c, int set) __attribute__((always_inline)) {
     if (wave == 0) {
       float* S = sc(c % 3);
-      const float lamc = seg_scan<64>(rdt[set] * A2);
+      const float lamc = seg_scan<64>(rdt[set] * (aTok ? rAt[set] * kLog2e : A2));
       const float lamEnd = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lamc), Q - 1));
       // next token's Delta, lambda: lane t + 1, or token 0 of chunk c + 1 (the
       // other register set; zeros past the end, i.e. Delta_L = 0) for t = Q - 1

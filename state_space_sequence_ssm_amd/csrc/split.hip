@@ -6,7 +6,7 @@
 // angle (same page, sec. 2) composes: with Phi_b the angle at the end of the
 // first segment, rotating by Phi_b + phi equals rotating by phi and then by
 // Phi_b.  So the state after the second segment is
-//   h_2 = exp(A sum_{t in seg 2} Delta_t) (h_1 + (1 - lambda_t1) Delta_t1 sum_r Btil_1[r] x_1[r]^T)
+//   h_2 = exp(sum_{t in seg 2} Delta_t A_t) (h_1 + (1 - lambda_t1) Delta_t1 sum_r Btil_1[r] x_1[r]^T)
 //         + Rot(Phi_b) h_rel,
 // where h_1, Btil_1, x_1, Phi_b are the end state and carry of the first
 // segment, t1 the second segment's first token (its beta term reaches back to
@@ -35,9 +35,12 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
   const size_t units = static_cast<size_t>(c.Bt) * c.H;
   __shared__ float red[kThreads / 64];
   __shared__ float sPhi[64];
-  // sum of Delta over the second segment
+  // sum of Delta A over the second segment
   float sdt = 0.f;
-  for (int t = c.t1 + tid; t < c.t2; t += kThreads) sdt += c.dt[(static_cast<size_t>(b) * c.Lfull + t) * c.H + hh];
+  for (int t = c.t1 + tid; t < c.t2; t += kThreads) {
+    const size_t o = (static_cast<size_t>(b) * c.Lfull + t) * c.H + hh;
+    sdt += c.dt[o] * (c.A_tok != nullptr ? c.A_tok[o] : 1.f);
+  }
   for (int o = 32; o > 0; o >>= 1) sdt += __shfl_xor(sdt, o);
   if ((tid & 63) == 0) red[tid >> 6] = sdt;
   const int J = c.N / 2;
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
   __syncthreads();
   float tot = 0.f;
   for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
-  const float decay = __expf(c.A[hh] * tot);
+  const float decay = __expf(c.A_tok != nullptr ? tot : c.A[hh] * tot);
   const size_t o1 = (static_cast<size_t>(b) * c.Lfull + c.t1) * c.H + hh;
   const float coef = (1.f - c.lam[o1]) * c.dt[o1];
 

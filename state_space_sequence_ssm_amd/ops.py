@@ -49,11 +49,13 @@ def _stream(stream) -> int:
 
 def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
                    *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
-                   want_state=True, want_carry=False, chunk=0, workspace=None, omega=None, stream=None):
+                   want_state=True, want_carry=False, chunk=0, workspace=None, omega=None, A_tok=None,
+                   stream=None):
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
     dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None (or
     instead omega [Bt,L,N/2] fp32: rates shared by the heads, theta = dt * omega
-    formed on chip, bf16 inputs only); optional
+    formed on chip, bf16 inputs only); A_tok [Bt,L,H] fp32: A per token (then
+    A may be None); optional
     carry-in h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
     Output tensors are allocated when not given.  workspace: a uint8 device
     tensor of at least prefill_workspace_bytes(...) bytes, None to allocate one
@@ -83,6 +85,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a.dt = _ptr(dt, f32, (Bt, L, H), "dt")
     a.lam = _ptr(lam, f32, (Bt, L, H), "lam")
     a.A = _ptr(A, f32, (H,), "A")
+    a.A_tok = _ptr(A_tok, f32, (Bt, L, H), "A_tok")
     a.theta = _ptr(theta, f32, (Bt, L, H, N // 2), "theta")
     a.omega = _ptr(omega, f32, (Bt, L, N // 2), "omega")
     a.h0 = _ptr(h0, f32, (Bt, H, N, P), "h0")
@@ -117,11 +120,13 @@ def prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=torch.bfloat16, rope=False)
     return _lib.load().m3_ssm_prefill_workspace_size(ctypes.byref(a))
 
 
-def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None, *, y=None, stream=None):
+def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None, *, y=None, A_tok=None,
+                       stream=None):
     """One decode token.  In/out (updated in place): h [Bt,H,N,P] fp32,
     phi [Bt,H,N/2] fp32 (None iff theta None), Bprev_rot [Bt,H,R,N] fp32,
     xprev [Bt,H,R,P].  Inputs x [Bt,H,R,P], B/C [Bt,H,R,N], dt/lam [Bt,H],
-    A [H], theta [Bt,H,N/2] or None.  Returns y [Bt,H,R,P]."""
+    A [H] (or A_tok [Bt,H]: this token's A; then A may be None), theta
+    [Bt,H,N/2] or None.  Returns y [Bt,H,R,P]."""
     Bt, H, R, P = x.shape
     N = B.shape[-1]
     f32 = torch.float32
@@ -140,6 +145,7 @@ def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None
     a.dt = _ptr(dt, f32, (Bt, H), "dt")
     a.lam = _ptr(lam, f32, (Bt, H), "lam")
     a.A = _ptr(A, f32, (H,), "A")
+    a.A_tok = _ptr(A_tok, f32, (Bt, H), "A_tok")
     a.theta = _ptr(theta, f32, (Bt, H, N // 2), "theta")
     a.y = _ptr(y, x.dtype, (Bt, H, R, P), "y")
     rc = _lib.load().m3_ssm_decode_step(ctypes.byref(a), _stream(stream))

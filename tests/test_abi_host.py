@@ -49,6 +49,8 @@ def test_prefill_validation():
     assert lib.m3_ssm_prefill(None, None) == _lib.M3_ERR_INVALID_ARG
     cases = [
         (lambda a: setattr(a, "x", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "A", None), _lib.M3_ERR_INVALID_ARG),  # neither A nor A_tok
+        (lambda a: (setattr(a, "A", None), setattr(a, "A_tok", 0x30200002)), _lib.M3_ERR_INVALID_ARG),  # misaligned
         (lambda a: setattr(a, "y", None), _lib.M3_ERR_INVALID_ARG),
         (lambda a: setattr(a, "L", 0), _lib.M3_ERR_INVALID_ARG),
         (lambda a: setattr(a, "R", 0), _lib.M3_ERR_INVALID_ARG),

@@ -263,6 +263,69 @@ def test_decode_chain(ops, case):
         assert np.max(angle_diff(host(state["phi"]), ref["phi"])) <= 1e-4
 
 
+# ----------------------------------------------------------------- A per token
+ATOK = [
+    # Bt, L, H, P, N, R, dtype, rope, carry, lam_const
+    (2, 131, 3, 64, 64, 1, "bf16", True, True, None),
+    (1, 100, 2, 64, 64, 4, "bf16", True, True, None),
+    (1, 90, 2, 64, 128, 1, "bf16", False, False, None),
+    (1, 150, 2, 64, 64, 1, "bf16", True, False, 0.5),   # the trapezoid itself (lambda = 1/2)
+    (1, 1500, 2, 64, 64, 1, "bf16", True, True, None),  # split, first half in two parts
+    (1, 200, 2, 16, 16, 1, "f32", True, True, None),
+]
+
+
+def _a_tok(shape, seed):
+    u = np.random.default_rng(seed).random(shape, dtype=np.float32)
+    return (-np.exp(u * np.float32(np.log(16.0)))).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", ATOK, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_A_tok(ops, case):
+    """A given per token (and lambda fixed at 1/2): the oracle on the same A."""
+    Bt, L, H, P, N, R, dt_, rope, carry, lamc = case
+    s = Shape(Bt, L, H, P, N, R, dt_, rope)
+    _say("prefill A_tok", case)
+    d = make_inputs(s, 5000 + L + N, h0=carry, carry=carry, lam_const=lamc)
+    a_tok = _a_tok((Bt, L, H), 6000 + L)
+    dd = to_device(d, s)
+    out = ops.m3_ssm_prefill(dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], None, dd["theta"], dd.get("h0"),
+                             dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"), want_carry=True, A_tok=dev(a_tok))
+    torch.cuda.synchronize()
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], a_tok, d["theta"], d.get("h0"),
+                            d.get("Bprev_rot"), d.get("xprev"), d.get("phi0"))
+    ey = orc.rel_l2(host(out["y"]), ref["y"])
+    eh = orc.rel_l2(host(out["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL[dt_] and eh <= TOL[dt_]
+    assert orc.rel_l2(host(out["Bprev_rot"]), ref["Bprev_rot"]) <= 1e-5
+
+
+def test_decode_A_tok(ops):
+    Bt, H, P, N, R, steps = 3, 4, 64, 64, 4, 6
+    s = Shape(Bt, steps, H, P, N, R, "bf16", True)
+    _say("decode A_tok")
+    d = make_inputs(s, 777, h0=True)
+    a_tok = _a_tok((Bt, steps, H), 778)
+    st = storage_dtype(s)
+    dec = {k: dev(np.moveaxis(d[k], 1, 0), st if k in ("x", "B", "C") else torch.float32)
+           for k in ("x", "B", "C", "dt", "lam", "theta")}
+    at = dev(np.moveaxis(a_tok, 1, 0))
+    state = dict(h=dev(d["h0"]), phi=dev(np.zeros((Bt, H, N // 2))), Bprev_rot=dev(np.zeros((Bt, H, R, N))),
+                 xprev=dev(np.zeros((Bt, H, R, P)), st))
+    ys = []
+    for t in range(steps):
+        ys.append(host(ops.m3_ssm_decode_step(state["h"], state["phi"], state["Bprev_rot"], state["xprev"],
+                                              dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t],
+                                              None, dec["theta"][t], A_tok=at[t])))
+    torch.cuda.synchronize()
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], a_tok, d["theta"], d["h0"])
+    ey = orc.rel_l2(np.stack(ys, axis=1), ref["y"])
+    eh = orc.rel_l2(host(state["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 def test_decode_config_full_size(ops):
     """Decode workload at full size (B=256, H=32, N=P=64, R=4) for a few steps,
     checked against the oracle on every (batch, head)."""
