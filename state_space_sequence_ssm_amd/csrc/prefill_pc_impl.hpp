@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const uint32_t off = (wave == 0 && lane < Q) ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
     rdt[set] = bloadf(rDt, off);
     rlam[set] = bloadf(rLam, off);
-    if (aTok) rAt[set] = bloadf(rAtok, off);  // uniform branch: no load without A_tok
+    rAt[set] = bloadf(rAtok, off);  // an empty range without A_tok: reads 0, no request
     if constexpr (ROPE) {  // consecutive lanes read consecutive 16 bytes of a token's row
 #pragma unroll
       for (int s = 0; s < kThU; ++s) {
@@ -473,13 +473,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if constexpr (ROPE) {
       const int tl = lane % Q, pg = lane / Q;
       float* tab = phiTab(c & 1);
+      const float dsc = om ? sc(c % 3)[6 * 64 + tl] : 1.f;  // theta = Delta * omega (exact x 1 otherwise)
 #pragma unroll
       for (int s = 0; s < TSL; ++s) {
         const int q4 = (s * kWaves + wave) * R + pg;  // uniform within a Q-lane segment
         if ((s * kWaves + wave) * R < NG) {
           constexpr f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
           f32x4 v = q4 < NG ? *reinterpret_cast<const f32x4*>(tab + tl * PH + 4 * q4) : zero4;
-          if (om) v *= sc(c % 3)[6 * 64 + tl];  // theta = Delta * omega
+          v *= dsc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = seg_scan<Q>(v[e]);
           if (q4 < NG) {
