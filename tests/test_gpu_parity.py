@@ -130,6 +130,44 @@ def test_prefill_omega(ops, case):
     assert np.max(angle_diff(host(out["phi"]), host(ref_gpu["phi"]))) <= 1e-4
 
 
+# ----------------------------------------------------------------- edge values
+EDGE = [
+    # name, Bt, L, H, P, N, R, rope
+    ("lambda0", 1, 97, 2, 64, 64, 1, True),     # pure beta term (lambda = 0): h_t = alpha h + beta B_{t-1} x_{t-1}^T
+    ("lambda1", 1, 97, 2, 64, 64, 2, True),     # Euler / Mamba-2 form (lambda = 1)
+    ("dt_zero_runs", 2, 130, 2, 64, 128, 1, False),  # Delta = 0 on whole chunks and single tokens
+    ("big_angles", 1, 70, 2, 32, 64, 4, True),  # angles far outside [-pi, pi]
+    ("many_units", 16, 20, 64, 16, 16, 1, True),  # 1024 (batch, head) units, one short ragged chunk
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: c[0])
+def test_prefill_edge_values(ops, case):
+    name, Bt, L, H, P, N, R, rope = case
+    s = Shape(Bt, L, H, P, N, R, "bf16", rope)
+    _say("prefill edge", case)
+    lamc = {"lambda0": 0.0, "lambda1": 1.0}.get(name)
+    d = make_inputs(s, 7000 + L, h0=True, carry=True, lam_const=lamc)
+    if name == "dt_zero_runs":
+        d["dt"][:, 64:128] = 0.0   # the whole second chunk
+        d["dt"][:, 5] = 0.0
+        d["dt"][:, 129] = 0.0      # the last token
+    if name == "big_angles":
+        d["theta"] = (d["theta"] * 500.0).astype(np.float32)
+        d["phi0"] = (d["phi0"] * 40.0).astype(np.float32)
+    dd = to_device(d, s)
+    out = _run_prefill(ops, dd, s, carry=True)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(d)
+    ey = orc.rel_l2(host(out["y"]), ref["y"])
+    eh = orc.rel_l2(host(out["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert orc.rel_l2(host(out["Bprev_rot"]), ref["Bprev_rot"]) <= 1e-4
+    if rope:
+        assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-3
+
+
 def test_prefill_deterministic(ops):
     s = Shape(2, 300, 4, 64, 64, 4, "bf16", True)
     dd = to_device(make_inputs(s, 77), s)
