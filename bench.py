@@ -466,6 +466,35 @@ def report_pmc(fetch_prefix, write_prefix):
     print("\n".join(lines))
 
 
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def report_mfma(prefix):
+    """MFMA counters of each timed kernel: bf16 flops executed (MOPS_BF16 x 512)
+    against the algorithmic count, and MFMA-busy cycles as a share of the
+    SIMD cycles of the dispatch (the MfmaUtil expression of rocprofv3)."""
+    acc = {}
+    for r in _csv_rows(prefix + "_counter_collection.csv"):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    algo = {"prefill_" + name: prefill_algo(*shp)[1] for name, shp in prefill_shapes().items()}
+    lines = ["| unit | kernel | dispatches | bf16 MFMA flops per launch (counter) | algorithmic flops per call "
+             "| MFMA busy (% of SIMD cycles) |", "|---|---|---|---|---|---|"]
+    for unit, k, g in unit_kernels():
+        if not unit.startswith("prefill"):
+            continue
+        hits = acc.get((k, g)) or next((v for (kk, _), v in acc.items() if kk == k), None)
+        if not hits or "SQ_VALU_MFMA_BUSY_CYCLES" not in hits:
+            continue
+        n = len(hits["SQ_VALU_MFMA_BUSY_CYCLES"])
+        mops = sum(hits.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])) / n * 512
+        busy = sum(hits["SQ_VALU_MFMA_BUSY_CYCLES"]) / n
+        gui = sum(hits["GRBM_GUI_ACTIVE"]) / n / XCDS
+        lines.append(f"| {unit} | `{k}` | {n} | {mops:.4g} | {algo[unit]:.4g} | {100 * busy / (gui * SIMDS):.1f} |")
+    print("\n".join(lines))
+
+
 def pmc_workload(torch, ops):
     """Untimed launches for counter collection (see the module docstring)."""
     # same-dtype copy_ becomes a DMA transfer, so the plain copy kernel is an
@@ -500,12 +529,16 @@ def main():
     ap.add_argument("--only", choices=("all", "prefill", "decode", "pmc"), default="all")
     ap.add_argument("--report-trace", metavar="PREFIX")
     ap.add_argument("--report-pmc", nargs=2, metavar=("FETCH_PREFIX", "WRITE_PREFIX"))
+    ap.add_argument("--report-mfma", metavar="PREFIX")
     args = ap.parse_args()
     if args.report_trace:
         report_trace(args.report_trace)
         return
     if args.report_pmc:
         report_pmc(*args.report_pmc)
+        return
+    if args.report_mfma:
+        report_mfma(args.report_mfma)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is "
