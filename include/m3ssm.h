@@ -76,16 +76,15 @@ typedef enum m3_dtype {
  *                                        alpha_t = exp(Delta_t A_tok_t)
  *   theta   [Bt, L, H, N/2]   float32    per-token rotation angles, or NULL
  *                                        for the real-valued SSM (no RoPE)
- *   omega   [Bt, L, N/2]      float32    alternative to theta (bf16 inputs
- *                                        only): rotation rates per token and
- *                                        pair, shared by all heads; the angle
+ *   omega   [Bt, L, N/2]      float32    alternative to theta: rotation
+ *                                        rates per token and pair, shared by
+ *                                        all heads; the angle
  *                                        is then theta_t = Delta_t * omega_t
  *                                        (the step times the rate, per head),
  *                                        formed on chip, which saves reading
  *                                        the per-head theta tensor.  Setting
  *                                        both theta and omega is
- *                                        M3_ERR_INVALID_ARG; omega with fp32
- *                                        inputs is M3_ERR_UNSUPPORTED.
+ *                                        M3_ERR_INVALID_ARG.
  *   Carry-in, each nullable (NULL = zeros, i.e. a fresh sequence):
  *   h0        [Bt, H, N, P]   float32    state before the first token
  *   Bprev_rot [Bt, H, R, N]   float32    rotated B of the token before

@@ -103,7 +103,6 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   const bool rope = a->theta != nullptr || a->omega != nullptr;
   if (!rope && (a->phi0 != nullptr || a->phi_out != nullptr)) return M3_ERR_INVALID_ARG;
   if (rope && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
-  if (a->omega != nullptr && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
   if (!pow2(a->R) || a->R > 64) return M3_ERR_UNSUPPORTED;
   if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
   if (a->chunk != 0 && a->chunk != 64 / a->R) return M3_ERR_UNSUPPORTED;

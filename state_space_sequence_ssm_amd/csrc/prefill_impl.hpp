@@ -110,7 +110,7 @@ struct Layout {
   static constexpr size_t oXT = oBwT + size_t(N) * PR * EB;
   static constexpr size_t oHT = oXT + size_t(P) * PR * EB;
   static constexpr size_t oScal = oHT + size_t(P) * PN * EB;
-  static constexpr int kScal = 5 * kRows + 4;  // Lam, gamma, delta, w, dec; chunk decay
+  static constexpr int kScal = 6 * kRows + 4;  // Lam, gamma, delta, w, dec, Delta; chunk decay
   static constexpr size_t oPhiC = oScal + sizeof(float) * kScal;
   static constexpr size_t oTheta = oPhiC + sizeof(float) * (N / 2);
   static constexpr size_t oCS = oTheta + sizeof(float) * kRows * (N / 2);
@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float* sDel = sGam + kRows;
   float* sW = sDel + kRows;
   float* sDec = sW + kRows;
-  float* sChunkDec = sDec + kRows;
+  float* sDt = sDec + kRows;  // Delta, for angles given as rates
+  float* sChunkDec = sDt + kRows;
   float* sPhiC = reinterpret_cast<float*>(smem + Lt::oPhiC);
   float* sTheta = reinterpret_cast<float*>(smem + Lt::oTheta);
   float* sCS = reinterpret_cast<float*>(smem + Lt::oCS);
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int hh = bh % p.H;
   const int L = p.L, H = p.H, R = p.R, lgR = p.log2R;
   const int Q = kRows >> lgR;  // tokens per chunk
-  const bool rope = p.theta != nullptr;
+  const bool om = p.omega != nullptr;  // angles as rates: theta = Delta * omega
+  const bool rope = p.theta != nullptr || om;
   const float Ah = p.A_tok != nullptr ? 0.f : p.A[hh];
   const int nch = (L + Q - 1) / Q;
 
@@ -204,8 +206,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           const int tl = j / (N / 8), q4 = j % (N / 8);
           const int t = s0 + tl;
           if (tl < Q && t < L)
-            v = *reinterpret_cast<const f32x4*>(p.theta + (static_cast<size_t>(b) * L + t) * H * (N / 2) +
-                                                static_cast<size_t>(hh) * (N / 2) + 4 * q4);
+            v = om ? *reinterpret_cast<const f32x4*>(p.omega + (static_cast<size_t>(b) * L + t) * (N / 2) + 4 * q4)
+                   : *reinterpret_cast<const f32x4*>(p.theta + (static_cast<size_t>(b) * L + t) * H * (N / 2) +
+                                                     static_cast<size_t>(hh) * (N / 2) + 4 * q4);
         }
         rawTh[s] = v;
       }
@@ -241,6 +244,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         sDel[lane] = del;
         sW[lane] = __expf(lamEnd - lamc) * del;
         sDec[lane] = __expf(lamc);
+        sDt[lane] = rdt;
       }
       if (lane == 0) sChunkDec[0] = __expf(lamEnd);
     }
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int total = Q * (N / 2);
     for (int e = tid; e < total; e += kThreads) {
       const int jp = e / Q, tl = e % Q;
-      float v = wave_inclusive_scan(sTheta[tl * (N / 2) + jp], Q);
+      float v = wave_inclusive_scan(sTheta[tl * (N / 2) + jp] * (om ? sDt[tl] : 1.f), Q);
       v += sPhiC[jp];
       float sn, cs;
       sincosf(v, &sn, &cs);
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 template <typename T, int N, int P>
 static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   using Lt = Layout<T, N, P>;
-  const bool rope = p.theta != nullptr;
+  const bool rope = p.theta != nullptr || p.omega != nullptr;
   const size_t lds = rope ? Lt::kBytesRope : Lt::kBytesReal;
   static size_t attr_bytes = 64 * 1024;  // dynamic LDS the kernel is cleared for
   if (lds > attr_bytes) {

@@ -54,7 +54,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
     dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None (or
     instead omega [Bt,L,N/2] fp32: rates shared by the heads, theta = dt * omega
-    formed on chip, bf16 inputs only); A_tok [Bt,L,H] fp32: A per token (then
+    formed on chip); A_tok [Bt,L,H] fp32: A per token (then
     A may be None); optional
     carry-in h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
     Output tensors are allocated when not given.  workspace: a uint8 device

@@ -66,8 +66,6 @@ def test_prefill_validation():
         (lambda a: (setattr(a, "theta", 0x30000000), setattr(a, "omega", 0x30100000)),
          _lib.M3_ERR_INVALID_ARG),  # two angle sources
         (lambda a: setattr(a, "omega", 0x30100008), _lib.M3_ERR_INVALID_ARG),  # misaligned
-        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "omega", 0x30100000)),
-         _lib.M3_ERR_UNSUPPORTED),  # rates need bf16 inputs
         (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "N", 128), setattr(a, "P", 128),
                     setattr(a, "theta", 0x30000000)), _lib.M3_ERR_UNSUPPORTED),  # LDS too large
     ]

@@ -94,12 +94,13 @@ def test_prefill_small(ops, case):
 
 # ----------------------------------------------------------------- angles from rates
 OMEGA = [
-    # Bt, L, H, P, N, R, carry  (bf16; theta = dt * omega formed on chip)
-    (2, 131, 3, 64, 64, 1, True),
-    (1, 100, 2, 64, 64, 4, True),
-    (1, 77, 2, 32, 128, 2, False),
-    (1, 45, 2, 16, 32, 8, True),
-    (1, 1500, 2, 64, 64, 1, True),  # split, first half in two parts
+    # Bt, L, H, P, N, R, carry, dtype  (theta = dt * omega formed on chip)
+    (2, 131, 3, 64, 64, 1, True, "bf16"),
+    (1, 100, 2, 64, 64, 4, True, "bf16"),
+    (1, 77, 2, 32, 128, 2, False, "bf16"),
+    (1, 45, 2, 16, 32, 8, True, "bf16"),
+    (1, 1500, 2, 64, 64, 1, True, "bf16"),  # split, first half in two parts
+    (2, 150, 2, 32, 32, 2, True, "f32"),
 ]
 
 
@@ -107,8 +108,8 @@ OMEGA = [
 def test_prefill_omega(ops, case):
     """Angles given as per-token rates shared by the heads: the same results as
     the oracle on theta = dt * omega, and as the call that is given that theta."""
-    Bt, L, H, P, N, R, carry = case
-    s = Shape(Bt, L, H, P, N, R, "bf16", True)
+    Bt, L, H, P, N, R, carry, dt_ = case
+    s = Shape(Bt, L, H, P, N, R, dt_, True)
     _say("prefill omega", case)
     d = make_inputs(s, 3000 + L + N, h0=carry, carry=carry)
     dd = to_device(d, s)
@@ -122,7 +123,7 @@ def test_prefill_omega(ops, case):
     ey = orc.rel_l2(host(out["y"]), ref["y"])
     eh = orc.rel_l2(host(out["h"]), ref["h"])
     _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
-    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert ey <= TOL[dt_] and eh <= TOL[dt_]
     assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-3
     # against the theta call: the products dt * omega agree to fp32 rounding
     assert orc.rel_l2(host(out["y"]), host(ref_gpu["y"])) <= 5e-3
