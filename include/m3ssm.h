@@ -163,14 +163,16 @@ size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args);
  *
  *   In/out (updated in place):
  *   h         [Bt, H, N, P]   float32    state
- *   phi       [Bt, H, N/2]    float32    cumulative angle (NULL iff theta NULL);
+ *   phi       [Bt, H, N/2]    float32    cumulative angle (NULL iff neither
+ *                                        theta nor omega is given);
  *                                        stored reduced modulo 2*pi
  *   Bprev_rot [Bt, H, R, N]   float32    rotated B of the previous token
  *   xprev     [Bt, H, R, P]   in_dtype   x of the previous token
  *   In:
  *   x [Bt,H,R,P], B, C [Bt,H,R,N] (in_dtype); dt, lam [Bt,H] float32;
  *   A [H] float32, or A_tok [Bt,H] float32 (A per (batch, head) for this
- *   token; then A may be NULL); theta [Bt,H,N/2] float32 or NULL.
+ *   token; then A may be NULL); theta [Bt,H,N/2] float32 or NULL, or instead
+ *   omega [Bt,N/2] float32 (rates shared by the heads: theta = dt * omega).
  *   Out: y [Bt, H, R, P] in_dtype.
  * Sizes: N, P in {16, 32, 64, 128}; R in 1..16.  A fresh sequence starts with
  * h = 0 (or any state), Bprev_rot = 0, xprev = 0, phi = 0.
@@ -191,6 +193,7 @@ typedef struct m3_decode_args {
   const float* theta;
   void* y;
   const float* A_tok; /* [Bt, H] A of this token, or NULL */
+  const float* omega; /* [Bt, N/2] rotation rates shared by the heads, or NULL */
 } m3_decode_args;
 
 int m3_ssm_decode_step(const m3_decode_args* args, void* stream);

@@ -38,7 +38,7 @@ class DecodeArgs(ctypes.Structure):
         ("Bt", _i32), ("H", _i32), ("P", _i32), ("N", _i32), ("R", _i32), ("in_dtype", _i32),
         ("h", _vp), ("phi", _vp), ("Bprev_rot", _vp), ("xprev", _vp),
         ("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp), ("lam", _vp), ("A", _vp), ("theta", _vp),
-        ("y", _vp), ("A_tok", _vp),
+        ("y", _vp), ("A_tok", _vp), ("omega", _vp),
     ]
 
 

@@ -209,11 +209,13 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   if (!a->h || !a->Bprev_rot || !a->xprev || !a->x || !a->B || !a->C || !a->dt || !a->lam || (!a->A && !a->A_tok) ||
       !a->y)
     return M3_ERR_INVALID_ARG;
-  if ((a->theta == nullptr) != (a->phi == nullptr)) return M3_ERR_INVALID_ARG;
-  if (a->theta != nullptr && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
+  if (a->theta != nullptr && a->omega != nullptr) return M3_ERR_INVALID_ARG;  // one angle source
+  const bool rope = a->theta != nullptr || a->omega != nullptr;
+  if (rope != (a->phi != nullptr)) return M3_ERR_INVALID_ARG;
+  if (rope && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
   if (a->R > 16) return M3_ERR_UNSUPPORTED;
   if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
-  const void* v16[] = {a->h, a->Bprev_rot, a->xprev, a->x, a->B, a->C, a->y, a->phi, a->theta};
+  const void* v16[] = {a->h, a->Bprev_rot, a->xprev, a->x, a->B, a->C, a->y, a->phi, a->theta, a->omega};
   for (const void* p : v16)
     if (!al16(p)) return M3_ERR_INVALID_ARG;
   if (!al4(a->dt) || !al4(a->lam) || !al4(a->A) || !al4(a->A_tok)) return M3_ERR_INVALID_ARG;
@@ -225,6 +227,7 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.theta = a->theta;
   p.y = a->y;
   p.A_tok = a->A_tok;
+  p.omega = a->omega;
   return hip_status(m3::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int c4 = tid % QP;
+  const bool rope = p.theta != nullptr || p.omega != nullptr;
   constexpr int KX = (RMAX * P + kDecThreads - 1) / kDecThreads;  // x elements per thread
   constexpr int KB = (RMAX * N + kDecThreads - 1) / kDecThreads;  // B, C elements per thread
   constexpr int kIters = (NQUAD + kDecThreads - 1) / kDecThreads;  // state quads per thread
@@ -82,9 +83,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
     }
     U.rth = 0.f;
     U.rph = 0.f;
-    if (p.theta != nullptr) {
+    if (rope) {
       const int j = tid < N / 2 ? tid : 0;
-      U.rth = __builtin_nontemporal_load(p.theta + static_cast<size_t>(bh) * (N / 2) + j);
+      const float* src = p.omega != nullptr ? p.omega + static_cast<size_t>(bh / p.H) * (N / 2)
+                                            : p.theta + static_cast<size_t>(bh) * (N / 2);
+      U.rth = __builtin_nontemporal_load(src + j);
       U.rph = p.phi[static_cast<size_t>(bh) * (N / 2) + j];
     }
     const float* h = p.h + static_cast<size_t>(bh) * N * P;
@@ -109,8 +112,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
     const float gamma = lm * dt;
 
     // ---- angles: Phi <- wrap(Phi + theta); table of cos/sin per pair
-    if (p.theta != nullptr && tid < N / 2) {
-      const float a = wrap_angle(U.rph + U.rth);
+    if (rope && tid < N / 2) {
+      const float a = wrap_angle(U.rph + (p.omega != nullptr ? dt * U.rth : U.rth));
       sPhi[tid] = a;
       float sn, cs;
       sincosf(a, &sn, &cs);
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
       const int j = e % (N / 2);
       float b0 = sBr[r * N + 2 * j], b1 = sBr[r * N + 2 * j + 1];
       float c0 = sCr[r * N + 2 * j], c1 = sCr[r * N + 2 * j + 1];
-      if (p.theta != nullptr) {
+      if (rope) {
         const float c = sCS[2 * j], sn = sCS[2 * j + 1];
         const float rb0 = c * b0 + sn * b1, rb1 = -sn * b0 + c * b1;
         const float rc0 = c * c0 + sn * c1, rc1 = -sn * c0 + c * c1;
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
       const int e = tid + i * kDecThreads;
       if (e < R * P) store_scalar(xprev + e, U.rx[i]);
     }
-    if (p.theta != nullptr && tid < N / 2) p.phi[static_cast<size_t>(bh) * (N / 2) + tid] = sPhi[tid];
+    if (rope && tid < N / 2) p.phi[static_cast<size_t>(bh) * (N / 2) + tid] = sPhi[tid];
     __syncthreads();
 
     // ---- state update, 16-byte coalesced: thread owns quad column c4, rows n

@@ -22,6 +22,7 @@ struct DecodeParams {
   const float* theta;
   void* y;
   const float* A_tok;  // [Bt, H] A of this token, or null (then A [H])
+  const float* omega;  // [Bt, N/2] rates shared by the heads (theta = dt * omega), or null
 };
 
 struct PrefillParams {

@@ -121,12 +121,13 @@ def prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=torch.bfloat16, rope=False)
 
 
 def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None, *, y=None, A_tok=None,
-                       stream=None):
+                       omega=None, stream=None):
     """One decode token.  In/out (updated in place): h [Bt,H,N,P] fp32,
     phi [Bt,H,N/2] fp32 (None iff theta None), Bprev_rot [Bt,H,R,N] fp32,
     xprev [Bt,H,R,P].  Inputs x [Bt,H,R,P], B/C [Bt,H,R,N], dt/lam [Bt,H],
     A [H] (or A_tok [Bt,H]: this token's A; then A may be None), theta
-    [Bt,H,N/2] or None.  Returns y [Bt,H,R,P]."""
+    [Bt,H,N/2] or None (or omega [Bt,N/2]: rates shared by the heads, theta =
+    dt * omega).  Returns y [Bt,H,R,P]."""
     Bt, H, R, P = x.shape
     N = B.shape[-1]
     f32 = torch.float32
@@ -147,6 +148,7 @@ def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None
     a.A = _ptr(A, f32, (H,), "A")
     a.A_tok = _ptr(A_tok, f32, (Bt, H), "A_tok")
     a.theta = _ptr(theta, f32, (Bt, H, N // 2), "theta")
+    a.omega = _ptr(omega, f32, (Bt, N // 2), "omega")
     a.y = _ptr(y, x.dtype, (Bt, H, R, P), "y")
     rc = _lib.load().m3_ssm_decode_step(ctypes.byref(a), _stream(stream))
     if rc != _lib.M3_OK:

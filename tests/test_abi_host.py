@@ -132,6 +132,10 @@ def test_decode_validation():
         (lambda a: setattr(a, "h", None), _lib.M3_ERR_INVALID_ARG),
         (lambda a: setattr(a, "theta", 0x30000000), _lib.M3_ERR_INVALID_ARG),  # theta without phi
         (lambda a: setattr(a, "phi", 0x30000000), _lib.M3_ERR_INVALID_ARG),  # phi without theta
+        (lambda a: setattr(a, "omega", 0x30000000), _lib.M3_ERR_INVALID_ARG),  # omega without phi
+        (lambda a: (setattr(a, "omega", 0x30000000), setattr(a, "theta", 0x30100000), setattr(a, "phi", 0x30200000)),
+         _lib.M3_ERR_INVALID_ARG),  # two angle sources
+        (lambda a: setattr(a, "A", None), _lib.M3_ERR_INVALID_ARG),  # neither A nor A_tok
         (lambda a: setattr(a, "R", 17), _lib.M3_ERR_UNSUPPORTED),
         (lambda a: setattr(a, "N", 24), _lib.M3_ERR_UNSUPPORTED),
         (lambda a: setattr(a, "Bt", 0), _lib.M3_ERR_INVALID_ARG),

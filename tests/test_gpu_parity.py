@@ -365,6 +365,33 @@ def test_decode_A_tok(ops):
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
+def test_decode_omega(ops):
+    """Decode steps with the angles given as rates shared by the heads: the
+    oracle on theta = dt * omega."""
+    Bt, H, P, N, R, steps = 2, 3, 64, 64, 4, 5
+    s = Shape(Bt, steps, H, P, N, R, "bf16", True)
+    _say("decode omega")
+    d = make_inputs(s, 888, h0=True)
+    st = storage_dtype(s)
+    dec = {k: dev(np.moveaxis(d[k], 1, 0), st if k in ("x", "B", "C") else torch.float32)
+           for k in ("x", "B", "C", "dt", "lam", "omega")}
+    state = dict(h=dev(d["h0"]), phi=dev(np.zeros((Bt, H, N // 2))), Bprev_rot=dev(np.zeros((Bt, H, R, N))),
+                 xprev=dev(np.zeros((Bt, H, R, P)), st))
+    A = dev(d["A"])
+    ys = []
+    for t in range(steps):
+        ys.append(host(ops.m3_ssm_decode_step(state["h"], state["phi"], state["Bprev_rot"], state["xprev"],
+                                              dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t],
+                                              A, None, omega=dec["omega"][t])))
+    torch.cuda.synchronize()
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"], d["h0"])
+    ey = orc.rel_l2(np.stack(ys, axis=1), ref["y"])
+    eh = orc.rel_l2(host(state["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert np.max(angle_diff(host(state["phi"]), ref["phi"])) <= 1e-4
+
+
 def test_decode_config_full_size(ops):
     """Decode workload at full size (B=256, H=32, N=P=64, R=4) for a few steps,
     checked against the oracle on every (batch, head)."""
