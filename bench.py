@@ -188,7 +188,7 @@ def time_prefill(torch, ops, inp, steps, warmup, mode=""):
 
 
 FLUSH_BYTES = 1 << 30  # four times the 256 MB Infinity Cache
-FLUSHED_RUNS = 9
+FLUSHED_RUNS = 51
 
 
 def flushed_ms(torch, run):
@@ -522,8 +522,8 @@ def pmc_workload(torch, ops):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "pmc"), default="all")
