@@ -324,8 +324,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const int quad = wave & 3;             // row tile (staging) and p-tile group (compute)
   const bool upper = (wave >> 2) & 1;    // piece half (staging) and i-tile pair (compute)
   const int units = p.Bt * p.H;
-  const int seg = blockIdx.x / units;
-  const int bh = blockIdx.x % units;
+  // Workgroups are dealt to the 8 XCDs in turn; renumber them so that each XCD
+  // walks a contiguous range of (segment, batch, head) units, i.e. whole token
+  // rows of a batch, which keeps its L2's address translations few.
+  int wg = blockIdx.x;
+  if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
+  const int seg = wg / units;
+  const int bh = wg % units;
   const int b = bh / p.H;
   const int hh = bh % p.H;
   const int H = p.H;
