@@ -325,11 +325,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const bool upper = (wave >> 2) & 1;    // piece half (staging) and i-tile pair (compute)
   const int units = p.Bt * p.H;
   // Workgroups are dealt to the 8 XCDs in turn; renumber them so that each XCD
-  // walks a contiguous range of (segment, batch, head) units: the heads of one
-  // token are adjacent in memory, so one XCD then reads whole token rows of a
-  // batch (measured 1-2% faster on the SISO workloads; the decode step, whose
-  // units are whole state blocks, measured 16% slower this way and keeps the
-  // plain order).
+  // walks a contiguous range of (segment, batch, head) units.  The heads of one
+  // token are adjacent in memory: Delta and lambda of 32 heads share one cache
+  // line, which every XCD holding one of those heads fetched again into its own
+  // L2 (HBM reads fell from 1.08x to 1.00x the algorithmic bytes, 1-2% faster).
+  // The decode step, whose units are whole state blocks, measured 16% slower
+  // this way and keeps the plain order.
   int wg = blockIdx.x;
   if ((gridDim.x & 7) == 0) wg = (wg & 7) * (gridDim.x >> 3) + (wg >> 3);
   const int seg = wg / units;
