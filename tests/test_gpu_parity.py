@@ -214,6 +214,8 @@ SPLIT = [
     (1, 1000, 1, 128, 128, 1, False, True),
     (3, 300, 2, 16, 16, 2, True, False),
     (1, 1500, 2, 64, 64, 1, True, True),     # first half walked as two parts, then joined
+    (2, 600, 4, 64, 64, 1, True, True),      # 16 workgroups: renumbered across the XCDs
+    (2, 1500, 4, 64, 64, 1, True, True),     # the same with the first half in two parts
     (2, 1100, 1, 64, 128, 1, False, True),
 ]
 
