@@ -164,8 +164,16 @@ def gen_prefill(torch, Bt, L, H, P, N, R, rope, seed):
 
 
 def time_prefill(torch, ops, inp, steps, warmup, mode=""):
+    hm = mode == "hm"  # x, B, C, y head-major [Bt, H, L, R, .]
+    if hm:
+        inp = dict(inp)
+        for k in ("x", "B", "C"):
+            inp[k] = inp[k].permute(0, 2, 1, 3, 4).contiguous()
     y = torch.empty_like(inp["x"])
-    Bt, L, H, R, P = inp["x"].shape
+    if hm:
+        Bt, H, L, R, P = inp["x"].shape
+    else:
+        Bt, L, H, R, P = inp["x"].shape
     N = inp["B"].shape[-1]
     hf = torch.empty((Bt, H, N, P), device="cuda", dtype=torch.float32)
 
@@ -178,7 +186,7 @@ def time_prefill(torch, ops, inp, steps, warmup, mode=""):
 
     def run():
         ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], A, theta,
-                           y=y, h_final=hf, workspace=ws, omega=omega, A_tok=a_tok)
+                           y=y, h_final=hf, workspace=ws, omega=omega, A_tok=a_tok, head_major=hm)
 
     for _ in range(max(warmup, 1)):
         run()
@@ -566,6 +574,8 @@ def main():
         runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
         runs += [(name + "_omega", shp, "omega") for name, shp in prefill_shapes().items() if shp[-1]]
         runs += [("siso_real_atok", prefill_shapes()["siso_real"], "atok")]
+        # and the SISO workloads with x, B, C, y head-major ([Bt, H, L, R, .])
+        runs += [(name + "_headmajor", prefill_shapes()[name], "hm") for name in ("siso_real", "siso_rope")]
         for i, (name, shp, mode) in enumerate(runs):
             Bt, L, H, P, N, R, rope = shp
             inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260100 + i)
@@ -575,6 +585,8 @@ def main():
             angles = "RoPE, angles from rates" if mode == "omega" else ("RoPE" if rope else "real")
             if mode == "atok":
                 angles += ", A per token"
+            if mode == "hm":
+                angles += ", head-major x/B/C/y"
             res = dict(workload=f"prefill {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
                                 f"{angles} bf16 chunk {Q_ROWS // R}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, kernel_ms=launch_ms,
@@ -641,7 +653,8 @@ def main():
         out["decode_roofline"] = {"bound": "hbm", "achieved": dres["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": dres["hbm_frac"], "traffic": traffic_for("decode"),
                                   "kernel": decode_kernel_name(*DECODE_SHAPE)}
-    for k in ("siso_rope", "mimo_rope", "siso_rope_omega", "mimo_rope_omega", "siso_real_atok"):
+    for k in ("siso_rope", "mimo_rope", "siso_rope_omega", "mimo_rope_omega", "siso_real_atok",
+              "siso_real_headmajor", "siso_rope_headmajor"):
         if k in results:
             out["prefill_" + k] = results[k]
     if "angles" in results:

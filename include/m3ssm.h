@@ -61,6 +61,12 @@ typedef enum m3_dtype {
   M3_BF16 = 1  /* bfloat16 stored as uint16 bit patterns */
 } m3_dtype;
 
+/* Order of the token and head axes of the prefill's x, B, C and y. */
+typedef enum m3_layout {
+  M3_TOKEN_MAJOR = 0, /* [Bt, L, H, R, .] (the default) */
+  M3_HEAD_MAJOR = 1   /* [Bt, H, L, R, .]: each head's rows one contiguous run */
+} m3_layout;
+
 /*
  * Prefill (chunked, whole sequence per (batch, head)).
  *
@@ -108,6 +114,12 @@ typedef enum m3_dtype {
  * workspace: optional, see m3_ssm_prefill_workspace_size; a non-NULL
  * workspace smaller than that size (or not 256-byte aligned) is
  * M3_ERR_INVALID_ARG.
+ * layout: M3_TOKEN_MAJOR (0, the shapes above) or M3_HEAD_MAJOR (1): x, B, C
+ * and y as [Bt, H, L, R, .] (dt, lam, A_tok, theta and omega keep the shapes
+ * above).  The arithmetic is the same, so both layouts give identical bits;
+ * head-major reads each (batch, head) walk as one contiguous run.  bf16 only
+ * (fp32 with M3_HEAD_MAJOR is M3_ERR_UNSUPPORTED); other values are
+ * M3_ERR_INVALID_ARG.
  */
 typedef struct m3_prefill_args {
   int32_t Bt, L, H, P, N, R, chunk;
@@ -132,6 +144,7 @@ typedef struct m3_prefill_args {
   size_t workspace_bytes;
   const float* omega;     /* [Bt, L, N/2] angular rates, or NULL (see above) */
   const float* A_tok;     /* [Bt, L, H] A per token, or NULL (see above) */
+  int32_t layout;         /* m3_layout of x, B, C, y (see above) */
 } m3_prefill_args;
 
 int m3_ssm_prefill(const m3_prefill_args* args, void* stream);

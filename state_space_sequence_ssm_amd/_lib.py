@@ -30,6 +30,7 @@ class PrefillArgs(ctypes.Structure):
         ("h0", _vp), ("Bprev_rot", _vp), ("xprev", _vp), ("phi0", _vp),
         ("y", _vp), ("h_final", _vp), ("Bprev_rot_out", _vp), ("xprev_out", _vp), ("phi_out", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("omega", _vp), ("A_tok", _vp),
+        ("layout", ctypes.c_int32),
     ]
 
 

@@ -64,6 +64,8 @@ struct PrefillParams {
   const float* Bprev_mid;
   const void* xprev_mid;
   const float* phi_mid;
+  // x, B, C, y head-major [Bt, H, L, R, .] instead of token-major (bf16 path)
+  int headMajor;
 };
 
 struct AnglesParams {

@@ -353,10 +353,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // sequence, and its successor adds the pending term through its carry-in)
   const size_t tok0 = static_cast<size_t>(b) * p.Lfull + t0;  // first (t, h) row / H
   const size_t tokB = static_cast<size_t>(L) * H;              // (t, h) pairs of the segment
-  const rsrc_t rX = make_rsrc(static_cast<const bf16_t*>(p.x) + tok0 * H * R * P, uint32_t(tokB * R * P * 2));
-  const rsrc_t rB = make_rsrc(static_cast<const bf16_t*>(p.B) + tok0 * H * R * N, uint32_t(tokB * R * N * 2));
-  const rsrc_t rC = make_rsrc(static_cast<const bf16_t*>(p.C) + tok0 * H * R * N, uint32_t(SO ? 0 : tokB * R * N * 2));
-  const rsrc_t rY = make_rsrc(SO ? p.x : static_cast<bf16_t*>(p.y) + tok0 * H * R * P, uint32_t(SO ? 0 : tokB * R * P * 2));
+  // x, B, C and y are token-major [Bt, L, H, R, .] (consecutive tokens of a
+  // head H * R rows apart) or head-major [Bt, H, L, R, .] (R rows apart); the
+  // resources start at this unit's first (token, rank) row and end after its
+  // last one, so tokens past the segment read zeros and their stores drop
+  const int tsR = p.headMajor ? R : H * R;  // rows between consecutive tokens
+  const size_t row0 = p.headMajor ? (static_cast<size_t>(bh) * p.Lfull + t0) * R : (tok0 * H + hh) * R;
+  const size_t rowsU = static_cast<size_t>(L - 1) * tsR + R;  // rows the segment spans
+  const rsrc_t rX = make_rsrc(static_cast<const bf16_t*>(p.x) + row0 * P, uint32_t(rowsU * P * 2));
+  const rsrc_t rB = make_rsrc(static_cast<const bf16_t*>(p.B) + row0 * N, uint32_t(rowsU * N * 2));
+  const rsrc_t rC = make_rsrc(static_cast<const bf16_t*>(p.C) + row0 * N, uint32_t(SO ? 0 : rowsU * N * 2));
+  const rsrc_t rY = make_rsrc(SO ? p.x : static_cast<bf16_t*>(p.y) + row0 * P, uint32_t(SO ? 0 : rowsU * P * 2));
   const rsrc_t rDt = make_rsrc(p.dt + tok0 * H, uint32_t(tokB * 4));
   const rsrc_t rLam = make_rsrc(p.lam + tok0 * H, uint32_t(tokB * 4));
   // A per token (null: the head's A for every token)
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     const int D = pc.kind == 2 ? P : N;
     int row, col;
     piece_rc(pc, row, col);
-    const uint32_t grow = static_cast<uint32_t>(((c * Q + (row >> LGR)) * H + hh) * R + (row & (R - 1)));
+    const uint32_t grow = static_cast<uint32_t>((c * Q + (row >> LGR)) * tsR + (row & (R - 1)));
     const uint32_t off = col < D ? (grow * D + col) * 2u : kBad;
     return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
   };
@@ -816,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
             if (kAllPt || quad + kPGroups * u < NPT) yacc[u] = mma(xfr[u][m], sop, yacc[u]);
         }
       }
-      const uint32_t yrow = static_cast<uint32_t>(((k * Q + ti) * H + hh) * R + (iRow & (R - 1))) * P;
+      const uint32_t yrow = static_cast<uint32_t>((k * Q + ti) * tsR + (iRow & (R - 1))) * P;
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
         const int pt = quad + kPGroups * u;
@@ -878,7 +885,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       const u32x2 lo = src[0], hi = src[1];
       const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
       const uint32_t off = (c >= 0 && e < kUnits)
-                               ? (static_cast<uint32_t>(((c * Q + (r >> LGR)) * H + hh) * R + (r & (R - 1))) * P + 8 * c8) * 2u
+                               ? (static_cast<uint32_t>((c * Q + (r >> LGR)) * tsR + (r & (R - 1))) * P + 8 * c8) * 2u
                                : kBad;
       bstore16(rY, off, v);
     }
@@ -1029,7 +1036,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if (bOut != nullptr) {
       for (int e = tid; e < R * (N / 2); e += kThreads) {
         const int r = e / (N / 2), q = e % (N / 2);
-        const bf16_t* src = static_cast<const bf16_t*>(p.B) + ((tok0 + t) * H + hh) * R * N + r * N;
+        const bf16_t* src = static_cast<const bf16_t*>(p.B) + (row0 + static_cast<size_t>(t) * tsR + r) * N;
         float a0 = bf16_to_f32(src[2 * q].bits), a1 = bf16_to_f32(src[2 * q + 1].bits);
         if constexpr (ROPE) {
           // Phi_{L-1} is the final angle carry (reduced modulo 2 pi)
@@ -1047,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if (xOut != nullptr)
       for (int e = tid; e < R * P; e += kThreads)
         xOut[static_cast<size_t>(bh) * R * P + e] =
-            static_cast<const bf16_t*>(p.x)[((tok0 + t) * H + hh) * R * P + e];
+            static_cast<const bf16_t*>(p.x)[(row0 + static_cast<size_t>(t) * tsR) * P + e];
   }
 }
 

@@ -50,7 +50,7 @@ def _stream(stream) -> int:
 def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
                    *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
                    want_state=True, want_carry=False, chunk=0, workspace=None, omega=None, A_tok=None,
-                   stream=None):
+                   head_major=False, stream=None):
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
     dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None (or
     instead omega [Bt,L,N/2] fp32: rates shared by the heads, theta = dt * omega
@@ -61,9 +61,13 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     tensor of at least prefill_workspace_bytes(...) bytes, None to allocate one
     when the library asks for it, or False to run without (unsplit).  Returns
     a dict with y and, as requested, h_final and the carry-out (Bprev_rot,
-    xprev, phi)."""
-    Bt, L, H, R, P = x.shape
+    xprev, phi).  head_major: x, B, C and y are [Bt,H,L,R,.] instead (bf16)."""
+    if head_major:
+        Bt, H, L, R, P = x.shape
+    else:
+        Bt, L, H, R, P = x.shape
     N = B.shape[-1]
+    big = (lambda D: (Bt, H, L, R, D)) if head_major else (lambda D: (Bt, L, H, R, D))
     f32 = torch.float32
     if y is None:
         y = torch.empty_like(x)
@@ -79,9 +83,10 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a = _lib.PrefillArgs()
     a.Bt, a.L, a.H, a.P, a.N, a.R, a.chunk = Bt, L, H, P, N, R, chunk
     a.in_dtype = _dtype_code(x)
-    a.x = _ptr(x, x.dtype, (Bt, L, H, R, P), "x")
-    a.B = _ptr(B, x.dtype, (Bt, L, H, R, N), "B")
-    a.C = _ptr(C, x.dtype, (Bt, L, H, R, N), "C")
+    a.layout = 1 if head_major else 0
+    a.x = _ptr(x, x.dtype, big(P), "x")
+    a.B = _ptr(B, x.dtype, big(N), "B")
+    a.C = _ptr(C, x.dtype, big(N), "C")
     a.dt = _ptr(dt, f32, (Bt, L, H), "dt")
     a.lam = _ptr(lam, f32, (Bt, L, H), "lam")
     a.A = _ptr(A, f32, (H,), "A")
@@ -92,7 +97,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a.Bprev_rot = _ptr(Bprev_rot, f32, (Bt, H, R, N), "Bprev_rot")
     a.xprev = _ptr(xprev, x.dtype, (Bt, H, R, P), "xprev")
     a.phi0 = _ptr(phi0, f32, (Bt, H, N // 2), "phi0")
-    a.y = _ptr(y, x.dtype, (Bt, L, H, R, P), "y")
+    a.y = _ptr(y, x.dtype, big(P), "y")
     a.h_final = _ptr(h_final, f32, (Bt, H, N, P), "h_final")
     a.Bprev_rot_out = _ptr(Bprev_rot_out, f32, (Bt, H, R, N), "Bprev_rot_out")
     a.xprev_out = _ptr(xprev_out, x.dtype, (Bt, H, R, P), "xprev_out")

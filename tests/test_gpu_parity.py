@@ -131,6 +131,44 @@ def test_prefill_omega(ops, case):
     assert np.max(angle_diff(host(out["phi"]), host(ref_gpu["phi"]))) <= 1e-4
 
 
+# ----------------------------------------------------------------- head-major layout
+HEADMAJOR = [
+    # Bt, L, H, P, N, R, rope, carry
+    (2, 131, 3, 64, 128, 1, False, True),
+    (2, 200, 3, 64, 64, 1, True, True),
+    (1, 100, 2, 64, 64, 4, True, True),
+    (1, 45, 2, 16, 32, 8, True, False),
+    (3, 70, 2, 128, 32, 2, True, True),
+    (1, 1500, 2, 64, 64, 1, True, True),  # split: first half walked in two parts, then both halves
+]
+
+
+@pytest.mark.parametrize("case", HEADMAJOR, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_head_major(ops, case):
+    """x, B, C and y head-major ([Bt,H,L,R,.]): bit for bit the token-major
+    call (the arithmetic is the same), and the oracle within tolerance."""
+    Bt, L, H, P, N, R, rope, carry = case
+    s = Shape(Bt, L, H, P, N, R, "bf16", rope)
+    _say("prefill head-major", case)
+    d = make_inputs(s, 5000 + L + N, h0=carry, carry=carry)
+    dd = to_device(d, s)
+    swap = lambda t: t.permute(0, 2, 1, 3, 4).contiguous()  # noqa: E731  token <-> head axes
+    out_t = _run_prefill(ops, dd, s, carry=True)
+    out_h = ops.m3_ssm_prefill(swap(dd["x"]), swap(dd["B"]), swap(dd["C"]), dd["dt"], dd["lam"], dd["A"],
+                               dd["theta"], dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"),
+                               want_state=True, want_carry=True, head_major=True)
+    torch.cuda.synchronize()
+    y_h = host(swap(out_h["y"]))
+    assert np.array_equal(y_h, host(out_t["y"]))
+    for k in ("h", "Bprev_rot", "xprev") + (("phi",) if rope else ()):
+        assert np.array_equal(host(out_h[k]), host(out_t[k])), k
+    ref = oracle_prefill(d)
+    ey = orc.rel_l2(y_h, ref["y"])
+    eh = orc.rel_l2(host(out_h["h"]), ref["h"])
+    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------- edge values
 EDGE = [
     # name, Bt, L, H, P, N, R, rope
