@@ -117,9 +117,8 @@ typedef enum m3_layout {
  * layout: M3_TOKEN_MAJOR (0, the shapes above) or M3_HEAD_MAJOR (1): x, B, C
  * and y as [Bt, H, L, R, .] (dt, lam, A_tok, theta and omega keep the shapes
  * above).  The arithmetic is the same, so both layouts give identical bits;
- * head-major reads each (batch, head) walk as one contiguous run.  bf16 only
- * (fp32 with M3_HEAD_MAJOR is M3_ERR_UNSUPPORTED); other values are
- * M3_ERR_INVALID_ARG.
+ * head-major reads each (batch, head) walk as one contiguous run.  Other
+ * values are M3_ERR_INVALID_ARG.
  */
 typedef struct m3_prefill_args {
   int32_t Bt, L, H, P, N, R, chunk;

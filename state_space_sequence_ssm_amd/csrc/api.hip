@@ -98,7 +98,6 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   if (a->Bt < 1 || a->L < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
   if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
   if (a->layout != M3_TOKEN_MAJOR && a->layout != M3_HEAD_MAJOR) return M3_ERR_INVALID_ARG;
-  if (a->layout == M3_HEAD_MAJOR && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
   if (!a->x || !a->B || !a->C || !a->dt || !a->lam || (!a->A && !a->A_tok) || !a->y) return M3_ERR_INVALID_ARG;
   if ((a->Bprev_rot == nullptr) != (a->xprev == nullptr)) return M3_ERR_INVALID_ARG;
   if (a->theta != nullptr && a->omega != nullptr) return M3_ERR_INVALID_ARG;  // one angle source

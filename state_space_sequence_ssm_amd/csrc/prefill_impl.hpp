@@ -161,9 +161,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const T* xg = static_cast<const T*>(p.x);
   const T* Bg = static_cast<const T*>(p.B);
   const T* Cg = static_cast<const T*>(p.C);
-  // element offset of (b, t, h, rank 0) rows
+  // element offset of (b, t, h, rank 0) rows: token-major [Bt, L, H, R, .]
+  // or head-major [Bt, H, L, R, .]
+  const bool hm = p.headMajor != 0;
   auto rowbase = [&](int t) -> size_t {
-    return ((static_cast<size_t>(b) * L + t) * H + hh) * static_cast<size_t>(R);
+    const size_t row = hm ? (static_cast<size_t>(b) * H + hh) * L + t : (static_cast<size_t>(b) * L + t) * H + hh;
+    return row * static_cast<size_t>(R);
   };
 
   // ------------------------------------------------------------ prefetch state

@@ -61,7 +61,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     tensor of at least prefill_workspace_bytes(...) bytes, None to allocate one
     when the library asks for it, or False to run without (unsplit).  Returns
     a dict with y and, as requested, h_final and the carry-out (Bprev_rot,
-    xprev, phi).  head_major: x, B, C and y are [Bt,H,L,R,.] instead (bf16)."""
+    xprev, phi).  head_major: x, B, C and y are [Bt,H,L,R,.] instead."""
     if head_major:
         Bt, H, L, R, P = x.shape
     else:

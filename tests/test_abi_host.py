@@ -69,8 +69,7 @@ def test_prefill_validation():
         (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "N", 128), setattr(a, "P", 128),
                     setattr(a, "theta", 0x30000000)), _lib.M3_ERR_UNSUPPORTED),  # LDS too large
         (lambda a: setattr(a, "layout", 2), _lib.M3_ERR_INVALID_ARG),  # no such layout
-        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "layout", 1)),
-         _lib.M3_ERR_UNSUPPORTED),  # head-major is bf16 only
+        (lambda a: setattr(a, "layout", -1), _lib.M3_ERR_INVALID_ARG),
     ]
     for mutate, code in cases:
         a = _good_prefill()

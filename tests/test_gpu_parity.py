@@ -133,13 +133,15 @@ def test_prefill_omega(ops, case):
 
 # ----------------------------------------------------------------- head-major layout
 HEADMAJOR = [
-    # Bt, L, H, P, N, R, rope, carry
-    (2, 131, 3, 64, 128, 1, False, True),
-    (2, 200, 3, 64, 64, 1, True, True),
-    (1, 100, 2, 64, 64, 4, True, True),
-    (1, 45, 2, 16, 32, 8, True, False),
-    (3, 70, 2, 128, 32, 2, True, True),
-    (1, 1500, 2, 64, 64, 1, True, True),  # split: first half walked in two parts, then both halves
+    # Bt, L, H, P, N, R, rope, carry, dtype
+    (2, 131, 3, 64, 128, 1, False, True, "bf16"),
+    (2, 200, 3, 64, 64, 1, True, True, "bf16"),
+    (1, 100, 2, 64, 64, 4, True, True, "bf16"),
+    (1, 45, 2, 16, 32, 8, True, False, "bf16"),
+    (3, 70, 2, 128, 32, 2, True, True, "bf16"),
+    (1, 1500, 2, 64, 64, 1, True, True, "bf16"),  # split: first half walked in two parts, then both halves
+    (2, 150, 3, 32, 32, 2, True, True, "f32"),
+    (1, 90, 2, 32, 16, 4, False, False, "f32"),
 ]
 
 
@@ -147,8 +149,8 @@ HEADMAJOR = [
 def test_prefill_head_major(ops, case):
     """x, B, C and y head-major ([Bt,H,L,R,.]): bit for bit the token-major
     call (the arithmetic is the same), and the oracle within tolerance."""
-    Bt, L, H, P, N, R, rope, carry = case
-    s = Shape(Bt, L, H, P, N, R, "bf16", rope)
+    Bt, L, H, P, N, R, rope, carry, dt_ = case
+    s = Shape(Bt, L, H, P, N, R, dt_, rope)
     _say("prefill head-major", case)
     d = make_inputs(s, 5000 + L + N, h0=carry, carry=carry)
     dd = to_device(d, s)
@@ -166,7 +168,7 @@ def test_prefill_head_major(ops, case):
     ey = orc.rel_l2(y_h, ref["y"])
     eh = orc.rel_l2(host(out_h["h"]), ref["h"])
     _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
-    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+    assert ey <= TOL[dt_] and eh <= TOL[dt_]
 
 
 # ----------------------------------------------------------------- edge values
