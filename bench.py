@@ -14,14 +14,20 @@ omega ~ N(0,1) per token and pair; decode state ~ N(0, 0.1^2)) and are
 resident in HBM before timing starts.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S]
-                       [--no-cpu-baseline] [--only prefill|decode|all|pmc]
+                       [--no-cpu-baseline] [--only prefill|decode|all|headline|pmc]
+                       [--group base|variants]
        python bench.py --report-trace PREFIX          (rocprofv3 kernel trace -> markdown)
-       python bench.py --report-pmc FETCH_PREFIX WRITE_PREFIX   (HBM counters -> markdown)
+       python bench.py --report-pmc FETCH_PREFIX WRITE_PREFIX [FETCH_PREFIX WRITE_PREFIX ...]
+       python bench.py --report-counters PREFIX [PREFIX ...]   (memory-pipe counters -> markdown)
 
---only pmc runs the counter workload: a plain device copy of known size (the
-scale for FETCH_SIZE / WRITE_SIZE), then two launches of each prefill kernel
-and three decode steps, untimed.  PREFIX is the rocprofv3 output prefix
-(-d DIR -o NAME gives DIR/NAME).
+--only headline times the headline workload alone (its own rows in a kernel
+trace).  --only pmc runs the counter workload of one --group: a plain device
+copy of known size (the scale for FETCH_SIZE / WRITE_SIZE), then a few
+untimed launches of each workload of the group ("base": the five workloads
+and the decode control at Bt=512; "variants": the prefill lines with angles
+as rates and A per token).  Within a group every workload runs a distinct
+kernel symbol or grid, so counter rows map to workloads.  PREFIX is the
+rocprofv3 output prefix (-d DIR -o NAME gives DIR/NAME).
 """
 from __future__ import annotations
 
@@ -54,7 +60,14 @@ def prefill_shapes():
 
 
 DECODE_SHAPE = (256, 32, 64, 64, 4)  # Bt, H, P, N, R
+# control: twice the batch, so the resident state (268 MB) exceeds the 256 MB Infinity Cache
+DECODE_SHAPE_BIG = (512, 32, 64, 64, 4)
+DECODE_BIG_STEPS = 200
 COPY_BYTES = 1 << 30                 # plain copy used to scale the HBM counters
+
+# prefill lines beside the plain workloads: (line name, workload, mode)
+VARIANTS = [("siso_rope_omega", "siso_rope", "omega"), ("mimo_rope_omega", "mimo_rope", "omega"),
+            ("siso_real_atok", "siso_real", "atok")]
 
 
 def ANGLES_GRID(Bt, H, J):
@@ -108,9 +121,19 @@ def unit_kernels():
             out.append(("prefill_" + name, prefill_kernel_name(*shp), Bt * H * 512))
     Bt, H, P, N, R = DECODE_SHAPE
     out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
+    Bt, H, P, N, R = DECODE_SHAPE_BIG
+    out.append(("decode_bt512", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
     out.append(("angles", "m3::angles_cumsum_kernel", ANGLES_GRID(Bt, H, N // 2)))
     return out
+
+
+def variant_unit_kernels():
+    """unit_kernels() of the variant lines (same kernels as their workloads)."""
+    base = {u: [] for u, _, _ in unit_kernels()}
+    for u, k, g in unit_kernels():
+        base[u].append((k, g))
+    return [("prefill_" + line, k, g) for line, wl, _ in VARIANTS for k, g in base["prefill_" + wl]]
 
 
 def prefill_algo(Bt, L, H, P, N, R, rope, omega=False, a_tok=False):
@@ -146,24 +169,11 @@ def decode_algo(Bt, H, P, N, R, rope):
 
 
 def gen_prefill(torch, Bt, L, H, P, N, R, rope, seed):
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    dev, bf, f32 = "cuda", torch.bfloat16, torch.float32
-    x = torch.randn((Bt, L, H, R, P), generator=g, device=dev, dtype=f32).to(bf)
-    B = (torch.randn((Bt, L, H, R, N), generator=g, device=dev, dtype=f32) / math.sqrt(N)).to(bf)
-    C = (torch.randn((Bt, L, H, R, N), generator=g, device=dev, dtype=f32) / math.sqrt(N)).to(bf)
-    dt = torch.nn.functional.softplus(torch.randn((Bt, L, H), generator=g, device=dev) - 4.0).contiguous()
-    lam = torch.sigmoid(torch.randn((Bt, L, H), generator=g, device=dev)).contiguous()
-    A = (-torch.exp(torch.rand((H,), generator=g, device=dev) * math.log(16.0))).contiguous()
-    theta = om = None
-    if rope:
-        om = torch.randn((Bt, L, N // 2), generator=g, device=dev)
-        theta = (dt[:, :, :, None] * om[:, :, None, :]).contiguous()
-    a_tok = (-torch.exp(torch.rand((Bt, L, H), generator=g, device=dev) * math.log(16.0))).contiguous()
-    return dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta, omega=om, A_tok=a_tok)
+    from synth.device_inputs import prefill_inputs
+    return prefill_inputs(Bt, L, H, P, N, R, rope, seed)
 
 
-def time_prefill(torch, ops, inp, steps, warmup, mode=""):
+def time_prefill(torch, ops, inp, steps, warmup, mode="", flushed=True):
     hm = mode == "hm"  # x, B, C, y head-major [Bt, H, L, R, .]
     if hm:
         inp = dict(inp)
@@ -192,7 +202,7 @@ def time_prefill(torch, ops, inp, steps, warmup, mode=""):
         run()
     torch.cuda.synchronize()
     ms = replay_ms(torch, [run] * steps)
-    return ms, ms, flushed_ms(torch, run)
+    return ms, ms, (flushed_ms(torch, run) if flushed else None)
 
 
 FLUSH_BYTES = 1 << 30  # four times the 256 MB Infinity Cache
@@ -263,27 +273,24 @@ def replay_ms(torch, launches):
     return e0.elapsed_time(e1) / len(launches)
 
 
-def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    dev, bf, f32 = "cuda", torch.bfloat16, torch.float32
+def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed, flushed=True):
+    """Per-step time of `steps` sequential decode steps (each with its own
+    token's inputs), captured in one graph; and the median of single steps,
+    each after a 1 GiB read that evicts the Infinity Cache (the state then
+    comes from HBM, not from the cache)."""
+    from synth.device_inputs import DecodeStream
+    gen = DecodeStream(Bt, H, P, N, R, seed)
     S = steps + warmup
-    x = torch.randn((S, Bt, H, R, P), generator=g, device=dev, dtype=f32).to(bf)
-    B = (torch.randn((S, Bt, H, R, N), generator=g, device=dev, dtype=f32) / math.sqrt(N)).to(bf)
-    C = (torch.randn((S, Bt, H, R, N), generator=g, device=dev, dtype=f32) / math.sqrt(N)).to(bf)
-    dt = torch.nn.functional.softplus(torch.randn((S, Bt, H), generator=g, device=dev) - 4.0).contiguous()
-    lam = torch.sigmoid(torch.randn((S, Bt, H), generator=g, device=dev)).contiguous()
-    A = (-torch.exp(torch.rand((H,), generator=g, device=dev) * math.log(16.0))).contiguous()
-    om = torch.randn((S, Bt, N // 2), generator=g, device=dev)
-    theta = (dt[:, :, :, None] * om[:, :, None, :]).contiguous()
-    h = (torch.randn((Bt, H, N, P), generator=g, device=dev) * 0.1).contiguous()
-    phi = torch.zeros((Bt, H, N // 2), device=dev)
-    Bp = torch.zeros((Bt, H, R, N), device=dev)
-    xp = torch.zeros((Bt, H, R, P), device=dev, dtype=bf)
-    y = torch.empty((Bt, H, R, P), device=dev, dtype=bf)
+    toks = [gen.step() for _ in range(S)]
+    h = gen.h0
+    phi = torch.zeros((Bt, H, N // 2), device="cuda")
+    Bp = torch.zeros((Bt, H, R, N), device="cuda")
+    xp = torch.zeros((Bt, H, R, P), device="cuda", dtype=torch.bfloat16)
+    y = torch.empty((Bt, H, R, P), device="cuda", dtype=torch.bfloat16)
 
     def step(t):
-        ops.m3_ssm_decode_step(h, phi, Bp, xp, x[t], B[t], C[t], dt[t], lam[t], A, theta[t], y=y)
+        d = toks[t]
+        ops.m3_ssm_decode_step(h, phi, Bp, xp, d["x"], d["B"], d["C"], d["dt"], d["lam"], gen.A, d["theta"], y=y)
 
     for t in range(warmup):
         step(t)
@@ -291,35 +298,89 @@ def time_decode(torch, ops, Bt, H, P, N, R, steps, warmup, seed):
     # the whole sequence of steps (each with its own token's inputs) is one graph
     per_step = replay_ms(torch, [(lambda t=t: step(t)) for t in range(warmup, warmup + steps)])
     ok = bool(torch.isfinite(h).all())
-    return per_step, per_step, ok
+    ev = flushed_ms(torch, lambda: step(warmup)) if flushed else None
+    return per_step, ev, ok
 
 
-def cpu_baseline(batch_items=6):
-    """The fp64 oracle, as it stands, on a bounded sample of the headline
-    prefill workload: `batch_items` sequences x all 32 heads x L 4096."""
+def _cpu_prefill_worker(item):
+    """One sequence (all 32 heads, L 4096) of the headline workload through the
+    oracle, single-threaded; returns its wall time."""
     import dataclasses
-
-    import numpy as np
-
-    from oracle import m3_oracle as orc
-    from synth.inputs import CONFIGS, SEED_BASE, make_inputs
-    s = dataclasses.replace(CONFIGS[1], Bt=batch_items)
-    d = make_inputs(s, SEED_BASE + 1)
-    t0 = time.perf_counter()
-    orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"])
-    dt = time.perf_counter() - t0
-    threads = 1
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([1] + [i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"])
+        threadpoolctl.threadpool_limits(1)
     except Exception:
         pass
-    return dict(value=s.Bt * s.L / dt, unit="tokens/s", cores=1,
-                kind="oracle",
-                sample=f"{s.Bt} sequences x L={s.L} x H={s.H} of the SISO real prefill (P=64, N=128), "
-                       f"fp64 numpy token loop, {dt:.1f} s wall, single process (BLAS pool {threads})",
-                seconds=dt)
+    from oracle import m3_oracle as orc
+    from synth.inputs import CONFIGS, SEED_BASE, make_inputs
+    s = dataclasses.replace(CONFIGS[1], Bt=1)
+    d = make_inputs(s, SEED_BASE + 1 + 1000 * item)
+    t0 = time.perf_counter()
+    orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"])
+    return time.perf_counter() - t0
+
+
+def _cpu_decode_worker(args):
+    """`steps` oracle decode steps of the decode workload on `nb` of its batch
+    items (all 32 heads), single-threaded; returns the wall time of the steps."""
+    part, nb, steps = args
+    import dataclasses
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except Exception:
+        pass
+    import numpy as np
+    from oracle import m3_oracle as orc
+    from synth.inputs import CONFIGS, SEED_BASE, make_inputs
+    s = dataclasses.replace(CONFIGS[4], Bt=nb, L=steps)
+    d = make_inputs(s, SEED_BASE + 4 + 1000 * part, h0=True)
+    th = orc.angles_from_rates(d["dt"], d["omega"])
+    h, R, N, P, H = d["h0"], s.R, s.N, s.P, s.H
+    Bp = np.zeros((nb, H, R, N))
+    xp = np.zeros((nb, H, R, P))
+    phi = np.zeros((nb, H, N // 2))
+    t0 = time.perf_counter()
+    for t in range(steps):
+        r = orc.decode_reference(h, Bp, xp, phi, d["x"][:, t], d["B"][:, t], d["C"][:, t], d["dt"][:, t],
+                                 d["lam"][:, t], d["A"], th[:, t])
+        h, Bp, xp, phi = r["h"], r["Bprev_rot"], r["xprev"], r["phi"]
+    return time.perf_counter() - t0
+
+
+CPU_WORKERS_MAX = 16  # the host-core share of one GPU on the benchmark boxes
+CPU_DECODE_STEPS = 10
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it stands, on a bounded sample of two workloads, in
+    a pool of single-threaded worker processes (one per host core, at most
+    CPU_WORKERS_MAX).  Run before anything touches the GPU: the workers are
+    started from a process that has not initialised it.
+    Prefill: one sequence of the headline workload per worker (all 32 heads,
+    L 4096), tokens/s = all the sample's tokens / wall time.  Decode:
+    CPU_DECODE_STEPS steps of the B=256 decode workload, its 256 batch items
+    shared among the workers, s/step = wall time / steps."""
+    import multiprocessing as mp
+    workers = max(1, min(os.cpu_count() or 1, CPU_WORKERS_MAX))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        per = pool.map(_cpu_prefill_worker, range(workers))
+        wall = time.perf_counter() - t0
+        Bt4 = DECODE_SHAPE[0]
+        parts = [(i, Bt4 // workers + (1 if i < Bt4 % workers else 0), CPU_DECODE_STEPS) for i in range(workers)]
+        t1 = time.perf_counter()
+        dper = pool.map(_cpu_decode_worker, [p for p in parts if p[1] > 0])
+        dwall = time.perf_counter() - t1
+    L = 4096
+    return dict(value=workers * L / wall, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"{workers} sequences x L={L} x H=32 of the SISO real prefill (P=64, N=128), one per "
+                       f"single-threaded worker process, fp64 numpy token loop, {wall:.1f} s wall "
+                       f"(per sequence {min(per):.1f}-{max(per):.1f} s); decode: {CPU_DECODE_STEPS} steps of "
+                       f"B=256 H=32 P=N=64 R=4 over the same workers, {dwall:.1f} s wall",
+                seconds=wall, decode_s_per_step=dwall / CPU_DECODE_STEPS,
+                decode_step_seconds_per_worker=max(dper) / CPU_DECODE_STEPS)
 
 
 def kernel_source_hash():
@@ -411,10 +472,25 @@ def report_trace(prefix):
     print("\n".join(lines))
 
 
-def report_pmc(fetch_prefix, write_prefix):
+def algo_bytes():
+    """Algorithmic bytes per call of every counted unit."""
+    algo = {}
+    for name, shp in prefill_shapes().items():
+        algo["prefill_" + name] = prefill_algo(*shp)[0]
+    for line, wl, mode in VARIANTS:
+        algo["prefill_" + line] = prefill_algo(*prefill_shapes()[wl], omega=mode == "omega", a_tok=mode == "atok")[0]
+    algo["decode"] = decode_algo(*DECODE_SHAPE, True)[0]
+    algo["decode_bt512"] = decode_algo(*DECODE_SHAPE_BIG, True)[0]
+    Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
+    algo["angles"] = 2 * Bt * L * H * (N // 2) * 4 + Bt * H * (N // 2) * 4
+    return algo
+
+
+def report_pmc(groups):
     """HBM bytes per launch of each timed kernel: FETCH_SIZE and WRITE_SIZE (KiB
     per dispatch), each scaled by what the same counter reads for the plain
-    copy of COPY_BYTES in the counter workload."""
+    copy of COPY_BYTES in the counter workload.  `groups`: (group, fetch
+    prefix, write prefix) of each counter run."""
     def per_kernel(prefix, counter):
         acc = {}
         for r in _csv_rows(prefix + "_counter_collection.csv"):
@@ -424,54 +500,100 @@ def report_pmc(fetch_prefix, write_prefix):
             acc.setdefault(key, []).append(float(r["Counter_Value"]) * 1024.0)
         return acc
 
-    fetch = per_kernel(fetch_prefix, "FETCH_SIZE")
-    write = per_kernel(write_prefix, "WRITE_SIZE")
-
     def copy_value(acc):
         cands = [(k, v) for k, v in acc.items() if "neg_kernel" in k[0]]
         k, v = max(cands, key=lambda kv: max(kv[1]))
         return k[0], sum(v) / len(v)
 
-    cname, cf = copy_value(fetch)
-    _, cw = copy_value(write)
-    sf, sw = COPY_BYTES / cf, COPY_BYTES / cw
-    units = {}
-    lines = [f"Scale: a plain elementwise copy (negation) of {COPY_BYTES} B (`{cname}`) reads FETCH_SIZE = {cf:.4g} B and "
-             f"WRITE_SIZE = {cw:.4g} B, so the factors are {sf:.4f} (fetch) and {sw:.4f} (write).", "",
-             "| unit | kernel | dispatches | FETCH_SIZE B | WRITE_SIZE B | scaled HBM B per launch "
-             "| algorithmic B per launch | ratio |", "|---|---|---|---|---|---|---|---|"]
-    algo = {}
-    for name, shp in prefill_shapes().items():
-        algo["prefill_" + name] = prefill_algo(*shp)[0]
-    Bt, H, P, N, R = DECODE_SHAPE
-    algo["decode"] = decode_algo(Bt, H, P, N, R, True)[0]
-    Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
-    algo["angles"] = 2 * Bt * L * H * (N // 2) * 4 + Bt * H * (N // 2) * 4
     def find(acc, k, g):  # the counter file gives the total grid: 2-D launches match by name
         if (k, g) in acc:
             return acc[(k, g)]
         hits = [v for (kk, _), v in acc.items() if kk == k]
         return hits[0] if len(hits) == 1 else None
 
-    for unit, k, g in unit_kernels():
-        fv, wv = find(fetch, k, g), find(write, k, g)
-        if not fv or not wv:
-            continue
-        f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)
-        tot = f_avg * sf + w_avg * sw
-        e = units.setdefault(unit, {"bytes_per_launch": 0, "fetch_bytes": 0, "write_bytes": 0})
-        e["bytes_per_launch"] += round(tot)  # per call of the entry point (all its launches)
-        e["fetch_bytes"] += round(f_avg * sf)
-        e["write_bytes"] += round(w_avg * sw)
-        lines.append(f"| {unit} | `{k}` | {len(fv)} | {f_avg:.4g} | {w_avg:.4g} | {tot:.4g} | {algo[unit]:.4g} "
-                     f"| {tot / algo[unit]:.3f} |")
+    algo = algo_bytes()
+    units, lines, scales = {}, [], {}
+    rows = ["| unit | kernel | dispatches | FETCH_SIZE B | WRITE_SIZE B | scaled HBM B per launch "
+            "| algorithmic B per launch | ratio |", "|---|---|---|---|---|---|---|---|"]
+    for group, fp, wp in groups:
+        fetch = per_kernel(fp, "FETCH_SIZE")
+        write = per_kernel(wp, "WRITE_SIZE")
+        cname, cf = copy_value(fetch)
+        _, cw = copy_value(write)
+        sf, sw = COPY_BYTES / cf, COPY_BYTES / cw
+        scales[group] = (sf, sw)
+        lines.append(f"Group {group}: a plain elementwise copy (negation) of {COPY_BYTES} B reads FETCH_SIZE = "
+                     f"{cf:.4g} B and WRITE_SIZE = {cw:.4g} B, so the factors are {sf:.4f} (fetch) and "
+                     f"{sw:.4f} (write).")
+        uk = unit_kernels() if group == "base" else variant_unit_kernels()
+        for unit, k, g in uk:
+            fv, wv = find(fetch, k, g), find(write, k, g)
+            if not fv or not wv:
+                continue
+            f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)
+            tot = f_avg * sf + w_avg * sw
+            e = units.setdefault(unit, {"bytes_per_launch": 0, "fetch_bytes": 0, "write_bytes": 0})
+            e["bytes_per_launch"] += round(tot)  # per call of the entry point (all its launches)
+            e["fetch_bytes"] += round(f_avg * sf)
+            e["write_bytes"] += round(w_avg * sw)
+            rows.append(f"| {unit} | `{k}` | {len(fv)} | {f_avg:.4g} | {w_avg:.4g} | {tot:.4g} | {algo[unit]:.4g} "
+                        f"| {tot / algo[unit]:.3f} |")
+    lines += [""] + rows
     lines += ["", "Per call of the entry point (a split prefill is several launches):", "",
               "| unit | HBM bytes per call | algorithmic bytes | ratio |", "|---|---|---|---|"]
     for unit, e in units.items():
         lines.append(f"| {unit} | {e['bytes_per_launch']:.4g} | {algo[unit]:.4g} | {e['bytes_per_launch'] / algo[unit]:.3f} |")
     lines += ["", "traffic-json: " + json.dumps({"source_hash": kernel_source_hash(), "units": units,
-                                                 "fetch_scale": sf, "write_scale": sw})]
+                                                 "scales": scales})]
     print("\n".join(lines))
+
+
+# Memory-pipe counters of the prefill kernels (one rocprofv3 pass each, within
+# the per-block limits): what the vector memory path is doing per cycle.
+COUNTER_PASSES = {
+    "ta": ["TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "GRBM_GUI_ACTIVE"],
+    "tcp": ["TCP_PENDING_STALL_CYCLES_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum",
+            "TCP_GATE_EN1_sum", "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_BUSY_CU_CYCLES",
+            "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE"],
+}
+
+
+def report_counters(prefixes):
+    """Per-dispatch averages of the memory-pipe counters of every timed kernel,
+    and derived ratios: TA busy share, L2 read latency per request (cycles),
+    share of CU cycles the vector L1 holds pending requests, LDS bank-conflict
+    cycles per LDS-active cycle."""
+    vals = {}
+    for prefix in prefixes:
+        for r in _csv_rows(prefix + "_counter_collection.csv"):
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    lines = ["| unit | kernel | counter | average per dispatch |", "|---|---|---|---|"]
+    derived = ["| unit | TA busy (% of GPU cycles, avg over TA) | TA address stalled by TC (cycles / CU / GPU cycle) "
+               "| L2 read latency (cycles / request) | vector-L1 pending stall (cycles / CU / GPU cycle) "
+               "| LDS bank-conflict / LDS-active cycles |", "|---|---|---|---|---|---|"]
+    seen = set()
+    for unit, k, g in unit_kernels() + variant_unit_kernels():
+        a = avg.get((k, g)) or next((v for (kk, _), v in avg.items() if kk == k), None)
+        if a is None or (k, g) in seen:
+            continue
+        seen.add((k, g))
+        for c in sorted(a):
+            lines.append(f"| {unit} | `{k}` | {c} | {a[c]:.4g} |")
+        gui = a.get("GRBM_GUI_ACTIVE", float("nan")) / XCDS
+        cus = SIMDS // 4
+
+        def ratio(n, d):
+            return f"{n / d:.3g}" if n == n and d and d == d else "-"
+        derived.append(
+            f"| {unit} | {ratio(100 * a.get('TA_BUSY_avr', float('nan')), gui)} "
+            f"| {ratio(a.get('TA_ADDR_STALLED_BY_TC_CYCLES_sum', float('nan')), gui * cus)} "
+            f"| {ratio(a.get('TCP_TCC_READ_REQ_LATENCY_sum', float('nan')), a.get('TCP_TCC_READ_REQ_sum', 0))} "
+            f"| {ratio(a.get('TCP_PENDING_STALL_CYCLES_sum', float('nan')), gui * cus)} "
+            f"| {ratio(a.get('SQ_LDS_BANK_CONFLICT', float('nan')), a.get('SQ_LDS_IDX_ACTIVE', 0))} |")
+    print("\n".join(derived + [""] + lines))
 
 
 SIMDS = 1024  # 256 CUs x 4 SIMDs
@@ -503,7 +625,7 @@ def report_mfma(prefix):
     print("\n".join(lines))
 
 
-def pmc_workload(torch, ops):
+def pmc_workload(torch, ops, group):
     """Untimed launches for counter collection (see the module docstring)."""
     # same-dtype copy_ becomes a DMA transfer, so the plain copy kernel is an
     # elementwise negation: it reads COPY_BYTES and writes COPY_BYTES
@@ -514,15 +636,23 @@ def pmc_workload(torch, ops):
     torch.cuda.synchronize()
     del a, b
     torch.cuda.empty_cache()
-    for i, (name, shp) in enumerate(prefill_shapes().items()):
+    if group == "base":
+        runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
+    else:
+        runs = [(line, prefill_shapes()[wl], mode) for line, wl, mode in VARIANTS]
+    for i, (name, shp, mode) in enumerate(runs):
+        print(f"# counter workload: prefill {name}", file=sys.stderr, flush=True)
         inp = gen_prefill(torch, *shp, seed=20260100 + i)
-        time_prefill(torch, ops, inp, 2, 0)
+        time_prefill(torch, ops, inp, 2, 0, mode, flushed=False)
         del inp
         torch.cuda.empty_cache()
-    Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
-    time_angles(torch, ops, Bt, L, H, N // 2, 2, 0, seed=20260110)
-    Bt, H, P, N, R = DECODE_SHAPE
-    time_decode(torch, ops, Bt, H, P, N, R, 3, 1, seed=20260104)
+    if group == "base":
+        Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
+        time_angles(torch, ops, Bt, L, H, N // 2, 2, 0, seed=20260110)
+        for shp in (DECODE_SHAPE, DECODE_SHAPE_BIG):
+            print(f"# counter workload: decode {shp}", file=sys.stderr, flush=True)
+            time_decode(torch, ops, *shp, 3, 1, seed=20260104, flushed=False)
+            torch.cuda.empty_cache()
     torch.cuda.synchronize()
     print("# counter workload done", file=sys.stderr, flush=True)
 
@@ -534,24 +664,40 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "pmc"), default="all")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "headline", "pmc"), default="all")
+    ap.add_argument("--group", choices=("base", "variants"), default="base")
     ap.add_argument("--report-trace", metavar="PREFIX")
-    ap.add_argument("--report-pmc", nargs=2, metavar=("FETCH_PREFIX", "WRITE_PREFIX"))
+    ap.add_argument("--report-pmc", nargs="+", metavar="GROUP FETCH_PREFIX WRITE_PREFIX")
     ap.add_argument("--report-mfma", metavar="PREFIX")
+    ap.add_argument("--report-counters", nargs="+", metavar="PREFIX")
     args = ap.parse_args()
     if args.report_trace:
         report_trace(args.report_trace)
         return
     if args.report_pmc:
-        report_pmc(*args.report_pmc)
+        a = args.report_pmc
+        if len(a) % 3:
+            ap.error("--report-pmc takes GROUP FETCH_PREFIX WRITE_PREFIX triples")
+        report_pmc([tuple(a[i:i + 3]) for i in range(0, len(a), 3)])
         return
     if args.report_mfma:
         report_mfma(args.report_mfma)
+        return
+    if args.report_counters:
+        report_counters(args.report_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is "
               "not built: (batch, head) units shard with no exchange, see the design notes.", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baseline's worker processes start before anything touches the GPU
+    cpu = None
+    if args.only == "all" and not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+        print(f"# cpu baseline: {cpu['value']:.0f} tokens/s on {cpu['cores']} cores, "
+              f"decode {cpu['decode_s_per_step']:.3f} s/step", file=sys.stderr, flush=True)
 
     import torch
 
@@ -561,21 +707,20 @@ def main():
         sys.exit(1)
 
     if args.only == "pmc":
-        pmc_workload(torch, ops)
+        pmc_workload(torch, ops, args.group)
         return
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded, device-generated, resident in HBM)"}
     results = {}
-    if args.only in ("all", "prefill"):
+    if args.only in ("all", "prefill", "headline"):
+        runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
         # the RoPE workloads also with their angles given as rates (theta = dt * omega on
         # chip), and the headline workload with A given per token
-        runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
-        runs += [(name + "_omega", shp, "omega") for name, shp in prefill_shapes().items() if shp[-1]]
-        runs += [("siso_real_atok", prefill_shapes()["siso_real"], "atok")]
-        # and the SISO workloads with x, B, C, y head-major ([Bt, H, L, R, .])
-        runs += [(name + "_headmajor", prefill_shapes()[name], "hm") for name in ("siso_real", "siso_rope")]
+        runs += [(line, prefill_shapes()[wl], mode) for line, wl, mode in VARIANTS]
+        if args.only == "headline":
+            runs = runs[:1]
         for i, (name, shp, mode) in enumerate(runs):
             Bt, L, H, P, N, R, rope = shp
             inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260100 + i)
@@ -585,8 +730,6 @@ def main():
             angles = "RoPE, angles from rates" if mode == "omega" else ("RoPE" if rope else "real")
             if mode == "atok":
                 angles += ", A per token"
-            if mode == "hm":
-                angles += ", head-major x/B/C/y"
             res = dict(workload=f"prefill {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
                                 f"{angles} bf16 chunk {Q_ROWS // R}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, kernel_ms=launch_ms,
@@ -614,17 +757,24 @@ def main():
         print(f"# {results['angles']['workload']}: {ms * 1e3:.1f} us, {results['angles']['gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
     if args.only in ("all", "decode"):
-        Bt, H, P, N, R = DECODE_SHAPE
-        per_step, kern, ok = time_decode(torch, ops, Bt, H, P, N, R, args.decode_steps, 20, seed=20260104)
-        byts, flops = decode_algo(Bt, H, P, N, R, True)
-        results["decode"] = dict(
-            workload=f"decode MIMO RoPE: Bt={Bt} H={H} P={P} N={N} R={R} bf16 inputs, fp32 state, "
-                     f"{args.decode_steps} sequential steps",
-            us_per_step=per_step * 1e3, kernel_us=kern * 1e3, gbs=byts / (kern * 1e-3) / 1e9,
-            hbm_frac=byts / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS, bytes=byts, flops=flops, finite=ok,
-            traffic=traffic_for("decode"))
-        print(f"# decode: {per_step * 1e3:.1f} us/step, {results['decode']['gbs']:.0f} GB/s "
-              f"({100 * results['decode']['hbm_frac']:.1f}% HBM)", file=sys.stderr, flush=True)
+        for key, shp, nsteps in (("decode", DECODE_SHAPE, args.decode_steps),
+                                 ("decode_bt512", DECODE_SHAPE_BIG, min(DECODE_BIG_STEPS, args.decode_steps))):
+            Bt, H, P, N, R = shp
+            per_step, ev, ok = time_decode(torch, ops, Bt, H, P, N, R, nsteps, 20, seed=20260104)
+            byts, flops = decode_algo(Bt, H, P, N, R, True)
+            state_mb = Bt * H * N * P * 4 / 1e6
+            results[key] = dict(
+                workload=f"decode MIMO RoPE: Bt={Bt} H={H} P={P} N={N} R={R} bf16 inputs, fp32 state "
+                         f"({state_mb:.0f} MB), {nsteps} sequential steps",
+                us_per_step=per_step * 1e3, kernel_us=per_step * 1e3, gbs=byts / (per_step * 1e-3) / 1e9,
+                hbm_frac=byts / (per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, bytes=byts, flops=flops, finite=ok,
+                us_after_cache_eviction=ev * 1e3,
+                gbs_after_cache_eviction=byts / (ev * 1e-3) / 1e9,
+                traffic=traffic_for(key))
+            print(f"# {key}: {per_step * 1e3:.1f} us/step, {results[key]['gbs']:.0f} GB/s "
+                  f"({100 * results[key]['hbm_frac']:.1f}% HBM); {ev * 1e3:.1f} us per single step after an "
+                  f"Infinity Cache eviction", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     head = results.get("siso_real")
     if head is not None:
@@ -650,17 +800,24 @@ def main():
     if "decode" in results:
         dres = results["decode"]
         out["decode"] = dres
-        out["decode_roofline"] = {"bound": "hbm", "achieved": dres["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": dres["hbm_frac"], "traffic": traffic_for("decode"),
-                                  "kernel": decode_kernel_name(*DECODE_SHAPE)}
-    for k in ("siso_rope", "mimo_rope", "siso_rope_omega", "mimo_rope_omega", "siso_real_atok",
-              "siso_real_headmajor", "siso_rope_headmajor"):
+        # the rate that the state streams from HBM: the slower of the graph-replayed
+        # steps (state possibly resident in the Infinity Cache between steps) and
+        # single steps after an eviction
+        hbm_gbs = min(dres["gbs"], dres["gbs_after_cache_eviction"])
+        out["decode_roofline"] = {"bound": "hbm", "achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": hbm_gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode"),
+                                  "kernel": decode_kernel_name(*DECODE_SHAPE),
+                                  "achieved_graph_replay": dres["gbs"],
+                                  "achieved_after_cache_eviction": dres["gbs_after_cache_eviction"]}
+    if "decode_bt512" in results:
+        out["decode_bt512"] = results["decode_bt512"]
+    for k in ["siso_rope", "mimo_rope"] + [line for line, _, _ in VARIANTS]:
         if k in results:
             out["prefill_" + k] = results[k]
     if "angles" in results:
         out["angles"] = results["angles"]
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -33,7 +33,8 @@ Readings where the pages are silent (each listed in the design notes):
 
 Parity: every function here is pinned by the not-gpu tests in
 tests/test_oracle_pins.py (closed forms, special cases, brute force, an
-independent complex-arithmetic recurrence, order of accuracy).
+independent complex-arithmetic recurrence, order of accuracy, hand-computed
+values of the comparator and of the normalisation).
 """
 from __future__ import annotations
 
@@ -61,6 +62,71 @@ def rotate_pairs(v: np.ndarray, phi: np.ndarray) -> np.ndarray:
     out[..., 0::2] = c * v0 + s * v1
     out[..., 1::2] = -s * v0 + c * v1
     return out
+
+
+def angles_from_rates(dt, omega):
+    """Per-token rotation angles from rates: theta[..., h, j] = Delta[..., h] *
+    omega[..., j].
+
+    [PB] sec. "Mamba-3": the rotation angle depends on the data because the
+    step Delta is selective, i.e. the angle of a token is its step times a
+    rate.  The rates omega are given per token and state pair and shared by
+    the heads (the workloads draw them that way).  dt [..., H]; omega [..., J]
+    -> theta [..., H, J] in float64 (the product of two fp32 values is exact).
+    """
+    dt = _f64(dt)
+    omega = _f64(omega)
+    return dt[..., :, None] * omega[..., None, :]
+
+
+def softplus(z):
+    """softplus(z) = log(1 + exp(z)), evaluated without overflow.  The positive
+    step Delta is the softplus of its raw value (the workloads draw Delta that
+    way)."""
+    return np.logaddexp(0.0, _f64(z))
+
+
+def rms_norm(v, weight=None, eps=0.0):
+    """RMS normalisation over the last axis: v / sqrt(mean(v^2) + eps), times an
+    optional per-element gain ``weight`` (broadcast over the leading axes).
+
+    [CH] sec. "Architecture and normalisation": B and C are RMS-normalised, by
+    analogy with QK normalisation in Transformers.  For B, C of shape
+    [..., R, N] each rank column (an N-vector) is normalised on its own.
+    """
+    v = _f64(v)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    out = v / np.sqrt(ms + eps)
+    if weight is not None:
+        out = out * _f64(weight)
+    return out
+
+
+def prologue(B, C, dt, *, bc_norm=False, B_norm_w=None, C_norm_w=None, eps=0.0,
+             B_bias=None, C_bias=None, dt_softplus=False, dt_bias=None):
+    """The steps just before the SSM core, applied to raw projections.
+
+    [CH] sec. "Architecture and normalisation": RMS normalisation of B and C
+    (``rms_norm`` per (token, head, rank) over N, gains ``B_norm_w``,
+    ``C_norm_w`` [N]), then learnable head-specific biases added after the
+    normalisation (``B_bias``, ``C_bias`` [H, R, N]); [CA] "Normalizzazioni"
+    and "Addio convoluzione corta" (biases on B and C after BCNorm).  The
+    step: Delta = softplus(dt + dt_bias[h]) when ``dt_softplus`` (dt_bias [H]
+    or None), else Delta = dt as given.
+    B, C [..., H, R, N] (token axes first); dt [..., H].  Returns float64
+    (B, C, Delta) ready for :func:`ssm_reference`.
+    """
+    B, C, dt = _f64(B), _f64(C), _f64(dt)
+    if bc_norm:
+        B = rms_norm(B, B_norm_w, eps)
+        C = rms_norm(C, C_norm_w, eps)
+    if B_bias is not None:
+        B = B + _f64(B_bias)
+    if C_bias is not None:
+        C = C + _f64(C_bias)
+    if dt_softplus:
+        dt = softplus(dt if dt_bias is None else dt + _f64(dt_bias))
+    return B, C, dt
 
 
 def coefficients(dt, lam, A):
@@ -101,16 +167,20 @@ def ssm_step(h, Bp, xp, phi, x_t, B_t, C_t, dt_t, lam_t, A, theta_t):
 
 
 def ssm_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
-                  xprev=None, phi0=None):
+                  xprev=None, phi0=None, omega=None):
     """Sequential fp64 oracle of the whole sequence (prefill semantics).
 
     x [Bt,L,H,R,P]; B, C [Bt,L,H,R,N]; dt, lam [Bt,L,H]; A [H] or per token
-    [Bt,L,H]; theta [Bt,L,H,N/2] or None; carry-in (all optional, zeros if None):
+    [Bt,L,H]; theta [Bt,L,H,N/2] or None, or instead omega [Bt,L,N/2] (rates:
+    theta = :func:`angles_from_rates`); carry-in (all optional, zeros if None):
     h0 [Bt,H,N,P], Bprev_rot [Bt,H,R,N], xprev [Bt,H,R,P], phi0 [Bt,H,N/2].
     Returns dict(y [Bt,L,H,R,P], h [Bt,H,N,P], Bprev_rot [Bt,H,R,N],
     xprev [Bt,H,R,P], phi [Bt,H,N/2] or None), all float64.
     """
     x, B, C, dt, lam, A = map(_f64, (x, B, C, dt, lam, A))
+    if omega is not None:
+        assert theta is None, "give theta or omega, not both"
+        theta = angles_from_rates(dt, omega)
     theta = _f64(theta)
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -129,10 +199,14 @@ def ssm_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
     return dict(y=y, h=h, Bprev_rot=Bp, xprev=xp, phi=phi)
 
 
-def decode_reference(h, Bprev_rot, xprev, phi, x, B, C, dt, lam, A, theta=None):
+def decode_reference(h, Bprev_rot, xprev, phi, x, B, C, dt, lam, A, theta=None, omega=None):
     """One decode step against a resident state: the same token update as the
     prefill loop.  Shapes as in :func:`ssm_step` (no time axis); A is [H] or
-    one per (batch, head) [Bt,H].  Returns dict(y, h, Bprev_rot, xprev, phi)."""
+    one per (batch, head) [Bt,H]; omega [Bt,N/2] (rates) instead of theta.
+    Returns dict(y, h, Bprev_rot, xprev, phi)."""
+    if omega is not None:
+        assert theta is None, "give theta or omega, not both"
+        theta = angles_from_rates(dt, omega)
     y, h2, Bp, xp, ph = ssm_step(_f64(h), _f64(Bprev_rot), _f64(xprev), _f64(phi),
                                  _f64(x), _f64(B), _f64(C), _f64(dt), _f64(lam),
                                  _f64(A), _f64(theta))
@@ -151,7 +225,7 @@ def rope_angles_cumsum(theta, phi0=None):
 
 
 def dual_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
-                   xprev=None, phi0=None):
+                   xprev=None, phi0=None, omega=None):
     """Materialised masked-attention (SSD dual) form, O(L^2) per (b, h).
 
     [PB] sec. "State Space Duality": with a scalar-times-identity transition the
@@ -166,6 +240,8 @@ def dual_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
     Returns y [Bt,L,H,R,P] (float64).
     """
     x, B, C, dt, lam, A = map(_f64, (x, B, C, dt, lam, A))
+    if omega is not None:
+        theta = angles_from_rates(dt, omega)
     Bt, L, H, R, P = x.shape
     N = B.shape[-1]
     if theta is not None:
@@ -206,7 +282,9 @@ def dual_reference(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None,
 
 
 def rel_l2(a, b) -> float:
-    """Relative L2 error ||a - b|| / ||b|| in float64 (parity metric)."""
+    """Relative L2 error ||a - b|| / ||b|| in float64 (the parity metric); the
+    plain ||a - b|| when b is all zeros.  Shapes must match exactly."""
+    assert np.shape(a) == np.shape(b), (np.shape(a), np.shape(b))
     a = np.asarray(a, dtype=F64)
     b = np.asarray(b, dtype=F64)
     den = np.linalg.norm(b.ravel())

@@ -63,5 +63,58 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(OBJ, "hostsan")
+SAN_LIB = os.path.join(SAN_DIR, "libm3ssm_hostsan.so")
+# host-side sanitizers only: each flag goes to the host compilation of api.hip
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that a host process must preload to
+    load the sanitized library."""
+    llvm = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm")
+    r = subprocess.run([os.path.join(llvm, "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return path
+
+
+def build_hostsan(verbose: bool = False) -> str:
+    """libm3ssm_hostsan.so: the host-side C-ABI layer (api.hip: argument
+    validation and dispatch) built with AddressSanitizer and UBSan, linked
+    with the regular kernel objects of the last build().  For host-only
+    tests of the validation paths (no kernel is launched)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ, os.path.splitext(x)[0] + ".o") for x in SOURCES if x != "api.hip"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: missing {missing}")
+    api_o = os.path.join(SAN_DIR, "api_hostsan.o")
+    cmd = [hipcc(), *cflags(), *SAN_FLAGS, "-c", os.path.join(CSRC, "api.hip"), "-o", api_o]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc (host sanitizers) failed:\n" + r.stdout + r.stderr)
+    # a plain host link: the objects already embed their device code
+    llvm = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm")
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    tmp = SAN_LIB + ".tmp"
+    cmd = [os.path.join(llvm, "bin", "clang++"), "-shared", "-fPIC", "-shared-libsan", "-fsanitize=address,undefined",
+           "-o", tmp, api_o, *objs, "-L" + rocm_lib, "-Wl,-rpath," + rocm_lib, "-lamdhip64"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("host-sanitizer link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--hostsan" in sys.argv:
+        print(build_hostsan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

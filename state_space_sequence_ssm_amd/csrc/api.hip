@@ -3,6 +3,8 @@
 // rejected without a GPU (the contract of include/m3ssm.h).
 #include <stdint.h>
 
+#include <atomic>
+
 #include "m3ssm.h"
 #include "m3ssm_internal.hpp"
 
@@ -19,23 +21,24 @@ bool al4(const void* p) { return p == nullptr || aligned(p, 4); }
 int hip_status(hipError_t e) { return e == hipSuccess ? M3_OK : M3_ERR_HIP; }
 
 // Compute units of the current device (cached per device; 256, the MI355X
-// count, when no device can be queried).
+// count, when no device can be queried).  The cache entries are atomics:
+// concurrent first calls store the same value.
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];  // zero-initialised (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return 256;
   }
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) {
       (void)hipGetLastError();
       v = 256;
     }
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 // Sequence split of the bf16 prefill: with fewer (batch, head) units than
@@ -93,7 +96,12 @@ size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args) {
   return s.on ? s.bytes : 0;
 }
 
-int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of a prefill call that depends on the arguments alone.
+int check_prefill(const m3_prefill_args* a) {
   if (a == nullptr) return M3_ERR_INVALID_ARG;
   if (a->Bt < 1 || a->L < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
   if (a->in_dtype != M3_F32 && a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
@@ -126,7 +134,13 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, rope)
                           : m3::prefill_lds_bytes_f32(a->N, a->P, rope);
   if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
+  return M3_OK;
+}
 
+// Launches of a validated prefill call; `ws` is the workspace (or null).
+int run_prefill(const m3_prefill_args* a, void* ws_ptr, size_t ws_bytes, void* stream) {
+  const bool rope = a->theta != nullptr || a->omega != nullptr;
+  const bool bf16 = a->in_dtype == M3_BF16;
   m3::PrefillParams p{};
   p.Bt = a->Bt; p.L = a->L; p.H = a->H; p.P = a->P; p.N = a->N; p.R = a->R;
   int lg = 0;
@@ -147,9 +161,9 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   if (!bf16) return hip_status(m3::launch_prefill_f32(p, st));
 
   const SplitPlan sp = split_plan(a);
-  if (!sp.on || a->workspace == nullptr) return hip_status(m3::launch_prefill_bf16(p, false, st));
-  if (a->workspace_bytes < sp.bytes || !aligned(a->workspace, 256)) return M3_ERR_INVALID_ARG;
-  unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+  if (!sp.on || ws_ptr == nullptr) return hip_status(m3::launch_prefill_bf16(p, false, st));
+  if (ws_bytes < sp.bytes || !aligned(ws_ptr, 256)) return M3_ERR_INVALID_ARG;
+  unsigned char* ws = static_cast<unsigned char*>(ws_ptr);
   const size_t u = size_t(a->Bt) * a->H;
   float* hMid = reinterpret_cast<float*>(ws + sp.oH);
   float* bMid = reinterpret_cast<float*>(ws + sp.oB);
@@ -202,6 +216,16 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   pb.xprev_mid = xCarry;
   pb.phi_mid = phiCarry;
   return hip_status(m3::launch_prefill_bf16(pb, false, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
+  const int rc = check_prefill(a);
+  if (rc != M3_OK) return rc;
+  return run_prefill(a, a->workspace, a->workspace_bytes, stream);
 }
 
 int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {

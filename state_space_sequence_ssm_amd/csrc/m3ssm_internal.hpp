@@ -4,7 +4,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace m3 {
+
+// A kernel that uses more than 64 KB of dynamic LDS must be cleared for it,
+// per device, before its first launch there.  `cleared` (one per kernel) has
+// bit d set once device d is done; the attribute is always set to the same
+// value (the most the kernel ever asks for), so concurrent first calls from
+// several host threads at worst repeat an idempotent call.
+inline hipError_t allow_lds(const void* fn, size_t max_bytes, std::atomic<uint64_t>& cleared) {
+  if (max_bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit != 0 && (cleared.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(max_bytes));
+  if (e == hipSuccess && bit != 0) cleared.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 struct DecodeParams {
   int Bt, H, P, N, R;

@@ -1,4 +1,5 @@
-// Fused chunked prefill of the Mamba-3 SSM core on gfx950 (CDNA4).
+// Fused chunked prefill of the Mamba-3 SSM core on gfx950 (CDNA4), fp32
+// inputs (x, B, C and y in float32; the bf16 path is prefill_pc_impl.hpp).
 //
 // Operation: the exponential-trapezoidal recurrence ("Znakomstvo s Mamba-3"
 // (chernovdev.ru), sec. 1, displayed recurrence) with cumulative RoPE on B
@@ -26,12 +27,11 @@
 //     while the current chunk computes (software prefetch);
 //   * the Delta/lambda scan is one wave64 inclusive scan; the angle scan is a
 //     segmented wave scan per rotation pair with a carry across chunks;
-//   * B and C are rotated in registers (fp32), rounded to bf16 and staged in
-//     LDS: C and B row-major, (w_j B_j)^T and X^T transposed, padded rows;
-//   * G^T = B C^T (16x16x32 bf16 MFMA, fp32 accumulate), masked in registers
-//     and fed straight back as the B operand of Y^T += X^T S^T (no LDS trip);
+//   * B and C are rotated in registers and staged in fp32 LDS tiles: C and B
+//     row-major, (w_j B_j)^T and X^T transposed, padded rows;
+//   * G^T = B C^T on the 16x16x4 fp32 MFMA, masked in registers, each of its
+//     four rows fed back as a k step of Y^T += X^T S^T (no LDS trip);
 //     Y^T += diag(exp Lam) H'^T C^T; H' = exp(Lam_e) H' + (wB)^T X.
-// fp32 inputs use the 16x16x4 fp32 MFMA with fp32 LDS tiles instead.
 #pragma once
 #include <type_traits>
 
@@ -44,24 +44,8 @@ constexpr int kRows = 64;         // (token, rank) rows per chunk tile
 constexpr int kThreads = 512;     // 8 waves
 constexpr int kWaves = kThreads / 64;
 
-template <bool BF>
-struct Mma;
-
-template <>
-struct Mma<true> {
-  using E = uint16_t;  // LDS element (bf16 bits)
-  using Frag = bf16x8;
-  static constexpr int K = 32;
-  __device__ static __forceinline__ Frag ld(const E* row, int kb, int g) {
-    return *reinterpret_cast<const bf16x8*>(row + kb * 32 + 8 * g);
-  }
-  __device__ static __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mma<false> {
+// 16x16x4 fp32 MFMA: operand k index 4 kb + g of row `row`.
+struct MmaF32 {
   using E = float;
   using Frag = float;
   static constexpr int K = 4;
@@ -71,11 +55,7 @@ struct Mma<false> {
   }
 };
 
-// Write `n` (4 or 8) fp32 values as one vector of LDS elements.
-__device__ __forceinline__ void lds_put4(uint16_t* p, float a, float b, float c, float d) {
-  u32x2 v = {pack_bf16x2(a, b), pack_bf16x2(c, d)};
-  *reinterpret_cast<u32x2*>(p) = v;
-}
+// Write 4 fp32 values as one 16-byte LDS store.
 __device__ __forceinline__ void lds_put4(float* p, float a, float b, float c, float d) {
   f32x4 v = {a, b, c, d};
   *reinterpret_cast<f32x4*>(p) = v;
@@ -83,11 +63,11 @@ __device__ __forceinline__ void lds_put4(float* p, float a, float b, float c, fl
 
 template <typename T, int N, int P>
 struct Layout {
-  static constexpr bool BF = std::is_same<T, bf16_t>::value;
-  using E = typename Mma<BF>::E;
+  static_assert(std::is_same<T, float>::value, "fp32 inputs only");
+  using E = MmaF32::E;
   static constexpr int EB = sizeof(E);
   static constexpr int VE = 16 / sizeof(T);   // input elements per 16-byte load
-  static constexpr int NK = N < Mma<BF>::K ? Mma<BF>::K : N;  // contraction length over n (zero padded)
+  static constexpr int NK = N < MmaF32::K ? MmaF32::K : N;  // contraction length over n (zero padded)
   static constexpr int PN = NK + 16 / EB;     // pitch of rows of length N (padded to NK)
   static constexpr int PR = kRows + 16 / EB;  // pitch of rows of length kRows
   static constexpr int NPT = P / 16;          // p tiles
@@ -121,7 +101,7 @@ struct Layout {
 template <typename T, int N, int P>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   using Lt = Layout<T, N, P>;
-  using M = Mma<Lt::BF>;
+  using M = MmaF32;
   using E = typename Lt::E;
   constexpr int VE = Lt::VE, PN = Lt::PN, PR = Lt::PR, NPT = Lt::NPT, NK = Lt::NK;
   constexpr int K = M::K;
@@ -293,18 +273,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         const int c0 = cb * VE;
         float v[4][VE];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if constexpr (Lt::BF) {
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[k][2 * q] = __uint_as_float(raw[s][k][q] << 16);
-              v[k][2 * q + 1] = __uint_as_float(raw[s][k][q] & 0xffff0000u);
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[k][q] = __uint_as_float(raw[s][k][q]);
-          }
-        }
+          for (int q = 0; q < 4; ++q) v[k][q] = __uint_as_float(raw[s][k][q]);
         if (kind < 2 && rope) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -463,42 +434,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       return acc;
     };
 
-    if constexpr (Lt::BF) {
 #pragma unroll
-      for (int m = 0; m < kRows / 32; ++m) {
-        if (2 * m <= it) {
-          const f32x4 s0 = gram_masked(2 * m);
-          const f32x4 s1 = (2 * m + 1 <= it) ? gram_masked(2 * m + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
-          u32x4 bw = {pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]),
-                      pack_bf16x2(s1[0], s1[1]), pack_bf16x2(s1[2], s1[3])};
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
+    for (int jt = 0; jt < kRows / 16; ++jt) {
+      if (jt <= it) {
+        const f32x4 sm = gram_masked(jt);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
           for (int k = 0; k < Lt::YT; ++k) {
             const int pt = ph + 2 * k;
             if (pt < NPT) {
-              const E* xr = sXT + (16 * pt + l16) * PR + 32 * m + 4 * g;
-              const u32x2 lo = *reinterpret_cast<const u32x2*>(xr);
-              const u32x2 hi = *reinterpret_cast<const u32x2*>(xr + 16);
-              u32x4 aw = {lo[0], lo[1], hi[0], hi[1]};
-              yacc[k] = M::mma(__builtin_bit_cast(bf16x8, aw), bop, yacc[k]);
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int jt = 0; jt < kRows / 16; ++jt) {
-        if (jt <= it) {
-          const f32x4 sm = gram_masked(jt);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-            for (int k = 0; k < Lt::YT; ++k) {
-              const int pt = ph + 2 * k;
-              if (pt < NPT) {
-                const float a = sXT[(16 * pt + l16) * PR + 16 * jt + 4 * g + jj];
-                yacc[k] = M::mma(a, sm[jj], yacc[k]);
-              }
+              const float a = sXT[(16 * pt + l16) * PR + 16 * jt + 4 * g + jj];
+              yacc[k] = M::mma(a, sm[jj], yacc[k]);
             }
           }
         }
@@ -580,13 +527,13 @@ static hipError_t launch_prefill_t(const PrefillParams& p, hipStream_t s) {
   using Lt = Layout<T, N, P>;
   const bool rope = p.theta != nullptr || p.omega != nullptr;
   const size_t lds = rope ? Lt::kBytesRope : Lt::kBytesReal;
-  static size_t attr_bytes = 64 * 1024;  // dynamic LDS the kernel is cleared for
-  if (lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, N, P>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_bytes = lds;
-  }
+  // cleared once per device for the larger of the two layouts that fit a CU
+  constexpr size_t kMax = 160 * 1024;
+  constexpr size_t kAllow = Lt::kBytesRope <= kMax && Lt::kBytesRope > Lt::kBytesReal ? Lt::kBytesRope
+                                                                                      : Lt::kBytesReal;
+  static std::atomic<uint64_t> cleared{0};
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&prefill_kernel<T, N, P>), kAllow, cleared);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_kernel<T, N, P>), dim3(p.Bt * p.H), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }

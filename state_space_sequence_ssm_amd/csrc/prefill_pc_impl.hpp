@@ -26,7 +26,8 @@
 //     resources that span the segment of one batch item (the range check
 //     zero-fills the ragged tail, so every wave issues the same loads every
 //     chunk and the wait counters stay static).  B and C are rotated pairwise
-//     in fp32 (hardware sin/cos of the cumulative angle), rounded to bf16 and
+//     in fp32 (hardware sin/cos of the cumulative angle, reduced modulo 2 pi
+//     by the angle scan), rounded to bf16 and
 //     stored row-major with X, in tiles whose 8-byte units are XOR-swizzled by
 //     row.  Wave 0 scans the decays of chunk k+2 (log2 units, one DPP wave
 //     scan); the raw angles of chunk k+2 go to the angle table.  Every wave
@@ -500,15 +501,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = seg_scan<Q>(v[e]);
           if (q4 < NG) {
+            // reduced modulo 2 pi: the hardware sin/cos that rotate B and C
+            // are accurate only for small arguments, and the running sum of a
+            // chunk can reach any size
             const f32x4 cin = *reinterpret_cast<const f32x4*>(phiC + 4 * q4);
             const f32x4 a = v + cin;
-            *reinterpret_cast<f32x4*>(tab + tl * PH + 4 * q4) = a;
-            if (tl == Q - 1) {
-              f32x4 w;
+            f32x4 w;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) w[e] = wrap_angle(a[e]);
-              *reinterpret_cast<f32x4*>(phiC + 4 * q4) = w;
-            }
+            for (int e = 0; e < 4; ++e) w[e] = wrap_angle(a[e]);
+            *reinterpret_cast<f32x4*>(tab + tl * PH + 4 * q4) = w;
+            if (tl == Q - 1) *reinterpret_cast<f32x4*>(phiC + 4 * q4) = w;
           }
         }
       }

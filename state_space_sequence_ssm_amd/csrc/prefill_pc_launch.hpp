@@ -11,13 +11,9 @@ template <int N, int P, int LGR, bool ROPE, bool SO>
 hipError_t launch(const PrefillParams& p, hipStream_t s) {
   using Lt = PcLayout<N, P>;
   const size_t lds = ROPE ? Lt::kBytesRope : Lt::kBytesReal;
-  static size_t attr_bytes = 64 * 1024;  // dynamic LDS this kernel has been cleared for
-  if (lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_pc_kernel<N, P, LGR, ROPE, SO>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_bytes = lds;
-  }
+  static std::atomic<uint64_t> cleared{0};  // devices this kernel is cleared on
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&prefill_pc_kernel<N, P, LGR, ROPE, SO>), lds, cleared);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_pc_kernel<N, P, LGR, ROPE, SO>), dim3(p.Bt * p.H * p.nseg), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }

@@ -6,10 +6,13 @@ of the method's arithmetic (no decay, no trapezoid weights, no rotation, no
 recurrence), so neither side can borrow the other's maths from here.
 
 Distributions (the workloads described for the Mamba-3 core):
-  x ~ N(0,1);  B, C ~ N(0,1)/sqrt(N);  Delta = softplus(z - 4), z ~ N(0,1);
+  x ~ N(0,1);  B, C ~ N(0,1)/sqrt(N);  Delta = softplus(z - 4), z ~ N(0,1)
+  (the raw z - 4 is returned too, for callers that form Delta themselves);
   lambda = sigmoid(z'), z' ~ N(0,1);  A = -exp(U(0, ln 16)) one scalar per
-  head;  theta = Delta * omega with omega ~ N(0,1) per token and state pair,
-  shared by all heads;  decode state h0 ~ N(0, 0.1^2).
+  head;  rotation rates omega ~ N(0,1) per token and state pair, shared by
+  all heads (the angles theta = Delta * omega are the method's arithmetic and
+  are formed by the oracle or on the device, not here);  decode state
+  h0 ~ N(0, 0.1^2).
 Draw order is fixed: x, B, C, z_Delta, z_lambda, u_A, omega, h0, then carry.
 bf16 tensors are drawn in fp32 and rounded to nearest-even, so both sides
 receive identical bits.
@@ -72,13 +75,14 @@ def _normal(rng, shape, scale=1.0):
 
 
 def make_inputs(s: Shape, seed: int, *, h0: bool = False, carry: bool = False,
-                lam_const: float | None = None, theta_zero: bool = False) -> dict:
+                lam_const: float | None = None, omega_zero: bool = False) -> dict:
     """Draw one batch of prefill inputs of shape ``s``.
 
     Returns fp32 numpy arrays (bf16-exact where ``s.dtype == 'bf16'``):
-    x [Bt,L,H,R,P]; B, C [Bt,L,H,R,N]; dt, lam [Bt,L,H]; A [H];
-    theta [Bt,L,H,N/2] or None; optional h0 [Bt,H,N,P] and carry-in
-    Bprev_rot [Bt,H,R,N] (fp32), xprev [Bt,H,R,P] (storage dtype), phi0 [Bt,H,N/2].
+    x [Bt,L,H,R,P]; B, C [Bt,L,H,R,N]; dt, lam [Bt,L,H]; dt_raw [Bt,L,H]
+    (dt = softplus(dt_raw) in fp32); A [H]; omega [Bt,L,N/2] or None (RoPE
+    shapes only); optional h0 [Bt,H,N,P] and carry-in Bprev_rot [Bt,H,R,N]
+    (fp32), xprev [Bt,H,R,P] (storage dtype), phi0 [Bt,H,N/2].
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     rnd = bf16_round if s.dtype == "bf16" else (lambda a: a.astype(np.float32))
@@ -88,19 +92,18 @@ def make_inputs(s: Shape, seed: int, *, h0: bool = False, carry: bool = False,
     z_dt = _normal(rng, (s.Bt, s.L, s.H))
     z_lam = _normal(rng, (s.Bt, s.L, s.H))
     u_A = rng.random(size=(s.H,), dtype=np.float32)
-    dt = _softplus(z_dt - np.float32(4.0)).astype(np.float32)
+    dt_raw = (z_dt - np.float32(4.0)).astype(np.float32)
+    dt = _softplus(dt_raw).astype(np.float32)
     lam = _sigmoid(z_lam).astype(np.float32)
     if lam_const is not None:
         lam = np.full_like(lam, np.float32(lam_const))
     A = (-np.exp(u_A * np.float32(np.log(16.0)))).astype(np.float32)
-    theta = omega = None
+    omega = None
     if s.rope:
         omega = _normal(rng, (s.Bt, s.L, s.N // 2))
-        theta = (dt[:, :, :, None] * omega[:, :, None, :]).astype(np.float32)
-        if theta_zero:
-            theta = np.zeros_like(theta)
+        if omega_zero:
             omega = np.zeros_like(omega)
-    out = dict(x=x, B=B, C=C, dt=dt, lam=lam, A=A, theta=theta, omega=omega,
+    out = dict(x=x, B=B, C=C, dt=dt, dt_raw=dt_raw, lam=lam, A=A, omega=omega,
                h0=None, Bprev_rot=None, xprev=None, phi0=None)
     if h0:
         out["h0"] = _normal(rng, (s.Bt, s.H, s.N, s.P), 0.1)
@@ -117,14 +120,14 @@ def make_decode_inputs(s: Shape, steps: int, seed: int) -> dict:
     and ``steps`` single-token inputs drawn like the prefill tensors with L=steps.
 
     Per-step tensors carry a leading step axis: x [steps,Bt,H,R,P], B, C
-    [steps,Bt,H,R,N], dt, lam [steps,Bt,H], theta [steps,Bt,H,N/2] or None.
+    [steps,Bt,H,R,N], dt, lam [steps,Bt,H], omega [steps,Bt,N/2] or None.
     """
     one = make_inputs(dataclasses.replace(s, L=steps), seed, h0=True)
     tr = lambda a: None if a is None else np.ascontiguousarray(np.moveaxis(a, 1, 0))
     return dict(
         h0=one["h0"], A=one["A"],
         x=tr(one["x"]), B=tr(one["B"]), C=tr(one["C"]),
-        dt=tr(one["dt"]), lam=tr(one["lam"]), theta=tr(one["theta"]),
+        dt=tr(one["dt"]), lam=tr(one["lam"]), omega=tr(one["omega"]),
     )
 
 

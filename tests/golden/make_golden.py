@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 from oracle import m3_oracle as orc  # noqa: E402
-from synth.inputs import Shape, make_inputs  # noqa: E402
+from tests.fixtures import Shape, make_inputs  # noqa: E402
 
 shape = Shape(Bt=1, L=20, H=2, P=4, N=6, R=2, dtype="bf16", rope=True)
 seed = 424242

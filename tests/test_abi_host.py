@@ -1,8 +1,12 @@
 """Host-side checks of the C ABI (no GPU): the library loads, exports every
-function the header declares, and rejects invalid arguments before any launch."""
+function the header declares, and rejects invalid arguments before any launch.
+The same checks also run against a build of the host-side layer with
+AddressSanitizer and UBSan (test_validation_under_host_sanitizers)."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -10,6 +14,10 @@ from state_space_sequence_ssm_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "m3ssm.h")
+# set by test_validation_under_host_sanitizers for the run in its subprocess
+_SAN_LIB = os.environ.get("M3SSM_HOSTSAN_LIB")
+if _SAN_LIB:
+    _lib.load(_SAN_LIB)  # every test below then calls the sanitized build
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
                                 reason="libm3ssm.so not built (run __graft_entry__.build())")
@@ -156,3 +164,24 @@ def test_angles_validation():
     assert f(0x1000, None, 0x2000, 1, 0, 1, 4, None) == _lib.M3_ERR_INVALID_ARG
     assert f(0x1000, None, 0x2000, 1, 5, 1, 3, None) == _lib.M3_ERR_UNSUPPORTED
     assert f(0x1004, None, 0x2000, 1, 5, 1, 4, None) == _lib.M3_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(_SAN_LIB is not None, reason="this is the sanitized run itself")
+def test_validation_under_host_sanitizers():
+    """Every host check above, again in a fresh process whose library has its
+    C-ABI layer built with AddressSanitizer and UBSan (no recovery: any
+    report fails the run)."""
+    from state_space_sequence_ssm_amd import build as b
+    try:
+        lib = b.build_hostsan()
+        rt = b.asan_runtime()
+    except RuntimeError as e:
+        pytest.skip(f"host sanitizer build unavailable: {e}")
+    env = dict(os.environ, M3SSM_HOSTSAN_LIB=lib, LD_PRELOAD=rt,
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", os.path.abspath(__file__)],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=900)
+    tail = (r.stdout + r.stderr)[-4000:]
+    assert r.returncode == 0, tail
+    assert "passed" in r.stdout and "ERROR: AddressSanitizer" not in tail and "runtime error" not in tail, tail

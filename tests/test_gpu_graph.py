@@ -7,7 +7,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from synth.inputs import Shape, make_inputs  # noqa: E402
+from tests.fixtures import Shape, make_inputs  # noqa: E402
 from tests.gpu_util import to_device  # noqa: E402
 
 pytestmark = pytest.mark.gpu

@@ -1,6 +1,7 @@
 """GPU parity: the HIP path through the C ABI vs the fp64 oracle on the same
 seeded inputs (relative L2 <= 2e-3 for fp32 inputs, <= 2e-2 for bf16 inputs,
-outputs and final states both checked)."""
+outputs and final states both checked).  Every output buffer is NaN-filled
+before the call, so a value a kernel failed to write cannot pass."""
 import dataclasses
 import sys
 
@@ -10,8 +11,10 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from oracle import m3_oracle as orc  # noqa: E402
-from synth.inputs import CONFIGS, SEED_BASE, Shape, make_decode_inputs, make_inputs  # noqa: E402
-from tests.gpu_util import TOL, angle_diff, dev, host, oracle_prefill, storage_dtype, to_device  # noqa: E402
+from tests.fixtures import CONFIGS, SEED_BASE, Shape, make_decode_inputs, make_inputs  # noqa: E402
+from synth.device_inputs import DecodeStream  # noqa: E402
+from tests.gpu_util import (TOL, angle_diff, decode, dev, host, oracle_prefill, oracle_units, prefill,  # noqa: E402
+                            prefill_d, sample_units, storage_dtype, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,9 +33,7 @@ def _say(*a):
 
 
 def _run_prefill(ops, dd, s, carry=False, **kw):
-    return ops.m3_ssm_prefill(dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], dd["A"], dd["theta"],
-                              dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"),
-                              want_state=True, want_carry=carry, **kw)
+    return prefill_d(ops, dd, carry=carry, **kw)
 
 
 # ----------------------------------------------------------------- angles
@@ -113,13 +114,14 @@ def test_prefill_omega(ops, case):
     _say("prefill omega", case)
     d = make_inputs(s, 3000 + L + N, h0=carry, carry=carry)
     dd = to_device(d, s)
-    kw = dict(want_state=True, want_carry=True)
     args = (dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], dd["A"])
     carry_in = (dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"))
-    out = ops.m3_ssm_prefill(*args, None, *carry_in, omega=dd["omega"], **kw)
-    ref_gpu = ops.m3_ssm_prefill(*args, dd["theta"], *carry_in, **kw)
+    out = prefill(ops, *args, None, *carry_in, omega=dd["omega"])
+    ref_gpu = prefill(ops, *args, dd["theta"], *carry_in)
     torch.cuda.synchronize()
-    ref = oracle_prefill(d)
+    # the reference angles come from the oracle's own theta = Delta * omega
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], None, d.get("h0"),
+                            d.get("Bprev_rot"), d.get("xprev"), d.get("phi0"), omega=d["omega"])
     ey = orc.rel_l2(host(out["y"]), ref["y"])
     eh = orc.rel_l2(host(out["h"]), ref["h"])
     _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
@@ -156,9 +158,9 @@ def test_prefill_head_major(ops, case):
     dd = to_device(d, s)
     swap = lambda t: t.permute(0, 2, 1, 3, 4).contiguous()  # noqa: E731  token <-> head axes
     out_t = _run_prefill(ops, dd, s, carry=True)
-    out_h = ops.m3_ssm_prefill(swap(dd["x"]), swap(dd["B"]), swap(dd["C"]), dd["dt"], dd["lam"], dd["A"],
-                               dd["theta"], dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"),
-                               want_state=True, want_carry=True, head_major=True)
+    out_h = prefill(ops, swap(dd["x"]), swap(dd["B"]), swap(dd["C"]), dd["dt"], dd["lam"], dd["A"],
+                    dd["theta"], dd.get("h0"), dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"),
+                    head_major=True)
     torch.cuda.synchronize()
     y_h = host(swap(out_h["y"]))
     assert np.array_equal(y_h, host(out_t["y"]))
@@ -178,6 +180,7 @@ EDGE = [
     ("lambda1", 1, 97, 2, 64, 64, 2, True),     # Euler / Mamba-2 form (lambda = 1)
     ("dt_zero_runs", 2, 130, 2, 64, 128, 1, False),  # Delta = 0 on whole chunks and single tokens
     ("big_angles", 1, 70, 2, 32, 64, 4, True),  # angles far outside [-pi, pi]
+    ("huge_angles_q64", 1, 200, 2, 64, 64, 1, True),  # ~16 rad per token: chunk sums near 1e3 rad
     ("many_units", 16, 20, 64, 16, 16, 1, True),  # 1024 (batch, head) units, one short ragged chunk
 ]
 
@@ -196,6 +199,11 @@ def test_prefill_edge_values(ops, case):
     if name == "big_angles":
         d["theta"] = (d["theta"] * 500.0).astype(np.float32)
         d["phi0"] = (d["phi0"] * 40.0).astype(np.float32)
+    if name == "huge_angles_q64":
+        # angles of ~16 rad per token: the running sum of a 64-token chunk
+        # reaches ~1e3 rad, the carry-in ~1e3 rad as well
+        d["theta"] = (np.sign(d["theta"]) * 16.0 + d["theta"]).astype(np.float32)
+        d["phi0"] = (d["phi0"] * 300.0).astype(np.float32)
     dd = to_device(d, s)
     out = _run_prefill(ops, dd, s, carry=True)
     torch.cuda.synchronize()
@@ -219,29 +227,38 @@ def test_prefill_deterministic(ops):
 
 
 # ----------------------------------------------------------------- prefill, full configs
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3])
 def test_prefill_config_full_size(ops, cfg):
-    """Full configuration sizes on the GPU (the benchmarked launch); the oracle
-    checks a sample of (batch, head) units one by one."""
+    """Full configuration sizes on the GPU, in the launch configuration the
+    benchmark times (the default workspace, i.e. the sequence split where the
+    library takes it).  The oracle checks 16 (batch, head) units one by one,
+    two in each eighth of the unit axis (the range one XCD walks), each to
+    the bar on its own; every output must be finite (written)."""
     s = CONFIGS[cfg]
     _say("prefill config", cfg, s)
     d = make_inputs(s, SEED_BASE + cfg)
     dd = to_device(d, s)
     out = _run_prefill(ops, dd, s, carry=True)
     torch.cuda.synchronize()
-    y = out["y"]
-    assert bool(torch.isfinite(y.float()).all())
-    sb = sorted({0, s.Bt - 1})
-    sh = sorted({0, s.H // 2, s.H - 1})
-    ref = oracle_prefill(d, sel_b=sb, sel_h=sh)
-    yg = host(y[sb][:, :, sh])
-    hg = host(out["h"][sb][:, sh])
-    ey, eh = orc.rel_l2(yg, ref["y"]), orc.rel_l2(hg, ref["h"])
-    _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+    for k in ("y", "h", "Bprev_rot", "xprev") + (("phi",) if s.rope else ()):
+        assert bool(torch.isfinite(out[k].float()).all()), k
+    units = sample_units(s.Bt * s.H) if s.Bt * s.H > 16 else list(range(s.Bt * s.H))
+    _say("  units", units)
+    ref = oracle_units(d, units, s.H)
     tol = TOL[s.dtype]
-    assert ey <= tol and eh <= tol
-    if s.rope:
-        assert np.max(angle_diff(host(out["phi"][sb][:, sh]), ref["phi"])) <= 1e-3
+    worst = 0.0
+    for i, u in enumerate(units):
+        b, h = divmod(u, s.H)
+        ey = orc.rel_l2(host(out["y"][b, :, h]), ref["y"][0, :, i])
+        eh = orc.rel_l2(host(out["h"][b, h]), ref["h"][0, i])
+        worst = max(worst, ey, eh)
+        assert ey <= tol and eh <= tol, (u, ey, eh)
+        assert orc.rel_l2(host(out["Bprev_rot"][b, h]), ref["Bprev_rot"][0, i]) <= 1e-5
+        assert np.array_equal(host(out["xprev"][b, h]), ref["xprev"][0, i])
+        if s.rope:
+            assert np.max(angle_diff(host(out["phi"][b, h]), ref["phi"][0, i])) <= 1e-3
+    _say(f"  worst per-unit rel_l2 {worst:.2e}")
 
 
 # ----------------------------------------------------------------- sequence split
@@ -298,10 +315,10 @@ def test_split_resume(ops, R, rope):
         _say("split-resume", R, rope, k)
         first = {n: (None if dd[n] is None else dd[n][:, :k].contiguous()) for n in ("x", "B", "C", "dt", "lam", "theta")}
         second = {n: (None if dd[n] is None else dd[n][:, k:].contiguous()) for n in ("x", "B", "C", "dt", "lam", "theta")}
-        a = ops.m3_ssm_prefill(first["x"], first["B"], first["C"], first["dt"], first["lam"], dd["A"], first["theta"],
-                               dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"], want_carry=True)
-        b = ops.m3_ssm_prefill(second["x"], second["B"], second["C"], second["dt"], second["lam"], dd["A"],
-                               second["theta"], a["h"], a["Bprev_rot"], a["xprev"], a["phi"], want_carry=True)
+        a = prefill(ops, first["x"], first["B"], first["C"], first["dt"], first["lam"], dd["A"], first["theta"],
+                    dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"])
+        b = prefill(ops, second["x"], second["B"], second["C"], second["dt"], second["lam"], dd["A"],
+                    second["theta"], a["h"], a["Bprev_rot"], a["xprev"], a["phi"])
         torch.cuda.synchronize()
         y = np.concatenate([host(a["y"]), host(b["y"])], axis=1)
         assert orc.rel_l2(y, ref["y"]) <= TOL["bf16"]
@@ -313,9 +330,8 @@ def test_split_resume(ops, R, rope):
 def _decode_chain(ops, dd_state, steps, dec, R, dtype, rope):
     ys = []
     for t in range(steps):
-        y = ops.m3_ssm_decode_step(dd_state["h"], dd_state["phi"], dd_state["Bprev_rot"], dd_state["xprev"],
-                                   dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t], dec["A"],
-                                   dec["theta"][t] if rope else None)
+        y = decode(ops, dd_state, dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t], dec["A"],
+                   dec["theta"][t] if rope else None)
         ys.append(host(y))
     torch.cuda.synchronize()
     return np.stack(ys, axis=1)
@@ -370,8 +386,8 @@ def test_prefill_A_tok(ops, case):
     d = make_inputs(s, 5000 + L + N, h0=carry, carry=carry, lam_const=lamc)
     a_tok = _a_tok((Bt, L, H), 6000 + L)
     dd = to_device(d, s)
-    out = ops.m3_ssm_prefill(dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], None, dd["theta"], dd.get("h0"),
-                             dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"), want_carry=True, A_tok=dev(a_tok))
+    out = prefill(ops, dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], None, dd["theta"], dd.get("h0"),
+                  dd.get("Bprev_rot"), dd.get("xprev"), dd.get("phi0"), A_tok=dev(a_tok))
     torch.cuda.synchronize()
     ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], a_tok, d["theta"], d.get("h0"),
                             d.get("Bprev_rot"), d.get("xprev"), d.get("phi0"))
@@ -396,9 +412,8 @@ def test_decode_A_tok(ops):
                  xprev=dev(np.zeros((Bt, H, R, P)), st))
     ys = []
     for t in range(steps):
-        ys.append(host(ops.m3_ssm_decode_step(state["h"], state["phi"], state["Bprev_rot"], state["xprev"],
-                                              dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t],
-                                              None, dec["theta"][t], A_tok=at[t])))
+        ys.append(host(decode(ops, state, dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t],
+                              None, dec["theta"][t], A_tok=at[t])))
     torch.cuda.synchronize()
     ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], a_tok, d["theta"], d["h0"])
     ey = orc.rel_l2(np.stack(ys, axis=1), ref["y"])
@@ -422,11 +437,10 @@ def test_decode_omega(ops):
     A = dev(d["A"])
     ys = []
     for t in range(steps):
-        ys.append(host(ops.m3_ssm_decode_step(state["h"], state["phi"], state["Bprev_rot"], state["xprev"],
-                                              dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t],
-                                              A, None, omega=dec["omega"][t])))
+        ys.append(host(decode(ops, state, dec["x"][t], dec["B"][t], dec["C"][t], dec["dt"][t], dec["lam"][t],
+                              A, None, omega=dec["omega"][t])))
     torch.cuda.synchronize()
-    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"], d["h0"])
+    ref = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], None, d["h0"], omega=d["omega"])
     ey = orc.rel_l2(np.stack(ys, axis=1), ref["y"])
     eh = orc.rel_l2(host(state["h"]), ref["h"])
     _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
@@ -460,16 +474,73 @@ def test_decode_config_full_size(ops):
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
+@pytest.mark.timeout(900)
+def test_decode_config4_all_steps(ops):
+    """The decode workload at full size (B=256, H=32, N=P=64, R=4) for all its
+    1000 sequential steps, inputs drawn on the device step by step: y of every
+    step, and the final state, B carry and angle, against the oracle on 16
+    (batch, head) units (two in each eighth of the unit axis).  Each step's y
+    buffer is NaN-filled before the call."""
+    s = CONFIGS[4]
+    steps = s.L
+    Bt, H, P, N, R = s.Bt, s.H, s.P, s.N, s.R
+    _say("decode config 4, all", steps, "steps")
+    gen = DecodeStream(Bt, H, P, N, R, seed=SEED_BASE + 4)
+    units = sample_units(Bt * H)
+    k = len(units)
+    idx = torch.tensor(units, device="cuda")
+    bidx = torch.tensor([u // H for u in units], device="cuda")
+    st = dict(h=gen.h0.clone(), phi=torch.zeros((Bt, H, N // 2), device="cuda"),
+              Bprev_rot=torch.zeros((Bt, H, R, N), device="cuda"),
+              xprev=torch.zeros((Bt, H, R, P), device="cuda", dtype=torch.bfloat16))
+    h0 = host(gen.h0.reshape(Bt * H, N, P)[idx])
+    U = Bt * H
+    rec = {n: [] for n in ("x", "B", "C", "dt", "lam", "omega", "theta", "y")}
+    for t in range(steps):
+        inp = gen.step()
+        y = decode(ops, st, inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], gen.A, inp["theta"])
+        rec["x"].append(inp["x"].reshape(U, R, P)[idx])
+        rec["B"].append(inp["B"].reshape(U, R, N)[idx])
+        rec["C"].append(inp["C"].reshape(U, R, N)[idx])
+        rec["dt"].append(inp["dt"].reshape(U)[idx])
+        rec["lam"].append(inp["lam"].reshape(U)[idx])
+        rec["omega"].append(inp["omega"][bidx])
+        rec["theta"].append(inp["theta"].reshape(U, N // 2)[idx])
+        rec["y"].append(y.reshape(U, R, P)[idx])
+        if t % 250 == 249:
+            _say("  step", t + 1)
+    torch.cuda.synchronize()
+    r = {n: torch.stack(v).float().cpu().numpy() for n, v in rec.items()}  # [steps, k, ...]
+    # the device angles are the fp32 rounding of the oracle's Delta * omega
+    th = np.stack([orc.angles_from_rates(r["dt"][:, i:i + 1], r["omega"][:, i])[:, 0] for i in range(k)], axis=1)
+    assert np.array_equal(th.astype(np.float32), r["theta"])
+    A = host(gen.A)[[u % H for u in units]]
+    ref = orc.ssm_reference(r["x"][None], r["B"][None], r["C"][None], r["dt"][None], r["lam"][None], A,
+                            th.astype(np.float32)[None], h0[None])
+    worst = 0.0
+    for t in range(steps):
+        e = orc.rel_l2(r["y"][t], ref["y"][0, t])
+        worst = max(worst, e)
+        assert e <= TOL["bf16"], (t, e)
+    _say(f"  worst per-step rel_l2 of y {worst:.2e}")
+    hs = host(st["h"].reshape(U, N, P)[idx])
+    bs = host(st["Bprev_rot"].reshape(U, R, N)[idx])
+    ps = host(st["phi"].reshape(U, N // 2)[idx])
+    for i in range(k):
+        assert orc.rel_l2(hs[i], ref["h"][0, i]) <= TOL["bf16"], i
+        assert orc.rel_l2(bs[i], ref["Bprev_rot"][0, i]) <= 1e-5, i
+        assert np.max(angle_diff(ps[i], ref["phi"][0, i])) <= 1e-3, i
+
+
 def test_prefill_then_decode(ops):
     """Prefill tokens [0, k) then decode [k, L) equals the oracle on [0, L)."""
     Bt, L, H, P, N, R, k = 2, 90, 2, 64, 64, 4, 70
     s = Shape(Bt, L, H, P, N, R, "bf16", True)
     d = make_inputs(s, 4242, h0=True, carry=True)
     dd = to_device(d, s)
-    a = ops.m3_ssm_prefill(dd["x"][:, :k].contiguous(), dd["B"][:, :k].contiguous(), dd["C"][:, :k].contiguous(),
-                           dd["dt"][:, :k].contiguous(), dd["lam"][:, :k].contiguous(), dd["A"],
-                           dd["theta"][:, :k].contiguous(), dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"],
-                           want_carry=True)
+    a = prefill(ops, dd["x"][:, :k].contiguous(), dd["B"][:, :k].contiguous(), dd["C"][:, :k].contiguous(),
+                dd["dt"][:, :k].contiguous(), dd["lam"][:, :k].contiguous(), dd["A"],
+                dd["theta"][:, :k].contiguous(), dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"])
     state = dict(h=a["h"], phi=a["phi"], Bprev_rot=a["Bprev_rot"], xprev=a["xprev"])
     dec = {n: dd[n][:, k:].transpose(0, 1).contiguous() for n in ("x", "B", "C", "dt", "lam", "theta")}
     dec["A"] = dd["A"]

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import m3_oracle as orc
-from synth.inputs import Shape, make_inputs
+from tests.fixtures import Shape, make_inputs
 
 
 
@@ -370,7 +370,7 @@ def test_oracle_golden_regression():
     path = os.path.join(os.path.dirname(__file__), "golden", "oracle_tiny.json")
     with open(path) as f:
         g = json.load(f)
-    from synth.inputs import make_inputs as mk
+    from tests.fixtures import make_inputs as mk
     s = Shape(**g["shape"])
     d = mk(s, g["seed"], h0=True, carry=True)
     out = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], d["theta"],
@@ -429,3 +429,114 @@ def test_chunked_shifted_state_decomposition(R, Q, rope):
             hfin[b, hh] = Hs
     assert orc.rel_l2(y, ref["y"]) <= 1e-12
     assert orc.rel_l2(hfin, ref["h"]) <= 1e-12
+
+
+# ---------------------------------------------------------------- comparator
+def test_rel_l2_hand_computed_values():
+    """The parity metric itself: ||a - b|| / ||b|| on hand-computed cases.  A
+    comparator that returned 0, or normalised by anything but ||b||, fails."""
+    a, b = np.array([3.0, 4.0]), np.array([0.0, 5.0])
+    assert abs(orc.rel_l2(a, b) - np.sqrt(10.0) / 5.0) <= 1e-15      # ||(3,-1)|| / 5
+    assert abs(orc.rel_l2(b, a) - np.sqrt(10.0) / 5.0) <= 1e-15      # ||a|| = 5 as well
+    assert abs(orc.rel_l2(2.0 * b, b) - 1.0) <= 1e-15
+    assert abs(orc.rel_l2(np.array([1.0, 1.0, 1.0, 1.0]), np.array([0.0, 2.0, 0.0, 0.0])) - 1.0) <= 1e-15
+    assert orc.rel_l2(b, b) == 0.0
+    # scale invariance, and every element counts (2-D input is flattened)
+    m_a = np.array([[1.0, 2.0], [3.0, 4.0]])
+    m_b = np.array([[1.0, 2.0], [3.0, 5.0]])
+    assert abs(orc.rel_l2(m_a, m_b) - 1.0 / np.sqrt(39.0)) <= 1e-15
+    assert abs(orc.rel_l2(1e-30 * m_a, 1e-30 * m_b) - 1.0 / np.sqrt(39.0)) <= 1e-14
+    assert abs(orc.rel_l2(1e30 * m_a, 1e30 * m_b) - 1.0 / np.sqrt(39.0)) <= 1e-14
+    # zero reference: the plain norm of the difference
+    assert abs(orc.rel_l2(np.array([3.0, 4.0]), np.zeros(2)) - 5.0) <= 1e-15
+    # mismatched shapes are an error, not a broadcast
+    with pytest.raises(AssertionError):
+        orc.rel_l2(np.zeros(3), np.zeros((3, 1)))
+
+
+# ---------------------------------------------------------------- angles from rates
+def test_angles_from_rates_scalar_loop_and_semantics():
+    rng = np.random.default_rng(5)
+    dt = rng.random((2, 3, 4)).astype(np.float32)
+    om = rng.standard_normal((2, 3, 5)).astype(np.float32)
+    th = orc.angles_from_rates(dt, om)
+    assert th.shape == (2, 3, 4, 5) and th.dtype == np.float64
+    for b in range(2):
+        for t in range(3):
+            for h in range(4):
+                for j in range(5):
+                    assert th[b, t, h, j] == float(dt[b, t, h]) * float(om[b, t, j])
+    # fp32 rounding of the exact product is the fp32 product
+    assert np.array_equal(th.astype(np.float32), dt[..., None] * om[:, :, None, :])
+    # a constant rate c gives cumulative angles c * (running sum of Delta)
+    d = _tiny(Bt=1, L=9, H=2, N=4, rope=True, seed=3)
+    om_c = np.full((1, 9, 2), 0.37)
+    phi = orc.rope_angles_cumsum(orc.angles_from_rates(d["dt"], om_c))
+    np.testing.assert_allclose(phi[0, :, 1, 0], 0.37 * np.cumsum(np.float64(d["dt"][0, :, 1])), rtol=1e-13)
+    # the oracle given omega equals the oracle given the angles
+    a = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"], omega=d["omega"])
+    b = orc.ssm_reference(d["x"], d["B"], d["C"], d["dt"], d["lam"], d["A"],
+                          orc.angles_from_rates(d["dt"], d["omega"]))
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["h"], b["h"])
+
+
+# ---------------------------------------------------------------- prologue
+def test_softplus_identities():
+    z = np.linspace(-30.0, 30.0, 121)
+    sp = orc.softplus(z)
+    np.testing.assert_allclose(sp - orc.softplus(-z), z, rtol=0, atol=1e-13)   # sp(z) - sp(-z) = z
+    np.testing.assert_allclose(np.expm1(sp), np.exp(z), rtol=1e-12)            # e^sp(z) = 1 + e^z
+    assert abs(orc.softplus(0.0) - np.log(2.0)) <= 1e-16
+    assert orc.softplus(800.0) == 800.0 and np.isfinite(orc.softplus(-800.0))
+    assert np.all(sp > 0) and np.all(np.diff(sp) > 0)
+
+
+def test_rms_norm_hand_computed_and_invariants():
+    # (3, 4): mean square 12.5
+    out = orc.rms_norm(np.array([3.0, 4.0]))
+    np.testing.assert_allclose(out, [3.0 / np.sqrt(12.5), 4.0 / np.sqrt(12.5)], rtol=1e-15)
+    # eps enters under the root: ones(4) with eps 3 -> 1 / sqrt(1 + 3) = 1/2
+    np.testing.assert_allclose(orc.rms_norm(np.ones(4), eps=3.0), 0.5, rtol=1e-15)
+    # each row (last axis) on its own: RMS 1, sign and positive scale
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((3, 2, 4, 6)) * rng.random((3, 2, 4, 1)) * 50.0
+    n = orc.rms_norm(v)
+    np.testing.assert_allclose(np.sqrt(np.mean(n * n, axis=-1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(orc.rms_norm(-v), -n, rtol=1e-15)
+    np.testing.assert_allclose(orc.rms_norm(v * 7.5), n, rtol=1e-13)
+    # gain: elementwise along the normalised axis
+    w = rng.random(6) + 0.5
+    np.testing.assert_allclose(orc.rms_norm(v, w), n * w, rtol=1e-14)
+
+
+def test_prologue_norm_bias_softplus():
+    s = Shape(2, 7, 3, 4, 6, 2, "f32", True)
+    d = make_inputs(s, 21)
+    rng = np.random.default_rng(22)
+    bB, bC = rng.standard_normal((3, 2, 6)), rng.standard_normal((3, 2, 6))
+    wB = rng.random(6) + 0.5
+    dtb = rng.standard_normal(3)
+    B2, C2, dt2 = orc.prologue(d["B"], d["C"], d["dt_raw"], bc_norm=True, B_norm_w=wB, eps=1e-6,
+                               B_bias=bB, C_bias=bC, dt_softplus=True, dt_bias=dtb)
+    # bias added after the norm: removing it leaves RMS-normalised rows (times the gain)
+    un = (B2 - bB) / wB
+    rms_raw = np.sqrt(np.mean(np.float64(d["B"]) ** 2, axis=-1))
+    np.testing.assert_allclose(np.sqrt(np.mean(un ** 2, axis=-1)), rms_raw / np.sqrt(rms_raw ** 2 + 1e-6), rtol=1e-12)
+    rms_c = np.sqrt(np.mean(np.float64(d["C"]) ** 2, axis=-1))
+    np.testing.assert_allclose(np.sqrt(np.mean((C2 - bC) ** 2, axis=-1)), rms_c / np.sqrt(rms_c ** 2 + 1e-6),
+                               rtol=1e-12)
+    # the head bias is per (head, rank, element), broadcast over batch and token
+    np.testing.assert_allclose((C2 - orc.rms_norm(d["C"], eps=1e-6))[1, 4], bC, rtol=1e-13)
+    # Delta = softplus(raw + bias[h]); without softplus Delta is passed through
+    np.testing.assert_allclose(np.log(np.expm1(dt2)), np.float64(d["dt_raw"]) + dtb, rtol=1e-10, atol=1e-12)
+    _, _, dt3 = orc.prologue(d["B"], d["C"], d["dt"])
+    assert np.array_equal(dt3, np.float64(d["dt"]))
+    # through the whole core: with the norm on, a positive per-row scale of the
+    # raw B and C changes nothing
+    sc = rng.random((2, 7, 3, 2, 1)) * 10 + 0.1
+    outs = []
+    for k in (1.0, sc):
+        Bq, Cq, dq = orc.prologue(d["B"] * k, d["C"] * k, d["dt_raw"], bc_norm=True, B_bias=bB, C_bias=bC,
+                                  dt_softplus=True)
+        outs.append(orc.ssm_reference(d["x"], Bq, Cq, dq, d["lam"], d["A"], omega=d["omega"]))
+    assert orc.rel_l2(outs[1]["y"], outs[0]["y"]) <= 1e-12
