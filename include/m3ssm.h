@@ -53,7 +53,9 @@ typedef enum m3_status {
   M3_OK = 0,
   M3_ERR_INVALID_ARG = -1, /* null required pointer, bad size, misalignment  */
   M3_ERR_UNSUPPORTED = -2, /* shape/dtype outside the compiled kernel tiles  */
-  M3_ERR_HIP = -3          /* a HIP launch or runtime error was reported     */
+  M3_ERR_HIP = -3,         /* a HIP launch or runtime error was reported     */
+  M3_ERR_SCRATCH = -4      /* m3_ssm_prefill_noalloc: the call needs more
+                              scratch than M3_NOALLOC_SCRATCH_BYTES          */
 } m3_status;
 
 typedef enum m3_dtype {
@@ -168,6 +170,28 @@ int m3_ssm_prefill(const m3_prefill_args* args, void* stream);
  * call, so concurrent calls need their own.  Depends only on the shape
  * fields (and the current device), not on pointers. */
 size_t m3_ssm_prefill_workspace_size(const m3_prefill_args* args);
+
+/*
+ * m3_ssm_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and kernels as m3_ssm_prefill, except that
+ * `workspace` must be NULL and `workspace_bytes` 0: where the call would use
+ * the optional workspace (m3_ssm_prefill_workspace_size > 0) it uses instead
+ * a static device buffer of M3_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends.  Nothing is allocated
+ * by the call (the buffer's address is looked up once per device, with the
+ * device current, on the first call there).  A call whose workspace size
+ * exceeds M3_NOALLOC_SCRATCH_BYTES (16 MiB) returns M3_ERR_SCRATCH without
+ * launching: on a 256-CU device every split shape with N * P <= 128 * 64
+ * fits (at most ~8.6 MB); at N = P = 128 calls with more than ~120 (batch,
+ * head) units do not (they can use m3_ssm_prefill with a workspace).  The
+ * buffer needs no clearing (each call writes what it reads), but every call
+ * on one device shares it: calls that overlap in time on one device (two
+ * streams, two host threads) race and give undefined results; serialise
+ * them, or use m3_ssm_prefill with a workspace per stream.
+ */
+#define M3_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int m3_ssm_prefill_noalloc(const m3_prefill_args* args, void* stream);
 
 /*
  * One decode token against a resident state (the same token update as the

@@ -15,6 +15,8 @@ M3_OK = 0
 M3_ERR_INVALID_ARG = -1
 M3_ERR_UNSUPPORTED = -2
 M3_ERR_HIP = -3
+M3_ERR_SCRATCH = -4
+NOALLOC_SCRATCH_BYTES = 16 << 20  # M3_NOALLOC_SCRATCH_BYTES
 M3_F32 = 0
 M3_BF16 = 1
 
@@ -43,7 +45,7 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("m3_ssm_prefill", "m3_ssm_prefill_workspace_size", "m3_ssm_decode_step",
+EXPORTS = ("m3_ssm_prefill", "m3_ssm_prefill_workspace_size", "m3_ssm_prefill_noalloc", "m3_ssm_decode_step",
            "m3_rope_angles_cumsum", "m3_status_string", "m3_version")
 
 _lib = None
@@ -61,6 +63,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.m3_ssm_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
     lib.m3_ssm_prefill.restype = ctypes.c_int
+    lib.m3_ssm_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+    lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
     lib.m3_ssm_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.m3_ssm_prefill_workspace_size.restype = ctypes.c_size_t
     lib.m3_ssm_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "m3ssm.h"
 #include "m3ssm_internal.hpp"
@@ -84,6 +85,7 @@ const char* m3_status_string(int status) {
     case M3_ERR_INVALID_ARG: return "invalid argument";
     case M3_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case M3_ERR_HIP: return "HIP runtime error";
+    case M3_ERR_SCRATCH: return "the call needs more scratch than the static buffer of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -218,6 +220,38 @@ int run_prefill(const m3_prefill_args* a, void* ws_ptr, size_t ws_bytes, void* s
   return hip_status(m3::launch_prefill_bf16(pb, false, st));
 }
 
+// Scratch of m3_ssm_prefill_noalloc: a device array in this library's code
+// object, so that every device it runs on holds one copy, allocated when the
+// code object is loaded there and kept until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the address
+// on each device comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kScratchBytes = M3_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address per device (guarded by g_scratch_mu)
+
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return M3_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return M3_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return M3_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return M3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +260,19 @@ int m3_ssm_prefill(const m3_prefill_args* a, void* stream) {
   const int rc = check_prefill(a);
   if (rc != M3_OK) return rc;
   return run_prefill(a, a->workspace, a->workspace_bytes, stream);
+}
+
+int m3_ssm_prefill_noalloc(const m3_prefill_args* a, void* stream) {
+  const int rc = check_prefill(a);
+  if (rc != M3_OK) return rc;
+  if (a->workspace != nullptr || a->workspace_bytes != 0) return M3_ERR_INVALID_ARG;
+  const SplitPlan sp = split_plan(a);
+  if (!sp.on) return run_prefill(a, nullptr, 0, stream);
+  if (sp.bytes > kScratchBytes) return M3_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rs = scratch_on_current_device(&ws);
+  if (rs != M3_OK) return rs;
+  return run_prefill(a, ws, kScratchBytes, stream);
 }
 
 int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {

@@ -50,7 +50,7 @@ def _stream(stream) -> int:
 def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
                    *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
                    want_state=True, want_carry=False, chunk=0, workspace=None, omega=None, A_tok=None,
-                   head_major=False, stream=None):
+                   head_major=False, noalloc=False, stream=None):
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
     dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None (or
     instead omega [Bt,L,N/2] fp32: rates shared by the heads, theta = dt * omega
@@ -61,7 +61,9 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     tensor of at least prefill_workspace_bytes(...) bytes, None to allocate one
     when the library asks for it, or False to run without (unsplit).  Returns
     a dict with y and, as requested, h_final and the carry-out (Bprev_rot,
-    xprev, phi).  head_major: x, B, C and y are [Bt,H,L,R,.] instead."""
+    xprev, phi).  head_major: x, B, C and y are [Bt,H,L,R,.] instead.
+    noalloc: call m3_ssm_prefill_noalloc (the library's static scratch in
+    place of a workspace; workspace must then be None)."""
     if head_major:
         Bt, H, L, R, P = x.shape
     else:
@@ -103,6 +105,13 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a.xprev_out = _ptr(xprev_out, x.dtype, (Bt, H, R, P), "xprev_out")
     a.phi_out = _ptr(phi_out, f32, (Bt, H, N // 2), "phi_out")
     lib = _lib.load()
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        rc = lib.m3_ssm_prefill_noalloc(ctypes.byref(a), _stream(stream))
+        if rc != _lib.M3_OK:
+            raise M3Error(rc, "m3_ssm_prefill_noalloc")
+        return dict(y=y, h=h_final, Bprev_rot=Bprev_rot_out, xprev=xprev_out, phi=phi_out)
     if workspace is not False:
         need = lib.m3_ssm_prefill_workspace_size(ctypes.byref(a))
         if need > 0:

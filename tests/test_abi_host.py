@@ -127,6 +127,34 @@ def test_prefill_workspace_validation():
     assert _rc_prefill(a) == _lib.M3_ERR_INVALID_ARG
 
 
+def test_prefill_noalloc_validation():
+    """The no-allocation entry point validates like m3_ssm_prefill, refuses a
+    workspace, and refuses (before any GPU call) a call whose split needs more
+    than its static scratch."""
+    lib = _lib.load()
+    f = lambda a: lib.m3_ssm_prefill_noalloc(ctypes.byref(a), None)  # noqa: E731
+    assert lib.m3_ssm_prefill_noalloc(None, None) == _lib.M3_ERR_INVALID_ARG
+    a = _good_prefill()
+    a.x = None
+    assert f(a) == _lib.M3_ERR_INVALID_ARG
+    a = _good_prefill()
+    a.R = 3
+    assert f(a) == _lib.M3_ERR_UNSUPPORTED
+    a = _good_prefill()
+    a.Bt, a.H, a.L = 1, 2, 1024  # takes the split
+    a.workspace, a.workspace_bytes = 0x40000000, 1 << 20
+    assert f(a) == _lib.M3_ERR_INVALID_ARG
+    # 128 units at N = P = 128 split, and need more than the 16 MiB scratch
+    a = _good_prefill()
+    a.Bt, a.H, a.L, a.N, a.P, a.R = 4, 32, 4096, 128, 128, 1
+    need = lib.m3_ssm_prefill_workspace_size(ctypes.byref(a))
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(a) == _lib.M3_ERR_SCRATCH
+    assert "scratch" in _lib.status_string(_lib.M3_ERR_SCRATCH)
+    a.P = 64  # the headline shape's state fits
+    assert 0 < lib.m3_ssm_prefill_workspace_size(ctypes.byref(a)) <= _lib.NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_validation():
     lib = _lib.load()
     assert lib.m3_ssm_decode_step(None, None) == _lib.M3_ERR_INVALID_ARG
