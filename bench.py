@@ -25,7 +25,8 @@ trace).  --only pmc runs the counter workload of one --group: a plain device
 copy of known size (the scale for FETCH_SIZE / WRITE_SIZE), then a few
 untimed launches of each workload of the group ("base": the five workloads
 and the decode control at Bt=512; "variants": the prefill lines with angles
-as rates and A per token).  Within a group every workload runs a distinct
+as rates and A per token; "prologue": the prefill lines with the prologue
+fused).  Within a group every workload runs a distinct
 kernel symbol or grid, so counter rows map to workloads.  PREFIX is the
 rocprofv3 output prefix (-d DIR -o NAME gives DIR/NAME).
 """
@@ -66,8 +67,12 @@ DECODE_BIG_STEPS = 200
 COPY_BYTES = 1 << 30                 # plain copy used to scale the HBM counters
 
 # prefill lines beside the plain workloads: (line name, workload, mode)
+# mode "pro": the prologue fused in front of the core -- raw B, C (RMS
+# normalisation with gains, head biases), raw step (softplus with a head bias)
+# and, with RoPE, angles as rates
 VARIANTS = [("siso_rope_omega", "siso_rope", "omega"), ("mimo_rope_omega", "mimo_rope", "omega"),
-            ("siso_real_atok", "siso_real", "atok")]
+            ("siso_real_atok", "siso_real", "atok"), ("siso_real_prologue", "siso_real", "pro"),
+            ("siso_rope_prologue", "siso_rope", "pro"), ("mimo_rope_prologue", "mimo_rope", "pro")]
 
 
 def ANGLES_GRID(Bt, H, J):
@@ -75,10 +80,10 @@ def ANGLES_GRID(Bt, H, J):
     return Bt * ((H * J // 4 + 7) // 8) * 256
 
 
-def prefill_kernel_name(Bt, L, H, P, N, R, rope, state_only=False):
+def prefill_kernel_name(Bt, L, H, P, N, R, rope, state_only=False, pro=False):
     """Kernel symbol (as rocprofv3 prints it) that runs a bf16 prefill shape."""
     return (f"m3::pc::prefill_pc_kernel<{N}, {P}, {int(math.log2(R))}, {'true' if rope else 'false'}, "
-            f"{'true' if state_only else 'false'}>")
+            f"{'true' if state_only else 'false'}, {'true' if pro else 'false'}>")
 
 
 def prefill_split(Bt, L, H, P, N, R, rope, cus=256):
@@ -103,22 +108,30 @@ def decode_kernel_name(Bt, H, P, N, R):
     return f"m3::decode_step_kernel<m3::bf16_t, {N}, {P}, {4 if R <= 4 else 16}>"
 
 
-def unit_kernels():
-    """(unit key, kernel symbol, launch grid in threads) of every timed launch;
-    a split prefill is several launches of one unit (the state-only walk of
+def prefill_unit_kernels(key, shp, pro=False):
+    """(unit key, kernel symbol, grid in threads) of the launches of one
+    prefill call; a split prefill is several launches (the state-only walk of
     the first half, in two parts joined by the combine kernel when it is long
     enough, then both halves)."""
+    Bt, L, H, P, N, R, rope = shp
+    out = []
+    if prefill_split(*shp):
+        two = prefill_two_part(*shp)
+        out.append((key, prefill_kernel_name(*shp, state_only=True, pro=pro), (2 if two else 1) * Bt * H * 512))
+        if two:
+            out.append((key, COMBINE_KERNEL, Bt * H * 256))  # grid x; y = 8 parts
+        out.append((key, prefill_kernel_name(*shp, pro=pro), 2 * Bt * H * 512))
+    else:
+        out.append((key, prefill_kernel_name(*shp, pro=pro), Bt * H * 512))
+    return out
+
+
+def unit_kernels():
+    """(unit key, kernel symbol, launch grid in threads) of every timed launch
+    of the plain workloads."""
     out = []
     for name, shp in prefill_shapes().items():
-        Bt, L, H, P, N, R, rope = shp
-        if prefill_split(*shp):
-            two = prefill_two_part(*shp)
-            out.append(("prefill_" + name, prefill_kernel_name(*shp, state_only=True), (2 if two else 1) * Bt * H * 512))
-            if two:
-                out.append(("prefill_" + name, COMBINE_KERNEL, Bt * H * 256))  # grid x; y = 8 parts
-            out.append(("prefill_" + name, prefill_kernel_name(*shp), 2 * Bt * H * 512))
-        else:
-            out.append(("prefill_" + name, prefill_kernel_name(*shp), Bt * H * 512))
+        out += prefill_unit_kernels("prefill_" + name, shp)
     Bt, H, P, N, R = DECODE_SHAPE
     out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
     Bt, H, P, N, R = DECODE_SHAPE_BIG
@@ -128,22 +141,31 @@ def unit_kernels():
     return out
 
 
-def variant_unit_kernels():
-    """unit_kernels() of the variant lines (same kernels as their workloads)."""
-    base = {u: [] for u, _, _ in unit_kernels()}
-    for u, k, g in unit_kernels():
-        base[u].append((k, g))
-    return [("prefill_" + line, k, g) for line, wl, _ in VARIANTS for k, g in base["prefill_" + wl]]
+# counter groups of the variant lines: within a group every line runs
+# distinct kernels (symbol and grid), so counter rows map to lines
+GROUPS = {"variants": [v for v in VARIANTS if v[2] != "pro"], "prologue": [v for v in VARIANTS if v[2] == "pro"]}
 
 
-def prefill_algo(Bt, L, H, P, N, R, rope, omega=False, a_tok=False):
+def variant_unit_kernels(group=None):
+    """unit_kernels() of the variant lines of `group` (all when None): the
+    kernels of their workloads, compiled with the prologue for mode "pro"."""
+    out = []
+    for line, wl, mode in (VARIANTS if group is None else GROUPS[group]):
+        out += prefill_unit_kernels("prefill_" + line, prefill_shapes()[wl], pro=mode == "pro")
+    return out
+
+
+def prefill_algo(Bt, L, H, P, N, R, rope, omega=False, a_tok=False, pro=False):
     """Algorithmic bytes (each input read once, each output written once) and
     MFMA flops (chunked-scan count 2L[Q R^2 (N+P) + 2 R N P] per (b,h), Q = 64/R).
     omega: the angles come as rates per token shared by the heads; a_tok: A is
-    given per token."""
+    given per token; pro: the prologue's gains [2][N], biases [2][H][R][N] and
+    step biases [H] are read too."""
     bf, f4 = 2, 4
     tok = Bt * L * H
     byts = tok * R * (P + 2 * N) * bf + tok * 2 * f4 + (tok if a_tok else H) * f4   # x, B, C, dt, lam, A
+    if pro:
+        byts += (2 * N + 2 * H * R * N + H) * f4
     if rope:
         byts += (Bt * L if omega else tok) * (N // 2) * f4        # omega or theta
     byts += tok * R * P * bf                                      # y
@@ -191,12 +213,24 @@ def time_prefill(torch, ops, inp, steps, warmup, mode="", flushed=True):
     nws = ops.prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=inp["x"].dtype, rope=inp["theta"] is not None)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else False
 
-    theta, omega = (None, inp["omega"]) if mode == "omega" else (inp["theta"], None)
+    theta, omega = (None, inp["omega"]) if mode in ("omega", "pro") else (inp["theta"], None)
     A, a_tok = (None, inp["A_tok"]) if mode == "atok" else (inp["A"], None)
+    dt, pro = inp["dt"], {}
+    if mode == "pro":  # raw step and pre-norm B, C; gains and biases drawn on the device
+        g = torch.Generator(device="cuda")
+        g.manual_seed(20260200)
+        R_ = inp["x"].shape[3]
+        dt = inp["dt_raw"]
+        pro = dict(bc_norm=True, bc_eps=1e-6, dt_softplus=True,
+                   B_norm_w=torch.rand((N,), generator=g, device="cuda") + 0.5,
+                   C_norm_w=torch.rand((N,), generator=g, device="cuda") + 0.5,
+                   B_bias=torch.randn((H, R_, N), generator=g, device="cuda") * 0.3,
+                   C_bias=torch.randn((H, R_, N), generator=g, device="cuda") * 0.3,
+                   dt_bias=torch.randn((H,), generator=g, device="cuda") * 0.5)
 
     def run():
-        ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], inp["dt"], inp["lam"], A, theta,
-                           y=y, h_final=hf, workspace=ws, omega=omega, A_tok=a_tok, head_major=hm)
+        ops.m3_ssm_prefill(inp["x"], inp["B"], inp["C"], dt, inp["lam"], A, theta,
+                           y=y, h_final=hf, workspace=ws, omega=omega, A_tok=a_tok, head_major=hm, **pro)
 
     for _ in range(max(warmup, 1)):
         run()
@@ -478,7 +512,9 @@ def algo_bytes():
     for name, shp in prefill_shapes().items():
         algo["prefill_" + name] = prefill_algo(*shp)[0]
     for line, wl, mode in VARIANTS:
-        algo["prefill_" + line] = prefill_algo(*prefill_shapes()[wl], omega=mode == "omega", a_tok=mode == "atok")[0]
+        shp = prefill_shapes()[wl]
+        algo["prefill_" + line] = prefill_algo(*shp, omega=mode == "omega" or (mode == "pro" and shp[-1]),
+                                               a_tok=mode == "atok", pro=mode == "pro")[0]
     algo["decode"] = decode_algo(*DECODE_SHAPE, True)[0]
     algo["decode_bt512"] = decode_algo(*DECODE_SHAPE_BIG, True)[0]
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
@@ -525,7 +561,7 @@ def report_pmc(groups):
         lines.append(f"Group {group}: a plain elementwise copy (negation) of {COPY_BYTES} B reads FETCH_SIZE = "
                      f"{cf:.4g} B and WRITE_SIZE = {cw:.4g} B, so the factors are {sf:.4f} (fetch) and "
                      f"{sw:.4f} (write).")
-        uk = unit_kernels() if group == "base" else variant_unit_kernels()
+        uk = unit_kernels() if group == "base" else variant_unit_kernels(group)
         for unit, k, g in uk:
             fv, wv = find(fetch, k, g), find(write, k, g)
             if not fv or not wv:
@@ -639,7 +675,7 @@ def pmc_workload(torch, ops, group):
     if group == "base":
         runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
     else:
-        runs = [(line, prefill_shapes()[wl], mode) for line, wl, mode in VARIANTS]
+        runs = [(line, prefill_shapes()[wl], mode) for line, wl, mode in GROUPS[group]]
     for i, (name, shp, mode) in enumerate(runs):
         print(f"# counter workload: prefill {name}", file=sys.stderr, flush=True)
         inp = gen_prefill(torch, *shp, seed=20260100 + i)
@@ -665,7 +701,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "headline", "pmc"), default="all")
-    ap.add_argument("--group", choices=("base", "variants"), default="base")
+    ap.add_argument("--group", choices=("base", "variants", "prologue"), default="base")
     ap.add_argument("--report-trace", metavar="PREFIX")
     ap.add_argument("--report-pmc", nargs="+", metavar="GROUP FETCH_PREFIX WRITE_PREFIX")
     ap.add_argument("--report-mfma", metavar="PREFIX")
@@ -726,10 +762,14 @@ def main():
             inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260100 + i)
             torch.cuda.synchronize()
             ms, launch_ms, flushed = time_prefill(torch, ops, inp, args.steps, args.warmup, mode)
-            byts, flops = prefill_algo(*shp, omega=mode == "omega", a_tok=mode == "atok")
-            angles = "RoPE, angles from rates" if mode == "omega" else ("RoPE" if rope else "real")
+            byts, flops = prefill_algo(*shp, omega=mode == "omega" or (mode == "pro" and rope),
+                                       a_tok=mode == "atok", pro=mode == "pro")
+            angles = "RoPE, angles from rates" if (mode == "omega" or (mode == "pro" and rope)) else (
+                "RoPE" if rope else "real")
             if mode == "atok":
                 angles += ", A per token"
+            if mode == "pro":
+                angles += ", prologue fused (B/C RMS norm with gains and head biases, Delta = softplus(raw + bias))"
             res = dict(workload=f"prefill {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
                                 f"{angles} bf16 chunk {Q_ROWS // R}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, kernel_ms=launch_ms,

@@ -121,7 +121,42 @@ typedef enum m3_layout {
  * above).  The arithmetic is the same, so both layouts give identical bits;
  * head-major reads each (batch, head) walk as one contiguous run.  Other
  * values are M3_ERR_INVALID_ARG.
+ * Prologue (optional steps fused in front of the core; all off when zero /
+ * NULL), see m3_prologue below: the B and C given are then the raw
+ * projections and dt the raw step.
  */
+/*
+ * The steps just before the SSM core, computed on chip ("Znakomstvo s
+ * Mamba-3" (chernovdev.ru), sec. "Architecture and normalisation": RMS
+ * normalisation of the B and C projections, by analogy with QK normalisation,
+ * then learnable head-specific biases added to B and C after it; "Mamba-3:
+ * un modello a spazio di stato progettato per l'inferenza" (cartesia.ai),
+ * "Normalizzazioni" and "Addio convoluzione corta"):
+ *   bc_norm      0 or 1: each (token, head, rank) row of B and of C, an
+ *                N-vector, becomes row / sqrt(mean(row^2) + bc_eps) times the
+ *                gain B_norm_w / C_norm_w [N] (NULL = 1); a row of zeros stays
+ *                zero.  bc_eps >= 0.
+ *   B_bias, C_bias  [H, R, N] float32 added after the normalisation (or to
+ *                the raw B / C without it), or NULL.
+ *   dt_softplus  0 or 1: Delta = softplus(dt + dt_bias[h]) (dt_bias [H] or
+ *                NULL; needs dt_softplus), the step made positive on chip.
+ * The rotation (RoPE) applies to the normalised and biased B and C, and the
+ * carried B (Bprev_rot, Bprev_rot_out) is that rotated B.  Gains and biases
+ * must be 4-byte aligned.  Other values are M3_ERR_INVALID_ARG; bf16 calls
+ * whose LDS with the B/C table exceeds a CU return M3_ERR_UNSUPPORTED
+ * (RoPE at N = 128, P = 64 with R >= 4).
+ */
+typedef struct m3_prologue {
+  int32_t bc_norm;
+  int32_t dt_softplus;
+  float bc_eps;
+  const float* B_norm_w;
+  const float* C_norm_w;
+  const float* B_bias;
+  const float* C_bias;
+  const float* dt_bias;
+} m3_prologue;
+
 typedef struct m3_prefill_args {
   int32_t Bt, L, H, P, N, R, chunk;
   int32_t in_dtype; /* m3_dtype */
@@ -146,6 +181,7 @@ typedef struct m3_prefill_args {
   const float* omega;     /* [Bt, L, N/2] angular rates, or NULL (see above) */
   const float* A_tok;     /* [Bt, L, H] A per token, or NULL (see above) */
   int32_t layout;         /* m3_layout of x, B, C, y (see above) */
+  m3_prologue pro;        /* steps fused in front of the core (zeros = none) */
 } m3_prefill_args;
 
 int m3_ssm_prefill(const m3_prefill_args* args, void* stream);
@@ -212,6 +248,8 @@ int m3_ssm_prefill_noalloc(const m3_prefill_args* args, void* stream);
  *   Out: y [Bt, H, R, P] in_dtype.
  * Sizes: N, P in {16, 32, 64, 128}; R in 1..16.  A fresh sequence starts with
  * h = 0 (or any state), Bprev_rot = 0, xprev = 0, phi = 0.
+ * pro: the same prologue as the prefill's (B, C, dt raw), so that a decode
+ * continues a prefill that used it.
  */
 typedef struct m3_decode_args {
   int32_t Bt, H, P, N, R;
@@ -230,6 +268,7 @@ typedef struct m3_decode_args {
   void* y;
   const float* A_tok; /* [Bt, H] A of this token, or NULL */
   const float* omega; /* [Bt, N/2] rotation rates shared by the heads, or NULL */
+  m3_prologue pro;    /* steps fused in front of the core (zeros = none) */
 } m3_decode_args;
 
 int m3_ssm_decode_step(const m3_decode_args* args, void* stream);

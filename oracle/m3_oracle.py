@@ -92,11 +92,15 @@ def rms_norm(v, weight=None, eps=0.0):
 
     [CH] sec. "Architecture and normalisation": B and C are RMS-normalised, by
     analogy with QK normalisation in Transformers.  For B, C of shape
-    [..., R, N] each rank column (an N-vector) is normalised on its own.
+    [..., R, N] each rank column (an N-vector) is normalised on its own.  A
+    row of zeros is returned as zeros (a reading: with eps = 0 the quotient
+    is undefined there; with eps > 0 it is zero anyway).
     """
     v = _f64(v)
     ms = np.mean(v * v, axis=-1, keepdims=True)
-    out = v / np.sqrt(ms + eps)
+    den = np.sqrt(ms + eps)
+    # a row of zeros stays zero (also with eps = 0, where 0/0 is undefined)
+    out = np.divide(v, den, out=np.zeros_like(v), where=ms > 0)
     if weight is not None:
         out = out * _f64(weight)
     return out

@@ -24,6 +24,11 @@ _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 
 
+class Prologue(ctypes.Structure):
+    _fields_ = [("bc_norm", _i32), ("dt_softplus", _i32), ("bc_eps", ctypes.c_float),
+                ("B_norm_w", _vp), ("C_norm_w", _vp), ("B_bias", _vp), ("C_bias", _vp), ("dt_bias", _vp)]
+
+
 class PrefillArgs(ctypes.Structure):
     _fields_ = [
         ("Bt", _i32), ("L", _i32), ("H", _i32), ("P", _i32), ("N", _i32), ("R", _i32), ("chunk", _i32),
@@ -32,7 +37,7 @@ class PrefillArgs(ctypes.Structure):
         ("h0", _vp), ("Bprev_rot", _vp), ("xprev", _vp), ("phi0", _vp),
         ("y", _vp), ("h_final", _vp), ("Bprev_rot_out", _vp), ("xprev_out", _vp), ("phi_out", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t), ("omega", _vp), ("A_tok", _vp),
-        ("layout", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("pro", Prologue),
     ]
 
 
@@ -41,7 +46,7 @@ class DecodeArgs(ctypes.Structure):
         ("Bt", _i32), ("H", _i32), ("P", _i32), ("N", _i32), ("R", _i32), ("in_dtype", _i32),
         ("h", _vp), ("phi", _vp), ("Bprev_rot", _vp), ("xprev", _vp),
         ("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp), ("lam", _vp), ("A", _vp), ("theta", _vp),
-        ("y", _vp), ("A_tok", _vp), ("omega", _vp),
+        ("y", _vp), ("A_tok", _vp), ("omega", _vp), ("pro", Prologue),
     ]
 
 

@@ -15,8 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libm3ssm.so")
-SOURCES = ["api.hip", "angles.hip", "decode.hip", "split.hip", "prefill_bf16.hip", "prefill_bf16_n16.hip",
-           "prefill_bf16_n32.hip", "prefill_bf16_n64.hip", "prefill_bf16_n128.hip", "prefill_f32.hip"]
+# the largest units first, so the parallel build ends sooner
+SOURCES = ["prefill_bf16_n128.hip", "prefill_bf16_n128_pro.hip", "prefill_bf16_n64.hip", "prefill_bf16_n64_pro.hip",
+           "prefill_bf16_n32.hip", "prefill_bf16_n32_pro.hip", "prefill_bf16_n16.hip", "prefill_bf16_n16_pro.hip",
+           "prefill_f32.hip", "decode.hip", "api.hip", "angles.hip", "split.hip", "prefill_bf16.hip"]
 ARCH = "gfx950"
 
 

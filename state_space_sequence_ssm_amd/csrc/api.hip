@@ -55,6 +55,29 @@ struct SplitPlan {
   size_t oH = 0, oB = 0, oX = 0, oPhi = 0, bytes = 0;
 };
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// The prologue's options are 0 or 1, eps finite and >= 0, gains only with the
+// normalisation, the step's bias only with the softplus, pointers 4-aligned.
+bool prologue_ok(const m3_prologue& q) {
+  if ((q.bc_norm != 0 && q.bc_norm != 1) || (q.dt_softplus != 0 && q.dt_softplus != 1)) return false;
+  if (!(q.bc_eps >= 0.f) || q.bc_eps > 3.0e38f) return false;  // also rejects NaN
+  if (!q.bc_norm && (q.B_norm_w != nullptr || q.C_norm_w != nullptr)) return false;
+  if (!q.dt_softplus && q.dt_bias != nullptr) return false;
+  return al4(q.B_norm_w) && al4(q.C_norm_w) && al4(q.B_bias) && al4(q.C_bias) && al4(q.dt_bias);
+}
+bool prologue_bc(const m3_prologue& q) { return q.bc_norm != 0 || q.B_bias != nullptr || q.C_bias != nullptr; }
+m3::Prologue to_internal(const m3_prologue& q) {
+  m3::Prologue r{};
+  r.bc_norm = q.bc_norm;
+  r.dt_softplus = q.dt_softplus;
+  r.eps = q.bc_eps;
+  r.B_w = q.B_norm_w;
+  r.C_w = q.C_norm_w;
+  r.B_bias = q.B_bias;
+  r.C_bias = q.C_bias;
+  r.dt_bias = q.dt_bias;
+  return r;
+}
 SplitPlan split_plan(const m3_prefill_args* a) {
   SplitPlan s;
   if (a->in_dtype != M3_BF16 || a->R < 1 || a->R > 8) return s;
@@ -122,6 +145,7 @@ int check_prefill(const m3_prefill_args* a) {
   for (const void* p : v16)
     if (!al16(p)) return M3_ERR_INVALID_ARG;
   if (!al4(a->dt) || !al4(a->lam) || !al4(a->A) || !al4(a->A_tok)) return M3_ERR_INVALID_ARG;
+  if (!prologue_ok(a->pro)) return M3_ERR_INVALID_ARG;
   const double elems = double(a->Bt) * a->L * a->H * a->R * (a->N > a->P ? a->N : a->P);
   if (elems > 4.0e18 || double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
   const bool bf16 = a->in_dtype == M3_BF16;
@@ -133,7 +157,7 @@ int check_prefill(const m3_prefill_args* a) {
     const double itemTh = double(a->L) * a->H * (a->N / 2) * 4.0;
     if (item > 2147483000.0 || itemTh > 2147483000.0) return M3_ERR_UNSUPPORTED;
   }
-  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, rope)
+  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, a->R, rope, prologue_bc(a->pro))
                           : m3::prefill_lds_bytes_f32(a->N, a->P, rope);
   if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
   return M3_OK;
@@ -159,6 +183,7 @@ int run_prefill(const m3_prefill_args* a, void* ws_ptr, size_t ws_bytes, void* s
   p.nseg = 1;
   p.segLen = a->L;
   p.headMajor = a->layout == M3_HEAD_MAJOR;
+  p.pro = to_internal(a->pro);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (!bf16) return hip_status(m3::launch_prefill_f32(p, st));
 
@@ -198,6 +223,8 @@ int run_prefill(const m3_prefill_args* a, void* ws_ptr, size_t ws_bytes, void* s
     c.t1 = sp.segA;
     c.t2 = sp.segLen;
     c.dt = a->dt; c.lam = a->lam; c.A = a->A; c.A_tok = a->A_tok;
+    c.dt_softplus = a->pro.dt_softplus;
+    c.dt_bias = a->pro.dt_bias;
     c.h = hMid;
     c.Bprev = bMid;
     c.x0 = xMid;
@@ -292,6 +319,7 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   for (const void* p : v16)
     if (!al16(p)) return M3_ERR_INVALID_ARG;
   if (!al4(a->dt) || !al4(a->lam) || !al4(a->A) || !al4(a->A_tok)) return M3_ERR_INVALID_ARG;
+  if (!prologue_ok(a->pro)) return M3_ERR_INVALID_ARG;
   if (double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
   m3::DecodeParams p{};
   p.Bt = a->Bt; p.H = a->H; p.P = a->P; p.N = a->N; p.R = a->R;
@@ -301,6 +329,7 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   p.y = a->y;
   p.A_tok = a->A_tok;
   p.omega = a->omega;
+  p.pro = to_internal(a->pro);
   return hip_status(m3::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -112,6 +112,16 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int width) {
   return v;
 }
 
+// softplus(z) = log(1 + e^z): the positive step Delta from its raw value
+// (for z > 15, e^-z is below half an fp32 ulp of z).
+__device__ __forceinline__ float softplus_f(float z) { return z > 15.f ? z : log1pf(__expf(z)); }
+
+// Delta of one token with the prologue's options: softplus of raw + bias, or
+// the value as given.  Tokens past the end (`valid` false) have Delta = 0.
+__device__ __forceinline__ float delta_of(float raw, bool softplus, float bias, bool valid) {
+  return !valid ? 0.f : (softplus ? softplus_f(raw + bias) : raw);
+}
+
 // Reduce an angle modulo 2*pi into [-pi, pi].
 __device__ __forceinline__ float wrap_angle(float a) {
   return a - kTwoPi * rintf(a * kInvTwoPi);

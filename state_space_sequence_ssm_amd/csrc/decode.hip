@@ -40,6 +40,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
   float* sPhi = sCS + N;             // new angle (wrapped)   [N/2]
   float* sBr = sPhi + N / 2;         // raw B_t               [R][N]
   float* sCr = sBr + R * N;          // raw C_t               [R][N]
+  float* sScale = sCr + R * N;       // 1 / RMS of the B, C rows (prologue)  [2][R]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -105,8 +106,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
     T* xprev = static_cast<T*>(p.xprev) + vecP;
     float* Bprev = p.Bprev_rot + vecN;
     float* h = p.h + static_cast<size_t>(bh) * N * P;
-    const float dt = p.dt[bh];
+    // Delta: softplus of the raw value plus the head's bias with the prologue
+    const bool proDt = p.pro.dt_softplus != 0;
+    const float dt = delta_of(p.dt[bh], proDt, proDt && p.pro.dt_bias != nullptr ? p.pro.dt_bias[hh] : 0.f, true);
     const float lm = p.lam[bh];
+    const bool proNorm = p.pro.bc_norm != 0;
+    const bool proBC = proNorm || p.pro.B_bias != nullptr || p.pro.C_bias != nullptr;
     const float alpha = __expf(dt * (p.A_tok != nullptr ? p.A_tok[bh] : p.A[hh]));
     const float beta = (1.f - lm) * dt * alpha;
     const float gamma = lm * dt;
@@ -139,12 +144,42 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
       }
     }
     __syncthreads();
+    // prologue: 1 / RMS of each rank's row of B (i < R) and C (i >= R), one
+    // row per wave at a time, lanes striding over N (a row of zeros stays zero)
+    if (proNorm) {
+      for (int i = wave; i < 2 * R; i += kDecThreads / 64) {
+        const float* row = (i < R ? sBr : sCr) + (i % R) * N;
+        float ss = 0.f;
+        for (int n = lane; n < N; n += 64) ss += row[n] * row[n];
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        if (lane == 0) sScale[i] = ss > 0.f ? rsqrtf(ss * (1.f / N) + p.pro.eps) : 0.f;
+      }
+      __syncthreads();
+    }
     // rotate B_t, C_t pairwise; write carry-out Btil_t, x_t, Phi
     for (int e = tid; e < R * (N / 2); e += kDecThreads) {
       const int r = e / (N / 2);
       const int j = e % (N / 2);
       float b0 = sBr[r * N + 2 * j], b1 = sBr[r * N + 2 * j + 1];
       float c0 = sCr[r * N + 2 * j], c1 = sCr[r * N + 2 * j + 1];
+      if (proBC) {  // normalised (gain, 1 / RMS) and biased as in the prefill
+        const size_t ob = (static_cast<size_t>(hh) * R + r) * N + 2 * j;
+        if (proNorm) {
+          const float sb = sScale[r], scl = sScale[R + r];
+          b0 *= sb * (p.pro.B_w != nullptr ? p.pro.B_w[2 * j] : 1.f);
+          b1 *= sb * (p.pro.B_w != nullptr ? p.pro.B_w[2 * j + 1] : 1.f);
+          c0 *= scl * (p.pro.C_w != nullptr ? p.pro.C_w[2 * j] : 1.f);
+          c1 *= scl * (p.pro.C_w != nullptr ? p.pro.C_w[2 * j + 1] : 1.f);
+        }
+        if (p.pro.B_bias != nullptr) {
+          b0 += p.pro.B_bias[ob];
+          b1 += p.pro.B_bias[ob + 1];
+        }
+        if (p.pro.C_bias != nullptr) {
+          c0 += p.pro.C_bias[ob];
+          c1 += p.pro.C_bias[ob + 1];
+        }
+      }
       if (rope) {
         const float c = sCS[2 * j], sn = sCS[2 * j + 1];
         const float rb0 = c * b0 + sn * b1, rb1 = -sn * b0 + c * b1;
@@ -226,7 +261,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeParams p
 
 template <typename T, int N, int P>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
-  const size_t lds = sizeof(float) * (5 * p.R * N + 6 * p.R * P + N + N / 2);
+  const size_t lds = sizeof(float) * (5 * p.R * N + 6 * p.R * P + N + N / 2 + 2 * p.R);
   if (p.R <= 4)
     hipLaunchKernelGGL((decode_step_kernel<T, N, P, 4>), dim3(p.Bt * p.H), dim3(kDecThreads), lds, s, p);
   else

@@ -25,6 +25,21 @@ inline hipError_t allow_lds(const void* fn, size_t max_bytes, std::atomic<uint64
   return e;
 }
 
+// Steps fused in front of the core (all off when zero / null):
+//   Delta = softplus(dt + dt_bias[h]) when dt_softplus (dt is then the raw
+//   value); each (token, head, rank) row of B and of C RMS-normalised over N,
+//   row / sqrt(mean(row^2) + eps) times the gain w[N], when bc_norm; then the
+//   head-specific biases [H, R, N] added to B and C.
+struct Prologue {
+  int bc_norm, dt_softplus;
+  float eps;
+  const float* B_w;     // [N] or null (gain 1)
+  const float* C_w;     // [N] or null
+  const float* B_bias;  // [H, R, N] or null
+  const float* C_bias;  // [H, R, N] or null
+  const float* dt_bias; // [H] or null
+};
+
 struct DecodeParams {
   int Bt, H, P, N, R;
   bool bf16;
@@ -42,6 +57,7 @@ struct DecodeParams {
   void* y;
   const float* A_tok;  // [Bt, H] A of this token, or null (then A [H])
   const float* omega;  // [Bt, N/2] rates shared by the heads (theta = dt * omega), or null
+  Prologue pro;
 };
 
 struct PrefillParams {
@@ -85,6 +101,7 @@ struct PrefillParams {
   const float* phi_mid;
   // x, B, C, y head-major [Bt, H, L, R, .] instead of token-major (bf16 path)
   int headMajor;
+  Prologue pro;
 };
 
 struct AnglesParams {
@@ -108,14 +125,18 @@ struct CombineParams {
   const float* lam;
   const float* A;
   const float* A_tok;  // [Bt, L, H] or null
+  int dt_softplus;     // dt holds raw values: Delta = softplus(dt + dt_bias[h])
+  const float* dt_bias;
   float* h;        // [2][Bt*H][N][P]: segment 0 end state -> joined state
   float* Bprev;    // [2][Bt*H][R][N]: segment 1's (relative frame) -> rotated in place
   const void* x0;  // [Bt*H][R][P] bf16: segment 0's last x
   float* phi;      // [2][Bt*H][N/2] or null: segment 1's relative angle -> absolute
 };
 hipError_t launch_split_combine(const CombineParams& c, hipStream_t s);
-// LDS bytes the prefill kernel needs for (N, P, rope); 0 if not compiled.
-size_t prefill_lds_bytes_bf16(int N, int P, bool rope);
+// LDS bytes the prefill kernel needs for (N, P, rope) and, with `pro_bc`
+// (B/C normalisation or biases), for its prologue table at rank R; 0 if not
+// compiled.
+size_t prefill_lds_bytes_bf16(int N, int P, int R, bool rope, bool pro_bc);
 size_t prefill_lds_bytes_f32(int N, int P, bool rope);
 
 }  // namespace m3

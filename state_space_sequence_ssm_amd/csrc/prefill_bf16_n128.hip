@@ -1,8 +1,8 @@
-// bf16 prefill instantiations for N = 128 (prefill_pc_impl.hpp).
+// bf16 prefill instantiations for N = 128, plain core (prefill_pc_impl.hpp).
 #include "prefill_pc_launch.hpp"
 
 namespace m3 {
 hipError_t launch_prefill_bf16_n128(const PrefillParams& p, bool state_only, hipStream_t s) {
-  return pc::launch_n<128>(p, state_only, s);
+  return pc::launch_n<128, false>(p, state_only, s);
 }
 }  // namespace m3

@@ -1,8 +1,8 @@
-// bf16 prefill instantiations for N = 64 (prefill_pc_impl.hpp).
+// bf16 prefill instantiations for N = 64, plain core (prefill_pc_impl.hpp).
 #include "prefill_pc_launch.hpp"
 
 namespace m3 {
 hipError_t launch_prefill_bf16_n64(const PrefillParams& p, bool state_only, hipStream_t s) {
-  return pc::launch_n<64>(p, state_only, s);
+  return pc::launch_n<64, false>(p, state_only, s);
 }
 }  // namespace m3

@@ -137,6 +137,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const bool rope = p.theta != nullptr || om;
   const float Ah = p.A_tok != nullptr ? 0.f : p.A[hh];
   const int nch = (L + Q - 1) / Q;
+  // steps fused in front of the core (normalisation and biases of B and C
+  // while staging, Delta = softplus(raw + bias) in the decay scan)
+  const bool proNorm = p.pro.bc_norm != 0;
+  const bool proBC = proNorm || p.pro.B_bias != nullptr || p.pro.C_bias != nullptr;
+  const bool proDt = p.pro.dt_softplus != 0;
+  const float dtBias = proDt && p.pro.dt_bias != nullptr ? p.pro.dt_bias[hh] : 0.f;
 
   const T* xg = static_cast<const T*>(p.x);
   const T* Bg = static_cast<const T*>(p.B);
@@ -153,12 +159,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   u32x4 raw[Lt::JS][4];
   f32x4 rawTh[Lt::TS];
   float rdt = 0.f, rlam = 0.f, rdtn = 0.f, rlamn = 0.f, rA = 0.f;
+  bool vdt = false, vdtn = false;  // the token (and the next one) exist
 
   auto issue_loads = [&](int c) {
     const int s0 = c * Q;
 #pragma unroll
     for (int s = 0; s < Lt::JS; ++s) {
       const int j = tid + s * kThreads;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) raw[s][k] = u32x4{0u, 0u, 0u, 0u};
       if (j < Lt::JOBS) {
         const T* base;
         int D, idx;
@@ -200,6 +209,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const int t = s0 + lane;
       rdt = rlam = rdtn = rlamn = 0.f;
       rA = Ah;
+      vdt = lane < Q && t < L;
+      vdtn = lane < Q && t + 1 < L;
       if (lane < Q && t < L) {
         const size_t o = (static_cast<size_t>(b) * L + t) * H + hh;
         rdt = p.dt[o];
@@ -216,18 +227,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   // stage A: per-token scalars (wave 0) and raw angles into LDS
   auto stage_scalars = [&]() {
     if (wave == 0) {
-      const float v = rdt * rA;
+      const float d = delta_of(rdt, proDt, dtBias, vdt), dn = delta_of(rdtn, proDt, dtBias, vdtn);
+      const float v = d * rA;
       const float lamc = wave_inclusive_scan(v, 64);
       const float lamEnd = __shfl(lamc, Q - 1, 64);
-      const float gam = rlam * rdt;
-      const float del = gam + (1.f - rlamn) * rdtn;
+      const float gam = rlam * d;
+      const float del = gam + (1.f - rlamn) * dn;
       if (lane < Q) {
         sLam[lane] = lamc;
         sGam[lane] = gam;
         sDel[lane] = del;
         sW[lane] = __expf(lamEnd - lamc) * del;
         sDec[lane] = __expf(lamc);
-        sDt[lane] = rdt;
+        sDt[lane] = d;
       }
       if (lane == 0) sChunkDec[0] = __expf(lamEnd);
     }
@@ -264,18 +276,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int s = 0; s < Lt::JS; ++s) {
       const int j = tid + s * kThreads;
+      const int kind = j < Lt::JB ? 0 : (j < 2 * Lt::JB ? 1 : 2);
+      const int idx = kind == 0 ? j : (kind == 1 ? j - Lt::JB : j - 2 * Lt::JB);
+      const int D = kind == 2 ? P : N;
+      const int cpr = D / VE;
+      const int rb = idx / cpr, cb = idx % cpr;
+      const int c0 = cb * VE;
+      float v[4][VE];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[k][q] = __uint_as_float(raw[s][k][q]);
+      // prologue: a row of B or C is N / VE consecutive lanes (aligned: B and C
+      // jobs start at multiples of 64), reduced with shuffles on every lane
+      float scl[4] = {1.f, 1.f, 1.f, 1.f};
+      if (proNorm) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float ss = 0.f;
+#pragma unroll
+          for (int q = 0; q < VE; ++q) ss += v[k][q] * v[k][q];
+#pragma unroll
+          for (int off = 1; off < N / VE; off <<= 1) ss += __shfl_xor(ss, off);
+          scl[k] = ss > 0.f ? rsqrtf(ss * (1.f / N) + p.pro.eps) : 0.f;
+        }
+      }
       if (j < Lt::JOBS) {
-        const int kind = j < Lt::JB ? 0 : (j < 2 * Lt::JB ? 1 : 2);
-        const int idx = kind == 0 ? j : (kind == 1 ? j - Lt::JB : j - 2 * Lt::JB);
-        const int D = kind == 2 ? P : N;
-        const int cpr = D / VE;
-        const int rb = idx / cpr, cb = idx % cpr;
-        const int c0 = cb * VE;
-        float v[4][VE];
+        if (proBC && kind < 2) {
+          const float* w = kind == 0 ? p.pro.B_w : p.pro.C_w;
+          const float* bias = kind == 0 ? p.pro.B_bias : p.pro.C_bias;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+          for (int k = 0; k < 4; ++k) {
+            const size_t ob = (static_cast<size_t>(hh) * R + ((4 * rb + k) & (R - 1))) * N + c0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[k][q] = __uint_as_float(raw[s][k][q]);
+            for (int q = 0; q < VE; ++q) {
+              if (proNorm) v[k][q] *= scl[k] * (w != nullptr ? w[c0 + q] : 1.f);
+              if (bias != nullptr) v[k][q] += bias[ob + q];
+            }
+          }
+        }
         if (kind < 2 && rope) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -369,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   {
     // H'_{-1} = h0 + (1 - lambda_0) Delta_0 sum_r Bprev_rot[r] xprev[r]^T
     const size_t o0 = static_cast<size_t>(b) * L * H + hh;
-    const float coef = (1.f - p.lam[o0]) * p.dt[o0];
+    const float coef = (1.f - p.lam[o0]) * delta_of(p.dt[o0], proDt, dtBias, true);
     const bool hasCarry = p.Bprev_rot != nullptr && p.xprev != nullptr;
 #pragma unroll
     for (int k = 0; k < Lt::HT; ++k) {

@@ -298,13 +298,32 @@ struct PcLayout {
   static constexpr size_t oY(bool rope) { return used2(rope); }
   static constexpr size_t kBytesReal = used2(false) + (stage_y(false) ? kYBytes : 0);
   static constexpr size_t kBytesRope = used2(true) + (stage_y(true) ? kYBytes : 0);
+  // Prologue table, appended only for calls that normalise or bias B and C:
+  // head biases of B and C [2][R][N], gains [2][N], then the exchange of row
+  // sums of squares between the two waves of a row tile [2 halves][2][64].
+  static constexpr size_t proFloats(int R) { return 2 * size_t(R) * N + 2 * size_t(N) + 4 * 64; }
+  static constexpr size_t bytes(bool rope, bool pro, int R) {
+    return (rope ? kBytesRope : kBytesReal) + (pro ? proFloats(R) * 4 : 0);
+  }
+  // B and C columns of one row are staged by both waves of a row tile (whole
+  // lines at R = 1: column blocks of 64; MFMA layout at R > 1: k blocks of 32)
+  static constexpr bool rows_split(bool fl) { return fl ? NCBN > 1 : NKB > 1; }
+  static constexpr bool has_bc(bool fl, int h) {
+    for (int s = 0; s < uph(fl); ++s) {
+      const Piece pc = piece(fl, h, s);
+      if (pc.kind == 0 || pc.kind == 1) return true;
+    }
+    return false;
+  }
 };
 
 // SO (state only): the walk keeps only what the state needs -- no C, no Gram
 // tiles, no readout, no y -- and ends with h_final and the carry-out.  It
 // produces the state in the middle of a sequence so that the second half can
 // run at the same time as the first.
-template <int N, int P, int LGR, bool ROPE, bool SO = false>
+// PRO: the call uses the prologue (B / C normalisation or biases, softplus of
+// the step); without it the kernel compiles to the plain core.
+template <int N, int P, int LGR, bool ROPE, bool SO = false, bool PRO = false>
 __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   using Lt = PcLayout<N, P>;
   constexpr int R = 1 << LGR;
@@ -371,6 +390,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   const bool aTok = p.A_tok != nullptr;
   const rsrc_t rAtok = make_rsrc(aTok ? p.A_tok + tok0 * H : p.dt, uint32_t(aTok ? tokB * 4 : 0));
   const float A2 = aTok ? 0.f : p.A[hh] * kLog2e;  // decays in log2 units
+  // steps fused in front of the core: B / C normalisation and head biases
+  // (applied while staging), Delta = softplus(raw + bias) (in the decay scan)
+  const bool proNorm = PRO && p.pro.bc_norm != 0;
+  const bool proBC = PRO && (proNorm || p.pro.B_bias != nullptr || p.pro.C_bias != nullptr);
+  const bool proDt = PRO && p.pro.dt_softplus != 0;
+  const float dtBias = proDt && p.pro.dt_bias != nullptr ? p.pro.dt_bias[hh] : 0.f;
+  const float proEps = p.pro.eps;
   // angles: theta [.., H, N/2] per (token, head), or omega [.., N/2] per token
   // (shared by the heads; scaled by Delta in the angle scan)
   const bool om = ROPE && p.omega != nullptr;
@@ -390,6 +416,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   constexpr bool kStageY = !SO && LGR == 0 && Lt::stage_y(ROPE);
   u32x2* sY = reinterpret_cast<u32x2*>(smem + Lt::oY(ROPE));  // [64][PY/4] 8-byte units
   auto phiTab = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oPhi) + s * kRows * PH; };
+  // prologue table (allocated only when proBC): biases [2][R][N], gains [2][N], exchange [2][2][64]
+  float* const proTab = reinterpret_cast<float*>(smem + (ROPE ? Lt::kBytesRope : Lt::kBytesReal));
+  float* const proW = proTab + 2 * R * N;
+  float* const proEx = proW + 2 * N;
 
   // ================================================================ staging state
   // chunk c's pieces live in register set c % 2 (two chunks in flight)
@@ -457,14 +487,19 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   auto stage_small = [&](int c, int set) __attribute__((always_inline)) {
     if (wave == 0) {
       float* S = sc(c % 3);
-      const float lamc = seg_scan<64>(rdt[set] * (aTok ? rAt[set] * kLog2e : A2));
+      // Delta (softplus of raw + bias with the prologue; tokens past the end
+      // have Delta = 0, which the zero-filled loads give without it)
+      const float dl = delta_of(rdt[set], proDt, dtBias, lane < Q && c * Q + lane < L);
+      const float lamc = seg_scan<64>(dl * (aTok ? rAt[set] * kLog2e : A2));
       const float lamEnd = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lamc), Q - 1));
       // next token's Delta, lambda: lane t + 1, or token 0 of chunk c + 1 (the
       // other register set; zeros past the end, i.e. Delta_L = 0) for t = Q - 1
-      const float dNext = __shfl_down(rdt[set], 1), lNext = __shfl_down(rlam[set], 1);
-      const float d0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rdt[set ^ 1]), 0));
+      const float dNext = __shfl_down(dl, 1), lNext = __shfl_down(rlam[set], 1);
+      const float d0 = delta_of(
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rdt[set ^ 1]), 0)), proDt, dtBias,
+          (c + 1) * Q < L);
       const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rlam[set ^ 1]), 0));
-      const float gam = rlam[set] * rdt[set];
+      const float gam = rlam[set] * dl;
       const float del = gam + (1.f - (lane == Q - 1 ? l0 : lNext)) * (lane == Q - 1 ? d0 : dNext);
       S[0 * 64 + lane] = lamc;
       S[1 * 64 + lane] = gam;
@@ -472,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       S[3 * 64 + lane] = __builtin_amdgcn_exp2f(lamEnd - lamc) * del;
       S[4 * 64 + lane] = __builtin_amdgcn_exp2f(lamc);
       if (lane == 0) S[5 * 64] = __builtin_amdgcn_exp2f(lamEnd);
-      S[6 * 64 + lane] = rdt[set];  // Delta, for angles given as rates
+      S[6 * 64 + lane] = dl;  // Delta, for angles given as rates
     }
     if constexpr (ROPE) {
       float* tab = phiTab(c & 1);
@@ -525,6 +560,97 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // which spreads the load issue over the staging work.  At R = 1 the upper
   // waves refill in the second phase instead: the loads of a chunk then do not
   // all queue at its start (measured 3-5% faster).
+  // ---------------------------------------------------------------- prologue of B, C
+  // sum of squares of the 8 bf16 values of one staging piece
+  auto sumsq8 = [](u32x4 v) __attribute__((always_inline)) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a0 = __uint_as_float(v[q] << 16), a1 = __uint_as_float(v[q] & 0xffff0000u);
+      a += a0 * a0 + a1 * a1;
+    }
+    return a;
+  };
+  // Row sums of squares -> 1 / RMS of the B (k = 0) and C (k = 1) rows that
+  // this lane stages: the lanes of one row add their pieces, and where the two
+  // waves of a row tile hold different columns of a row they swap their sums
+  // through LDS (behind a workgroup barrier: both halves call this).
+  // `rowOf(s)` is the row index slot of piece s (0 .. NRS-1), `row(slot)` its row.
+  auto row_scales = [&](const u32x4 (&src)[UPH], auto HALF, auto NRS_, auto rowOf, auto rowAt, auto reduce,
+                        float (&rsc)[2][decltype(NRS_)::value]) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    constexpr int NRS = decltype(NRS_)::value;
+    float ss[2][NRS];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < NRS; ++i) ss[k][i] = 0.f;
+    if constexpr (Lt::has_bc(kFL, h)) {
+#pragma unroll
+      for (int s = 0; s < UPH; ++s) {
+        const Piece pc = Lt::piece(kFL, h, s);
+        if (pc.kind == 0 || (pc.kind == 1 && !SO)) ss[pc.kind][rowOf(pc)] += sumsq8(src[s]);
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < NRS; ++i) ss[k][i] = reduce(ss[k][i]);
+    }
+    if constexpr (Lt::rows_split(kFL)) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < NRS; ++i) proEx[(h * 2 + k) * 64 + rowAt(i)] = ss[k][i];  // same value on a row's lanes
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < NRS; ++i) ss[k][i] += proEx[((1 - h) * 2 + k) * 64 + rowAt(i)];
+    }
+    // a row of zeros (tokens past the end) stays zero: a finite scale
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < NRS; ++i) rsc[k][i] = ss[k][i] > 0.f ? rsqrtf(ss[k][i] * (1.f / N) + proEps) : 0.f;
+  };
+  // bf16 piece -> 8 fp32 values, with the prologue's gain, scale and bias
+  // applied to B / C pieces (columns past N stay zero)
+  auto unpack_pro = [&](u32x4 v, int kind, int row, int col, float scale, float (&f)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = __uint_as_float(v[q] << 16);
+      f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+    }
+    if (proBC && kind < 2 && col < N) {
+      const float* bias = proTab + (kind * R + (row & (R - 1))) * N + col;
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias), b1 = *reinterpret_cast<const f32x4*>(bias + 4);
+      if (proNorm) {
+        const float* w = proW + kind * N + col;
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w) * scale, w1 = *reinterpret_cast<const f32x4*>(w + 4) * scale;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] = f[e] * w0[e] + b0[e];
+          f[4 + e] = f[4 + e] * w1[e] + b1[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[e] += b0[e];
+          f[4 + e] += b1[e];
+        }
+      }
+    }
+  };
+  // rotate 4 pairs of fp32 values and round them to bf16
+  auto rotate_pack = [](const float (&f)[8], const float (&cs)[4], const float (&sn)[4]) __attribute__((always_inline)) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a0 = f[2 * q], a1 = f[2 * q + 1];
+      o[q] = ROPE ? pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0) : pack_bf16x2(a0, a1);
+    }
+    return o;
+  };
   auto build_slot_fl = [&](int c, u32x4 (&src)[UPH], auto HALF) __attribute__((always_inline)) {
     constexpr int h = decltype(HALF)::value;
     constexpr bool kRefill = !(kLateRefill && h == 1);
@@ -532,6 +658,18 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     uint16_t* sB = slotB(s2);
     uint16_t* sC = slotC(s2);
     const float* tab = phiTab(c & 1);
+    // whole-line pieces: piece i of a unit covers rows 16 quad + (64 / cpr) i + lane / cpr
+    constexpr int cprN = Lt::cpr(N), IPN = Lt::ipu(N);
+    float rsc[2][IPN];
+    if (proNorm)
+      row_scales(src, HALF, std::integral_constant<int, IPN>{}, [](const Piece pc) { return pc.i; },
+                 [&](int i) { return 16 * quad + (64 / cprN) * i + lane / cprN; },
+                 [](float v) {
+#pragma unroll
+                   for (int off = 1; off < cprN; off <<= 1) v += __shfl_xor(v, off);
+                   return v;
+                 },
+                 rsc);
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < UPH; ++s) {
@@ -543,7 +681,6 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       if (pc.kind == 2) {
         store_x(s2, row, col, v);
       } else {
-        u32x4 o = v;
         if constexpr (ROPE) {
           if (pc.kind == 0) {  // B precedes C of the same rows and columns: C reuses sin/cos
             const int q = col < N ? (col >> 1) : 0;
@@ -554,14 +691,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
               cs[e] = __cosf(a[e]);
             }
           }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float a0 = __uint_as_float(v[q] << 16), a1 = __uint_as_float(v[q] & 0xffff0000u);
-            o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
-          }
         }
+        float f[8];
+        unpack_pro(v, pc.kind, row, col, proNorm ? rsc[pc.kind][pc.i] : 1.f, f);
         // B and C feed the Gram tiles and the readout, B also the state
-        *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(row, col)) = o;
+        *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(row, col)) = rotate_pack(f, cs, sn);
       }
       if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
     }
@@ -573,6 +707,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     uint16_t* sB = slotB(s2);
     uint16_t* sC = slotC(s2);
     const float* tab = phiTab(c & 1);
+    // MFMA-layout pieces: every piece of this lane is row 16 quad + l16 (k blocks
+    // differ); the four lanes g of a row hold its columns 8 g .. of a k block
+    float rsc[2][1];
+    if (proNorm)
+      row_scales(src, HALF, std::integral_constant<int, 1>{}, [](const Piece) { return 0; },
+                 [&](int) { return 16 * quad + l16; },
+                 [](float v) {
+                   v += __shfl_xor(v, 16);
+                   return v + __shfl_xor(v, 32);
+                 },
+                 rsc);
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < UPH; ++s) {
@@ -592,7 +737,6 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
         continue;
       }
-      u32x4 o = v;
       if constexpr (ROPE) {
         if (pc.kind == 0) {  // B comes first for a k-block; C reuses its sin/cos
           const int q = (N >= 32 || 16 * pc.cb + 4 * g < N / 2) ? 16 * pc.cb + 4 * g : 0;
@@ -603,14 +747,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
             cs[e] = __cosf(a[e]);
           }
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a0 = __uint_as_float(v[q] << 16), a1 = __uint_as_float(v[q] & 0xffff0000u);
-          o[q] = pack_bf16x2(cs[q] * a0 + sn[q] * a1, cs[q] * a1 - sn[q] * a0);
-        }
       }
+      float f[8];
+      unpack_pro(v, pc.kind, 16 * quad + l16, col, proNorm ? rsc[pc.kind][0] : 1.f, f);
       // B and C feed the Gram tiles and the readout, B also the state
-      *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(16 * quad + l16, col)) = o;
+      *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(16 * quad + l16, col)) = rotate_pack(f, cs, sn);
       if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
     }
   };
@@ -899,7 +1040,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     constexpr int h = decltype(HALF)::value;
     constexpr int nb = kSplit && h ? NTW : 0;
     const size_t o0 = tok0 * H + hh;
-    const float coef = (1.f - p.lam[o0]) * p.dt[o0];
+    const float coef = (1.f - p.lam[o0]) * delta_of(p.dt[o0], proDt, dtBias, true);
     const bool hasCarry = cBprev != nullptr && cXprev != nullptr;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -936,6 +1077,20 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   if constexpr (ROPE)
     for (int q = tid; q < N / 2; q += kThreads)
       phiC[q] = cPhi0 != nullptr ? cPhi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
+  if (proBC) {  // this head's biases and the gains (visible after the prologue's first barrier)
+    for (int e = tid; e < 2 * R * N + 2 * N; e += kThreads) {
+      float v;
+      if (e < R * N)
+        v = p.pro.B_bias != nullptr ? p.pro.B_bias[static_cast<size_t>(hh) * R * N + e] : 0.f;
+      else if (e < 2 * R * N)
+        v = p.pro.C_bias != nullptr ? p.pro.C_bias[static_cast<size_t>(hh) * R * N + e - R * N] : 0.f;
+      else if (e < 2 * R * N + N)
+        v = p.pro.B_w != nullptr ? p.pro.B_w[e - 2 * R * N] : 1.f;
+      else
+        v = p.pro.C_w != nullptr ? p.pro.C_w[e - 2 * R * N - N] : 1.f;
+      proTab[e] = v;
+    }
+  }
   // retire the prologue's state and carry loads here, so no wait on them is
   // left for the loop to repeat every chunk
   __builtin_amdgcn_s_waitcnt(0);
@@ -1036,10 +1191,29 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   {
     const int t = L - 1;
     if (bOut != nullptr) {
+      // with the prologue, B_{L-1} normalised (1 / RMS of each rank's row in
+      // the exchange area, free after the walk) and biased as when staged
+      if (proNorm) {
+        if (tid < R) {
+          const bf16_t* src = static_cast<const bf16_t*>(p.B) + (row0 + static_cast<size_t>(t) * tsR + tid) * N;
+          float ss = 0.f;
+          for (int n = 0; n < N; ++n) {
+            const float v = bf16_to_f32(src[n].bits);
+            ss += v * v;
+          }
+          proEx[tid] = ss > 0.f ? rsqrtf(ss * (1.f / N) + proEps) : 0.f;
+        }
+        __syncthreads();
+      }
       for (int e = tid; e < R * (N / 2); e += kThreads) {
         const int r = e / (N / 2), q = e % (N / 2);
         const bf16_t* src = static_cast<const bf16_t*>(p.B) + (row0 + static_cast<size_t>(t) * tsR + r) * N;
         float a0 = bf16_to_f32(src[2 * q].bits), a1 = bf16_to_f32(src[2 * q + 1].bits);
+        if (proBC) {
+          const float sc0 = proNorm ? proEx[r] * proW[2 * q] : 1.f, sc1 = proNorm ? proEx[r] * proW[2 * q + 1] : 1.f;
+          a0 = a0 * sc0 + proTab[r * N + 2 * q];
+          a1 = a1 * sc1 + proTab[r * N + 2 * q + 1];
+        }
         if constexpr (ROPE) {
           // Phi_{L-1} is the final angle carry (reduced modulo 2 pi)
           float sn, cs;

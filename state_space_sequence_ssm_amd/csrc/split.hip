@@ -36,10 +36,12 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
   __shared__ float red[kThreads / 64];
   __shared__ float sPhi[64];
   // sum of Delta A over the second segment
+  const bool sp = c.dt_softplus != 0;
+  const float dtb = sp && c.dt_bias != nullptr ? c.dt_bias[hh] : 0.f;
   float sdt = 0.f;
   for (int t = c.t1 + tid; t < c.t2; t += kThreads) {
     const size_t o = (static_cast<size_t>(b) * c.Lfull + t) * c.H + hh;
-    sdt += c.dt[o] * (c.A_tok != nullptr ? c.A_tok[o] : 1.f);
+    sdt += delta_of(c.dt[o], sp, dtb, true) * (c.A_tok != nullptr ? c.A_tok[o] : 1.f);
   }
   for (int o = 32; o > 0; o >>= 1) sdt += __shfl_xor(sdt, o);
   if ((tid & 63) == 0) red[tid >> 6] = sdt;
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void split_combine_kernel(CombineParams c
   for (int w = 0; w < kThreads / 64; ++w) tot += red[w];
   const float decay = __expf(c.A_tok != nullptr ? tot : c.A[hh] * tot);
   const size_t o1 = (static_cast<size_t>(b) * c.Lfull + c.t1) * c.H + hh;
-  const float coef = (1.f - c.lam[o1]) * c.dt[o1];
+  const float coef = (1.f - c.lam[o1]) * delta_of(c.dt[o1], sp, dtb, true);
 
   float* h1 = c.h + static_cast<size_t>(bh) * c.N * c.P;
   const float* hrel = c.h + (units + bh) * c.N * c.P;

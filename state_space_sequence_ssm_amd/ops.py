@@ -47,10 +47,25 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _prologue(pro, H, R, N, bc_norm, bc_eps, B_norm_w, C_norm_w, B_bias, C_bias, dt_softplus, dt_bias):
+    """Fill the m3_prologue of an argument structure (steps fused in front of
+    the core: B / C RMS normalisation, head biases, Delta = softplus)."""
+    f32 = torch.float32
+    pro.bc_norm = 1 if bc_norm else 0
+    pro.dt_softplus = 1 if dt_softplus else 0
+    pro.bc_eps = float(bc_eps)
+    pro.B_norm_w = _ptr(B_norm_w, f32, (N,), "B_norm_w")
+    pro.C_norm_w = _ptr(C_norm_w, f32, (N,), "C_norm_w")
+    pro.B_bias = _ptr(B_bias, f32, (H, R, N), "B_bias")
+    pro.C_bias = _ptr(C_bias, f32, (H, R, N), "C_bias")
+    pro.dt_bias = _ptr(dt_bias, f32, (H,), "dt_bias")
+
+
 def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
                    *, y=None, h_final=None, Bprev_rot_out=None, xprev_out=None, phi_out=None,
                    want_state=True, want_carry=False, chunk=0, workspace=None, omega=None, A_tok=None,
-                   head_major=False, noalloc=False, stream=None):
+                   head_major=False, noalloc=False, bc_norm=False, bc_eps=1e-6, B_norm_w=None, C_norm_w=None,
+                   B_bias=None, C_bias=None, dt_softplus=False, dt_bias=None, stream=None):
     """Chunked prefill.  Shapes: x [Bt,L,H,R,P], B/C [Bt,L,H,R,N] (bf16 or fp32),
     dt/lam [Bt,L,H] fp32, A [H] fp32, theta [Bt,L,H,N/2] fp32 or None (or
     instead omega [Bt,L,N/2] fp32: rates shared by the heads, theta = dt * omega
@@ -63,7 +78,11 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a dict with y and, as requested, h_final and the carry-out (Bprev_rot,
     xprev, phi).  head_major: x, B, C and y are [Bt,H,L,R,.] instead.
     noalloc: call m3_ssm_prefill_noalloc (the library's static scratch in
-    place of a workspace; workspace must then be None)."""
+    place of a workspace; workspace must then be None).
+    Prologue (computed on chip; B, C and dt are then the raw projections):
+    bc_norm / bc_eps / B_norm_w, C_norm_w [N]: RMS normalisation of each B and
+    C row; B_bias, C_bias [H,R,N]: head biases added after it; dt_softplus /
+    dt_bias [H]: Delta = softplus(dt + dt_bias)."""
     if head_major:
         Bt, H, L, R, P = x.shape
     else:
@@ -104,6 +123,7 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     a.Bprev_rot_out = _ptr(Bprev_rot_out, f32, (Bt, H, R, N), "Bprev_rot_out")
     a.xprev_out = _ptr(xprev_out, x.dtype, (Bt, H, R, P), "xprev_out")
     a.phi_out = _ptr(phi_out, f32, (Bt, H, N // 2), "phi_out")
+    _prologue(a.pro, H, R, N, bc_norm, bc_eps, B_norm_w, C_norm_w, B_bias, C_bias, dt_softplus, dt_bias)
     lib = _lib.load()
     if noalloc:
         if workspace is not None:
@@ -135,13 +155,15 @@ def prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=torch.bfloat16, rope=False)
 
 
 def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None, *, y=None, A_tok=None,
-                       omega=None, stream=None):
+                       omega=None, bc_norm=False, bc_eps=1e-6, B_norm_w=None, C_norm_w=None, B_bias=None,
+                       C_bias=None, dt_softplus=False, dt_bias=None, stream=None):
     """One decode token.  In/out (updated in place): h [Bt,H,N,P] fp32,
     phi [Bt,H,N/2] fp32 (None iff theta None), Bprev_rot [Bt,H,R,N] fp32,
     xprev [Bt,H,R,P].  Inputs x [Bt,H,R,P], B/C [Bt,H,R,N], dt/lam [Bt,H],
     A [H] (or A_tok [Bt,H]: this token's A; then A may be None), theta
     [Bt,H,N/2] or None (or omega [Bt,N/2]: rates shared by the heads, theta =
-    dt * omega).  Returns y [Bt,H,R,P]."""
+    dt * omega).  The prologue arguments are those of m3_ssm_prefill.
+    Returns y [Bt,H,R,P]."""
     Bt, H, R, P = x.shape
     N = B.shape[-1]
     f32 = torch.float32
@@ -164,6 +186,7 @@ def m3_ssm_decode_step(h, phi, Bprev_rot, xprev, x, B, C, dt, lam, A, theta=None
     a.theta = _ptr(theta, f32, (Bt, H, N // 2), "theta")
     a.omega = _ptr(omega, f32, (Bt, N // 2), "omega")
     a.y = _ptr(y, x.dtype, (Bt, H, R, P), "y")
+    _prologue(a.pro, H, R, N, bc_norm, bc_eps, B_norm_w, C_norm_w, B_bias, C_bias, dt_softplus, dt_bias)
     rc = _lib.load().m3_ssm_decode_step(ctypes.byref(a), _stream(stream))
     if rc != _lib.M3_OK:
         raise M3Error(rc, "m3_ssm_decode_step")

@@ -116,6 +116,34 @@ def test_prefill_workspace_size(Bt, H, L, N, P, R, rope, split):
     assert lib.m3_ssm_prefill_workspace_size(None) == 0
 
 
+def _pro_cases():
+    """Invalid prologues (each a mutation of m3_prologue) -> M3_ERR_INVALID_ARG."""
+    return [
+        lambda q: setattr(q, "bc_norm", 2),
+        lambda q: setattr(q, "dt_softplus", -1),
+        lambda q: (setattr(q, "bc_norm", 1), setattr(q, "bc_eps", -1e-3)),
+        lambda q: (setattr(q, "bc_norm", 1), setattr(q, "bc_eps", float("nan"))),
+        lambda q: (setattr(q, "bc_norm", 1), setattr(q, "bc_eps", float("inf"))),
+        lambda q: setattr(q, "B_norm_w", 0x50000000),            # gain without the normalisation
+        lambda q: setattr(q, "dt_bias", 0x50000000),             # step bias without the softplus
+        lambda q: setattr(q, "C_bias", 0x50000002),              # misaligned
+        lambda q: (setattr(q, "bc_norm", 1), setattr(q, "C_norm_w", 0x50000001)),
+    ]
+
+
+def test_prologue_validation():
+    lib = _lib.load()
+    for mutate in _pro_cases():
+        a = _good_prefill()
+        mutate(a.pro)
+        assert _rc_prefill(a) == _lib.M3_ERR_INVALID_ARG
+    # the B/C table does not fit next to RoPE N = 128, P = 64 tiles at R = 4
+    a = _good_prefill()
+    a.N, a.P, a.R, a.theta = 128, 64, 4, 0x30000000
+    a.pro.bc_norm = 1
+    assert _rc_prefill(a) == _lib.M3_ERR_UNSUPPORTED
+
+
 def test_prefill_workspace_validation():
     a = _good_prefill()
     a.Bt, a.H, a.L, a.R = 1, 2, 1024, 1
@@ -183,6 +211,10 @@ def test_decode_validation():
         a = good()
         mutate(a)
         assert lib.m3_ssm_decode_step(ctypes.byref(a), None) == code
+    for mutate in _pro_cases():
+        a = good()
+        mutate(a.pro)
+        assert lib.m3_ssm_decode_step(ctypes.byref(a), None) == _lib.M3_ERR_INVALID_ARG
 
 
 def test_angles_validation():

@@ -540,3 +540,12 @@ def test_prologue_norm_bias_softplus():
                                   dt_softplus=True)
         outs.append(orc.ssm_reference(d["x"], Bq, Cq, dq, d["lam"], d["A"], omega=d["omega"]))
     assert orc.rel_l2(outs[1]["y"], outs[0]["y"]) <= 1e-12
+
+
+def test_rms_norm_zero_rows_stay_zero():
+    v = np.zeros((2, 5))
+    v[1] = [1.0, -2.0, 0.5, 0.0, 3.0]
+    for eps in (0.0, 1e-6):
+        out = orc.rms_norm(v, eps=eps)
+        assert np.array_equal(out[0], np.zeros(5))
+        np.testing.assert_allclose(out[1], v[1] / np.sqrt(np.mean(v[1] ** 2) + eps), rtol=1e-15)
