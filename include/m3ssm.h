@@ -142,9 +142,7 @@ typedef enum m3_layout {
  *                NULL; needs dt_softplus), the step made positive on chip.
  * The rotation (RoPE) applies to the normalised and biased B and C, and the
  * carried B (Bprev_rot, Bprev_rot_out) is that rotated B.  Gains and biases
- * must be 4-byte aligned.  Other values are M3_ERR_INVALID_ARG; bf16 calls
- * whose LDS with the B/C table exceeds a CU return M3_ERR_UNSUPPORTED
- * (RoPE at N = 128, P = 64 with R >= 4).
+ * must be 4-byte aligned.  Other values are M3_ERR_INVALID_ARG.
  */
 typedef struct m3_prologue {
   int32_t bc_norm;

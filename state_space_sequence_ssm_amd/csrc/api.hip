@@ -65,7 +65,6 @@ bool prologue_ok(const m3_prologue& q) {
   if (!q.dt_softplus && q.dt_bias != nullptr) return false;
   return al4(q.B_norm_w) && al4(q.C_norm_w) && al4(q.B_bias) && al4(q.C_bias) && al4(q.dt_bias);
 }
-bool prologue_bc(const m3_prologue& q) { return q.bc_norm != 0 || q.B_bias != nullptr || q.C_bias != nullptr; }
 m3::Prologue to_internal(const m3_prologue& q) {
   m3::Prologue r{};
   r.bc_norm = q.bc_norm;
@@ -157,7 +156,7 @@ int check_prefill(const m3_prefill_args* a) {
     const double itemTh = double(a->L) * a->H * (a->N / 2) * 4.0;
     if (item > 2147483000.0 || itemTh > 2147483000.0) return M3_ERR_UNSUPPORTED;
   }
-  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, a->R, rope, prologue_bc(a->pro))
+  const size_t lds = bf16 ? m3::prefill_lds_bytes_bf16(a->N, a->P, a->R, rope, a->pro.bc_norm != 0)
                           : m3::prefill_lds_bytes_f32(a->N, a->P, rope);
   if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
   return M3_OK;

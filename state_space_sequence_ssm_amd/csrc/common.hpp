@@ -112,9 +112,16 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int width) {
   return v;
 }
 
-// softplus(z) = log(1 + e^z): the positive step Delta from its raw value
-// (for z > 15, e^-z is below half an fp32 ulp of z).
-__device__ __forceinline__ float softplus_f(float z) { return z > 15.f ? z : log1pf(__expf(z)); }
+// softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|): the positive step
+// Delta from its raw value, without branches.  log1p(u), u in (0, 1], from
+// the hardware log of w = fl(1 + u) scaled by u / (w - 1), which cancels the
+// rounding of 1 + u (Goldberg's form; exact u when w rounds to 1).
+__device__ __forceinline__ float softplus_f(float z) {
+  const float u = __expf(-fabsf(z));
+  const float w = 1.f + u;
+  const float lp = w == 1.f ? u : __logf(w) * (u / (w - 1.f));
+  return fmaxf(z, 0.f) + lp;
+}
 
 // Delta of one token with the prologue's options: softplus of raw + bias, or
 // the value as given.  Tokens past the end (`valid` false) have Delta = 0.

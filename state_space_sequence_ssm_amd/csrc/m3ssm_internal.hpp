@@ -134,7 +134,7 @@ struct CombineParams {
 };
 hipError_t launch_split_combine(const CombineParams& c, hipStream_t s);
 // LDS bytes the prefill kernel needs for (N, P, rope) and, with `pro_bc`
-// (B/C normalisation or biases), for its prologue table at rank R; 0 if not
+// (B / C normalisation), for the row-sum exchange of its prologue; 0 if not
 // compiled.
 size_t prefill_lds_bytes_bf16(int N, int P, int R, bool rope, bool pro_bc);
 size_t prefill_lds_bytes_f32(int N, int P, bool rope);

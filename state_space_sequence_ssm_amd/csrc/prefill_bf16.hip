@@ -30,11 +30,12 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, bool state_only, hipStrea
 namespace {
 template <int N>
 size_t lds_pc_n(int P, int R, bool rope, bool pro) {
+  (void)R;
   switch (P) {
-    case 16: return pc::PcLayout<N, 16>::bytes(rope, pro, R);
-    case 32: return pc::PcLayout<N, 32>::bytes(rope, pro, R);
-    case 64: return pc::PcLayout<N, 64>::bytes(rope, pro, R);
-    case 128: return pc::PcLayout<N, 128>::bytes(rope, pro, R);
+    case 16: return pc::PcLayout<N, 16>::bytes(rope, pro);
+    case 32: return pc::PcLayout<N, 32>::bytes(rope, pro);
+    case 64: return pc::PcLayout<N, 64>::bytes(rope, pro);
+    case 128: return pc::PcLayout<N, 128>::bytes(rope, pro);
   }
   return 0;
 }

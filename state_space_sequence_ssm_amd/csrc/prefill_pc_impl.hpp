@@ -298,13 +298,11 @@ struct PcLayout {
   static constexpr size_t oY(bool rope) { return used2(rope); }
   static constexpr size_t kBytesReal = used2(false) + (stage_y(false) ? kYBytes : 0);
   static constexpr size_t kBytesRope = used2(true) + (stage_y(true) ? kYBytes : 0);
-  // Prologue table, appended only for calls that normalise or bias B and C:
-  // head biases of B and C [2][R][N], gains [2][N], then the exchange of row
-  // sums of squares between the two waves of a row tile [2 halves][2][64].
-  static constexpr size_t proFloats(int R) { return 2 * size_t(R) * N + 2 * size_t(N) + 4 * 64; }
-  static constexpr size_t bytes(bool rope, bool pro, int R) {
-    return (rope ? kBytesRope : kBytesReal) + (pro ? proFloats(R) * 4 : 0);
-  }
+  // Prologue: the exchange of row sums of squares between the two waves of a
+  // row tile [2 halves][2 (B, C)][64 rows], appended only for calls that
+  // normalise B and C (gains and biases live in registers).
+  static constexpr size_t kProBytes = 4 * 64 * 4;
+  static constexpr size_t bytes(bool rope, bool pro) { return (rope ? kBytesRope : kBytesReal) + (pro ? kProBytes : 0); }
   // B and C columns of one row are staged by both waves of a row tile (whole
   // lines at R = 1: column blocks of 64; MFMA layout at R > 1: k blocks of 32)
   static constexpr bool rows_split(bool fl) { return fl ? NCBN > 1 : NKB > 1; }
@@ -314,6 +312,27 @@ struct PcLayout {
       if (pc.kind == 0 || pc.kind == 1) return true;
     }
     return false;
+  }
+  // column blocks of B / C staged by half h: the first one and how many
+  static constexpr int bc_first(bool fl, int h) {
+    for (int s = 0; s < uph(fl); ++s)
+      if (piece(fl, h, s).kind == 0) return piece(fl, h, s).cb;
+    return 0;
+  }
+  static constexpr int bc_blocks(bool fl, int h) {
+    int n = 0, last = -1;
+    for (int s = 0; s < uph(fl); ++s) {
+      const Piece pc = piece(fl, h, s);
+      if (pc.kind == 0 && pc.cb != last) {
+        ++n;
+        last = pc.cb;
+      }
+    }
+    return n;
+  }
+  static constexpr int bc_blocks_max(bool fl) {
+    return bc_blocks(fl, 0) > bc_blocks(fl, 1) ? (bc_blocks(fl, 0) > 0 ? bc_blocks(fl, 0) : 1)
+                                               : (bc_blocks(fl, 1) > 0 ? bc_blocks(fl, 1) : 1);
   }
 };
 
@@ -416,10 +435,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   constexpr bool kStageY = !SO && LGR == 0 && Lt::stage_y(ROPE);
   u32x2* sY = reinterpret_cast<u32x2*>(smem + Lt::oY(ROPE));  // [64][PY/4] 8-byte units
   auto phiTab = [&](int s) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + Lt::oPhi) + s * kRows * PH; };
-  // prologue table (allocated only when proBC): biases [2][R][N], gains [2][N], exchange [2][2][64]
-  float* const proTab = reinterpret_cast<float*>(smem + (ROPE ? Lt::kBytesRope : Lt::kBytesReal));
-  float* const proW = proTab + 2 * R * N;
-  float* const proEx = proW + 2 * N;
+  // row sums of squares exchanged by the two waves of a row tile [2][2][64]
+  // (allocated only when the call normalises B and C)
+  float* const proEx = reinterpret_cast<float*>(smem + (ROPE ? Lt::kBytesRope : Lt::kBytesReal));
 
   // ================================================================ staging state
   // chunk c's pieces live in register set c % 2 (two chunks in flight)
@@ -613,31 +631,45 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
 #pragma unroll
       for (int i = 0; i < NRS; ++i) rsc[k][i] = ss[k][i] > 0.f ? rsqrtf(ss[k][i] * (1.f / N) + proEps) : 0.f;
   };
-  // bf16 piece -> 8 fp32 values, with the prologue's gain, scale and bias
-  // applied to B / C pieces (columns past N stay zero)
-  auto unpack_pro = [&](u32x4 v, int kind, int row, int col, float scale, float (&f)[8]) __attribute__((always_inline)) {
+  // Gains and biases of the B / C columns this lane stages: the same in every
+  // chunk (one column block per half with whole lines at R = 1; the half's k
+  // blocks and the lane's rank in the MFMA layout), so they stay in registers:
+  // pw = gain (1 without the normalisation), pb = bias (0 without it; 0 in
+  // columns past N as well, which must stay zero).
+  constexpr int NBH = Lt::bc_blocks_max(kFL);
+  float pw[2][NBH][8], pb[2][NBH][8];
+  auto load_pro = [&](auto HALF) __attribute__((always_inline)) {
+    constexpr int h = decltype(HALF)::value;
+    const int r = kFL ? 0 : ((16 * quad + l16) & (R - 1));
+#pragma unroll
+    for (int j = 0; j < NBH; ++j) {
+      const int cb = Lt::bc_first(kFL, h) + j;
+      const int col = kFL ? 64 * cb + 8 * (lane % Lt::cpr(N)) : 32 * cb + 8 * g;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float* w = k == 0 ? p.pro.B_w : p.pro.C_w;
+        const float* b = k == 0 ? p.pro.B_bias : p.pro.C_bias;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool in = col + e < N && j < Lt::bc_blocks(kFL, h);
+          pw[k][j][e] = (proNorm && w != nullptr && in) ? w[col + e] : 1.f;
+          pb[k][j][e] = (b != nullptr && in) ? b[(static_cast<size_t>(hh) * R + r) * N + col + e] : 0.f;
+        }
+      }
+    }
+  };
+  // bf16 piece -> 8 fp32 values; B / C pieces (kind < 2) of column block j
+  // get gain x scale and bias (one fma each)
+  auto unpack_pro = [&](u32x4 v, int kind, int j, float scale, float (&f)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       f[2 * q] = __uint_as_float(v[q] << 16);
       f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
     }
-    if (proBC && kind < 2 && col < N) {
-      const float* bias = proTab + (kind * R + (row & (R - 1))) * N + col;
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias), b1 = *reinterpret_cast<const f32x4*>(bias + 4);
-      if (proNorm) {
-        const float* w = proW + kind * N + col;
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w) * scale, w1 = *reinterpret_cast<const f32x4*>(w + 4) * scale;
+    if constexpr (PRO) {
+      if (kind < 2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[e] = f[e] * w0[e] + b0[e];
-          f[4 + e] = f[4 + e] * w1[e] + b1[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f[e] += b0[e];
-          f[4 + e] += b1[e];
-        }
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * (scale * pw[kind][j][e]) + pb[kind][j][e];
       }
     }
   };
@@ -664,9 +696,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if (proNorm)
       row_scales(src, HALF, std::integral_constant<int, IPN>{}, [](const Piece pc) { return pc.i; },
                  [&](int i) { return 16 * quad + (64 / cprN) * i + lane / cprN; },
-                 [](float v) {
-#pragma unroll
-                   for (int off = 1; off < cprN; off <<= 1) v += __shfl_xor(v, off);
+                 [](float v) {  // the cpr (4 or 8) aligned lanes of a row, by DPP
+                   v += dpp<0xB1, 0xF, false>(v);  // quad_perm [1,0,3,2]
+                   v += dpp<0x4E, 0xF, false>(v);  // quad_perm [2,3,0,1]
+                   if constexpr (cprN == 8) v += dpp<0x141, 0xF, false>(v);  // row_half_mirror
                    return v;
                  },
                  rsc);
@@ -693,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           }
         }
         float f[8];
-        unpack_pro(v, pc.kind, row, col, proNorm ? rsc[pc.kind][pc.i] : 1.f, f);
+        unpack_pro(v, pc.kind, 0, proNorm ? rsc[pc.kind][pc.i] : 1.f, f);
         // B and C feed the Gram tiles and the readout, B also the state
         *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(row, col)) = rotate_pack(f, cs, sn);
       }
@@ -749,7 +782,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         }
       }
       float f[8];
-      unpack_pro(v, pc.kind, 16 * quad + l16, col, proNorm ? rsc[pc.kind][0] : 1.f, f);
+      unpack_pro(v, pc.kind, pc.cb - Lt::bc_first(kFL, h), proNorm ? rsc[pc.kind][0] : 1.f, f);
       // B and C feed the Gram tiles and the readout, B also the state
       *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(16 * quad + l16, col)) = rotate_pack(f, cs, sn);
       if constexpr (kRefill) src[s] = load_piece(c + kSets, s, HALF);
@@ -1077,20 +1110,6 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   if constexpr (ROPE)
     for (int q = tid; q < N / 2; q += kThreads)
       phiC[q] = cPhi0 != nullptr ? cPhi0[static_cast<size_t>(bh) * (N / 2) + q] : 0.f;
-  if (proBC) {  // this head's biases and the gains (visible after the prologue's first barrier)
-    for (int e = tid; e < 2 * R * N + 2 * N; e += kThreads) {
-      float v;
-      if (e < R * N)
-        v = p.pro.B_bias != nullptr ? p.pro.B_bias[static_cast<size_t>(hh) * R * N + e] : 0.f;
-      else if (e < 2 * R * N)
-        v = p.pro.C_bias != nullptr ? p.pro.C_bias[static_cast<size_t>(hh) * R * N + e - R * N] : 0.f;
-      else if (e < 2 * R * N + N)
-        v = p.pro.B_w != nullptr ? p.pro.B_w[e - 2 * R * N] : 1.f;
-      else
-        v = p.pro.C_w != nullptr ? p.pro.C_w[e - 2 * R * N - N] : 1.f;
-      proTab[e] = v;
-    }
-  }
   // retire the prologue's state and carry loads here, so no wait on them is
   // left for the loop to repeat every chunk
   __builtin_amdgcn_s_waitcnt(0);
@@ -1143,9 +1162,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     }
   };
   if (!upper) {
+    if constexpr (PRO) load_pro(std::integral_constant<int, 0>{});
     prologue(std::integral_constant<int, 0>{});
     walk(std::integral_constant<int, 0>{});
   } else {
+    if constexpr (PRO) load_pro(std::integral_constant<int, 1>{});
     prologue(std::integral_constant<int, 1>{});
     walk(std::integral_constant<int, 1>{});
   }
@@ -1210,9 +1231,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         const bf16_t* src = static_cast<const bf16_t*>(p.B) + (row0 + static_cast<size_t>(t) * tsR + r) * N;
         float a0 = bf16_to_f32(src[2 * q].bits), a1 = bf16_to_f32(src[2 * q + 1].bits);
         if (proBC) {
-          const float sc0 = proNorm ? proEx[r] * proW[2 * q] : 1.f, sc1 = proNorm ? proEx[r] * proW[2 * q + 1] : 1.f;
-          a0 = a0 * sc0 + proTab[r * N + 2 * q];
-          a1 = a1 * sc1 + proTab[r * N + 2 * q + 1];
+          const float* w = p.pro.B_w;
+          const float* bb = p.pro.B_bias != nullptr ? p.pro.B_bias + (static_cast<size_t>(hh) * R + r) * N : nullptr;
+          const float sc0 = proNorm ? proEx[r] * (w != nullptr ? w[2 * q] : 1.f) : 1.f;
+          const float sc1 = proNorm ? proEx[r] * (w != nullptr ? w[2 * q + 1] : 1.f) : 1.f;
+          a0 = a0 * sc0 + (bb != nullptr ? bb[2 * q] : 0.f);
+          a1 = a1 * sc1 + (bb != nullptr ? bb[2 * q + 1] : 0.f);
         }
         if constexpr (ROPE) {
           // Phi_{L-1} is the final angle carry (reduced modulo 2 pi)

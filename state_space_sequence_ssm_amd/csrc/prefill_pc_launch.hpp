@@ -11,12 +11,9 @@ namespace pc {
 template <int N, int P, int LGR, bool ROPE, bool SO, bool PRO>
 hipError_t launch_k(const PrefillParams& p, hipStream_t s) {
   using Lt = PcLayout<N, P>;
-  const bool pro_bc = p.pro.bc_norm != 0 || p.pro.B_bias != nullptr || p.pro.C_bias != nullptr;
-  const size_t lds = Lt::bytes(ROPE, pro_bc, 1 << LGR);
-  // cleared once per device for the most this kernel asks for (with the
-  // prologue table when that fits a CU)
-  constexpr size_t kWith = Lt::bytes(ROPE, PRO, 1 << LGR);
-  constexpr size_t kAllow = kWith <= 160 * 1024 ? kWith : Lt::bytes(ROPE, false, 1 << LGR);
+  const size_t lds = Lt::bytes(ROPE, PRO && p.pro.bc_norm != 0);
+  // cleared once per device for the most this kernel asks for
+  constexpr size_t kAllow = Lt::bytes(ROPE, PRO);
   static std::atomic<uint64_t> cleared{0};  // devices this kernel is cleared on
   hipError_t e = allow_lds(reinterpret_cast<const void*>(&prefill_pc_kernel<N, P, LGR, ROPE, SO, PRO>), kAllow,
                            cleared);

@@ -137,11 +137,6 @@ def test_prologue_validation():
         a = _good_prefill()
         mutate(a.pro)
         assert _rc_prefill(a) == _lib.M3_ERR_INVALID_ARG
-    # the B/C table does not fit next to RoPE N = 128, P = 64 tiles at R = 4
-    a = _good_prefill()
-    a.N, a.P, a.R, a.theta = 128, 64, 4, 0x30000000
-    a.pro.bc_norm = 1
-    assert _rc_prefill(a) == _lib.M3_ERR_UNSUPPORTED
 
 
 def test_prefill_workspace_validation():
