@@ -217,6 +217,122 @@ def decode_reference(h, Bprev_rot, xprev, phi, x, B, C, dt, lam, A, theta=None, 
     return dict(y=y, h=h2, Bprev_rot=Bp, xprev=xp, phi=ph)
 
 
+def ssm_backward(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
+                 dy=None, dh_final=None):
+    """Gradients of a loss through the sequential recurrence (reverse mode),
+    float64.  The loss reaches the core through y (upstream gradient dy, the
+    shape of y) and the final state h (dh_final [Bt,H,N,P], optional); the
+    carry-out (rotated B, x, angle) is not differentiated.
+
+    The pages print no backward pass; this is the plain adjoint of the
+    token loop of :func:`ssm_reference` ([CH] sec. 1-3), derived here.
+    With g_t = dloss/dh_t (the adjoint state) and u_t = sum_r Btil_t[r] x_t[r]^T:
+        g_t   = Ctil_t dy_t^T + alpha_{t+1} g_{t+1}    (g_{L-1} adds dh_final)
+        du_t  = gamma_t g_t + beta_{t+1} g_{t+1}         (beta_L := 0)
+        dBtil_t[r] = du_t x_t[r],  dx_t[r] = du_t^T Btil_t[r],  dCtil_t[r] = h_t dy_t[r]
+        dalpha_t = <g_t, h_{t-1}>,  dbeta_t = <g_t, u_{t-1}>,  dgamma_t = <g_t, u_t>
+    then through alpha = exp(Delta A), beta = (1 - lambda) Delta alpha,
+    gamma = lambda Delta; through the rotation Btil = R(Phi)^T B (a pair's
+    angle gradient is dBtil_0 Btil_1 - dBtil_1 Btil_0, summed over ranks and
+    over B and C), and Phi_t = Phi_{-1} + sum_{s<=t} theta_s (so dtheta is the
+    reverse cumulative sum of dPhi, and dphi0 its total).  The carry-in
+    enters as h_{-1} = h0 and u_{-1} = sum_r Bprev_rot[r] xprev[r]^T.
+    Returns dict(dx, dB, dC, ddt, dlam, dA (shape of A), dtheta (or None),
+    dh0, dBprev_rot, dxprev, dphi0 (or None)).
+    """
+    x, B, C, dt, lam, A = map(_f64, (x, B, C, dt, lam, A))
+    theta = _f64(theta)
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dy = np.zeros_like(x) if dy is None else _f64(dy)
+    h = np.zeros((Bt, H, N, P)) if h0 is None else _f64(h0).copy()
+    Bp = np.zeros((Bt, H, R, N)) if Bprev_rot is None else _f64(Bprev_rot).copy()
+    xp = np.zeros((Bt, H, R, P)) if xprev is None else _f64(xprev).copy()
+    per_tok = A.ndim != 1
+    # ---- forward, keeping every state and the rotated inputs
+    phi = None
+    if theta is not None:
+        phi = np.zeros((Bt, H, N // 2)) if phi0 is None else _f64(phi0).copy()
+        Phi = phi[:, None] + np.cumsum(theta, axis=1)          # [Bt,L,H,N/2]
+        Br, Cr = rotate_pairs(B, Phi), rotate_pairs(C, Phi)
+    else:
+        Br, Cr = B, C
+    hs = np.zeros((L + 1, Bt, H, N, P))  # hs[t + 1] = h_t, hs[0] = h_{-1}
+    hs[0] = h
+    us = np.zeros((L + 1, Bt, H, N, P))  # us[t + 1] = u_t, us[0] = u_{-1}
+    us[0] = np.einsum("bhrn,bhrp->bhnp", Bp, xp)
+    al = np.zeros((Bt, L, H))
+    be = np.zeros((Bt, L, H))
+    ga = np.zeros((Bt, L, H))
+    for t in range(L):
+        A_t = A if not per_tok else A[:, t]
+        a_, b_, g_ = coefficients(dt[:, t], lam[:, t], A_t)
+        al[:, t], be[:, t], ga[:, t] = a_, b_, g_
+        us[t + 1] = np.einsum("bhrn,bhrp->bhnp", Br[:, t], x[:, t])
+        hs[t + 1] = (a_[..., None, None] * hs[t] + b_[..., None, None] * us[t]
+                     + g_[..., None, None] * us[t + 1])
+    # ---- reverse
+    g_next = np.zeros((Bt, H, N, P)) if dh_final is None else _f64(dh_final).copy()
+    a_next = np.zeros((Bt, H))
+    b_next = np.zeros((Bt, H))
+    dx = np.zeros_like(x)
+    dBr = np.zeros_like(Br)
+    dCr = np.zeros_like(Cr)
+    dal = np.zeros((Bt, L, H))
+    dbe = np.zeros((Bt, L, H))
+    dga = np.zeros((Bt, L, H))
+    g_after = None  # g_{t+1}
+    for t in range(L - 1, -1, -1):
+        g_t = np.einsum("bhrn,bhrp->bhnp", Cr[:, t], dy[:, t])
+        if t == L - 1:
+            g_t = g_t + g_next  # dh_final
+        else:
+            g_t = g_t + a_next[..., None, None] * g_after
+        dCr[:, t] = np.einsum("bhnp,bhrp->bhrn", hs[t + 1], dy[:, t])
+        du = ga[:, t][..., None, None] * g_t
+        if t < L - 1:
+            du = du + b_next[..., None, None] * g_after
+        dBr[:, t] = np.einsum("bhnp,bhrp->bhrn", du, x[:, t])
+        dx[:, t] = np.einsum("bhnp,bhrn->bhrp", du, Br[:, t])
+        dal[:, t] = np.einsum("bhnp,bhnp->bh", g_t, hs[t])
+        dbe[:, t] = np.einsum("bhnp,bhnp->bh", g_t, us[t])
+        dga[:, t] = np.einsum("bhnp,bhnp->bh", g_t, us[t + 1])
+        a_next, b_next, g_after = al[:, t], be[:, t], g_t
+    g0 = g_after  # g_0
+    dh0 = al[:, 0][..., None, None] * g0
+    du_m1 = be[:, 0][..., None, None] * g0
+    dBprev = np.einsum("bhnp,bhrp->bhrn", du_m1, xp)
+    dxprev = np.einsum("bhnp,bhrn->bhrp", du_m1, Bp)
+    # ---- scalars: alpha = exp(dt A), beta = (1 - lam) dt alpha, gamma = lam dt
+    A_full = A[None, None, :] if not per_tok else A
+    ddt = dal * A_full * al + dbe * ((1 - lam) * al + A_full * be) + dga * lam
+    dlam = -dbe * dt * al + dga * dt
+    dA_tok = dt * (dal * al + dbe * be)
+    dA = dA_tok if per_tok else dA_tok.sum(axis=(0, 1))
+    # ---- rotation
+    dtheta = dphi0 = None
+    if theta is not None:
+        c = np.cos(Phi)[..., None, :]
+        s_ = np.sin(Phi)[..., None, :]
+
+        def unrot(dv):  # dv [.., R, N] in the rotated frame -> input frame
+            out = np.empty_like(dv)
+            out[..., 0::2] = c * dv[..., 0::2] - s_ * dv[..., 1::2]
+            out[..., 1::2] = s_ * dv[..., 0::2] + c * dv[..., 1::2]
+            return out
+
+        dB = unrot(dBr)
+        dC = unrot(dCr)
+        dPhi = (dBr[..., 0::2] * Br[..., 1::2] - dBr[..., 1::2] * Br[..., 0::2]
+                + dCr[..., 0::2] * Cr[..., 1::2] - dCr[..., 1::2] * Cr[..., 0::2]).sum(axis=-2)  # [Bt,L,H,N/2]
+        dtheta = np.flip(np.cumsum(np.flip(dPhi, axis=1), axis=1), axis=1)
+        dphi0 = dPhi.sum(axis=1)
+    else:
+        dB, dC = dBr, dCr
+    return dict(dx=dx, dB=dB, dC=dC, ddt=ddt, dlam=dlam, dA=dA, dtheta=dtheta, dh0=dh0,
+                dBprev_rot=dBprev, dxprev=dxprev, dphi0=dphi0)
+
+
 def rope_angles_cumsum(theta, phi0=None):
     """Inclusive cumulative angle Phi_t = Phi_{-1} + sum_{s<=t} theta_s along the
     sequence axis ([CH] sec. 2: rotations aggregated over all time steps).

@@ -549,3 +549,82 @@ def test_rms_norm_zero_rows_stay_zero():
         out = orc.rms_norm(v, eps=eps)
         assert np.array_equal(out[0], np.zeros(5))
         np.testing.assert_allclose(out[1], v[1] / np.sqrt(np.mean(v[1] ** 2) + eps), rtol=1e-15)
+
+
+# ---------------------------------------------------------------- backward
+def _loss(d, dy, dhf, **over):
+    a = {k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta", "h0", "Bprev_rot", "xprev", "phi0")}
+    a.update(over)
+    out = orc.ssm_reference(**a)
+    return float(np.sum(dy * out["y"]) + np.sum(dhf * out["h"])), out
+
+
+def _bwd_case(rope=True, carry=True, a_tok=False, seed=41, L=7, R=2):
+    s = Shape(1, L, 2, 3, 4, R, "f32", rope)
+    d = {k: (None if v is None else np.float64(v)) for k, v in make_inputs(s, seed, h0=carry, carry=carry).items()}
+    rng = np.random.default_rng(seed + 1)
+    if a_tok:
+        d["A"] = -np.exp(rng.random((1, L, 2)) * np.log(16.0))
+    if rope:
+        d["theta"] = d["theta"] * 20.0  # angles of order one per token
+    dy = rng.standard_normal(d["x"].shape)
+    dhf = rng.standard_normal((1, 2, 4, 3))
+    return d, dy, dhf, rng
+
+
+@pytest.mark.parametrize("rope,carry,a_tok", [(True, True, False), (False, False, False), (True, True, True),
+                                              (False, True, True)])
+def test_backward_matches_finite_differences(rope, carry, a_tok):
+    """Directional derivatives of loss = <dy, y> + <dh_final, h_final> by
+    central differences (fp64, step 1e-6) against <gradient, direction>, for
+    every differentiated input."""
+    d, dy, dhf, rng = _bwd_case(rope, carry, a_tok)
+    g = orc.ssm_backward(**{k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta", "h0", "Bprev_rot",
+                                              "xprev", "phi0")}, dy=dy, dh_final=dhf)
+    names = [("x", "dx"), ("B", "dB"), ("C", "dC"), ("dt", "ddt"), ("lam", "dlam"), ("A", "dA")]
+    if rope:
+        names += [("theta", "dtheta"), ("phi0", "dphi0")]
+    if carry:
+        names += [("h0", "dh0"), ("Bprev_rot", "dBprev_rot"), ("xprev", "dxprev")]
+    eps = 1e-6
+    for inp, gname in names:
+        v = rng.standard_normal(d[inp].shape)
+        lp, _ = _loss(d, dy, dhf, **{inp: d[inp] + eps * v})
+        lm, _ = _loss(d, dy, dhf, **{inp: d[inp] - eps * v})
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(g[gname] * v))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (inp, fd, an)
+
+
+def test_backward_elementwise_step_gradient():
+    """Every element of dDelta and dlambda by central differences (the
+    scalars that reach the decay, the trapezoid weights and the next token)."""
+    d, dy, dhf, _ = _bwd_case(True, True, False, seed=43, L=5, R=1)
+    g = orc.ssm_backward(**{k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta", "h0", "Bprev_rot",
+                                              "xprev", "phi0")}, dy=dy, dh_final=dhf)
+    eps = 1e-6
+    for inp, gname in (("dt", "ddt"), ("lam", "dlam")):
+        for idx in np.ndindex(*d[inp].shape):
+            v = np.zeros_like(d[inp])
+            v[idx] = 1.0
+            lp, _ = _loss(d, dy, dhf, **{inp: d[inp] + eps * v})
+            lm, _ = _loss(d, dy, dhf, **{inp: d[inp] - eps * v})
+            assert abs((lp - lm) / (2 * eps) - g[gname][idx]) <= 1e-7 * max(1.0, abs(g[gname][idx])), (inp, idx)
+
+
+def test_backward_homogeneity_identities():
+    """y and h_final are linear in (x, h0, xprev) jointly, y is linear in C
+    (h_final does not depend on C), and without a carried B both are linear
+    in B: so <grad, input> returns the loss (or its y part)."""
+    d, dy, dhf, _ = _bwd_case(True, True, False, seed=47)
+    args = {k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta", "h0", "Bprev_rot", "xprev", "phi0")}
+    g = orc.ssm_backward(**args, dy=dy, dh_final=dhf)
+    loss, out = _loss(d, dy, dhf)
+    lin = np.sum(g["dx"] * d["x"]) + np.sum(g["dh0"] * d["h0"]) + np.sum(g["dxprev"] * d["xprev"])
+    assert abs(lin - loss) <= 1e-11 * max(1.0, abs(loss))
+    assert abs(np.sum(g["dC"] * d["C"]) - np.sum(dy * out["y"])) <= 1e-11 * max(1.0, abs(loss))
+    d2, dy2, dhf2, _ = _bwd_case(True, False, False, seed=48)
+    args2 = {k: d2[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta")}
+    g2 = orc.ssm_backward(**args2, dy=dy2, dh_final=dhf2)
+    loss2, _ = _loss(d2, dy2, dhf2)
+    assert abs(np.sum(g2["dB"] * d2["B"]) - loss2) <= 1e-11 * max(1.0, abs(loss2))
