@@ -628,3 +628,141 @@ def test_backward_homogeneity_identities():
     g2 = orc.ssm_backward(**args2, dy=dy2, dh_final=dhf2)
     loss2, _ = _loss(d2, dy2, dhf2)
     assert abs(np.sum(g2["dB"] * d2["B"]) - loss2) <= 1e-11 * max(1.0, abs(loss2))
+
+
+@pytest.mark.parametrize("R,Q,rope,a_tok", [(1, 4, True, False), (2, 3, True, False), (1, 5, False, True),
+                                            (4, 2, True, True)])
+def test_chunked_backward_decomposition(R, Q, rope, a_tok):
+    """The chunked backward the GPU kernel evaluates, written out with numpy:
+    a forward chunk walk keeps the shifted state entering each chunk; a
+    reverse chunk walk carries the adjoint G of that state and per chunk
+    forms the two Gram matrices C B^T and dY X^T, the masked products
+    dX = S1^T dY + w B G, dB = S2^T C + w X G^T, dC = S2 B + E dY H^T, the
+    adjoint G <- D G + C^T E dY, and the scalar gradients through the mask,
+    the readout decay E, the column weights w and the chunk decay D.  Must
+    equal the token-loop adjoint."""
+    L = 11
+    s = Shape(1, L, 2, 3, 4, R, "f32", rope)
+    d = {k: (None if v is None else np.float64(v)) for k, v in make_inputs(s, 61 + R + Q, h0=True, carry=True).items()}
+    rng = np.random.default_rng(62)
+    if a_tok:
+        d["A"] = -np.exp(rng.random((1, L, 2)) * np.log(16.0))
+    dy = rng.standard_normal(d["x"].shape)
+    dhf = rng.standard_normal((1, 2, 4, 3))
+    ref = orc.ssm_backward(**{k: d[k] for k in ("x", "B", "C", "dt", "lam", "A", "theta", "h0", "Bprev_rot",
+                                                "xprev", "phi0")}, dy=dy, dh_final=dhf)
+    x, B, C, dt, lam = (d[k] for k in ("x", "B", "C", "dt", "lam"))
+    Afull = d["A"] if a_tok else np.broadcast_to(d["A"][None, None, :], dt.shape)
+    Bt_, _, H, _, P = x.shape
+    N = B.shape[-1]
+    if rope:
+        Phi = orc.rope_angles_cumsum(d["theta"], d["phi0"])
+        Br, Cr = orc.rotate_pairs(B, Phi), orc.rotate_pairs(C, Phi)
+    else:
+        Br, Cr = B, C
+    dx = np.zeros_like(x)
+    dBr = np.zeros_like(B)
+    dCr = np.zeros_like(C)
+    ddt = np.zeros_like(dt)
+    dlam = np.zeros_like(dt)
+    dA = np.zeros_like(dt)
+    for hh in range(H):
+        b = 0
+        a = dt[b, :, hh] * Afull[b, :, hh]
+        chunks = [(s0, min(s0 + Q, L)) for s0 in range(0, L, Q)]
+
+        def scal(s0, e):
+            Lam = np.cumsum(a[s0:e])
+            gam = lam[b, s0:e, hh] * dt[b, s0:e, hh]
+            nd = np.zeros(e - s0)
+            nd[:-1] = (1 - lam[b, s0 + 1:e, hh]) * dt[b, s0 + 1:e, hh]
+            if e < L:
+                nd[-1] = (1 - lam[b, e, hh]) * dt[b, e, hh]
+            return Lam, gam, gam + nd
+
+        # forward walk: shifted state entering each chunk
+        u_m1 = d["Bprev_rot"][b, hh].T @ d["xprev"][b, hh]
+        Hs = d["h0"][b, hh] + (1 - lam[b, 0, hh]) * dt[b, 0, hh] * u_m1
+        Hin = []
+        for s0, e in chunks:
+            Hin.append(Hs)
+            Lam, gam, dl = scal(s0, e)
+            tok = np.repeat(np.arange(e - s0), R)
+            w = np.exp(Lam[-1] - Lam[tok]) * dl[tok]
+            Bm = Br[b, s0:e, hh].reshape(-1, N)
+            Xm = x[b, s0:e, hh].reshape(-1, P)
+            Hs = np.exp(Lam[-1]) * Hs + Bm.T @ (w[:, None] * Xm)
+        # reverse walk
+        G = dhf[b, hh].copy()
+        for c in range(len(chunks) - 1, -1, -1):
+            s0, e = chunks[c]
+            n = e - s0
+            Lam, gam, dl = scal(s0, e)
+            tok = np.repeat(np.arange(n), R)
+            Cm = Cr[b, s0:e, hh].reshape(-1, N)
+            Bm = Br[b, s0:e, hh].reshape(-1, N)
+            Xm = x[b, s0:e, hh].reshape(-1, P)
+            dYm = dy[b, s0:e, hh].reshape(-1, P)
+            Hc = Hin[c]
+            ti, tj = tok[:, None], tok[None, :]
+            Mt = np.where(tj < ti, np.exp(Lam[ti] - Lam[tj]) * dl[tj], 0.0)
+            Mt = np.where(tj == ti, gam[ti], Mt)
+            E = np.exp(Lam)
+            w = np.exp(Lam[-1] - Lam) * dl
+            D = np.exp(Lam[-1])
+            G1 = Cm @ Bm.T
+            G2 = dYm @ Xm.T
+            S1, S2 = Mt * G1, Mt * G2
+            BG = Bm @ G
+            dYH = dYm @ Hc.T
+            dx[b, s0:e, hh] = (S1.T @ dYm + w[tok][:, None] * BG).reshape(n, R, P)
+            dBr[b, s0:e, hh] = (S2.T @ Cm + w[tok][:, None] * (Xm @ G.T)).reshape(n, R, N)
+            dCr[b, s0:e, hh] = (S2 @ Bm + E[tok][:, None] * dYH).reshape(n, R, N)
+            # token-level scalar gradients
+            dMr = G1 * G2
+            dM = np.zeros((n, n))
+            np.add.at(dM, (ti.repeat(n * R, 1), tj.repeat(n * R, 0)), dMr)
+            dE = np.bincount(tok, weights=np.sum(dYH * Cm, axis=1), minlength=n)
+            dw = np.bincount(tok, weights=np.sum(BG * Xm, axis=1), minlength=n)
+            dD = np.sum(G * Hc)
+            T, J = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+            Mtok = np.where(J < T, np.exp(Lam[T] - Lam[J]) * dl[J], 0.0)
+            dLam = (np.sum(dM * Mtok, axis=1) - np.sum(dM * Mtok, axis=0) + dE * E - dw * w)
+            dLam[-1] += np.sum(dw * w) + dD * D
+            ddl = np.sum(np.where(T > J, dM * np.exp(Lam[T] - Lam[J]), 0.0), axis=0) + dw * np.exp(Lam[-1] - Lam)
+            dgam = np.diag(dM) + ddl
+            da = np.flip(np.cumsum(np.flip(dLam)))
+            dtt = dt[b, s0:e, hh]
+            ddt[b, s0:e, hh] += da * Afull[b, s0:e, hh] + dgam * lam[b, s0:e, hh]
+            dA[b, s0:e, hh] += da * dtt
+            dlam[b, s0:e, hh] += dgam * dtt
+            # delta_t's next-token term: tokens s0+1..e-1 here, token e in the next chunk
+            ddt[b, s0 + 1:e, hh] += ddl[:-1] * (1 - lam[b, s0 + 1:e, hh])
+            dlam[b, s0 + 1:e, hh] -= ddl[:-1] * dt[b, s0 + 1:e, hh]
+            if e < L:
+                ddt[b, e, hh] += ddl[-1] * (1 - lam[b, e, hh])
+                dlam[b, e, hh] -= ddl[-1] * dt[b, e, hh]
+            G = D * G + Cm.T @ (E[tok][:, None] * dYm)
+        # carry-in: H'_{-1} = h0 + kappa u_{-1}, kappa = (1 - lam_0) Delta_0, and
+        # G is now the adjoint of H'_{-1}
+        assert orc.rel_l2(G, ref["dh0"][b, hh]) <= 1e-12
+        dkap = np.sum(G * u_m1)
+        ddt[b, 0, hh] += dkap * (1 - lam[b, 0, hh])
+        dlam[b, 0, hh] -= dkap * dt[b, 0, hh]
+        kap = (1 - lam[b, 0, hh]) * dt[b, 0, hh]
+        assert orc.rel_l2((kap * G @ d["xprev"][b, hh].T).T, ref["dBprev_rot"][b, hh]) <= 1e-12
+        assert orc.rel_l2((kap * G.T @ d["Bprev_rot"][b, hh].T).T, ref["dxprev"][b, hh]) <= 1e-12
+    assert orc.rel_l2(dx, ref["dx"]) <= 1e-12
+    assert orc.rel_l2(ddt, ref["ddt"]) <= 1e-12
+    assert orc.rel_l2(dlam, ref["dlam"]) <= 1e-12
+    assert orc.rel_l2(dA if a_tok else dA.sum(axis=(0, 1)), ref["dA"]) <= 1e-12
+    if rope:
+        c_, s_ = np.cos(Phi)[..., None, :], np.sin(Phi)[..., None, :]
+        for dv, key in ((dBr, "dB"), (dCr, "dC")):
+            dr = np.empty_like(dv)
+            dr[..., 0::2] = c_ * dv[..., 0::2] - s_ * dv[..., 1::2]
+            dr[..., 1::2] = s_ * dv[..., 0::2] + c_ * dv[..., 1::2]
+            assert orc.rel_l2(dr, ref[key]) <= 1e-12
+    else:
+        assert orc.rel_l2(dBr, ref["dB"]) <= 1e-12
+        assert orc.rel_l2(dCr, ref["dC"]) <= 1e-12
