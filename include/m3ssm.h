@@ -272,6 +272,66 @@ typedef struct m3_decode_args {
 int m3_ssm_decode_step(const m3_decode_args* args, void* stream);
 
 /*
+ * Backward pass of the prefill: gradients of a loss that reaches the core
+ * through y (upstream gradient dy) and the final state (dh_final), by reverse-
+ * mode differentiation of the chunked evaluation ("La dualita: Mamba-2 e
+ * Mamba-3", sec. "Perche conviene: i tensor core") of the recurrence
+ * ("Znakomstvo s Mamba-3", sec. 1-3); the pages print no backward pass.  The
+ * carry-out (rotated B, x, angle) is not differentiated.
+ *
+ *   Forward inputs (as given to m3_ssm_prefill, token-major): x, B, C [Bt, L,
+ *   H, R, .] bf16; dt, lam [Bt, L, H]; A [H] or A_tok [Bt, L, H]; theta [Bt, L,
+ *   H, N/2] or NULL; carry-in h0, Bprev_rot, xprev, phi0 (nullable).
+ *   Upstream: dy [Bt, L, H, R, P] bf16; dh_final [Bt, H, N, P] float32 or NULL.
+ *   Gradients (outputs): dx, dB, dC (bf16, shapes of x, B, C); ddt, dlam [Bt,
+ *   L, H] float32; dA: [H] when A is given (summed over batch and tokens),
+ *   [Bt, L, H] when A_tok is given; dtheta [Bt, L, H, N/2] (required iff
+ *   theta); dh0 [Bt, H, N, P], dBprev_rot [Bt, H, R, N] (float32), dxprev
+ *   [Bt, H, R, P] (bf16), dphi0 [Bt, H, N/2]: each nullable.
+ *   workspace: required, m3_ssm_prefill_backward_workspace_size bytes,
+ *   256-byte aligned (the shifted state and the angle entering every chunk
+ *   of every (batch, head), written by the kernel's forward state walk).
+ * Sizes: bf16 only (M3_ERR_UNSUPPORTED for float32); N, P in {16, 32, 64,
+ * 128} whose tiles fit the LDS of a CU (N = P = 128 does not:
+ * M3_ERR_UNSUPPORTED); R a power of two <= 8; chunks of 64 / R tokens.
+ * Gradients are deterministic (no atomics).
+ */
+typedef struct m3_backward_args {
+  int32_t Bt, L, H, P, N, R;
+  int32_t in_dtype;       /* m3_dtype: M3_BF16 */
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* A;
+  const float* A_tok;
+  const float* theta;
+  const float* h0;
+  const float* Bprev_rot;
+  const void* xprev;
+  const float* phi0;
+  const void* dy;
+  const float* dh_final;
+  void* dx;
+  void* dB;
+  void* dC;
+  float* ddt;
+  float* dlam;
+  float* dA;
+  float* dtheta;
+  float* dh0;
+  float* dBprev_rot;
+  void* dxprev;
+  float* dphi0;
+  void* workspace;
+  size_t workspace_bytes;
+} m3_backward_args;
+
+size_t m3_ssm_prefill_backward_workspace_size(const m3_backward_args* args);
+int m3_ssm_prefill_backward(const m3_backward_args* args, void* stream);
+
+/*
  * Inclusive cumulative rotation angle ("Znakomstvo s Mamba-3", sec. 2: the
  * rotations are aggregated over all time steps):
  *   phi[b, t, h, j] = phi0[b, h, j] + sum_{s <= t} theta[b, s, h, j].

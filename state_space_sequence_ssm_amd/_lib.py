@@ -50,7 +50,19 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class BackwardArgs(ctypes.Structure):
+    _fields_ = [
+        ("Bt", _i32), ("L", _i32), ("H", _i32), ("P", _i32), ("N", _i32), ("R", _i32), ("in_dtype", _i32),
+        ("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp), ("lam", _vp), ("A", _vp), ("A_tok", _vp), ("theta", _vp),
+        ("h0", _vp), ("Bprev_rot", _vp), ("xprev", _vp), ("phi0", _vp), ("dy", _vp), ("dh_final", _vp),
+        ("dx", _vp), ("dB", _vp), ("dC", _vp), ("ddt", _vp), ("dlam", _vp), ("dA", _vp), ("dtheta", _vp),
+        ("dh0", _vp), ("dBprev_rot", _vp), ("dxprev", _vp), ("dphi0", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 EXPORTS = ("m3_ssm_prefill", "m3_ssm_prefill_workspace_size", "m3_ssm_prefill_noalloc", "m3_ssm_decode_step",
+           "m3_ssm_prefill_backward", "m3_ssm_prefill_backward_workspace_size",
            "m3_rope_angles_cumsum", "m3_status_string", "m3_version")
 
 _lib = None
@@ -72,6 +84,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.m3_ssm_prefill_noalloc.restype = ctypes.c_int
     lib.m3_ssm_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.m3_ssm_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.m3_ssm_prefill_backward.argtypes = [ctypes.POINTER(BackwardArgs), _vp]
+    lib.m3_ssm_prefill_backward.restype = ctypes.c_int
+    lib.m3_ssm_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(BackwardArgs)]
+    lib.m3_ssm_prefill_backward_workspace_size.restype = ctypes.c_size_t
     lib.m3_ssm_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
     lib.m3_ssm_decode_step.restype = ctypes.c_int
     lib.m3_rope_angles_cumsum.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]

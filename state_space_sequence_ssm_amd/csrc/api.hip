@@ -332,6 +332,90 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
   return hip_status(m3::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Backward workspace: states [units][chunks][N*P], angles [units][chunks][N/2],
+// per-unit dA sums [units] (A per head)
+struct BwPlan {
+  size_t oSt = 0, oPh = 0, oDA = 0, bytes = 0;
+};
+BwPlan bw_plan(const m3_backward_args* a) {
+  BwPlan w;
+  const size_t u = size_t(a->Bt) * a->H;
+  const int R = a->R > 0 ? a->R : 1;
+  const size_t nch = (size_t(a->L) + (64 / R) - 1) / (64 / R);
+  w.oSt = 0;
+  w.oPh = up256(w.oSt + u * nch * a->N * a->P * 4);
+  w.oDA = up256(w.oPh + (a->theta != nullptr ? u * nch * (a->N / 2) * 4 : 0));
+  w.bytes = up256(w.oDA + u * 4);
+  return w;
+}
+
+int check_backward(const m3_backward_args* a) {
+  if (a == nullptr) return M3_ERR_INVALID_ARG;
+  if (a->Bt < 1 || a->L < 1 || a->H < 1 || a->R < 1 || a->N < 1 || a->P < 1) return M3_ERR_INVALID_ARG;
+  if (a->in_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
+  if (!a->x || !a->B || !a->C || !a->dt || !a->lam || (!a->A && !a->A_tok) || !a->dy) return M3_ERR_INVALID_ARG;
+  if (!a->dx || !a->dB || !a->dC || !a->ddt || !a->dlam || !a->dA || !a->workspace) return M3_ERR_INVALID_ARG;
+  if (a->A != nullptr && a->A_tok != nullptr) return M3_ERR_INVALID_ARG;  // one decay source
+  if ((a->Bprev_rot == nullptr) != (a->xprev == nullptr)) return M3_ERR_INVALID_ARG;
+  if ((a->theta == nullptr) != (a->dtheta == nullptr)) return M3_ERR_INVALID_ARG;
+  if (a->theta == nullptr && (a->phi0 != nullptr || a->dphi0 != nullptr)) return M3_ERR_INVALID_ARG;
+  if (a->theta != nullptr && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
+  if (!pow2(a->R) || a->R > 8) return M3_ERR_UNSUPPORTED;
+  if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
+  const void* v16[] = {a->x, a->B, a->C, a->dy, a->dx, a->dB, a->dC, a->theta, a->dtheta, a->h0, a->dh_final,
+                       a->dh0, a->Bprev_rot, a->dBprev_rot, a->xprev, a->dxprev, a->phi0, a->dphi0};
+  for (const void* p : v16)
+    if (!al16(p)) return M3_ERR_INVALID_ARG;
+  if (!al4(a->dt) || !al4(a->lam) || !al4(a->A) || !al4(a->A_tok) || !al4(a->ddt) || !al4(a->dlam) || !al4(a->dA))
+    return M3_ERR_INVALID_ARG;
+  const double item = double(a->L) * a->H * a->R * (a->N > a->P ? a->N : a->P) * 2.0;
+  if (item > 4.0e18 || double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
+  const size_t lds = m3::backward_lds_bytes(a->N, a->P, a->theta != nullptr);
+  if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
+  const BwPlan w = bw_plan(a);
+  if (a->workspace_bytes < w.bytes || !aligned(a->workspace, 256)) return M3_ERR_INVALID_ARG;
+  return M3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t m3_ssm_prefill_backward_workspace_size(const m3_backward_args* a) {
+  if (a == nullptr || a->Bt < 1 || a->L < 1 || a->H < 1 || a->N < 1 || a->P < 1 || a->R < 1) return 0;
+  return bw_plan(a).bytes;
+}
+
+int m3_ssm_prefill_backward(const m3_backward_args* a, void* stream) {
+  const int rc = check_backward(a);
+  if (rc != M3_OK) return rc;
+  const BwPlan w = bw_plan(a);
+  unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+  m3::BackwardParams p{};
+  p.Bt = a->Bt; p.L = a->L; p.H = a->H; p.P = a->P; p.N = a->N; p.R = a->R;
+  int lg = 0;
+  while ((1 << lg) < a->R) ++lg;
+  p.log2R = lg;
+  p.x = a->x; p.B = a->B; p.C = a->C; p.dt = a->dt; p.lam = a->lam; p.A = a->A; p.A_tok = a->A_tok;
+  p.theta = a->theta; p.h0 = a->h0; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev; p.phi0 = a->phi0;
+  p.dy = a->dy; p.dh_final = a->dh_final;
+  p.dx = a->dx; p.dB = a->dB; p.dC = a->dC; p.ddt = a->ddt; p.dlam = a->dlam;
+  p.dA_tok = a->A_tok != nullptr ? a->dA : nullptr;
+  p.dA_part = a->A_tok != nullptr ? nullptr : reinterpret_cast<float*>(ws + w.oDA);
+  p.dtheta = a->dtheta; p.dh0 = a->dh0; p.dBprev_rot = a->dBprev_rot; p.dxprev = a->dxprev; p.dphi0 = a->dphi0;
+  p.states = reinterpret_cast<float*>(ws + w.oSt);
+  p.phis = a->theta != nullptr ? reinterpret_cast<float*>(ws + w.oPh) : nullptr;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = m3::launch_backward(p, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (a->A_tok == nullptr) e = m3::launch_backward_dA(p.dA_part, a->dA, a->Bt, a->H, st);
+  return hip_status(e);
+}
+
 int m3_rope_angles_cumsum(const float* theta, const float* phi0, float* phi, int32_t Bt, int32_t L,
                           int32_t H, int32_t npairs, void* stream) {
   if (theta == nullptr || phi == nullptr) return M3_ERR_INVALID_ARG;

@@ -134,4 +134,50 @@ __device__ __forceinline__ float wrap_angle(float a) {
   return a - kTwoPi * rintf(a * kInvTwoPi);
 }
 
+// ---------------------------------------------------------------- MFMA and LDS fragments
+// D (16 x 16, fp32) += A (16 x 32) B (32 x 16) on bf16 operands: lane (g =
+// lane / 16, l16 = lane % 16) supplies row l16 of A and column l16 of B at
+// eight k positions, and holds D[4 g + 0..3][l16] (gfx950 v_mfma_f32_16x16x32_bf16).
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 cat8(u32x2 lo, u32x2 hi) {
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return as_bf16x8(v);
+}
+__device__ __forceinline__ u32x2 pack4(f32x4 v) { return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}; }
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  In each group of 16
+// lanes, lane 4e + q reads 4 bf16 at its own address; afterwards lane i holds
+// element i % 4 of lanes 4e + i / 4, e = 0..3.  With lane 4e + q pointing at
+// columns c0 + 4q..+3 of row r_e of a row-major matrix, lane i receives column
+// c0 + i of rows r_0..r_3: four k values of an MFMA operand column.
+typedef short tr4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) tr4_t* lds_tr4_ptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p)));
+}
+template <int CTRL, int ROWMASK, bool BOUND>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF, BOUND));
+}
+// Inclusive scan over aligned segments of W lanes (W a power of two, 8..64):
+// row_shr 1/2/4/8 within rows of 16, then row_bcast 15 / 31 across rows.
+template <int W>
+__device__ __forceinline__ float seg_scan(float v) {
+  const int sl = threadIdx.x & (W - 1);
+  float t;
+  t = dpp<0x111, 0xF, true>(v);
+  v += (W >= 16 || sl >= 1) ? t : 0.f;
+  t = dpp<0x112, 0xF, true>(v);
+  v += (W >= 16 || sl >= 2) ? t : 0.f;
+  t = dpp<0x114, 0xF, true>(v);
+  v += (W >= 16 || sl >= 4) ? t : 0.f;
+  if constexpr (W >= 16) v += dpp<0x118, 0xF, true>(v);
+  if constexpr (W >= 32) v += dpp<0x142, 0xA, false>(v);
+  if constexpr (W >= 64) v += dpp<0x143, 0xC, false>(v);
+  return v;
+}
+
+
 }  // namespace m3

@@ -104,6 +104,44 @@ struct PrefillParams {
   Prologue pro;
 };
 
+// Backward of the bf16 prefill (backward.hip): forward inputs, upstream
+// gradients, gradient outputs and the workspace of chunk-entry states.
+struct BackwardParams {
+  int Bt, L, H, P, N, R, log2R;
+  const void* x;
+  const void* B;
+  const void* C;
+  const float* dt;
+  const float* lam;
+  const float* A;      // [H] or null
+  const float* A_tok;  // [Bt, L, H] or null
+  const float* theta;  // [Bt, L, H, N/2] or null
+  const float* h0;
+  const float* Bprev_rot;
+  const void* xprev;
+  const float* phi0;
+  const void* dy;        // [Bt, L, H, R, P] bf16
+  const float* dh_final; // [Bt, H, N, P] or null
+  void* dx;
+  void* dB;
+  void* dC;
+  float* ddt;
+  float* dlam;
+  float* dA_tok;    // [Bt, L, H] when A_tok is given
+  float* dA_part;   // [Bt * H] per-unit sums of dA (workspace) when A is per head
+  float* dtheta;    // [Bt, L, H, N/2] or null
+  float* dh0;
+  float* dBprev_rot;
+  void* dxprev;
+  float* dphi0;
+  float* states;    // [Bt * H][chunks][N * P] shifted state entering each chunk (fp32)
+  float* phis;      // [Bt * H][chunks][N/2] angle entering each chunk
+};
+hipError_t launch_backward(const BackwardParams& p, hipStream_t s);
+// dA [H] = sum over the batch of the per-unit sums
+hipError_t launch_backward_dA(const float* part, float* dA, int Bt, int H, hipStream_t s);
+size_t backward_lds_bytes(int N, int P, bool rope);
+
 struct AnglesParams {
   const float* theta;
   const float* phi0;

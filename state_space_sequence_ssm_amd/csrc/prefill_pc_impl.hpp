@@ -72,15 +72,6 @@ constexpr uint32_t kBad = 0x7FFFFFF0u;  // buffer offset past any valid range ->
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ bf16x8 cat8(u32x2 lo, u32x2 hi) {
-  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-  return as_bf16x8(v);
-}
-__device__ __forceinline__ u32x2 pack4(f32x4 v) { return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}; }
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
@@ -92,16 +83,6 @@ __device__ __forceinline__ float bloadf(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ f32x4 bloadf4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  In each group of 16
-// lanes, lane 4e + q reads 4 bf16 at its own address; afterwards lane i holds
-// element i % 4 of lanes 4e + i / 4, e = 0..3.  With lane 4e + q pointing at
-// columns c0 + 4q..+3 of row r_e of a row-major matrix, lane i receives column
-// c0 + i of rows r_0..r_3: four k values of an MFMA operand column.
-typedef short tr4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) tr4_t* lds_tr4_ptr;
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p)));
 }
 // Row-major bf16 tiles of D columns (D = 32, 64 or 128) keep their 8-byte
 // units XOR-swizzled by row.  Measured on gfx950: an 8-byte read (plain or
@@ -154,28 +135,6 @@ __device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
 __device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
-template <int CTRL, int ROWMASK, bool BOUND>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF, BOUND));
-}
-// Inclusive scan over aligned segments of W lanes (W a power of two, 8..64):
-// row_shr 1/2/4/8 within rows of 16, then row_bcast 15 / 31 across rows.
-template <int W>
-__device__ __forceinline__ float seg_scan(float v) {
-  const int sl = threadIdx.x & (W - 1);
-  float t;
-  t = dpp<0x111, 0xF, true>(v);
-  v += (W >= 16 || sl >= 1) ? t : 0.f;
-  t = dpp<0x112, 0xF, true>(v);
-  v += (W >= 16 || sl >= 2) ? t : 0.f;
-  t = dpp<0x114, 0xF, true>(v);
-  v += (W >= 16 || sl >= 4) ? t : 0.f;
-  if constexpr (W >= 16) v += dpp<0x118, 0xF, true>(v);
-  if constexpr (W >= 32) v += dpp<0x142, 0xA, false>(v);
-  if constexpr (W >= 64) v += dpp<0x143, 0xC, false>(v);
-  return v;
-}
-
 // One staging load instruction: instruction i of the unit (16 rows x column
 // block cb of B, C or X: kind 0, 1, 2).  Lanes read whole 128-byte lines, 8
 // lanes per row (64-byte rows when the block is narrower), so each load asks

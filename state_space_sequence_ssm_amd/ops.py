@@ -145,6 +145,70 @@ def m3_ssm_prefill(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xpr
     return dict(y=y, h=h_final, Bprev_rot=Bprev_rot_out, xprev=xprev_out, phi=phi_out)
 
 
+def m3_ssm_prefill_backward(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=None, xprev=None, phi0=None,
+                            *, dy, dh_final=None, A_tok=None, want_carry_grads=False, workspace=None,
+                            out=None, stream=None):
+    """Gradients of the prefill for upstream dy [Bt,L,H,R,P] (bf16) and
+    dh_final [Bt,H,N,P] (fp32, optional).  Forward inputs as for
+    m3_ssm_prefill (bf16, token-major).  Returns a dict with dx, dB, dC (bf16),
+    ddt, dlam (fp32 [Bt,L,H]), dA ([H], or [Bt,L,H] with A_tok), dtheta (with
+    theta) and, with want_carry_grads, dh0, dBprev_rot, dxprev, dphi0.  `out`:
+    optional dict of preallocated gradient tensors (any subset of those keys)."""
+    Bt, L, H, R, P = x.shape
+    N = B.shape[-1]
+    f32, dev = torch.float32, x.device
+    given = out
+    out = dict(dx=torch.empty_like(x), dB=torch.empty_like(B), dC=torch.empty_like(C),
+               ddt=torch.empty((Bt, L, H), device=dev, dtype=f32), dlam=torch.empty((Bt, L, H), device=dev, dtype=f32),
+               dA=torch.empty((Bt, L, H) if A_tok is not None else (H,), device=dev, dtype=f32),
+               dtheta=None if theta is None else torch.empty_like(theta),
+               dh0=None, dBprev_rot=None, dxprev=None, dphi0=None)
+    if want_carry_grads:
+        out["dh0"] = torch.empty((Bt, H, N, P), device=dev, dtype=f32)
+        if Bprev_rot is not None:
+            out["dBprev_rot"] = torch.empty((Bt, H, R, N), device=dev, dtype=f32)
+            out["dxprev"] = torch.empty((Bt, H, R, P), device=dev, dtype=x.dtype)
+        if theta is not None:
+            out["dphi0"] = torch.empty((Bt, H, N // 2), device=dev, dtype=f32)
+    for k, v in (given or {}).items():
+        out[k] = v
+    a = _lib.BackwardArgs()
+    a.Bt, a.L, a.H, a.P, a.N, a.R = Bt, L, H, P, N, R
+    a.in_dtype = _dtype_code(x)
+    big = lambda D: (Bt, L, H, R, D)  # noqa: E731
+    a.x = _ptr(x, x.dtype, big(P), "x")
+    a.B = _ptr(B, x.dtype, big(N), "B")
+    a.C = _ptr(C, x.dtype, big(N), "C")
+    a.dt = _ptr(dt, f32, (Bt, L, H), "dt")
+    a.lam = _ptr(lam, f32, (Bt, L, H), "lam")
+    a.A = _ptr(A, f32, (H,), "A")
+    a.A_tok = _ptr(A_tok, f32, (Bt, L, H), "A_tok")
+    a.theta = _ptr(theta, f32, (Bt, L, H, N // 2), "theta")
+    a.h0 = _ptr(h0, f32, (Bt, H, N, P), "h0")
+    a.Bprev_rot = _ptr(Bprev_rot, f32, (Bt, H, R, N), "Bprev_rot")
+    a.xprev = _ptr(xprev, x.dtype, (Bt, H, R, P), "xprev")
+    a.phi0 = _ptr(phi0, f32, (Bt, H, N // 2), "phi0")
+    a.dy = _ptr(dy, x.dtype, big(P), "dy")
+    a.dh_final = _ptr(dh_final, f32, (Bt, H, N, P), "dh_final")
+    shapes = dict(dx=big(P), dB=big(N), dC=big(N), ddt=(Bt, L, H), dlam=(Bt, L, H),
+                  dA=(Bt, L, H) if A_tok is not None else (H,), dtheta=(Bt, L, H, N // 2), dh0=(Bt, H, N, P),
+                  dBprev_rot=(Bt, H, R, N), dxprev=(Bt, H, R, P), dphi0=(Bt, H, N // 2))
+    for k in ("dx", "dB", "dC", "dxprev"):
+        setattr(a, k, _ptr(out[k], x.dtype, shapes[k], k))
+    for k in ("ddt", "dlam", "dA", "dtheta", "dh0", "dBprev_rot", "dphi0"):
+        setattr(a, k, _ptr(out[k], f32, shapes[k], k))
+    lib = _lib.load()
+    need = lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(workspace, torch.uint8, None, "workspace")
+    a.workspace_bytes = workspace.numel()
+    rc = lib.m3_ssm_prefill_backward(ctypes.byref(a), _stream(stream))
+    if rc != _lib.M3_OK:
+        raise M3Error(rc, "m3_ssm_prefill_backward")
+    return out
+
+
 def prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=torch.bfloat16, rope=False):
     """Bytes of the optional prefill workspace for this shape (0: none used)."""
     a = _lib.PrefillArgs()
