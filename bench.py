@@ -175,6 +175,52 @@ def prefill_algo(Bt, L, H, P, N, R, rope, omega=False, a_tok=False, pro=False):
     return byts, flops
 
 
+def backward_algo(Bt, L, H, P, N, R, rope):
+    """Algorithmic bytes and MFMA flops of the backward: x, B, C, dy (bf16),
+    Delta, lambda (and theta) read once; dx, dB, dC (bf16), dDelta, dlambda
+    (and dtheta) written once; A and dA per head.  Flops per chunk of Q
+    tokens (64 rows) and (b, h): the two Gram products, S1^T dY, B G, S2^T C,
+    X G^T, S2 B, dY H^T, the adjoint update and the forward state walk,
+    2 * 64 * (3 * 64 N + 2 * 64 P + 5 N P)."""
+    bf, f4 = 2, 4
+    tok = Bt * L * H
+    byts = 2 * tok * R * (2 * P + 2 * N) * bf + 2 * tok * 2 * f4 + 2 * H * f4
+    if rope:
+        byts += 2 * tok * (N // 2) * f4
+    chunks = Bt * H * ((L + (64 // R) - 1) // (64 // R))
+    flops = chunks * 2 * 64 * (3 * 64 * N + 2 * 64 * P + 5 * N * P)
+    return byts, flops
+
+
+def backward_kernel_name(rope, N, P):
+    return f"m3::bw::backward_kernel<{N}, {P}, {'true' if rope else 'false'}>"
+
+
+def time_backward(torch, ops, inp, steps, warmup):
+    """Average duration of the backward of one prefill workload (gradients of
+    every input; upstream dy drawn N(0,1) in bf16, dh_final N(0,1))."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260300)
+    x = inp["x"]
+    Bt, L, H, R, P = x.shape
+    N = inp["B"].shape[-1]
+    dy = torch.randn(x.shape, generator=g, device="cuda").to(torch.bfloat16)
+    dhf = torch.randn((Bt, H, N, P), generator=g, device="cuda")
+    out = ops.m3_ssm_prefill_backward(x, inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], inp["theta"],
+                                      dy=dy, dh_final=dhf)
+    ws = torch.empty(ops.backward_workspace_bytes(Bt, L, H, P, N, R, rope=inp["theta"] is not None),
+                     dtype=torch.uint8, device="cuda")
+
+    def run():
+        ops.m3_ssm_prefill_backward(x, inp["B"], inp["C"], inp["dt"], inp["lam"], inp["A"], inp["theta"], dy=dy,
+                                    dh_final=dhf, workspace=ws, out=out)
+
+    for _ in range(max(warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    return replay_ms(torch, [run] * steps)
+
+
 def decode_algo(Bt, H, P, N, R, rope):
     bf, f4 = 2, 4
     u = Bt * H
@@ -700,7 +746,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "headline", "pmc"), default="all")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "headline", "backward", "pmc"), default="all")
     ap.add_argument("--group", choices=("base", "variants", "prologue"), default="base")
     ap.add_argument("--report-trace", metavar="PREFIX")
     ap.add_argument("--report-pmc", nargs="+", metavar="GROUP FETCH_PREFIX WRITE_PREFIX")
@@ -787,6 +833,25 @@ def main():
                   f"{flushed:.3f} ms per launch after an Infinity Cache eviction", file=sys.stderr, flush=True)
             del inp
             torch.cuda.empty_cache()
+    if args.only in ("all", "prefill", "backward"):
+        for i, (name, shp) in enumerate(prefill_shapes().items()):
+            Bt, L, H, P, N, R, rope = shp
+            inp = gen_prefill(torch, Bt, L, H, P, N, R, rope, seed=20260400 + i)
+            ms = time_backward(torch, ops, inp, max(args.steps // 5, 3), max(args.warmup // 5, 1))
+            byts, flops = backward_algo(*shp)
+            res = dict(workload=f"backward {name}: Bt={Bt} L={L} H={H} P={P} N={N} R={R} "
+                                f"{'RoPE' if rope else 'real'} bf16, gradients of x, B, C, Delta, lambda, A"
+                                f"{', theta' if rope else ''}",
+                       tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, gbs=byts / (ms * 1e-3) / 1e9,
+                       tflops=flops / (ms * 1e-3) / 1e12, bytes=byts, flops=flops,
+                       kernel=backward_kernel_name(rope, N, P), traffic=traffic_for("backward_" + name))
+            res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
+            res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFS
+            results["backward_" + name] = res
+            print(f"# {res['workload']}: {ms:.3f} ms, {res['tokens_per_s']:.3e} tok/s, {res['gbs']:.0f} GB/s "
+                  f"({100 * res['hbm_frac']:.1f}% HBM), {res['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            del inp
+            torch.cuda.empty_cache()
     if args.only in ("all", "prefill"):
         Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
         ms, byts = time_angles(torch, ops, Bt, L, H, N // 2, args.steps, args.warmup, seed=20260110)
@@ -851,6 +916,9 @@ def main():
                                   "achieved_after_cache_eviction": dres["gbs_after_cache_eviction"]}
     if "decode_bt512" in results:
         out["decode_bt512"] = results["decode_bt512"]
+    for name in prefill_shapes():
+        if "backward_" + name in results:
+            out["backward_" + name] = results["backward_" + name]
     for k in ["siso_rope", "mimo_rope"] + [line for line, _, _ in VARIANTS]:
         if k in results:
             out["prefill_" + k] = results[k]

@@ -18,7 +18,9 @@
 //   dM = (C B^T) o (dY X^T), dE_i = <dY_i H^T, Ctil_i>, dw_j = <(B G)_j, x_j>,
 //   dD = <G, H>  -> Lam, delta, gamma -> Delta, lambda, A
 // and through the rotation dB = R(Phi) dBtil, dPhi = dBtil_0 Btil_1 -
-// dBtil_1 Btil_0 per pair (likewise for C), dtheta = reverse running sum of dPhi.
+// dBtil_1 Btil_0 per pair (likewise for C); dtheta_t, the sum of dPhi over
+// tokens >= t, is <dh_final, J h_final> - <G, J H> at each chunk start (the
+// state carried across it) plus this chunk's dPhi after t.
 //
 // MI355X design.  One 512-thread workgroup (8 wave64) per (batch, head).  It
 // first walks the chunks forward for the state only (B and X staged in LDS,
@@ -321,6 +323,30 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   }
 
   // ================================================================ backward walk
+  // dtheta at a chunk start s has a closed form: a common extra rotation of
+  // every token from s on changes only the state carried across s, so
+  // dtheta_s = <dh_final, J h_final> - <G, J H> per pair, H the shifted state
+  // entering the chunk, G its gradient, J the derivative of the pair rotation
+  // (J (v0, v1) = (v1, -v0)).  Inside a chunk dtheta is that value at the next
+  // chunk start plus a running sum of at most Q tokens' dPhi: no sum over the
+  // whole sequence, whose terms would mostly cancel.  Per-pair partial sums of
+  // <., J .> (row p reduced over the 16 lanes of a tile) go to sAnc [PT][J].
+  float* const sAnc = reinterpret_cast<float*>(sS1);  // free from the G update to the next Gram phase
+  auto turn_parts = [&](int m, f32x4 gv, f32x4 hv) __attribute__((always_inline)) {
+    const float v0 = seg_scan<16>(gv[0] * hv[1] - gv[1] * hv[0]);
+    const float v1 = seg_scan<16>(gv[2] * hv[3] - gv[3] * hv[2]);
+    if (l16 == 15) {
+      const int q = 8 * tile_nt(m) + 2 * g;
+      sAnc[tile_pt(m) * J + q] = v0;
+      sAnc[tile_pt(m) * J + q + 1] = v1;
+    }
+  };
+  auto turn_sum = [&](int q) {
+    float s = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) s += sAnc[pt * J + q];
+    return s;
+  };
   // G (gradient of the shifted state) starts from dh_final
 #pragma unroll
   for (int m = 0; m < STW; ++m) {
@@ -331,13 +357,27 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         a[jj] = p.dh_final[static_cast<size_t>(bh) * N * P + static_cast<size_t>(16 * tile_nt(m) + 4 * g + jj) * P +
                            16 * tile_pt(m) + l16];
     }
+    if constexpr (ROPE)
+      if (tile_ok(m)) turn_parts(m, a, acc[m]);  // acc is the final state here
     acc[m] = a;
   }
-  float thCarry = 0.f;                          // sum of dPhi over later tokens (thread 64 + q)
+  float Tq = 0.f;                               // <dh_final, J h_final> of pair q (thread 64 + q)
+  if constexpr (ROPE) {
+    __syncthreads();
+    const int q = tid - 64;
+    if (q >= 0 && q < J) Tq = turn_sum(q);
+  }
+  float thCarry = 0.f;                          // dtheta at the next chunk start, then the running sum (thread 64 + q)
   float pendDt = 0.f, pendLam = 0.f;            // first token of the later chunk (wave 0, lane 0)
   int pendTok = -1;
   float dAsum = 0.f;                            // sum of dA over tokens (wave 0, lane 0)
+  f32x4 hsave[STW];                             // the shifted state entering the chunk (fp32)
   for (int c = nch - 1; c >= 0; --c) {
+    if constexpr (ROPE) {
+      // dtheta at the start of chunk c + 1, from the parts its pass left in sAnc
+      const int q = tid - 64;
+      if (c < nch - 1 && q >= 0 && q < J) thCarry = Tq - turn_sum(q);
+    }
     scalars(c);
     angles_load(c);
     __syncthreads();
@@ -358,6 +398,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (!tile_ok(m)) continue;
         const f32x4 hv =
             *reinterpret_cast<const f32x4*>(stBase + (static_cast<size_t>(c) * NST + wave + kWaves * m) * 256 + lane * 4);
+        hsave[m] = hv;
         const int at = (16 * tile_pt(m) + l16) * PN + 16 * tile_nt(m) + 4 * g;
         *reinterpret_cast<u32x2*>(sHT + at) = pack4(hv);
         *reinterpret_cast<u32x2*>(sGT + at) = pack4(acc[m]);
@@ -473,28 +514,40 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         f32x4 dc = c1 + E[tl] * c2;
         // dE_i part: <(dY H^T)_i, Ctil_i> over the four columns
         const u32x2 cv = *reinterpret_cast<const u32x2*>(sCr + r * PN + 16 * nt + 4 * g);
-        const u32x2 bv = *reinterpret_cast<const u32x2*>(sBr + r * PN + 16 * nt + 4 * g);
         const float cr[4] = {__uint_as_float(cv[0] << 16), __uint_as_float(cv[0] & 0xffff0000u),
                              __uint_as_float(cv[1] << 16), __uint_as_float(cv[1] & 0xffff0000u)};
-        const float br[4] = {__uint_as_float(bv[0] << 16), __uint_as_float(bv[0] & 0xffff0000u),
-                             __uint_as_float(bv[1] << 16), __uint_as_float(bv[1] & 0xffff0000u)};
         float s = c2[0] * cr[0] + c2[1] * cr[1] + c2[2] * cr[2] + c2[3] * cr[3];
         s += __shfl_xor(s, 16);
         s += __shfl_xor(s, 32);
         if (g == 0) sEp[nt * 64 + r] = s;
         if constexpr (ROPE) {
-          // back through the rotation; the pair's angle gradient from B and C
+          // Back through the rotation, then the pair's angle gradient.  A
+          // rotation commutes with the quarter turn J, so db~ . J b~ equals
+          // (R^T db~) . J b: the angle gradient is taken against the
+          // unrotated inputs, exact in bf16, instead of the bf16-rounded
+          // rotated tiles (whose rounding would bias the long running sums
+          // of dtheta).
+          u32x2 bu = {0u, 0u}, cu = {0u, 0u};
+          if (valid(c, r)) {
+            bu = *reinterpret_cast<const u32x2*>(Bg + grow(c, r) * N + 16 * nt + 4 * g);
+            cu = *reinterpret_cast<const u32x2*>(Cg + grow(c, r) * N + 16 * nt + 4 * g);
+          }
+          const float bx[4] = {__uint_as_float(bu[0] << 16), __uint_as_float(bu[0] & 0xffff0000u),
+                               __uint_as_float(bu[1] << 16), __uint_as_float(bu[1] & 0xffff0000u)};
+          const float cx[4] = {__uint_as_float(cu[0] << 16), __uint_as_float(cu[0] & 0xffff0000u),
+                               __uint_as_float(cu[1] << 16), __uint_as_float(cu[1] & 0xffff0000u)};
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int q = 8 * nt + 2 * g + h2;
             const float ang = sPhi[tl * J + q];
             const float cs = __cosf(ang), sn = __sinf(ang);
             const float d0 = db[2 * h2], d1 = db[2 * h2 + 1], e0 = dc[2 * h2], e1 = dc[2 * h2 + 1];
-            sDPhi[r * J + q] = d0 * br[2 * h2 + 1] - d1 * br[2 * h2] + e0 * cr[2 * h2 + 1] - e1 * cr[2 * h2];
             db[2 * h2] = cs * d0 - sn * d1;
             db[2 * h2 + 1] = sn * d0 + cs * d1;
             dc[2 * h2] = cs * e0 - sn * e1;
             dc[2 * h2 + 1] = sn * e0 + cs * e1;
+            sDPhi[r * J + q] = db[2 * h2] * bx[2 * h2 + 1] - db[2 * h2 + 1] * bx[2 * h2] +
+                               dc[2 * h2] * cx[2 * h2 + 1] - dc[2 * h2 + 1] * cx[2 * h2];
           }
         }
         if (valid(c, r)) {
@@ -516,6 +569,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
     }
     __syncthreads();
+    if constexpr (ROPE) {
+      // parts of <G, J H> for the start of this chunk (read at the next chunk's pass)
+#pragma unroll
+      for (int m = 0; m < STW; ++m)
+        if (tile_ok(m)) turn_parts(m, acc[m], hsave[m]);
+    }
 
     // ---- per-token scalar gradients (wave 0, lane = token)
     if (wave == 0) {
@@ -589,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
     }
     if constexpr (ROPE) {
-      // dtheta_t = sum of dPhi over tokens >= t (threads 64 + q)
+      // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens >= t (threads 64 + q)
       const int q = tid - 64;
       if (q >= 0 && q < J) {
         for (int tl = Q - 1; tl >= 0; --tl) {

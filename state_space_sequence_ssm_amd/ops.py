@@ -209,6 +209,14 @@ def m3_ssm_prefill_backward(x, B, C, dt, lam, A, theta=None, h0=None, Bprev_rot=
     return out
 
 
+def backward_workspace_bytes(Bt, L, H, P, N, R, rope=False):
+    """Bytes of the workspace m3_ssm_prefill_backward needs for this shape."""
+    a = _lib.BackwardArgs()
+    a.Bt, a.L, a.H, a.P, a.N, a.R = Bt, L, H, P, N, R
+    a.theta = 1 if rope else None  # only NULL-ness is read
+    return _lib.load().m3_ssm_prefill_backward_workspace_size(ctypes.byref(a))
+
+
 def prefill_workspace_bytes(Bt, L, H, P, N, R, dtype=torch.bfloat16, rope=False):
     """Bytes of the optional prefill workspace for this shape (0: none used)."""
     a = _lib.PrefillArgs()

@@ -240,3 +240,48 @@ def test_validation_under_host_sanitizers():
     tail = (r.stdout + r.stderr)[-4000:]
     assert r.returncode == 0, tail
     assert "passed" in r.stdout and "ERROR: AddressSanitizer" not in tail and "runtime error" not in tail, tail
+
+
+def _good_backward():
+    a = _lib.BackwardArgs()
+    a.Bt, a.L, a.H, a.P, a.N, a.R, a.in_dtype = 2, 100, 3, 64, 64, 1, _lib.M3_BF16
+    for i, f in enumerate(("x", "B", "C", "dt", "lam", "A", "dy", "dx", "dB", "dC", "ddt", "dlam", "dA")):
+        setattr(a, f, 0x10000000 + 0x100000 * i)
+    a.workspace = 0x40000000
+    a.workspace_bytes = _lib.load().m3_ssm_prefill_backward_workspace_size(ctypes.byref(a))
+    return a
+
+
+def test_backward_validation_and_workspace():
+    lib = _lib.load()
+    f = lambda a: lib.m3_ssm_prefill_backward(ctypes.byref(a), None)  # noqa: E731
+    assert lib.m3_ssm_prefill_backward(None, None) == _lib.M3_ERR_INVALID_ARG
+    a = _good_backward()
+    # states of every chunk (2 x 3 units, 2 chunks of 64, 64 x 64 fp32) and per-unit dA sums
+    assert a.workspace_bytes == _up256(6 * 2 * 64 * 64 * 4) + _up256(6 * 4)
+    cases = [
+        (lambda a: setattr(a, "dy", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "dA", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "workspace", None), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "workspace_bytes", a.workspace_bytes - 1), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "workspace", 0x40000010), _lib.M3_ERR_INVALID_ARG),  # not 256-aligned
+        (lambda a: setattr(a, "in_dtype", _lib.M3_F32), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "theta", 0x30000000), _lib.M3_ERR_INVALID_ARG),   # theta without dtheta
+        (lambda a: setattr(a, "dtheta", 0x30000000), _lib.M3_ERR_INVALID_ARG),  # dtheta without theta
+        (lambda a: setattr(a, "A_tok", 0x30000000), _lib.M3_ERR_INVALID_ARG),   # both A and A_tok
+        (lambda a: setattr(a, "Bprev_rot", 0x30000000), _lib.M3_ERR_INVALID_ARG),
+        (lambda a: setattr(a, "R", 16), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: (setattr(a, "N", 128), setattr(a, "P", 128)), _lib.M3_ERR_UNSUPPORTED),  # LDS
+        (lambda a: setattr(a, "dx", 0x10000008), _lib.M3_ERR_INVALID_ARG),
+    ]
+    for mutate, code in cases:
+        a = _good_backward()
+        mutate(a)
+        if code == _lib.M3_ERR_UNSUPPORTED and a.N == 128:
+            a.workspace_bytes = lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a))
+        assert f(a) == code
+    # with RoPE the angle entering every chunk is kept too
+    a = _good_backward()
+    a.theta, a.dtheta = 0x30000000, 0x30100000
+    assert lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a)) == (
+        _up256(6 * 2 * 64 * 64 * 4) + _up256(6 * 2 * 32 * 4) + _up256(6 * 4))

@@ -21,6 +21,26 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
+def _dphi(theta, axis):
+    """Per-token angle gradients dPhi_t = dtheta_t - dtheta_{t+1} (dtheta is
+    their reverse running sum): checked as well, so that an error in single
+    tokens cannot hide in the sums."""
+    d = np.array(theta, dtype=np.float64)
+    cur = [slice(None)] * d.ndim
+    nxt = [slice(None)] * d.ndim
+    cur[axis], nxt[axis] = slice(0, -1), slice(1, None)
+    d[tuple(cur)] -= np.array(theta, dtype=np.float64)[tuple(nxt)]
+    return d
+
+
+def _check(got_k, ref_k, k, errs, axis=1):
+    errs[k] = orc.rel_l2(got_k, ref_k)
+    assert errs[k] <= TOL, (k, errs[k])
+    if k == "dtheta":
+        errs["dPhi"] = orc.rel_l2(_dphi(got_k, axis), _dphi(ref_k, axis))
+        assert errs["dPhi"] <= TOL, ("dPhi", errs["dPhi"])
+
+
 @pytest.fixture(scope="module")
 def ops():
     if not torch.cuda.is_available():
@@ -90,10 +110,8 @@ def test_backward_vs_oracle(ops, case):
     for k in keys:
         g = host(got[k])
         assert np.all(np.isfinite(g)), k
-        errs[k] = orc.rel_l2(g, ref[k])
+        _check(g, ref[k], k, errs)
     _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, e in errs.items():
-        assert e <= TOL, (k, e)
 
 
 def test_backward_deterministic(ops):
@@ -110,3 +128,37 @@ def test_backward_deterministic(ops):
     for k in a:
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_backward_config_full_size(ops, cfg):
+    """The backward at the prefill workloads' full sizes; the oracle's adjoint
+    checks four (batch, head) units spread over the unit axis, one by one."""
+    from tests.fixtures import CONFIGS, SEED_BASE
+    from tests.gpu_util import pick_units, sample_units
+    s = CONFIGS[cfg]
+    _say("backward config", cfg, s)
+    d = make_inputs(s, SEED_BASE + cfg)
+    rng = np.random.default_rng(SEED_BASE + 100 + cfg)
+    dy = bf16_round(rng.standard_normal((s.Bt, s.L, s.H, s.R, s.P)).astype(np.float32))
+    dhf = rng.standard_normal((s.Bt, s.H, s.N, s.P)).astype(np.float32)
+    dd = to_device(d, s)
+    out = _nan_out(dd, s.Bt, s.L, s.H, s.P, s.N, s.R, s.rope, False, False)
+    got = ops.m3_ssm_prefill_backward(dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], dd["A"], dd["theta"],
+                                      dy=dev(dy, torch.bfloat16), dh_final=dev(dhf), want_carry_grads=True, out=out)
+    torch.cuda.synchronize()
+    units = sample_units(s.Bt * s.H, ranges=4, per_range=1)
+    sub = pick_units(dict(d, dy=dy), units, s.H)
+    dhf_s = np.stack([dhf[u // s.H, u % s.H] for u in units])[None]
+    ref = orc.ssm_backward(sub["x"], sub["B"], sub["C"], sub["dt"], sub["lam"], sub["A"], sub["theta"],
+                           dy=sub["dy"], dh_final=dhf_s)
+    keys = ["dx", "dB", "dC", "ddt", "dlam", "dh0"] + (["dtheta"] if s.rope else [])
+    for i, u in enumerate(units):
+        b, h = divmod(u, s.H)
+        errs = {}
+        for k in keys:
+            g = host(got[k][b, :, h] if k not in ("dh0",) else got[k][b, h])
+            r = ref[k][0, :, i] if k not in ("dh0",) else ref[k][0, i]
+            _check(g, r, k, errs, axis=0)  # [L, ...]: the token axis is 0 here
+        _say(f"  unit {u}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))

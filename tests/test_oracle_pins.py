@@ -692,6 +692,12 @@ def test_chunked_backward_decomposition(R, Q, rope, a_tok):
             Bm = Br[b, s0:e, hh].reshape(-1, N)
             Xm = x[b, s0:e, hh].reshape(-1, P)
             Hs = np.exp(Lam[-1]) * Hs + Bm.T @ (w[:, None] * Xm)
+
+        def turn(G_, H_):
+            # per pair q: <G, J H> over the pair's two rows, J the derivative of the
+            # pair rotation at angle 0 (J (v0, v1) = (v1, -v0))
+            return np.sum(G_[0::2] * H_[1::2] - G_[1::2] * H_[0::2], axis=1)
+        Tq = turn(dhf[b, hh], Hs)  # Hs is now the final state
         # reverse walk
         G = dhf[b, hh].copy()
         for c in range(len(chunks) - 1, -1, -1):
@@ -743,6 +749,14 @@ def test_chunked_backward_decomposition(R, Q, rope, a_tok):
                 ddt[b, e, hh] += ddl[-1] * (1 - lam[b, e, hh])
                 dlam[b, e, hh] -= ddl[-1] * dt[b, e, hh]
             G = D * G + Cm.T @ (E[tok][:, None] * dYm)
+            if rope:
+                # a common extra rotation of every token from s0 on changes only the
+                # state carried across s0: dtheta at a chunk start is
+                # <dh_final, J h_final> - <G, J H> with H the shifted state entering
+                # the chunk and G its adjoint (no running sum over later tokens)
+                assert np.allclose(ref["dtheta"][b, s0, hh], Tq - turn(G, Hc), rtol=1e-10, atol=1e-12)
+                if c == 0:
+                    assert np.allclose(ref["dphi0"][b, hh], Tq - turn(G, Hc), rtol=1e-10, atol=1e-12)
         # carry-in: H'_{-1} = h0 + kappa u_{-1}, kappa = (1 - lam_0) Delta_0, and
         # G is now the adjoint of H'_{-1}
         assert orc.rel_l2(G, ref["dh0"][b, hh]) <= 1e-12
