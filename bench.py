@@ -64,6 +64,10 @@ DECODE_SHAPE = (256, 32, 64, 64, 4)  # Bt, H, P, N, R
 # control: twice the batch, so the resident state (268 MB) exceeds the 256 MB Infinity Cache
 DECODE_SHAPE_BIG = (512, 32, 64, 64, 4)
 DECODE_BIG_STEPS = 200
+# the decode at higher MIMO rank, the B=256 shape otherwise: rank-R update and
+# readout (4 R N P flops per unit) against the same 32 KB state stream
+DECODE_RANKS = {"decode_r8": (256, 32, 64, 64, 8), "decode_r16": (256, 32, 64, 64, 16)}
+DECODE_RANK_STEPS = 200
 COPY_BYTES = 1 << 30                 # plain copy used to scale the HBM counters
 
 # prefill lines beside the plain workloads: (line name, workload, mode)
@@ -105,7 +109,14 @@ COMBINE_KERNEL = "m3::(anonymous namespace)::split_combine_kernel"
 
 
 def decode_kernel_name(Bt, H, P, N, R):
-    return f"m3::decode_step_kernel<m3::bf16_t, {N}, {P}, {4 if R <= 4 else 16}>"
+    # bf16 decode steps run on the matrix cores (rank bound 4 or 16 in registers)
+    return f"m3::dmma::decode_mma_kernel<{N}, {P}, {4 if R <= 4 else 16}>"
+
+
+def decode_grid(N, P):
+    """Threads per launch of the matrix-core decode: one workgroup of
+    64 max(1, N P / 4096) threads per (batch, head)."""
+    return 64 * max(1, (N // 16) * (P // 16) // 16)
 
 
 def prefill_unit_kernels(key, shp, pro=False):
@@ -133,9 +144,9 @@ def unit_kernels():
     for name, shp in prefill_shapes().items():
         out += prefill_unit_kernels("prefill_" + name, shp)
     Bt, H, P, N, R = DECODE_SHAPE
-    out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
+    out.append(("decode", decode_kernel_name(Bt, H, P, N, R), Bt * H * decode_grid(N, P)))
     Bt, H, P, N, R = DECODE_SHAPE_BIG
-    out.append(("decode_bt512", decode_kernel_name(Bt, H, P, N, R), Bt * H * 256))
+    out.append(("decode_bt512", decode_kernel_name(Bt, H, P, N, R), Bt * H * decode_grid(N, P)))
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
     out.append(("angles", "m3::angles_cumsum_kernel", ANGLES_GRID(Bt, H, N // 2)))
     return out
@@ -563,6 +574,8 @@ def algo_bytes():
                                                a_tok=mode == "atok", pro=mode == "pro")[0]
     algo["decode"] = decode_algo(*DECODE_SHAPE, True)[0]
     algo["decode_bt512"] = decode_algo(*DECODE_SHAPE_BIG, True)[0]
+    for key, shp in DECODE_RANKS.items():
+        algo[key] = decode_algo(*shp, True)[0]
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
     algo["angles"] = 2 * Bt * L * H * (N // 2) * 4 + Bt * H * (N // 2) * 4
     return algo
@@ -862,8 +875,10 @@ def main():
         print(f"# {results['angles']['workload']}: {ms * 1e3:.1f} us, {results['angles']['gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
     if args.only in ("all", "decode"):
-        for key, shp, nsteps in (("decode", DECODE_SHAPE, args.decode_steps),
-                                 ("decode_bt512", DECODE_SHAPE_BIG, min(DECODE_BIG_STEPS, args.decode_steps))):
+        lines = [("decode", DECODE_SHAPE, args.decode_steps),
+                 ("decode_bt512", DECODE_SHAPE_BIG, min(DECODE_BIG_STEPS, args.decode_steps))]
+        lines += [(k, shp, min(DECODE_RANK_STEPS, args.decode_steps)) for k, shp in DECODE_RANKS.items()]
+        for key, shp, nsteps in lines:
             Bt, H, P, N, R = shp
             per_step, ev, ok = time_decode(torch, ops, Bt, H, P, N, R, nsteps, 20, seed=20260104)
             byts, flops = decode_algo(Bt, H, P, N, R, True)
@@ -875,9 +890,12 @@ def main():
                 hbm_frac=byts / (per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, bytes=byts, flops=flops, finite=ok,
                 us_after_cache_eviction=ev * 1e3,
                 gbs_after_cache_eviction=byts / (ev * 1e-3) / 1e9,
+                tflops=flops / (per_step * 1e-3) / 1e12,
+                kernel=decode_kernel_name(Bt, H, P, N, R),
                 traffic=traffic_for(key))
             print(f"# {key}: {per_step * 1e3:.1f} us/step, {results[key]['gbs']:.0f} GB/s "
-                  f"({100 * results[key]['hbm_frac']:.1f}% HBM); {ev * 1e3:.1f} us per single step after an "
+                  f"({100 * results[key]['hbm_frac']:.1f}% HBM, {results[key]['tflops']:.1f} TFLOP/s on the "
+                  f"matrix cores); {ev * 1e3:.1f} us per single step after an "
                   f"Infinity Cache eviction", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
 
@@ -914,8 +932,9 @@ def main():
                                   "kernel": decode_kernel_name(*DECODE_SHAPE),
                                   "achieved_graph_replay": dres["gbs"],
                                   "achieved_after_cache_eviction": dres["gbs_after_cache_eviction"]}
-    if "decode_bt512" in results:
-        out["decode_bt512"] = results["decode_bt512"]
+    for key in ["decode_bt512"] + list(DECODE_RANKS):
+        if key in results:
+            out[key] = results[key]
     for name in prefill_shapes():
         if "backward_" + name in results:
             out["backward_" + name] = results["backward_" + name]

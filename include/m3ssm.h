@@ -246,6 +246,10 @@ int m3_ssm_prefill_noalloc(const m3_prefill_args* args, void* stream);
  *   Out: y [Bt, H, R, P] in_dtype.
  * Sizes: N, P in {16, 32, 64, 128}; R in 1..16.  A fresh sequence starts with
  * h = 0 (or any state), Bprev_rot = 0, xprev = 0, phi = 0.
+ * With bf16 inputs, N in {32, 64, 128} and P in {64, 128} the rank-2R update
+ * and the readout run on the matrix cores ("Znakomstvo s Mamba-3", sec. 3: with
+ * MIMO the update is a matrix product); other shapes and fp32 inputs on the
+ * vector ALUs.  Both keep the state in fp32.
  * pro: the same prologue as the prefill's (B, C, dt raw), so that a decode
  * continues a prefill that used it.
  */

@@ -150,6 +150,9 @@ struct AnglesParams {
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+// decode step on the matrix cores: bf16, N in {32, 64, 128}, P in {64, 128}, R <= 16
+bool decode_mma_supported(const DecodeParams& p);
+hipError_t launch_decode_mma(const DecodeParams& p, hipStream_t s);
 // state_only: the walk that produces the state and carry only (no y)
 hipError_t launch_prefill_bf16(const PrefillParams& p, bool state_only, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillParams& p, hipStream_t s);

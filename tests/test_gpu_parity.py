@@ -337,8 +337,20 @@ def _decode_chain(ops, dd_state, steps, dec, R, dtype, rope):
     return np.stack(ys, axis=1)
 
 
-@pytest.mark.parametrize("case", [(3, 2, 64, 64, 4, "bf16", True, 40), (2, 3, 32, 16, 1, "f32", False, 25),
-                                  (2, 2, 128, 128, 16, "bf16", True, 6), (1, 2, 16, 32, 3, "f32", True, 10)])
+DECODE_CHAIN = [
+    # Bt, H, P, N, R, dtype, rope, steps
+    (3, 2, 64, 64, 4, "bf16", True, 40), (2, 3, 32, 16, 1, "f32", False, 25),
+    (2, 2, 128, 128, 16, "bf16", True, 6), (1, 2, 16, 32, 3, "f32", True, 10),
+    # the matrix-core step: one wave with 8 or 16 state tiles, two and four waves
+    (2, 3, 64, 32, 2, "bf16", True, 20), (2, 2, 128, 32, 1, "bf16", True, 15),
+    (2, 2, 64, 128, 8, "bf16", True, 12), (1, 3, 128, 64, 16, "bf16", False, 10),
+    (2, 2, 64, 64, 16, "bf16", True, 25), (1, 2, 64, 64, 3, "bf16", True, 30),
+    # bf16 on the vector ALUs (P = 32 is outside the matrix-core step)
+    (2, 2, 32, 64, 4, "bf16", True, 12),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CHAIN, ids=lambda c: "-".join(map(str, c)))
 def test_decode_chain(ops, case):
     Bt, H, P, N, R, dt_, rope, steps = case
     _say("decode chain", case)
@@ -398,8 +410,11 @@ def test_prefill_A_tok(ops, case):
     assert orc.rel_l2(host(out["Bprev_rot"]), ref["Bprev_rot"]) <= 1e-5
 
 
-def test_decode_A_tok(ops):
-    Bt, H, P, N, R, steps = 3, 4, 64, 64, 4, 6
+@pytest.mark.parametrize("shape", [(3, 4, 64, 64, 4), (2, 2, 128, 64, 16), (1, 2, 32, 64, 4)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_decode_A_tok(ops, shape):
+    Bt, H, P, N, R = shape
+    steps = 6
     s = Shape(Bt, steps, H, P, N, R, "bf16", True)
     _say("decode A_tok")
     d = make_inputs(s, 777, h0=True)
@@ -422,10 +437,13 @@ def test_decode_A_tok(ops):
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
-def test_decode_omega(ops):
+@pytest.mark.parametrize("shape", [(2, 3, 64, 64, 4), (2, 2, 64, 128, 8), (2, 2, 32, 64, 2)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_decode_omega(ops, shape):
     """Decode steps with the angles given as rates shared by the heads: the
     oracle on theta = dt * omega."""
-    Bt, H, P, N, R, steps = 2, 3, 64, 64, 4, 5
+    Bt, H, P, N, R = shape
+    steps = 5
     s = Shape(Bt, steps, H, P, N, R, "bf16", True)
     _say("decode omega")
     d = make_inputs(s, 888, h0=True)
@@ -474,18 +492,12 @@ def test_decode_config_full_size(ops):
     assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
 
 
-@pytest.mark.timeout(900)
-def test_decode_config4_all_steps(ops):
-    """The decode workload at full size (B=256, H=32, N=P=64, R=4) for all its
-    1000 sequential steps, inputs drawn on the device step by step: y of every
-    step, and the final state, B carry and angle, against the oracle on 16
-    (batch, head) units (two in each eighth of the unit axis).  Each step's y
-    buffer is NaN-filled before the call."""
-    s = CONFIGS[4]
-    steps = s.L
-    Bt, H, P, N, R = s.Bt, s.H, s.P, s.N, s.R
-    _say("decode config 4, all", steps, "steps")
-    gen = DecodeStream(Bt, H, P, N, R, seed=SEED_BASE + 4)
+def _decode_stream_check(ops, Bt, H, P, N, R, steps, seed):
+    """`steps` sequential decode steps at full shape, inputs drawn on the
+    device step by step: y of every step, and the final state, B carry and
+    angle, against the oracle on 16 (batch, head) units (two in each eighth
+    of the unit axis).  Each step's y buffer is NaN-filled before the call."""
+    gen = DecodeStream(Bt, H, P, N, R, seed=seed)
     units = sample_units(Bt * H)
     k = len(units)
     idx = torch.tensor(units, device="cuda")
@@ -522,14 +534,32 @@ def test_decode_config4_all_steps(ops):
         e = orc.rel_l2(r["y"][t], ref["y"][0, t])
         worst = max(worst, e)
         assert e <= TOL["bf16"], (t, e)
-    _say(f"  worst per-step rel_l2 of y {worst:.2e}")
     hs = host(st["h"].reshape(U, N, P)[idx])
     bs = host(st["Bprev_rot"].reshape(U, R, N)[idx])
     ps = host(st["phi"].reshape(U, N // 2)[idx])
+    worst_h = max(orc.rel_l2(hs[i], ref["h"][0, i]) for i in range(k))
+    _say(f"  worst per-step rel_l2 of y {worst:.2e}, worst per-unit rel_l2 of h {worst_h:.2e}")
     for i in range(k):
         assert orc.rel_l2(hs[i], ref["h"][0, i]) <= TOL["bf16"], i
         assert orc.rel_l2(bs[i], ref["Bprev_rot"][0, i]) <= 1e-5, i
         assert np.max(angle_diff(ps[i], ref["phi"][0, i])) <= 1e-3, i
+
+
+@pytest.mark.timeout(900)
+def test_decode_config4_all_steps(ops):
+    """The decode workload at full size (B=256, H=32, N=P=64, R=4) for all its
+    1000 sequential steps (see _decode_stream_check)."""
+    s = CONFIGS[4]
+    _say("decode config 4, all", s.L, "steps")
+    _decode_stream_check(ops, s.Bt, s.H, s.P, s.N, s.R, s.L, SEED_BASE + 4)
+
+
+@pytest.mark.parametrize("R", [8, 16])
+def test_decode_rank_lines_full_shape(ops, R):
+    """The decode at rank 8 and 16, the B=256 shape otherwise (H=32,
+    N=P=64), over the 200 steps the benchmark times."""
+    _say("decode full shape, R", R)
+    _decode_stream_check(ops, 256, 32, 64, 64, R, 200, SEED_BASE + 40 + R)
 
 
 def test_prefill_then_decode(ops):

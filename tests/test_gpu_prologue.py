@@ -142,7 +142,10 @@ def test_prologue_zero_bias_is_the_plain_call(ops):
 
 
 @pytest.mark.parametrize("case", [(3, 2, 64, 64, 4, "bf16", True, 30), (2, 3, 32, 128, 1, "f32", False, 12),
-                                  (2, 2, 16, 16, 3, "bf16", True, 10)])
+                                  (2, 2, 16, 16, 3, "bf16", True, 10), (2, 2, 64, 64, 16, "bf16", True, 10),
+                                  (1, 2, 64, 128, 8, "bf16", True, 8), (2, 2, 128, 32, 2, "bf16", False, 8),
+                                  (2, 2, 32, 64, 4, "bf16", True, 8)],
+                         ids=lambda c: "-".join(map(str, c)))
 def test_decode_prologue_chain(ops, case):
     """Decode steps with the prologue: the oracle's prologue on every token."""
     Bt, H, P, N, R, dt_, rope, steps = case
