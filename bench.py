@@ -195,9 +195,13 @@ def backward_algo(Bt, L, H, P, N, R, rope):
     2 * 64 * (3 * 64 N + 2 * 64 P + 5 N P)."""
     bf, f4 = 2, 4
     tok = Bt * L * H
-    byts = 2 * tok * R * (2 * P + 2 * N) * bf + 2 * tok * 2 * f4 + 2 * H * f4
+    byts = (tok * R * (2 * P + 2 * N) * bf      # x, dy, B, C read
+            + tok * R * (P + 2 * N) * bf        # dx, dB, dC written
+            + 2 * tok * 2 * f4                  # Delta, lambda read; their gradients written
+            + 2 * Bt * H * N * P * f4           # dh_final read, dh0 written
+            + 2 * H * f4)                       # A read, dA written
     if rope:
-        byts += 2 * tok * (N // 2) * f4
+        byts += 2 * tok * (N // 2) * f4        # theta read, dtheta written
     chunks = Bt * H * ((L + (64 // R) - 1) // (64 // R))
     flops = chunks * 2 * 64 * (3 * 64 * N + 2 * 64 * P + 5 * N * P)
     return byts, flops

@@ -29,8 +29,13 @@
  * aligned; theta / phi pointers must be 16-byte aligned.
  * All pointers are device pointers (hipMalloc'd or equivalent) unless noted.
  * The caller owns every buffer, including the optional prefill workspace; the
- * library allocates nothing and keeps no state between calls, so calls on
- * different streams are independent (given separate workspaces).
+ * library allocates nothing.  Between calls it keeps only per-device caches,
+ * each safe under concurrent first calls from several host threads: the
+ * compute-unit count (atomics), which kernels have had their dynamic-LDS
+ * limit raised (an atomic bit mask per kernel) and the address of the
+ * no-allocation scratch (under a mutex).  Calls on different streams are
+ * independent given separate workspaces (m3_ssm_prefill_noalloc shares its
+ * scratch per device).
  * `stream` is a hipStream_t (NULL = the null stream).  All calls are
  * asynchronous with respect to the host; results are visible after the
  * stream is synchronised.  Results are deterministic (no atomics).
