@@ -33,6 +33,8 @@
 // consecutive columns of one row: 8-byte stores, and whole rotation pairs in
 // registers.  Reductions run in a fixed order (no atomics): results are
 // bit-reproducible.
+#include <type_traits>
+
 #include "common.hpp"
 #include "m3ssm_internal.hpp"
 
@@ -169,18 +171,66 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   for (int e = tid; e < static_cast<int>(Lt::kBytes / 4); e += kThreads) reinterpret_cast<float*>(smem)[e] = 0.f;
   __syncthreads();
 
-  // per-token scalars of chunk c (wave 0, lane = token): Lam (log2 units),
-  // gamma, delta, E, w, and the raw Delta, lambda, A of the chunk's tokens and
-  // of the next token (index Q)
-  auto scalars = [&](int c) __attribute__((always_inline)) {
+  // ---- staging of a chunk, split into its global loads (into registers,
+  // issued a chunk ahead so that they overlap the previous chunk's products)
+  // and the LDS stores that consume them.  Every load is unconditional: an
+  // index past the end reads this tensor's first element instead, and the
+  // value is zeroed when it is stored, so no wait sits where a load is issued.
+  constexpr int UB = (kRows * (N / 8) + kThreads - 1) / kThreads;  // 16-byte units of a B or C tile per thread
+  constexpr int UX = (kRows * (P / 8) + kThreads - 1) / kThreads;  // of an x or dy tile
+  constexpr int UT = ROPE ? (kRows * J + kThreads - 1) / kThreads : 1;  // theta values (Q J <= 64 J)
+  struct Stage {
+    u32x4 b[UB], c[UB], x[UX], dy[UX];
+    float th[UT];
+    float dt, lam, At, dn, ln;  // wave 0, lane = token of the chunk (and the next token)
+  };
+  auto load_tile = [&](int c, const bf16_t* src, auto DD, u32x4* dst) __attribute__((always_inline)) {
+    constexpr int D = decltype(DD)::value;
+    constexpr int U = (kRows * (D / 8) + kThreads - 1) / kThreads;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int e = tid + i * kThreads;
+      const int r = e / (D / 8), k8 = e % (D / 8);
+      const bool ok = e < kRows * (D / 8) && valid(c, r);
+      dst[i] = *reinterpret_cast<const u32x4*>(src + (ok ? grow(c, r) * D + 8 * k8 : 0));
+    }
+  };
+  // per-token scalars of chunk c (wave 0, lane = token): the raw Delta, lambda,
+  // A of the chunk's tokens and of the next token (index Q)
+  auto load_scalars = [&](int c, Stage& S) __attribute__((always_inline)) {
     if (wave != 0) return;
     const int t = lane;
     const bool v0 = t < Q && c * Q + t < L;
     const bool v1 = t < Q && c * Q + t + 1 < L;
     const size_t o = (static_cast<size_t>(b) * L + c * Q + t) * H + hh;
-    const float dt = v0 ? p.dt[o] : 0.f, lm = v0 ? p.lam[o] : 0.f;
-    const float At = v0 ? (p.A_tok != nullptr ? p.A_tok[o] : Ah) : 0.f;
-    const float dn = v1 ? p.dt[o + H] : 0.f, ln = v1 ? p.lam[o + H] : 0.f;
+    const size_t o0 = v0 ? o : 0, o1 = v1 ? o + H : 0;
+    S.dt = p.dt[o0];
+    S.lam = p.lam[o0];
+    S.At = p.A_tok != nullptr ? p.A_tok[o0] : Ah;
+    S.dn = p.dt[o1];
+    S.ln = p.lam[o1];
+  };
+  auto load_theta = [&](int c, Stage& S) __attribute__((always_inline)) {
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int i = 0; i < UT; ++i) {
+        const int e = tid + i * kThreads;
+        const int tl = e / J, q = e % J;
+        const int t = c * Q + tl;
+        const bool ok = e < Q * J && t < L;
+        S.th[i] = p.theta[ok ? ((static_cast<size_t>(b) * L + t) * H + hh) * J + q : 0];
+      }
+    }
+  };
+  // Lam (log2 units), gamma, delta, E, w and the raw values into the scalar table
+  auto store_scalars = [&](int c, const Stage& S) __attribute__((always_inline)) {
+    if (wave != 0) return;
+    const int t = lane;
+    const bool v0 = t < Q && c * Q + t < L;
+    const bool v1 = t < Q && c * Q + t + 1 < L;
+    const float dt = v0 ? S.dt : 0.f, lm = v0 ? S.lam : 0.f;
+    const float At = v0 ? S.At : 0.f;
+    const float dn = v1 ? S.dn : 0.f, ln = v1 ? S.ln : 0.f;
     const float lam2 = seg_scan<64>(dt * At * kLog2e);
     const float lamE = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lam2), Q - 1));
     const float gam = lm * dt;
@@ -200,14 +250,15 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       sc[kMisc * kSc + 1] = lamE;
     }
   };
-  // cumulative angles of chunk c: raw theta into the table (all threads),
-  // then threads q < J add them up from the carry (reduced modulo 2 pi)
-  auto angles_load = [&](int c) __attribute__((always_inline)) {
+  // raw theta of chunk c into the angle table (threads q < J then add them up
+  // from the carry, reduced modulo 2 pi)
+  auto store_theta = [&](int c, const Stage& S) __attribute__((always_inline)) {
     if constexpr (ROPE) {
-      for (int e = tid; e < Q * J; e += kThreads) {
+#pragma unroll
+      for (int i = 0; i < UT; ++i) {
+        const int e = tid + i * kThreads;
         const int tl = e / J, q = e % J;
-        const int t = c * Q + tl;
-        sPhi[tl * J + q] = t < L ? p.theta[((static_cast<size_t>(b) * L + t) * H + hh) * J + q] : 0.f;
+        if (e < Q * J) sPhi[tl * J + q] = c * Q + tl < L ? S.th[i] : 0.f;
       }
     }
   };
@@ -219,12 +270,14 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     }
     return a;
   };
-  // stage rows of a B / C (rotated) or x / dy tile of chunk c into LDS (bf16)
-  auto stage_bc = [&](int c, const bf16_t* src, uint16_t* dst) __attribute__((always_inline)) {
-    for (int e = tid; e < kRows * (N / 8); e += kThreads) {
+  // rows of a B / C tile (rotated) or x / dy tile of chunk c into LDS (bf16)
+  auto store_bc = [&](int c, const u32x4* src, uint16_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < UB; ++i) {
+      const int e = tid + i * kThreads;
+      if (e >= kRows * (N / 8)) break;
       const int r = e / (N / 8), k8 = e % (N / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid(c, r)) v = *reinterpret_cast<const u32x4*>(src + grow(c, r) * N + 8 * k8);
+      u32x4 v = valid(c, r) ? src[i] : u32x4{0u, 0u, 0u, 0u};
       if constexpr (ROPE) {
         const float* ang = sPhi + (r >> lgR) * J + 4 * k8;
 #pragma unroll
@@ -239,11 +292,13 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       *reinterpret_cast<u32x2*>(d + 4) = u32x2{v[2], v[3]};
     }
   };
-  auto stage_xp = [&](int c, const bf16_t* src, uint16_t* dst) __attribute__((always_inline)) {
-    for (int e = tid; e < kRows * (P / 8); e += kThreads) {
+  auto store_xp = [&](int c, const u32x4* src, uint16_t* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < UX; ++i) {
+      const int e = tid + i * kThreads;
+      if (e >= kRows * (P / 8)) break;
       const int r = e / (P / 8), k8 = e % (P / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid(c, r)) v = *reinterpret_cast<const u32x4*>(src + grow(c, r) * P + 8 * k8);
+      const u32x4 v = valid(c, r) ? src[i] : u32x4{0u, 0u, 0u, 0u};
       uint16_t* d = dst + r * PP + 8 * k8;
       *reinterpret_cast<u32x2*>(d) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(d + 4) = u32x2{v[2], v[3]};
@@ -287,9 +342,19 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   if constexpr (ROPE)
     for (int q = tid; q < J; q += kThreads) phiC[q] = p.phi0 != nullptr ? p.phi0[static_cast<size_t>(bh) * J + q] : 0.f;
   __syncthreads();
+  using NC = std::integral_constant<int, N>;
+  using PC = std::integral_constant<int, P>;
+  Stage S;
+  auto load_fwd = [&](int c) __attribute__((always_inline)) {
+    load_scalars(c, S);
+    load_theta(c, S);
+    load_tile(c, Bg, NC{}, S.b);
+    load_tile(c, xg, PC{}, S.x);
+  };
+  load_fwd(0);
   for (int c = 0; c < nch; ++c) {
-    scalars(c);
-    angles_load(c);
+    store_scalars(c, S);
+    store_theta(c, S);
     __syncthreads();
     if constexpr (ROPE) {
       if (tid < J) {
@@ -298,8 +363,9 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
       __syncthreads();
     }
-    stage_bc(c, Bg, sBr);
-    stage_xp(c, xg, sX);
+    store_bc(c, S.b, sBr);
+    store_xp(c, S.x, sX);
+    if (c + 1 < nch) load_fwd(c + 1);  // in flight during this chunk's products
     // the shifted state entering chunk c, in the accumulator layout
 #pragma unroll
     for (int m = 0; m < STW; ++m)
@@ -372,23 +438,39 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   int pendTok = -1;
   float dAsum = 0.f;                            // sum of dA over tokens (wave 0, lane 0)
   f32x4 hsave[STW];                             // the shifted state entering the chunk (fp32)
+  f32x4 hpre[STW];                              // the same, loaded a chunk ahead
+  float phPre = 0.f;                            // the angle entering the chunk (tid < J), loaded a chunk ahead
+  auto load_rev = [&](int c) __attribute__((always_inline)) {
+    load_scalars(c, S);
+    load_theta(c, S);
+    load_tile(c, Cg, NC{}, S.c);
+    load_tile(c, Bg, NC{}, S.b);
+    load_tile(c, xg, PC{}, S.x);
+    load_tile(c, dYg, PC{}, S.dy);
+    if constexpr (ROPE) phPre = phBase[static_cast<size_t>(c) * J + (tid < J ? tid : 0)];
+#pragma unroll
+    for (int m = 0; m < STW; ++m)
+      hpre[m] = *reinterpret_cast<const f32x4*>(
+          stBase + (static_cast<size_t>(c) * NST + (tile_ok(m) ? wave + kWaves * m : 0)) * 256 + lane * 4);
+  };
+  load_rev(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     if constexpr (ROPE) {
       // dtheta at the start of chunk c + 1, from the parts its pass left in sAnc
       const int q = tid - 64;
       if (c < nch - 1 && q >= 0 && q < J) thCarry = Tq - turn_sum(q);
     }
-    scalars(c);
-    angles_load(c);
+    store_scalars(c, S);
+    store_theta(c, S);
     __syncthreads();
     if constexpr (ROPE) {
-      if (tid < J) (void)angles_scan(phBase[static_cast<size_t>(c) * J + tid], tid);
+      if (tid < J) (void)angles_scan(phPre, tid);
       __syncthreads();
     }
-    stage_bc(c, Cg, sCr);
-    stage_bc(c, Bg, sBr);
-    stage_xp(c, xg, sX);
-    stage_xp(c, dYg, sDY);
+    store_bc(c, S.c, sCr);
+    store_bc(c, S.b, sBr);
+    store_xp(c, S.x, sX);
+    store_xp(c, S.dy, sDY);
     {
       // H^T from the forward walk's dump and G^T from the accumulators (own tiles);
       // dD = <G, H> from the fp32 values
@@ -396,8 +478,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
         if (!tile_ok(m)) continue;
-        const f32x4 hv =
-            *reinterpret_cast<const f32x4*>(stBase + (static_cast<size_t>(c) * NST + wave + kWaves * m) * 256 + lane * 4);
+        const f32x4 hv = hpre[m];
         hsave[m] = hv;
         const int at = (16 * tile_pt(m) + l16) * PN + 16 * tile_nt(m) + 4 * g;
         *reinterpret_cast<u32x2*>(sHT + at) = pack4(hv);
@@ -408,6 +489,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       for (int off = 32; off > 0; off >>= 1) dd += __shfl_xor(dd, off);
       if (lane == 0) sDp[wave] = dd;
     }
+    if (c > 0) load_rev(c - 1);  // in flight during this chunk's products
     __syncthreads();
 
     // ---- Gram tiles (i tile it >= j tile jt): G1 = C B^T, G2 = dY X^T, masks
