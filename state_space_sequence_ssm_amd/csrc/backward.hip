@@ -57,6 +57,7 @@ struct Lay {
   static constexpr int NST = NT * PT;                      // 16 x 16 state tiles
   static constexpr int STW = (NST + kWaves - 1) / kWaves;  // state tiles per wave
   static constexpr int J = N / 2;
+  static constexpr int JP = J + 1;  // angle-table row pitch (odd: a column spreads over the banks)
   // bf16 tiles (element offsets)
   static constexpr size_t oCr = 0;                           // [64][PN] rotated C
   static constexpr size_t oBr = oCr + size_t(kRows) * PN;    // [64][PN] rotated B
@@ -77,8 +78,8 @@ struct Lay {
   static constexpr size_t fW = fE + NT * 64;            // [PT][64] column-weight gradient parts
   static constexpr size_t fD = fW + PT * 64;            // [16] per-wave parts
   static constexpr size_t fPhiC = fD + 16;              // [J] angle carry (forward walk)
-  static constexpr size_t fPhi = fPhiC + J;             // [64][J] angles of the chunk's tokens
-  static constexpr size_t fDPhi = fPhi + (ROPE ? 64 * J : 0);  // [64 rows][J] angle gradients
+  static constexpr size_t fPhi = fPhiC + J;             // [64][JP] angles of the chunk's tokens
+  static constexpr size_t fDPhi = fPhi + (ROPE ? 64 * JP : 0);  // [64 rows][J] angle gradients
   static constexpr size_t fEnd = fDPhi + (ROPE ? 64 * J : 0);
   static constexpr size_t kBytes = fBase + fEnd * 4;
 };
@@ -101,7 +102,7 @@ template <int N, int P, bool ROPE>
 __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   using Lt = Lay<N, P, ROPE>;
   constexpr int PN = Lt::PN, PP = Lt::PP, PR = Lt::PR, NT = Lt::NT, PT = Lt::PT, NST = Lt::NST;
-  constexpr int STW = Lt::STW, J = Lt::J, NKB = Lt::NK / 32, PKB = Lt::PK / 32;
+  constexpr int STW = Lt::STW, J = Lt::J, JP = Lt::JP, NKB = Lt::NK / 32, PKB = Lt::PK / 32;
   constexpr int kSc = Lt::kSc;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* const sm16 = reinterpret_cast<uint16_t*>(smem);
@@ -258,17 +259,49 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       for (int i = 0; i < UT; ++i) {
         const int e = tid + i * kThreads;
         const int tl = e / J, q = e % J;
-        if (e < Q * J) sPhi[tl * J + q] = c * Q + tl < L ? S.th[i] : 0.f;
+        if (e < Q * J) sPhi[tl * JP + q] = c * Q + tl < L ? S.th[i] : 0.f;
       }
     }
   };
-  auto angles_scan = [&](float carry, int q) __attribute__((always_inline)) {
-    float a = carry;
-    for (int tl = 0; tl < Q; ++tl) {
-      a = wrap_angle(a + sPhi[tl * J + q]);
-      sPhi[tl * J + q] = a;
+  // inclusive scan over aligned segments of Q lanes (Q = 64 / R, 8..64, a
+  // runtime power of two): row_shr 1/2/4/8 within rows of 16, then
+  // row_bcast 15 / 31 across rows, each step masked to the segment
+  auto seg_scan_q = [&](float v) __attribute__((always_inline)) {
+    const int sl = lane & (Q - 1);
+    float t = dpp<0x111, 0xF, true>(v);
+    v += sl >= 1 ? t : 0.f;
+    t = dpp<0x112, 0xF, true>(v);
+    v += sl >= 2 ? t : 0.f;
+    t = dpp<0x114, 0xF, true>(v);
+    v += sl >= 4 ? t : 0.f;
+    t = dpp<0x118, 0xF, true>(v);
+    v += sl >= 8 ? t : 0.f;
+    t = dpp<0x142, 0xA, false>(v);
+    v += Q >= 32 ? t : 0.f;
+    t = dpp<0x143, 0xC, false>(v);
+    v += Q >= 64 ? t : 0.f;
+    return v;
+  };
+  // cumulative angles of chunk c in place in the table (after a barrier since
+  // its raw theta was stored): lane = token, one segment of Q lanes per pair,
+  // the pair's carry in phiC, replaced by the chunk's last angle; every angle
+  // reduced modulo 2 pi.  With `dump`, the angle entering the chunk is
+  // written to the workspace for the reverse walk.
+  auto scan_angles = [&](int c, bool dump) __attribute__((always_inline)) {
+    if constexpr (ROPE) {
+      const int tl = lane & (Q - 1);
+      for (int q0 = wave * R; q0 < J; q0 += kWaves * R) {  // R pairs per wave pass
+        const int q = q0 + (lane >> (6 - lgR));
+        const bool ok = q < J;
+        const float v = seg_scan_q(ok ? sPhi[tl * JP + q] : 0.f);
+        if (ok) {
+          const float cin = phiC[q];
+          sPhi[tl * JP + q] = wrap_angle(cin + v);
+          if (dump && tl == 0) phBase[static_cast<size_t>(c) * J + q] = cin;
+          if (tl == Q - 1) phiC[q] = wrap_angle(cin + v);
+        }
+      }
     }
-    return a;
   };
   // rows of a B / C tile (rotated) or x / dy tile of chunk c into LDS (bf16)
   auto store_bc = [&](int c, const u32x4* src, uint16_t* dst) __attribute__((always_inline)) {
@@ -279,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       const int r = e / (N / 8), k8 = e % (N / 8);
       u32x4 v = valid(c, r) ? src[i] : u32x4{0u, 0u, 0u, 0u};
       if constexpr (ROPE) {
-        const float* ang = sPhi + (r >> lgR) * J + 4 * k8;
+        const float* ang = sPhi + (r >> lgR) * JP + 4 * k8;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float a0 = __uint_as_float(v[q] << 16), a1 = __uint_as_float(v[q] & 0xffff0000u);
@@ -357,10 +390,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     store_theta(c, S);
     __syncthreads();
     if constexpr (ROPE) {
-      if (tid < J) {
-        phBase[static_cast<size_t>(c) * J + tid] = phiC[tid];  // angle entering the chunk
-        phiC[tid] = angles_scan(phiC[tid], tid);
-      }
+      scan_angles(c, true);
       __syncthreads();
     }
     store_bc(c, S.b, sBr);
@@ -462,9 +492,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     }
     store_scalars(c, S);
     store_theta(c, S);
+    if (ROPE && tid < J) phiC[tid] = phPre;  // the angle entering the chunk (forward walk's dump)
     __syncthreads();
     if constexpr (ROPE) {
-      if (tid < J) (void)angles_scan(phPre, tid);
+      scan_angles(c, false);
       __syncthreads();
     }
     store_bc(c, S.c, sCr);
@@ -603,33 +634,23 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         s += __shfl_xor(s, 32);
         if (g == 0) sEp[nt * 64 + r] = s;
         if constexpr (ROPE) {
-          // Back through the rotation, then the pair's angle gradient.  A
-          // rotation commutes with the quarter turn J, so db~ . J b~ equals
-          // (R^T db~) . J b: the angle gradient is taken against the
-          // unrotated inputs, exact in bf16, instead of the bf16-rounded
-          // rotated tiles (whose rounding would bias the long running sums
-          // of dtheta).
-          u32x2 bu = {0u, 0u}, cu = {0u, 0u};
-          if (valid(c, r)) {
-            bu = *reinterpret_cast<const u32x2*>(Bg + grow(c, r) * N + 16 * nt + 4 * g);
-            cu = *reinterpret_cast<const u32x2*>(Cg + grow(c, r) * N + 16 * nt + 4 * g);
-          }
-          const float bx[4] = {__uint_as_float(bu[0] << 16), __uint_as_float(bu[0] & 0xffff0000u),
-                               __uint_as_float(bu[1] << 16), __uint_as_float(bu[1] & 0xffff0000u)};
-          const float cx[4] = {__uint_as_float(cu[0] << 16), __uint_as_float(cu[0] & 0xffff0000u),
-                               __uint_as_float(cu[1] << 16), __uint_as_float(cu[1] & 0xffff0000u)};
+          // the pair's angle gradient from the rotated tiles (dtheta adds at
+          // most a chunk of these to the chunk-start value, so their bf16
+          // rounding does not accumulate), then back through the rotation
+          const u32x2 bv = *reinterpret_cast<const u32x2*>(sBr + r * PN + 16 * nt + 4 * g);
+          const float br[4] = {__uint_as_float(bv[0] << 16), __uint_as_float(bv[0] & 0xffff0000u),
+                               __uint_as_float(bv[1] << 16), __uint_as_float(bv[1] & 0xffff0000u)};
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int q = 8 * nt + 2 * g + h2;
-            const float ang = sPhi[tl * J + q];
+            const float ang = sPhi[tl * JP + q];
             const float cs = __cosf(ang), sn = __sinf(ang);
             const float d0 = db[2 * h2], d1 = db[2 * h2 + 1], e0 = dc[2 * h2], e1 = dc[2 * h2 + 1];
+            sDPhi[r * J + q] = d0 * br[2 * h2 + 1] - d1 * br[2 * h2] + e0 * cr[2 * h2 + 1] - e1 * cr[2 * h2];
             db[2 * h2] = cs * d0 - sn * d1;
             db[2 * h2 + 1] = sn * d0 + cs * d1;
             dc[2 * h2] = cs * e0 - sn * e1;
             dc[2 * h2 + 1] = sn * e0 + cs * e1;
-            sDPhi[r * J + q] = db[2 * h2] * bx[2 * h2 + 1] - db[2 * h2 + 1] * bx[2 * h2] +
-                               dc[2 * h2] * cx[2 * h2 + 1] - dc[2 * h2 + 1] * cx[2 * h2];
           }
         }
         if (valid(c, r)) {
