@@ -155,6 +155,10 @@ def unit_kernels():
 # counter groups of the variant lines: within a group every line runs
 # distinct kernels (symbol and grid), so counter rows map to lines
 GROUPS = {"variants": [v for v in VARIANTS if v[2] != "pro"], "prologue": [v for v in VARIANTS if v[2] == "pro"]}
+# counter groups with no prefill variant: the decode at rank 8 and at rank 16
+# (one kernel symbol and grid, so a run each) and the three backward lines
+OTHER_GROUPS = ("decode_r8", "decode_r16", "backward")
+ALL_GROUPS = ("base",) + tuple(GROUPS) + OTHER_GROUPS
 
 
 def variant_unit_kernels(group=None):
@@ -164,6 +168,28 @@ def variant_unit_kernels(group=None):
     for line, wl, mode in (VARIANTS if group is None else GROUPS[group]):
         out += prefill_unit_kernels("prefill_" + line, prefill_shapes()[wl], pro=mode == "pro")
     return out
+
+
+def backward_unit_kernels():
+    """(unit key, kernel symbol, grid) of the backward lines: one 512-thread
+    workgroup per (batch, head); the per-head dA reduction is a few hundred
+    bytes and left out."""
+    return [("backward_" + name, backward_kernel_name(shp[6], shp[4], shp[3]), shp[0] * shp[2] * 512)
+            for name, shp in prefill_shapes().items()]
+
+
+def group_units(group):
+    """(unit key, kernel symbol, grid) of every counted launch of a counter group."""
+    if group == "base":
+        return unit_kernels()
+    if group in GROUPS:
+        return variant_unit_kernels(group)
+    if group in DECODE_RANKS:
+        Bt, H, P, N, R = DECODE_RANKS[group]
+        return [(group, decode_kernel_name(Bt, H, P, N, R), Bt * H * decode_grid(N, P))]
+    if group == "backward":
+        return backward_unit_kernels()
+    raise ValueError(group)
 
 
 def prefill_algo(Bt, L, H, P, N, R, rope, omega=False, a_tok=False, pro=False):
@@ -545,7 +571,11 @@ def report_trace(prefix):
         grp.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
         meta[key] = (r["Workgroup_Size_X"], r["LDS_Block_Size"], r["VGPR_Count"], r["Accum_VGPR_Count"],
                      r["SGPR_Count"], r["Scratch_Size"])
-    units = {(k, g): u for u, k, g in unit_kernels()}
+    units = {}
+    for cgroup in ALL_GROUPS:  # launches of several lines on one symbol and grid share a row
+        for u, k, g in group_units(cgroup):
+            if u not in units.get((k, g), ""):
+                units[(k, g)] = units[(k, g)] + " / " + u if (k, g) in units else u
     lines = ["| unit | kernel | grid (threads) | block | calls | avg us | median us | min us | max us "
              "| LDS B | arch VGPR | acc VGPR | SGPR | scratch |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -580,6 +610,8 @@ def algo_bytes():
     algo["decode_bt512"] = decode_algo(*DECODE_SHAPE_BIG, True)[0]
     for key, shp in DECODE_RANKS.items():
         algo[key] = decode_algo(*shp, True)[0]
+    for name, shp in prefill_shapes().items():
+        algo["backward_" + name] = backward_algo(*shp)[0]
     Bt, L, H, P, N, R, _ = prefill_shapes()["siso_rope"]
     algo["angles"] = 2 * Bt * L * H * (N // 2) * 4 + Bt * H * (N // 2) * 4
     return algo
@@ -624,8 +656,7 @@ def report_pmc(groups):
         lines.append(f"Group {group}: a plain elementwise copy (negation) of {COPY_BYTES} B reads FETCH_SIZE = "
                      f"{cf:.4g} B and WRITE_SIZE = {cw:.4g} B, so the factors are {sf:.4f} (fetch) and "
                      f"{sw:.4f} (write).")
-        uk = unit_kernels() if group == "base" else variant_unit_kernels(group)
-        for unit, k, g in uk:
+        for unit, k, g in group_units(group):
             fv, wv = find(fetch, k, g), find(write, k, g)
             if not fv or not wv:
                 continue
@@ -674,7 +705,7 @@ def report_counters(prefixes):
                "| L2 read latency (cycles / request) | vector-L1 pending stall (cycles / CU / GPU cycle) "
                "| LDS bank-conflict / LDS-active cycles |", "|---|---|---|---|---|---|"]
     seen = set()
-    for unit, k, g in unit_kernels() + variant_unit_kernels():
+    for unit, k, g in [u for grp in ALL_GROUPS for u in group_units(grp)]:
         a = avg.get((k, g)) or next((v for (kk, _), v in avg.items() if kk == k), None)
         if a is None or (k, g) in seen:
             continue
@@ -708,11 +739,19 @@ def report_mfma(prefix):
         key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
         acc.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     algo = {"prefill_" + name: prefill_algo(*shp)[1] for name, shp in prefill_shapes().items()}
+    for name, shp in prefill_shapes().items():
+        algo["backward_" + name] = backward_algo(*shp)[1]
+    algo["decode"] = decode_algo(*DECODE_SHAPE, True)[1]
+    algo["decode_bt512"] = decode_algo(*DECODE_SHAPE_BIG, True)[1]
+    for key, shp in DECODE_RANKS.items():
+        algo[key] = decode_algo(*shp, True)[1]
     lines = ["| unit | kernel | dispatches | bf16 MFMA flops per launch (counter) | algorithmic flops per call "
              "| MFMA busy (% of SIMD cycles) |", "|---|---|---|---|---|---|"]
-    for unit, k, g in unit_kernels():
-        if not unit.startswith("prefill"):
+    seen = set()
+    for unit, k, g in [u for grp in ALL_GROUPS for u in group_units(grp)]:
+        if unit not in algo or (k, g) in seen or "combine" in k:
             continue
+        seen.add((k, g))
         hits = acc.get((k, g)) or next((v for (kk, _), v in acc.items() if kk == k), None)
         if not hits or "SQ_VALU_MFMA_BUSY_CYCLES" not in hits:
             continue
@@ -735,6 +774,22 @@ def pmc_workload(torch, ops, group):
     torch.cuda.synchronize()
     del a, b
     torch.cuda.empty_cache()
+    if group in DECODE_RANKS:
+        print(f"# counter workload: {group}", file=sys.stderr, flush=True)
+        time_decode(torch, ops, *DECODE_RANKS[group], 3, 1, seed=20260104, flushed=False)
+        torch.cuda.synchronize()
+        print("# counter workload done", file=sys.stderr, flush=True)
+        return
+    if group == "backward":
+        for i, (name, shp) in enumerate(prefill_shapes().items()):
+            print(f"# counter workload: backward {name}", file=sys.stderr, flush=True)
+            inp = gen_prefill(torch, *shp, seed=20260300 + i)
+            time_backward(torch, ops, inp, 2, 0)
+            del inp
+            torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        print("# counter workload done", file=sys.stderr, flush=True)
+        return
     if group == "base":
         runs = [(name, shp, "") for name, shp in prefill_shapes().items()]
     else:
@@ -764,7 +819,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "headline", "backward", "pmc"), default="all")
-    ap.add_argument("--group", choices=("base", "variants", "prologue"), default="base")
+    ap.add_argument("--group", choices=ALL_GROUPS, default="base")
     ap.add_argument("--report-trace", metavar="PREFIX")
     ap.add_argument("--report-pmc", nargs="+", metavar="GROUP FETCH_PREFIX WRITE_PREFIX")
     ap.add_argument("--report-mfma", metavar="PREFIX")
