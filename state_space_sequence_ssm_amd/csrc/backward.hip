@@ -79,8 +79,9 @@ struct Lay {
   static constexpr size_t fD = fW + PT * 64;            // [16] per-wave parts
   static constexpr size_t fPhiC = fD + 16;              // [J] angle carry (forward walk)
   static constexpr size_t fPhi = fPhiC + J;             // [64][JP] angles of the chunk's tokens
-  static constexpr size_t fDPhi = fPhi + (ROPE ? 64 * JP : 0);  // [64 rows][J] angle gradients
-  static constexpr size_t fEnd = fDPhi + (ROPE ? 64 * J : 0);
+  static constexpr size_t fDPhi = fPhi + (ROPE ? 64 * JP : 0);  // [64 rows][JP] angle gradients
+  static constexpr size_t fThC = fDPhi + (ROPE ? 64 * JP : 0);   // [J] dtheta at the next chunk start
+  static constexpr size_t fEnd = fThC + (ROPE ? J : 0);
   static constexpr size_t kBytes = fBase + fEnd * 4;
 };
 // scalar rows of fSc
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   float* const phiC = f32 + Lt::fPhiC;
   float* const sPhi = f32 + Lt::fPhi;
   float* const sDPhi = f32 + Lt::fDPhi;
+  float* const sThC = f32 + Lt::fThC;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -377,15 +379,17 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   __syncthreads();
   using NC = std::integral_constant<int, N>;
   using PC = std::integral_constant<int, P>;
-  Stage S;
-  auto load_fwd = [&](int c) __attribute__((always_inline)) {
+  // Forward walk: little work per chunk, so two chunks of loads are in
+  // flight (register sets S0 and S1 in turn, the loop unrolled by two so that
+  // they are indexed statically).
+  Stage S0, S1;
+  auto load_fwd = [&](int c, Stage& S) __attribute__((always_inline)) {
     load_scalars(c, S);
     load_theta(c, S);
     load_tile(c, Bg, NC{}, S.b);
     load_tile(c, xg, PC{}, S.x);
   };
-  load_fwd(0);
-  for (int c = 0; c < nch; ++c) {
+  auto fwd_chunk = [&](int c, Stage& S) __attribute__((always_inline)) {
     store_scalars(c, S);
     store_theta(c, S);
     __syncthreads();
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     }
     store_bc(c, S.b, sBr);
     store_xp(c, S.x, sX);
-    if (c + 1 < nch) load_fwd(c + 1);  // in flight during this chunk's products
+    if (c + 2 < nch) load_fwd(c + 2, S);  // in flight during the next two chunks
     // the shifted state entering chunk c, in the accumulator layout
 #pragma unroll
     for (int m = 0; m < STW; ++m)
@@ -416,6 +420,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       acc[m] = a;
     }
     __syncthreads();
+  };
+  load_fwd(0, S0);
+  if (nch > 1) load_fwd(1, S1);
+  for (int c = 0; c < nch; c += 2) {
+    fwd_chunk(c, S0);
+    if (c + 1 < nch) fwd_chunk(c + 1, S1);
   }
 
   // ================================================================ backward walk
@@ -463,10 +473,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     const int q = tid - 64;
     if (q >= 0 && q < J) Tq = turn_sum(q);
   }
-  float thCarry = 0.f;                          // dtheta at the next chunk start, then the running sum (thread 64 + q)
   float pendDt = 0.f, pendLam = 0.f;            // first token of the later chunk (wave 0, lane 0)
   int pendTok = -1;
   float dAsum = 0.f;                            // sum of dA over tokens (wave 0, lane 0)
+  Stage& S = S0;                                // the reverse walk's loads, one chunk ahead
   f32x4 hsave[STW];                             // the shifted state entering the chunk (fp32)
   f32x4 hpre[STW];                              // the same, loaded a chunk ahead
   float phPre = 0.f;                            // the angle entering the chunk (tid < J), loaded a chunk ahead
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     if constexpr (ROPE) {
       // dtheta at the start of chunk c + 1, from the parts its pass left in sAnc
       const int q = tid - 64;
-      if (c < nch - 1 && q >= 0 && q < J) thCarry = Tq - turn_sum(q);
+      if (q >= 0 && q < J) sThC[q] = c < nch - 1 ? Tq - turn_sum(q) : 0.f;
     }
     store_scalars(c, S);
     store_theta(c, S);
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
             const float ang = sPhi[tl * JP + q];
             const float cs = __cosf(ang), sn = __sinf(ang);
             const float d0 = db[2 * h2], d1 = db[2 * h2 + 1], e0 = dc[2 * h2], e1 = dc[2 * h2 + 1];
-            sDPhi[r * J + q] = d0 * br[2 * h2 + 1] - d1 * br[2 * h2] + e0 * cr[2 * h2 + 1] - e1 * cr[2 * h2];
+            sDPhi[r * JP + q] = d0 * br[2 * h2 + 1] - d1 * br[2 * h2] + e0 * cr[2 * h2 + 1] - e1 * cr[2 * h2];
             db[2 * h2] = cs * d0 - sn * d1;
             db[2 * h2 + 1] = sn * d0 + cs * d1;
             dc[2 * h2] = cs * e0 - sn * e1;
@@ -751,15 +761,22 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
     }
     if constexpr (ROPE) {
-      // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens >= t (threads 64 + q)
-      const int q = tid - 64;
-      if (q >= 0 && q < J) {
-        for (int tl = Q - 1; tl >= 0; --tl) {
-          float s = 0.f;
-          for (int rr = 0; rr < R; ++rr) s += sDPhi[(tl * R + rr) * J + q];
-          thCarry += s;
-          const int t = c * Q + tl;
-          if (t < L) p.dtheta[((static_cast<size_t>(b) * L + t) * H + hh) * J + q] = thCarry;
+      // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens
+      // >= t: a segmented scan over the tokens in reverse order (lane tl holds
+      // token Q - 1 - tl), one segment of Q lanes per pair
+      const int tl = lane & (Q - 1), tok = Q - 1 - tl;
+      for (int q0 = wave * R; q0 < J; q0 += kWaves * R) {  // R pairs per wave pass
+        const int q = q0 + (lane >> (6 - lgR));
+        const bool ok = q < J;
+        float v = 0.f;
+        if (ok)
+          for (int rr = 0; rr < R; ++rr) v += sDPhi[(tok * R + rr) * JP + q];
+        v = seg_scan_q(v);
+        if (ok) {
+          const float d = sThC[q] + v;
+          const int t = c * Q + tok;
+          if (t < L) p.dtheta[((static_cast<size_t>(b) * L + t) * H + hh) * J + q] = d;
+          if (t == 0 && p.dphi0 != nullptr) p.dphi0[static_cast<size_t>(bh) * J + q] = d;
         }
       }
     }
@@ -817,10 +834,6 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
           for (int n = 0; n < N; ++n) s += sG[n * P + pc] * p.Bprev_rot[(static_cast<size_t>(bh) * R + rr) * N + n];
           static_cast<bf16_t*>(p.dxprev)[(static_cast<size_t>(bh) * R + rr) * P + pc].bits = f32_to_bf16(kappa * s);
         }
-    }
-    if constexpr (ROPE) {
-      const int q = tid - 64;
-      if (q >= 0 && q < J && p.dphi0 != nullptr) p.dphi0[static_cast<size_t>(bh) * J + q] = thCarry;
     }
   }
 }
