@@ -374,6 +374,8 @@ int check_backward(const m3_backward_args* a) {
     return M3_ERR_INVALID_ARG;
   const double item = double(a->L) * a->H * a->R * (a->N > a->P ? a->N : a->P) * 2.0;
   if (item > 4.0e18 || double(a->Bt) * a->H > 2147483647.0) return M3_ERR_INVALID_ARG;
+  // the kernel addresses one batch item's gradients with 32-bit buffer offsets
+  if (item > 2147483000.0 || double(a->L) * a->H * (a->N / 2) * 4.0 > 2147483000.0) return M3_ERR_UNSUPPORTED;
   const size_t lds = m3::backward_lds_bytes(a->N, a->P, a->theta != nullptr);
   if (lds == 0 || lds > kMaxLds) return M3_ERR_UNSUPPORTED;
   const BwPlan w = bw_plan(a);

@@ -140,6 +140,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   const float Ah = p.A_tok != nullptr ? 0.f : p.A[hh];
   float* const stBase = p.states + static_cast<size_t>(bh) * nch * NST * 256;
   float* const phBase = ROPE ? p.phis + static_cast<size_t>(bh) * nch * J : nullptr;
+  const rsrc_t rPh = make_rsrc(ROPE ? static_cast<const void*>(phBase) : static_cast<const void*>(p.dt),
+                               ROPE ? static_cast<uint32_t>(nch * J * 4) : 0u);
 
   // global element offset of row r (token, rank) of chunk c; valid only for tokens < L
   auto grow = [&](int c, int r) -> size_t {
@@ -147,6 +149,26 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     return ((static_cast<size_t>(b) * L + t) * H + hh) * R + (r & (R - 1));
   };
   auto valid = [&](int c, int r) { return c * Q + (r >> lgR) < L; };
+  // Output resources spanning this unit's rows (tokens): an out-of-range
+  // offset (kBad) drops a store, so every wave issues the same number of
+  // stores every chunk and the wait for a chunk's early loads is not held up
+  // by the previous chunk's stores.
+  const size_t row0 = (static_cast<size_t>(b) * L * H + hh) * R;  // token 0, rank 0 of this unit
+  const uint32_t rowsU = static_cast<uint32_t>((static_cast<size_t>(L - 1) * H + 1) * R);
+  const size_t tok0 = static_cast<size_t>(b) * L * H + hh;
+  const uint32_t toksU = static_cast<uint32_t>(static_cast<size_t>(L - 1) * H + 1);
+  const rsrc_t rdX = make_rsrc(static_cast<bf16_t*>(p.dx) + row0 * P, rowsU * P * 2u);
+  const rsrc_t rdB = make_rsrc(static_cast<bf16_t*>(p.dB) + row0 * N, rowsU * N * 2u);
+  const rsrc_t rdC = make_rsrc(static_cast<bf16_t*>(p.dC) + row0 * N, rowsU * N * 2u);
+  const rsrc_t rDdt = make_rsrc(p.ddt + tok0, toksU * 4u);
+  const rsrc_t rDlam = make_rsrc(p.dlam + tok0, toksU * 4u);
+  const rsrc_t rDAt = make_rsrc(p.dA_tok != nullptr ? p.dA_tok + tok0 : p.ddt, p.dA_tok != nullptr ? toksU * 4u : 0u);
+  const rsrc_t rDth = make_rsrc(ROPE ? p.dtheta + tok0 * J : p.ddt, ROPE ? toksU * J * 4u : 0u);
+  // row of (chunk c, tile row r) relative to row0, and its token's offset in a [Bt, L, H] tensor
+  auto rrow = [&](int c, int r) -> uint32_t {
+    return static_cast<uint32_t>((c * Q + (r >> lgR)) * H * R + (r & (R - 1)));
+  };
+  auto toff = [&](int t) -> uint32_t { return static_cast<uint32_t>(t) * static_cast<uint32_t>(H) * 4u; };
   // MFMA operand fragments: rows r0 + l16 of a row-major tile (k along the
   // row), or columns c0 + l16 of a tile whose rows are k (transposing read);
   // both take k = 32 kb + {4g..4g+3, 16+4g..16+4g+3}
@@ -296,12 +318,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         const int q = q0 + (lane >> (6 - lgR));
         const bool ok = q < J;
         const float v = seg_scan_q(ok ? sPhi[tl * JP + q] : 0.f);
+        const float cin = ok ? phiC[q] : 0.f;
         if (ok) {
-          const float cin = phiC[q];
           sPhi[tl * JP + q] = wrap_angle(cin + v);
-          if (dump && tl == 0) phBase[static_cast<size_t>(c) * J + q] = cin;
           if (tl == Q - 1) phiC[q] = wrap_angle(cin + v);
         }
+        bstoref(rPh, (dump && ok && tl == 0) ? static_cast<uint32_t>(c * J + q) * 4u : kBad, cin);
       }
     }
   };
@@ -403,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     // the shifted state entering chunk c, in the accumulator layout
 #pragma unroll
     for (int m = 0; m < STW; ++m)
-      if (tile_ok(m))
+      if (NST % kWaves == 0 || tile_ok(m))
         *reinterpret_cast<f32x4*>(stBase + (static_cast<size_t>(c) * NST + wave + kWaves * m) * 256 + lane * 4) = acc[m];
     __syncthreads();
     // H <- D H + Btil^T (w X): k = the chunk's 64 rows
@@ -593,11 +615,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     {
       const float* w = sc + kW * kSc;
       const float* E = sc + kE * kSc;
-      bf16_t* dXg = static_cast<bf16_t*>(p.dx);
-      bf16_t* dBg = static_cast<bf16_t*>(p.dB);
-      bf16_t* dCg = static_cast<bf16_t*>(p.dC);
       // ---- dX^T tiles: [p][j] = (S1^T dY)^T + w_j (B G)^T
-      for (int k = wave; k < 4 * PT; k += kWaves) {
+      // (compile-time trip counts, fully unrolled: the same stores in every wave)
+#pragma unroll
+      for (int it = 0; it < (4 * PT + kWaves - 1) / kWaves; ++it) {
+        const int k = wave + kWaves * it;
+        if ((4 * PT) % kWaves != 0 && k >= 4 * PT) break;
         const int jt = k / PT, pt = k % PT;
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -608,7 +631,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         const int j = 16 * jt + l16;
         const float wj = w[j >> lgR];
         const f32x4 dx = a1 + wj * a2;
-        if (valid(c, j)) *reinterpret_cast<u32x2*>(dXg + grow(c, j) * P + 16 * pt + 4 * g) = pack4(dx);
+        bstore8(rdX, valid(c, j) ? (rrow(c, j) * P + 16 * pt + 4 * g) * 2u : kBad, pack4(dx));
         // dw_j part: <(B G)_j, x_j> over this tile's four columns
         const u32x2 xv = *reinterpret_cast<const u32x2*>(sX + j * PP + 16 * pt + 4 * g);
         float s = a2[0] * __uint_as_float(xv[0] << 16) + a2[1] * __uint_as_float(xv[0] & 0xffff0000u) +
@@ -618,7 +641,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (g == 0) sWp[pt * 64 + j] = s;
       }
       // ---- dB^T and dC^T tiles of the same rows (row tile t, n tile nt)
-      for (int k = wave; k < 4 * NT; k += kWaves) {
+#pragma unroll(NT >= 8 ? 1 : 4)
+      for (int it = 0; it < (4 * NT + kWaves - 1) / kWaves; ++it) {
+        const int k = wave + kWaves * it;
+        if ((4 * NT) % kWaves != 0 && k >= 4 * NT) break;
         const int t = k / NT, nt = k % NT;
         f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f},
               c2 = {0.f, 0.f, 0.f, 0.f};
@@ -663,10 +689,9 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
             dc[2 * h2 + 1] = sn * e0 + cs * e1;
           }
         }
-        if (valid(c, r)) {
-          *reinterpret_cast<u32x2*>(dBg + grow(c, r) * N + 16 * nt + 4 * g) = pack4(db);
-          *reinterpret_cast<u32x2*>(dCg + grow(c, r) * N + 16 * nt + 4 * g) = pack4(dc);
-        }
+        const uint32_t ob = valid(c, r) ? (rrow(c, r) * N + 16 * nt + 4 * g) * 2u : kBad;
+        bstore8(rdB, ob, pack4(db));
+        bstore8(rdC, ob, pack4(dc));
       }
       // ---- G <- D G + Ctil^T (E dY) on the own tiles (G^T in LDS keeps the old G)
       const float D = sc[kMisc * kSc];
@@ -689,7 +714,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (tile_ok(m)) turn_parts(m, acc[m], hsave[m]);
     }
 
-    // ---- per-token scalar gradients (wave 0, lane = token)
+    // ---- per-token scalar gradients (wave 0, lane = token); every wave issues
+    // the stores, with dropped offsets outside wave 0
+    float stDt = 0.f, stLam = 0.f, stA = 0.f, stPdt = 0.f, stPlam = 0.f;
+    uint32_t offT = kBad, offA = kBad, offP = kBad;
     if (wave == 0) {
       const int t = lane;
       float rlo = 0.f, rdg = 0.f, clo = 0.f, cdd = 0.f, dE = 0.f, dw = 0.f;
@@ -736,13 +764,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         glam -= ddlPrev * dtv;
       }
       const float dA = da * dtv;
-      const size_t o = (static_cast<size_t>(b) * L + c * Q + t) * H + hh;
       const bool v = t < Q && c * Q + t < L;
-      if (v && t >= 1) {
-        p.ddt[o] = gdt;
-        p.dlam[o] = glam;
-      }
-      if (v && p.dA_tok != nullptr) p.dA_tok[o] = dA;
+      stDt = gdt;
+      stLam = glam;
+      stA = dA;
+      if (v && t >= 1) offT = toff(c * Q + t);
+      if (v) offA = toff(c * Q + t);
       float sA = v ? dA : 0.f;
       for (int off = 32; off > 0; off >>= 1) sA += __shfl_xor(sA, off);
       // the later chunk's first token takes this chunk's last delta term
@@ -750,9 +777,9 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       if (t == 0) {
         if (pendTok >= 0) {
           const float dn = sc[kDt * kSc + Q], ln = sc[kLamb * kSc + Q];
-          const size_t op = (static_cast<size_t>(b) * L + pendTok) * H + hh;
-          p.ddt[op] = pendDt + ddlLast * (1.f - ln);
-          p.dlam[op] = pendLam - ddlLast * dn;
+          offP = toff(pendTok);
+          stPdt = pendDt + ddlLast * (1.f - ln);
+          stPlam = pendLam - ddlLast * dn;
         }
         pendDt = gdt;
         pendLam = glam;
@@ -760,24 +787,30 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         dAsum += sA;
       }
     }
+    bstoref(rDdt, offT, stDt);
+    bstoref(rDlam, offT, stLam);
+    bstoref(rDAt, offA, stA);
+    bstoref(rDdt, offP, stPdt);
+    bstoref(rDlam, offP, stPlam);
     if constexpr (ROPE) {
       // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens
       // >= t: a segmented scan over the tokens in reverse order (lane tl holds
       // token Q - 1 - tl), one segment of Q lanes per pair
+      // (a compile-time number of passes, R pairs per wave each: the same
+      // stores in every wave; passes past the last pair store nothing)
       const int tl = lane & (Q - 1), tok = Q - 1 - tl;
-      for (int q0 = wave * R; q0 < J; q0 += kWaves * R) {  // R pairs per wave pass
-        const int q = q0 + (lane >> (6 - lgR));
+#pragma unroll
+      for (int it = 0; it < (J + kWaves - 1) / kWaves; ++it) {
+        const int q = (wave + kWaves * it) * R + (lane >> (6 - lgR));
         const bool ok = q < J;
         float v = 0.f;
         if (ok)
           for (int rr = 0; rr < R; ++rr) v += sDPhi[(tok * R + rr) * JP + q];
         v = seg_scan_q(v);
-        if (ok) {
-          const float d = sThC[q] + v;
-          const int t = c * Q + tok;
-          if (t < L) p.dtheta[((static_cast<size_t>(b) * L + t) * H + hh) * J + q] = d;
-          if (t == 0 && p.dphi0 != nullptr) p.dphi0[static_cast<size_t>(bh) * J + q] = d;
-        }
+        const float d = (ok ? sThC[q] : 0.f) + v;
+        const int t = c * Q + tok;
+        bstoref(rDth, (ok && t < L) ? (static_cast<uint32_t>(t) * H * J + q) * 4u : kBad, d);
+        if (ok && t == 0) sThC[q] = d;  // dtheta of token 0 = dphi0, written after the walk
       }
     }
     __syncthreads();
@@ -786,6 +819,9 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   // ================================================================ carry-in
   // G is now the gradient of H_{-1} = h0 + kappa u_{-1}
   {
+    if constexpr (ROPE)
+      if (p.dphi0 != nullptr)
+        for (int q = tid; q < J; q += kThreads) p.dphi0[static_cast<size_t>(bh) * J + q] = sThC[q];
     float dk = 0.f;
 #pragma unroll
     for (int m = 0; m < STW; ++m) {

@@ -68,22 +68,6 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPGroups = 4;  // p tiles are dealt round-robin over wave & 3
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr uint32_t kBad = 0x7FFFFFF0u;  // buffer offset past any valid range -> reads 0
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ float bloadf(rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ f32x4 bloadf4(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 // Row-major bf16 tiles of D columns (D = 32, 64 or 128) keep their 8-byte
 // units XOR-swizzled by row.  Measured on gfx950: an 8-byte read (plain or
 // transposing) is served 32 lanes at a time from 64 four-byte banks, a
@@ -128,12 +112,6 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 w0, f32x4 w1) {
     o[q] = pack_bf16x2(wa * __uint_as_float(v[q] << 16), wb * __uint_as_float(v[q] & 0xffff0000u));
   }
   return as_bf16x8(o);
-}
-__device__ __forceinline__ void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
-}
-__device__ __forceinline__ void bstore16(rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 // One staging load instruction: instruction i of the unit (16 rows x column
 // block cb of B, C or X: kind 0, 1, 2).  Lanes read whole 128-byte lines, 8
