@@ -298,8 +298,9 @@ int m3_ssm_decode_step(const m3_decode_args* args, void* stream);
  *   theta); dh0 [Bt, H, N, P], dBprev_rot [Bt, H, R, N] (float32), dxprev
  *   [Bt, H, R, P] (bf16), dphi0 [Bt, H, N/2]: each nullable.
  *   workspace: required, m3_ssm_prefill_backward_workspace_size bytes,
- *   256-byte aligned (the shifted state and the angle entering every chunk
- *   of every (batch, head), written by the kernel's forward state walk).
+ *   256-byte aligned (the shifted state, in bf16, and the angle entering
+ *   every chunk of every (batch, head), written by the kernel's forward
+ *   state walk).
  * Sizes: bf16 only (M3_ERR_UNSUPPORTED for float32); N, P in {16, 32, 64,
  * 128} whose tiles fit the LDS of a CU (N = P = 128 does not:
  * M3_ERR_UNSUPPORTED); R a power of two <= 8; chunks of 64 / R tokens.

@@ -336,7 +336,7 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
 
 namespace {
 
-// Backward workspace: states [units][chunks][N*P], angles [units][chunks][N/2],
+// Backward workspace: states [units][chunks][N*P] (bf16), angles [units][chunks][N/2],
 // per-unit dA sums [units] (A per head)
 struct BwPlan {
   size_t oSt = 0, oPh = 0, oDA = 0, bytes = 0;
@@ -347,7 +347,7 @@ BwPlan bw_plan(const m3_backward_args* a) {
   const int R = a->R > 0 ? a->R : 1;
   const size_t nch = (size_t(a->L) + (64 / R) - 1) / (64 / R);
   w.oSt = 0;
-  w.oPh = up256(w.oSt + u * nch * a->N * a->P * 4);
+  w.oPh = up256(w.oSt + u * nch * a->N * a->P * 2);
   w.oDA = up256(w.oPh + (a->theta != nullptr ? u * nch * (a->N / 2) * 4 : 0));
   w.bytes = up256(w.oDA + u * 4);
   return w;
@@ -409,7 +409,7 @@ int m3_ssm_prefill_backward(const m3_backward_args* a, void* stream) {
   p.dA_tok = a->A_tok != nullptr ? a->dA : nullptr;
   p.dA_part = a->A_tok != nullptr ? nullptr : reinterpret_cast<float*>(ws + w.oDA);
   p.dtheta = a->dtheta; p.dh0 = a->dh0; p.dBprev_rot = a->dBprev_rot; p.dxprev = a->dxprev; p.dphi0 = a->dphi0;
-  p.states = reinterpret_cast<float*>(ws + w.oSt);
+  p.states = ws + w.oSt;
   p.phis = a->theta != nullptr ? reinterpret_cast<float*>(ws + w.oPh) : nullptr;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = m3::launch_backward(p, st);

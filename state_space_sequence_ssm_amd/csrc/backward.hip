@@ -138,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   const bf16_t* Cg = static_cast<const bf16_t*>(p.C);
   const bf16_t* dYg = static_cast<const bf16_t*>(p.dy);
   const float Ah = p.A_tok != nullptr ? 0.f : p.A[hh];
-  float* const stBase = p.states + static_cast<size_t>(bh) * nch * NST * 256;
+  // chunk-entry states, bf16 in the accumulator tile order (one 8-byte unit per lane per tile)
+  uint16_t* const stBase = static_cast<uint16_t*>(p.states) + static_cast<size_t>(bh) * nch * NST * 256;
   float* const phBase = ROPE ? p.phis + static_cast<size_t>(bh) * nch * J : nullptr;
   const rsrc_t rPh = make_rsrc(ROPE ? static_cast<const void*>(phBase) : static_cast<const void*>(p.dt),
                                ROPE ? static_cast<uint32_t>(nch * J * 4) : 0u);
@@ -426,7 +427,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
 #pragma unroll
     for (int m = 0; m < STW; ++m)
       if (NST % kWaves == 0 || tile_ok(m))
-        *reinterpret_cast<f32x4*>(stBase + (static_cast<size_t>(c) * NST + wave + kWaves * m) * 256 + lane * 4) = acc[m];
+        *reinterpret_cast<u32x2*>(stBase + (static_cast<size_t>(c) * NST + wave + kWaves * m) * 256 + lane * 4) =
+            pack4(acc[m]);
     __syncthreads();
     // H <- D H + Btil^T (w X): k = the chunk's 64 rows
     const float D = sc[kMisc * kSc];
@@ -499,8 +501,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   int pendTok = -1;
   float dAsum = 0.f;                            // sum of dA over tokens (wave 0, lane 0)
   Stage& S = S0;                                // the reverse walk's loads, one chunk ahead
-  f32x4 hsave[STW];                             // the shifted state entering the chunk (fp32)
-  f32x4 hpre[STW];                              // the same, loaded a chunk ahead
+  u32x2 hsave[STW];                             // the shifted state entering the chunk (bf16)
+  u32x2 hpre[STW];                              // the same (bf16), loaded a chunk ahead
   float phPre = 0.f;                            // the angle entering the chunk (tid < J), loaded a chunk ahead
   auto load_rev = [&](int c) __attribute__((always_inline)) {
     load_scalars(c, S);
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     if constexpr (ROPE) phPre = phBase[static_cast<size_t>(c) * J + (tid < J ? tid : 0)];
 #pragma unroll
     for (int m = 0; m < STW; ++m)
-      hpre[m] = *reinterpret_cast<const f32x4*>(
+      hpre[m] = *reinterpret_cast<const u32x2*>(
           stBase + (static_cast<size_t>(c) * NST + (tile_ok(m) ? wave + kWaves * m : 0)) * 256 + lane * 4);
   };
   load_rev(nch - 1);
@@ -535,16 +537,16 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     store_xp(c, S.x, sX);
     store_xp(c, S.dy, sDY);
     {
-      // H^T from the forward walk's dump and G^T from the accumulators (own tiles);
-      // dD = <G, H> from the fp32 values
+      // H^T from the forward walk's (bf16) dump and G^T from the accumulators
+      // (own tiles); dD = <G, H> from G in fp32 and the bf16 state
       float dd = 0.f;
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
         if (!tile_ok(m)) continue;
-        const f32x4 hv = hpre[m];
-        hsave[m] = hv;
+        const f32x4 hv = unpack4(hpre[m]);
+        hsave[m] = hpre[m];
         const int at = (16 * tile_pt(m) + l16) * PN + 16 * tile_nt(m) + 4 * g;
-        *reinterpret_cast<u32x2*>(sHT + at) = pack4(hv);
+        *reinterpret_cast<u32x2*>(sHT + at) = hpre[m];
         *reinterpret_cast<u32x2*>(sGT + at) = pack4(acc[m]);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) dd += acc[m][jj] * hv[jj];
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       // parts of <G, J H> for the start of this chunk (read at the next chunk's pass)
 #pragma unroll
       for (int m = 0; m < STW; ++m)
-        if (tile_ok(m)) turn_parts(m, acc[m], hsave[m]);
+        if (tile_ok(m)) turn_parts(m, acc[m], unpack4(hsave[m]));
     }
 
     // ---- per-token scalar gradients (wave 0, lane = token); every wave issues

@@ -147,6 +147,10 @@ __device__ __forceinline__ bf16x8 cat8(u32x2 lo, u32x2 hi) {
   return as_bf16x8(v);
 }
 __device__ __forceinline__ u32x2 pack4(f32x4 v) { return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}; }
+__device__ __forceinline__ f32x4 unpack4(u32x2 u) {
+  return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+               __uint_as_float(u[1] & 0xffff0000u)};
+}
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16).  In each group of 16
 // lanes, lane 4e + q reads 4 bf16 at its own address; afterwards lane i holds
 // element i % 4 of lanes 4e + i / 4, e = 0..3.  With lane 4e + q pointing at

@@ -134,7 +134,7 @@ struct BackwardParams {
   float* dBprev_rot;
   void* dxprev;
   float* dphi0;
-  float* states;    // [Bt * H][chunks][N * P] shifted state entering each chunk (fp32)
+  void* states;     // [Bt * H][chunks][N * P] shifted state entering each chunk (bf16, accumulator tile order)
   float* phis;      // [Bt * H][chunks][N/2] angle entering each chunk
 };
 hipError_t launch_backward(const BackwardParams& p, hipStream_t s);

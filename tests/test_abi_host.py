@@ -257,8 +257,8 @@ def test_backward_validation_and_workspace():
     f = lambda a: lib.m3_ssm_prefill_backward(ctypes.byref(a), None)  # noqa: E731
     assert lib.m3_ssm_prefill_backward(None, None) == _lib.M3_ERR_INVALID_ARG
     a = _good_backward()
-    # states of every chunk (2 x 3 units, 2 chunks of 64, 64 x 64 fp32) and per-unit dA sums
-    assert a.workspace_bytes == _up256(6 * 2 * 64 * 64 * 4) + _up256(6 * 4)
+    # states of every chunk (2 x 3 units, 2 chunks of 64, 64 x 64 bf16) and per-unit dA sums
+    assert a.workspace_bytes == _up256(6 * 2 * 64 * 64 * 2) + _up256(6 * 4)
     cases = [
         (lambda a: setattr(a, "dy", None), _lib.M3_ERR_INVALID_ARG),
         (lambda a: setattr(a, "dA", None), _lib.M3_ERR_INVALID_ARG),
@@ -284,4 +284,4 @@ def test_backward_validation_and_workspace():
     a = _good_backward()
     a.theta, a.dtheta = 0x30000000, 0x30100000
     assert lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a)) == (
-        _up256(6 * 2 * 64 * 64 * 4) + _up256(6 * 2 * 32 * 4) + _up256(6 * 4))
+        _up256(6 * 2 * 64 * 64 * 2) + _up256(6 * 2 * 32 * 4) + _up256(6 * 4))
