@@ -170,12 +170,36 @@ def variant_unit_kernels(group=None):
     return out
 
 
+def backward_split(Bt, L, H, P, N, R, rope, cus=256):
+    """Split chunk of the library's backward for this shape, 0 when it does
+    not split (the rule of m3_ssm_prefill_backward_workspace_size): at most
+    half as many units as compute units and at least 8 chunks."""
+    Q = 64 // R
+    nch = (L + Q - 1) // Q
+    if 2 * Bt * H > cus or nch < 8:
+        return 0
+    return min(max((nch * 9 + 8) // 16, 4), nch - 4)
+
+
+SPLIT_JOIN_KERNEL = "m3::bw::split_join_kernel"
+
+
 def backward_unit_kernels():
-    """(unit key, kernel symbol, grid) of the backward lines: one 512-thread
-    workgroup per (batch, head); the per-head dA reduction is a few hundred
-    bytes and left out."""
-    return [("backward_" + name, backward_kernel_name(shp[6], shp[4], shp[3]), shp[0] * shp[2] * 512)
-            for name, shp in prefill_shapes().items()]
+    """(unit key, kernel symbol, grid x in threads) of the backward lines: one
+    512-thread workgroup per (batch, head), or with the split the pre and main
+    launches (two segments in grid y) and the joining kernel; the per-head dA
+    reduction is a few hundred bytes and left out."""
+    out = []
+    for name, shp in prefill_shapes().items():
+        Bt, L, H, P, N, R, rope = shp
+        cm = backward_split(*shp)
+        if cm:
+            out += [("backward_" + name, backward_kernel_name(rope, N, P, 1), Bt * H * 512),
+                    ("backward_" + name, backward_kernel_name(rope, N, P, 2), Bt * H * 512),
+                    ("backward_" + name, SPLIT_JOIN_KERNEL, (Bt * cm * (64 // R) if rope else 1) * 256)]
+        else:
+            out.append(("backward_" + name, backward_kernel_name(rope, N, P), Bt * H * 512))
+    return out
 
 
 def group_units(group):
@@ -233,8 +257,10 @@ def backward_algo(Bt, L, H, P, N, R, rope):
     return byts, flops
 
 
-def backward_kernel_name(rope, N, P):
-    return f"m3::bw::backward_kernel<{N}, {P}, {'true' if rope else 'false'}>"
+def backward_kernel_name(rope, N, P, mode=0):
+    """Backward kernel symbol: mode 0 the whole walk, 1 and 2 the split's pre
+    and main launches."""
+    return f"m3::bw::backward_kernel<{N}, {P}, {'true' if rope else 'false'}, {mode}>"
 
 
 def time_backward(torch, ops, inp, steps, warmup):
@@ -916,7 +942,8 @@ def main():
                                 f"{', theta' if rope else ''}",
                        tokens_per_s=Bt * L / (ms * 1e-3), ms_per_step=ms, gbs=byts / (ms * 1e-3) / 1e9,
                        tflops=flops / (ms * 1e-3) / 1e12, bytes=byts, flops=flops,
-                       kernel=backward_kernel_name(rope, N, P), traffic=traffic_for("backward_" + name))
+                       kernel=backward_kernel_name(rope, N, P, 2 if backward_split(*shp) else 0),
+                       traffic=traffic_for("backward_" + name))
             res["hbm_frac"] = res["gbs"] / HBM_PEAK_GBS
             res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFS
             results["backward_" + name] = res

@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libm3ssm.so")
 # the largest units first, so the parallel build ends sooner
 SOURCES = ["prefill_bf16_n128.hip", "prefill_bf16_n128_pro.hip", "prefill_bf16_n64.hip", "prefill_bf16_n64_pro.hip",
            "prefill_bf16_n32.hip", "prefill_bf16_n32_pro.hip", "prefill_bf16_n16.hip", "prefill_bf16_n16_pro.hip",
-           "backward.hip", "prefill_f32.hip", "decode.hip", "decode_mma.hip", "api.hip", "angles.hip", "split.hip", "prefill_bf16.hip"]
+           "backward_main.hip", "backward.hip", "backward_pre.hip", "prefill_f32.hip", "decode.hip", "decode_mma.hip",
+           "api.hip", "angles.hip", "split.hip", "prefill_bf16.hip"]
 ARCH = "gfx950"
 
 

@@ -336,20 +336,48 @@ int m3_ssm_decode_step(const m3_decode_args* a, void* stream) {
 
 namespace {
 
-// Backward workspace: states [units][chunks][N*P] (bf16), angles [units][chunks][N/2],
-// per-unit dA sums [units] (A per head)
+// Backward workspace: states [units][chunks][N*P] (bf16), angles
+// [units][chunks][N/2], per-unit dA sums [segments][units] (A per head); with
+// the sequence split also the values joined at chunk cm: the state and its
+// gradient's relative sum [units][N*P] (float32), the angle, the decay, the
+// dtheta there and the two segments' parts of that token's Delta and lambda
+// gradients.
+constexpr int kBwMinSegChunks = 4;  // both segments of a split keep at least this many chunks
 struct BwPlan {
-  size_t oSt = 0, oPh = 0, oDA = 0, bytes = 0;
+  int cm = 0;  // split chunk (0: none)
+  size_t oSt = 0, oPh = 0, oDA = 0, oH = 0, oG = 0, oPhM = 0, oDc = 0, oDth = 0, oTok = 0, bytes = 0;
 };
 BwPlan bw_plan(const m3_backward_args* a) {
   BwPlan w;
   const size_t u = size_t(a->Bt) * a->H;
   const int R = a->R > 0 ? a->R : 1;
   const size_t nch = (size_t(a->L) + (64 / R) - 1) / (64 / R);
+  // Split with fewer (batch, head) units than half the compute units: two
+  // workgroups per unit.  In the main launch segment 1 walks its chunks
+  // forward and backward and segment 0 backward only, so segment 0 takes
+  // about 9/16 of the chunks.
+  if (2 * u <= size_t(device_cus()) && nch >= size_t(2 * kBwMinSegChunks)) {
+    size_t cm = (nch * 9 + 8) / 16;
+    if (cm < size_t(kBwMinSegChunks)) cm = kBwMinSegChunks;
+    if (cm > nch - kBwMinSegChunks) cm = nch - kBwMinSegChunks;
+    w.cm = int(cm);
+  }
+  const size_t J = size_t(a->N / 2 > 0 ? a->N / 2 : 1);
+  const size_t NP = size_t(a->N) * a->P;
   w.oSt = 0;
-  w.oPh = up256(w.oSt + u * nch * a->N * a->P * 2);
-  w.oDA = up256(w.oPh + (a->theta != nullptr ? u * nch * (a->N / 2) * 4 : 0));
-  w.bytes = up256(w.oDA + u * 4);
+  w.oPh = up256(w.oSt + u * nch * NP * 2);
+  w.oDA = up256(w.oPh + (a->theta != nullptr ? u * nch * J * 4 : 0));
+  size_t end = up256(w.oDA + (w.cm > 0 ? 2 : 1) * u * 4);
+  if (w.cm > 0) {
+    w.oH = end;
+    w.oG = up256(w.oH + u * NP * 4);
+    w.oPhM = up256(w.oG + u * NP * 4);
+    w.oDc = up256(w.oPhM + u * J * 4);
+    w.oDth = up256(w.oDc + u * 4);
+    w.oTok = up256(w.oDth + u * J * 4);
+    end = up256(w.oTok + 2 * u * 2 * 4);
+  }
+  w.bytes = end;
   return w;
 }
 
@@ -411,10 +439,19 @@ int m3_ssm_prefill_backward(const m3_backward_args* a, void* stream) {
   p.dtheta = a->dtheta; p.dh0 = a->dh0; p.dBprev_rot = a->dBprev_rot; p.dxprev = a->dxprev; p.dphi0 = a->dphi0;
   p.states = ws + w.oSt;
   p.phis = a->theta != nullptr ? reinterpret_cast<float*>(ws + w.oPh) : nullptr;
+  p.cm = w.cm;
+  if (w.cm > 0) {
+    p.sH = reinterpret_cast<float*>(ws + w.oH);
+    p.sG = reinterpret_cast<float*>(ws + w.oG);
+    p.sPhiM = reinterpret_cast<float*>(ws + w.oPhM);
+    p.sDc = reinterpret_cast<float*>(ws + w.oDc);
+    p.sDth = reinterpret_cast<float*>(ws + w.oDth);
+    p.sTok = reinterpret_cast<float*>(ws + w.oTok);
+  }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = m3::launch_backward(p, st);
   if (e != hipSuccess) return hip_status(e);
-  if (a->A_tok == nullptr) e = m3::launch_backward_dA(p.dA_part, a->dA, a->Bt, a->H, st);
+  if (a->A_tok == nullptr) e = m3::launch_backward_dA(p.dA_part, a->dA, (w.cm > 0 ? 2 : 1) * a->Bt, a->H, st);
   return hip_status(e);
 }
 

@@ -136,8 +136,19 @@ struct BackwardParams {
   float* dphi0;
   void* states;     // [Bt * H][chunks][N * P] shifted state entering each chunk (bf16, accumulator tile order)
   float* phis;      // [Bt * H][chunks][N/2] angle entering each chunk
+  // sequence split at chunk cm (0: none); dA_part is then [2][Bt * H]
+  int cm;
+  float* sH;        // [Bt * H][N * P] shifted state entering chunk cm
+  float* sPhiM;     // [Bt * H][N/2] angle entering chunk cm
+  float* sG;        // [Bt * H][N * P] segment 1's relative part of the gradient entering chunk cm
+  float* sDc;       // [Bt * H] decay over segment 1
+  float* sDth;      // [Bt * H][N/2] dtheta at token cm Q
+  float* sTok;      // [2][Bt * H][2] the two segments' parts of token cm Q's Delta and lambda gradients
 };
+// one walk per (batch, head), or with cm > 0 the split's pre, main and join launches
 hipError_t launch_backward(const BackwardParams& p, hipStream_t s);
+hipError_t launch_backward_pre(const BackwardParams& p, hipStream_t s);
+hipError_t launch_backward_main(const BackwardParams& p, hipStream_t s);
 // dA [H] = sum over the batch of the per-unit sums
 hipError_t launch_backward_dA(const float* part, float* dA, int Bt, int H, hipStream_t s);
 size_t backward_lds_bytes(int N, int P, bool rope);

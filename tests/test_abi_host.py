@@ -285,3 +285,27 @@ def test_backward_validation_and_workspace():
     a.theta, a.dtheta = 0x30000000, 0x30100000
     assert lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a)) == (
         _up256(6 * 2 * 64 * 64 * 2) + _up256(6 * 2 * 32 * 4) + _up256(6 * 4))
+
+
+def test_backward_split_workspace():
+    """With few (batch, head) units and enough chunks the backward splits the
+    sequence (two workgroups per unit; 256 compute units are assumed when no
+    device can be queried): its workspace adds the values joined at the split
+    chunk and a second set of dA sums."""
+    lib = _lib.load()
+    a = _good_backward()
+    a.L = 600  # 10 chunks of 64 tokens, 6 units
+    a.theta, a.dtheta = 0x30000000, 0x30100000
+    u, nch, NP, J = 6, 10, 64 * 64, 32
+    want = (_up256(u * nch * NP * 2) + _up256(u * nch * J * 4) + _up256(2 * u * 4)  # states, angles, dA sums
+            + 2 * _up256(u * NP * 4)                                                # state and gradient sum
+            + _up256(u * J * 4) + _up256(u * 4) + _up256(u * J * 4) + _up256(2 * u * 2 * 4))
+    assert lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a)) == want
+    # 7 chunks: too short to split
+    a.L = 7 * 64
+    assert lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a)) == (
+        _up256(u * 7 * NP * 2) + _up256(u * 7 * J * 4) + _up256(u * 4))
+    # more units than half the compute units: no split
+    a.L, a.Bt, a.H = 600, 1, 129
+    assert lib.m3_ssm_prefill_backward_workspace_size(ctypes.byref(a)) == (
+        _up256(129 * nch * NP * 2) + _up256(129 * nch * J * 4) + _up256(129 * 4))

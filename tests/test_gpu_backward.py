@@ -80,6 +80,14 @@ CASES = [
     (1, 1, 2, 64, 64, 1, True, True, False),
     (1, 200, 2, 128, 64, 1, True, True, False),
     (1, 96, 3, 16, 128, 2, True, True, False),
+    # sequence split (at most 128 units and at least 8 chunks): the split
+    # chunk lands mid-sequence, ragged tails, with and without RoPE, carry
+    # and per-token A
+    (1, 600, 2, 64, 64, 4, True, True, False),
+    (2, 530, 3, 64, 128, 1, False, True, False),
+    (1, 300, 2, 32, 32, 8, True, False, True),
+    (2, 517, 2, 16, 16, 2, True, True, False),
+    (1, 512, 1, 128, 64, 1, True, False, False),
 ]
 
 
@@ -114,11 +122,12 @@ def test_backward_vs_oracle(ops, case):
     _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
 
 
-def test_backward_deterministic(ops):
-    s = Shape(2, 150, 2, 64, 64, 4, "bf16", True)
+@pytest.mark.parametrize("L", [150, 600])  # 600: the split walk
+def test_backward_deterministic(ops, L):
+    s = Shape(2, L, 2, 64, 64, 4, "bf16", True)
     d = make_inputs(s, 15500, h0=True, carry=True)
     dd = to_device(d, s)
-    dy = dev(bf16_round(np.random.default_rng(7).standard_normal((2, 150, 2, 4, 64)).astype(np.float32)),
+    dy = dev(bf16_round(np.random.default_rng(7).standard_normal((2, L, 2, 4, 64)).astype(np.float32)),
              torch.bfloat16)
     run = lambda: ops.m3_ssm_prefill_backward(dd["x"], dd["B"], dd["C"], dd["dt"], dd["lam"], dd["A"],  # noqa: E731
                                               dd["theta"], dd["h0"], dd["Bprev_rot"], dd["xprev"], dd["phi0"], dy=dy,
