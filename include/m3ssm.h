@@ -114,8 +114,10 @@ typedef enum m3_layout {
  * Sizes: Bt, L, H >= 1; N, P in {16, 32, 64, 128}; R a power of two <= 64;
  * combinations whose chunk tiles exceed the 160 KB LDS of a CU return
  * M3_ERR_UNSUPPORTED (fp32 with RoPE at N = 128, and fp32 at N = P = 128);
- * chunk = tokens per chunk, 0 selects 64 / R (the only value supported:
- * one chunk tile always holds 64 (token, rank) rows).
+ * chunk = tokens per chunk Q of the chunked evaluation, 0 selects 64 / R.
+ * A chunk tile holds 64 (token, rank) rows: the bf16 path takes only
+ * Q = 64 / R; the fp32 path also any smaller power of two (the tile's rows
+ * past Q R then stay empty).  Results do not depend on Q beyond rounding.
  * Outputs must not alias inputs.  Passing the carry-out of one call as the
  * carry-in of the next continues the sequence exactly.
  * workspace: optional, see m3_ssm_prefill_workspace_size; a non-NULL

@@ -138,7 +138,11 @@ int check_prefill(const m3_prefill_args* a) {
   if (rope && (a->N % 2) != 0) return M3_ERR_INVALID_ARG;
   if (!pow2(a->R) || a->R > 64) return M3_ERR_UNSUPPORTED;
   if (!tile_dim(a->N) || !tile_dim(a->P)) return M3_ERR_UNSUPPORTED;
-  if (a->chunk != 0 && a->chunk != 64 / a->R) return M3_ERR_UNSUPPORTED;
+  // chunk: 64 / R tokens (0 selects it); the fp32 path also takes a smaller
+  // power of two, the bf16 path no other
+  if (a->chunk < 0 || (a->chunk != 0 && a->chunk != 64 / a->R &&
+                       (a->in_dtype != M3_F32 || !pow2(a->chunk) || a->chunk * a->R > 64)))
+    return M3_ERR_UNSUPPORTED;
   const void* v16[] = {a->x, a->B, a->C, a->y, a->theta, a->omega, a->h0, a->Bprev_rot, a->xprev,
                        a->phi0, a->h_final, a->Bprev_rot_out, a->xprev_out, a->phi_out};
   for (const void* p : v16)
@@ -178,6 +182,7 @@ int run_prefill(const m3_prefill_args* a, void* ws_ptr, size_t ws_bytes, void* s
   p.h0 = a->h0; p.Bprev_rot = a->Bprev_rot; p.xprev = a->xprev; p.phi0 = a->phi0;
   p.y = a->y; p.h_final = a->h_final; p.Bprev_rot_out = a->Bprev_rot_out; p.xprev_out = a->xprev_out;
   p.phi_out = a->phi_out;
+  p.chunk = a->chunk;
   p.Lfull = a->L;
   p.nseg = 1;
   p.segLen = a->L;

@@ -128,6 +128,14 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   constexpr int PN = Lt::PN, PP = Lt::PP, PR = Lt::PR, NT = Lt::NT, PT = Lt::PT, NST = Lt::NST;
   constexpr int STW = Lt::STW, J = Lt::J, JP = Lt::JP, NKB = Lt::NK / 32, PKB = Lt::PK / 32;
   constexpr int kSc = Lt::kSc;
+  // Register budget of the reverse walk: below the largest tiles with RoPE or
+  // P = 128 the operand fragments of a wave's fixed tiles are held across a
+  // chunk's products (at those tiles the extra live registers would spill).
+  // Without RoPE the next chunk's loads are then issued after the products,
+  // which frees their registers there; with RoPE that would queue the dtheta
+  // stores behind them, so they go out after the staging as otherwise.
+  constexpr bool kHoist = !(ROPE && (N >= 128 || P >= 128)) && !(P >= 128 && N >= 64);
+  constexpr bool kLateLoads = kHoist && !ROPE;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* const sm16 = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const sCr = sm16 + Lt::oCr;
@@ -171,11 +179,6 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   const rsrc_t rPh = make_rsrc(ROPE ? static_cast<const void*>(phBase) : static_cast<const void*>(p.dt),
                                ROPE ? static_cast<uint32_t>(nch * J * 4) : 0u);
 
-  // global element offset of row r (token, rank) of chunk c; valid only for tokens < L
-  auto grow = [&](int c, int r) -> size_t {
-    const int t = c * Q + (r >> lgR);
-    return ((static_cast<size_t>(b) * L + t) * H + hh) * R + (r & (R - 1));
-  };
   auto valid = [&](int c, int r) { return c * Q + (r >> lgR) < L; };
   // Output resources spanning this unit's rows (tokens): an out-of-range
   // offset (kBad) drops a store, so every wave issues the same number of
@@ -192,6 +195,16 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   const rsrc_t rDlam = make_rsrc(p.dlam + tok0, toksU * 4u);
   const rsrc_t rDAt = make_rsrc(p.dA_tok != nullptr ? p.dA_tok + tok0 : p.ddt, p.dA_tok != nullptr ? toksU * 4u : 0u);
   const rsrc_t rDth = make_rsrc(ROPE ? p.dtheta + tok0 * J : p.ddt, ROPE ? toksU * J * 4u : 0u);
+  // Input resources over the same rows: a row past the end reads zeros, so a
+  // load needs no branch and its offset is a short 32-bit sum.
+  const rsrc_t rXi = make_rsrc(xg + row0 * P, rowsU * P * 2u);
+  const rsrc_t rBi = make_rsrc(Bg + row0 * N, rowsU * N * 2u);
+  const rsrc_t rCi = make_rsrc(Cg + row0 * N, rowsU * N * 2u);
+  const rsrc_t rDYi = make_rsrc(dYg + row0 * P, rowsU * P * 2u);
+  const rsrc_t rDti = make_rsrc(p.dt + tok0, toksU * 4u);
+  const rsrc_t rLmi = make_rsrc(p.lam + tok0, toksU * 4u);
+  const rsrc_t rAti = make_rsrc(p.A_tok != nullptr ? p.A_tok + tok0 : p.dt, p.A_tok != nullptr ? toksU * 4u : 0u);
+  const rsrc_t rThi = make_rsrc(ROPE ? p.theta + tok0 * J : p.dt, ROPE ? toksU * J * 4u : 0u);
   // row of (chunk c, tile row r) relative to row0, and its token's offset in a [Bt, L, H] tensor
   auto rrow = [&](int c, int r) -> uint32_t {
     return static_cast<uint32_t>((c * Q + (r >> lgR)) * H * R + (r & (R - 1)));
@@ -237,15 +250,14 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     float th[UT];
     float dt, lam, At, dn, ln;  // wave 0, lane = token of the chunk (and the next token)
   };
-  auto load_tile = [&](int c, const bf16_t* src, auto DD, u32x4* dst) __attribute__((always_inline)) {
+  auto load_tile = [&](int c, rsrc_t src, auto DD, u32x4* dst) __attribute__((always_inline)) {
     constexpr int D = decltype(DD)::value;
     constexpr int U = (kRows * (D / 8) + kThreads - 1) / kThreads;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
       const int e = tid + i * kThreads;
       const int r = e / (D / 8), k8 = e % (D / 8);
-      const bool ok = e < kRows * (D / 8) && valid(c, r);
-      dst[i] = *reinterpret_cast<const u32x4*>(src + (ok ? grow(c, r) * D + 8 * k8 : 0));
+      dst[i] = bload16(src, e < kRows * (D / 8) ? rrow(c, r) * (D * 2u) + 16u * k8 : kBad);
     }
   };
   // per-token scalars of chunk c (wave 0, lane = token): the raw Delta, lambda,
@@ -253,15 +265,13 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   auto load_scalars = [&](int c, Stage& S) __attribute__((always_inline)) {
     if (wave != 0) return;
     const int t = lane;
-    const bool v0 = t < Q && c * Q + t < L;
-    const bool v1 = t < Q && c * Q + t + 1 < L;
-    const size_t o = (static_cast<size_t>(b) * L + c * Q + t) * H + hh;
-    const size_t o0 = v0 ? o : 0, o1 = v1 ? o + H : 0;
-    S.dt = p.dt[o0];
-    S.lam = p.lam[o0];
-    S.At = p.A_tok != nullptr ? p.A_tok[o0] : Ah;
-    S.dn = p.dt[o1];
-    S.ln = p.lam[o1];
+    const uint32_t o0 = t < Q ? toff(c * Q + t) : kBad, o1 = t < Q ? toff(c * Q + t + 1) : kBad;
+    S.dt = bloadf(rDti, o0);
+    S.lam = bloadf(rLmi, o0);
+    const float at = bloadf(rAti, o0);
+    S.At = p.A_tok != nullptr ? at : Ah;
+    S.dn = bloadf(rDti, o1);
+    S.ln = bloadf(rLmi, o1);
   };
   auto load_theta = [&](int c, Stage& S) __attribute__((always_inline)) {
     if constexpr (ROPE) {
@@ -269,9 +279,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       for (int i = 0; i < UT; ++i) {
         const int e = tid + i * kThreads;
         const int tl = e / J, q = e % J;
-        const int t = c * Q + tl;
-        const bool ok = e < Q * J && t < L;
-        S.th[i] = p.theta[ok ? ((static_cast<size_t>(b) * L + t) * H + hh) * J + q : 0];
+        S.th[i] = bloadf(rThi, e < Q * J ? (static_cast<uint32_t>(c * Q + tl) * H * J + q) * 4u : kBad);
       }
     }
   };
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       const int e = tid + i * kThreads;
       if (e >= kRows * (N / 8)) break;
       const int r = e / (N / 8), k8 = e % (N / 8);
-      u32x4 v = valid(c, r) ? src[i] : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = src[i];  // zeros past the end
       if constexpr (ROPE) {
         const float* ang = sPhi + (r >> lgR) * JP + 4 * k8;
 #pragma unroll
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       const int e = tid + i * kThreads;
       if (e >= kRows * (P / 8)) break;
       const int r = e / (P / 8), k8 = e % (P / 8);
-      const u32x4 v = valid(c, r) ? src[i] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 v = src[i];  // zeros past the end
       uint16_t* d = dst + r * PP + 8 * k8;
       *reinterpret_cast<u32x2*>(d) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(d + 4) = u32x2{v[2], v[3]};
@@ -396,6 +404,13 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   auto tile_ok = [&](int m) { return wave + kWaves * m < NST; };
   auto tile_nt = [&](int m) { return (wave + kWaves * m) / PT; };
   auto tile_pt = [&](int m) { return (wave + kWaves * m) % PT; };
+  // this unit's chunk-entry states (bf16, 512 bytes per tile); an absent tile
+  // of the last round is a dropped access
+  const rsrc_t rSt = make_rsrc(stBase, static_cast<uint32_t>(nch) * NST * 512u);
+  auto st_off = [&](int c, int m) -> uint32_t {
+    return (NST % kWaves == 0 || tile_ok(m)) ? (static_cast<uint32_t>(c) * NST + wave + kWaves * m) * 512u + lane * 8u
+                                              : kBad;
+  };
   // carried term u_{-1}[n][p] = sum_r Bprev_rot[r][n] xprev[r][p]
   const bool carry = p.Bprev_rot != nullptr && p.xprev != nullptr;
   auto u_prev = [&](int n, int pc) {
@@ -452,8 +467,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   auto load_fwd = [&](int c, Stage& S) __attribute__((always_inline)) {
     load_scalars(c, S);
     load_theta(c, S);
-    load_tile(c, Bg, NC{}, S.b);
-    load_tile(c, xg, PC{}, S.x);
+    load_tile(c, rBi, NC{}, S.b);
+    load_tile(c, rXi, PC{}, S.x);
   };
   auto fwd_chunk = [&](int c, Stage& S) __attribute__((always_inline)) {
     store_scalars(c, S);
@@ -468,10 +483,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     if (c + 2 < cB) load_fwd(c + 2, S);  // in flight during the next two chunks
     // the shifted state entering chunk c, in the accumulator layout
 #pragma unroll
-    for (int m = 0; m < STW; ++m)
-      if (NST % kWaves == 0 || tile_ok(m))
-        *reinterpret_cast<u32x2*>(stBase + (static_cast<size_t>(c) * NST + wave + kWaves * m) * 256 + lane * 4) =
-            pack4(acc[m]);
+    for (int m = 0; m < STW; ++m) bstore8(rSt, st_off(c, m), pack4(acc[m]));
     __syncthreads();
     // H <- D H + Btil^T (w X): k = the chunk's 64 rows
     const float D = sc[kMisc * kSc];
@@ -518,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     auto load_gs = [&](int c, Stage& S) __attribute__((always_inline)) {
       load_scalars(c, S);
       load_theta(c, S);
-      load_tile(c, Cg, NC{}, S.c);
-      load_tile(c, dYg, PC{}, S.dy);
+      load_tile(c, rCi, NC{}, S.c);
+      load_tile(c, rDYi, PC{}, S.dy);
     };
     auto gs_chunk = [&](int c, Stage& S) __attribute__((always_inline)) {
       store_scalars(c, S);
@@ -637,15 +649,13 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   auto load_rev = [&](int c) __attribute__((always_inline)) {
     load_scalars(c, S);
     load_theta(c, S);
-    load_tile(c, Cg, NC{}, S.c);
-    load_tile(c, Bg, NC{}, S.b);
-    load_tile(c, xg, PC{}, S.x);
-    load_tile(c, dYg, PC{}, S.dy);
-    if constexpr (ROPE) phPre = phBase[static_cast<size_t>(c) * J + (tid < J ? tid : 0)];
+    load_tile(c, rCi, NC{}, S.c);
+    load_tile(c, rBi, NC{}, S.b);
+    load_tile(c, rXi, PC{}, S.x);
+    load_tile(c, rDYi, PC{}, S.dy);
+    if constexpr (ROPE) phPre = bloadf(rPh, tid < J ? static_cast<uint32_t>(c * J + tid) * 4u : kBad);
 #pragma unroll
-    for (int m = 0; m < STW; ++m)
-      hpre[m] = *reinterpret_cast<const u32x2*>(
-          stBase + (static_cast<size_t>(c) * NST + (tile_ok(m) ? wave + kWaves * m : 0)) * 256 + lane * 4);
+    for (int m = 0; m < STW; ++m) hpre[m] = bload8(rSt, st_off(c, m));
   };
   load_rev(cB - 1);
   for (int c = cB - 1; c >= cA; --c) {
@@ -684,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       for (int off = 32; off > 0; off >>= 1) dd += __shfl_xor(dd, off);
       if (lane == 0) sDp[wave] = dd;
     }
-    if (c > cA) load_rev(c - 1);  // in flight during this chunk's products
+    if (!kLateLoads && c > cA) load_rev(c - 1);  // in flight during this chunk's products
     __syncthreads();
 
     // ---- Gram tiles (i tile it >= j tile jt): G1 = C B^T, G2 = dY X^T, masks
@@ -747,19 +757,50 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     {
       const float* w = sc + kW * kSc;
       const float* E = sc + kE * kSc;
+      // The p tile of every dX pass and the n tile of every dB / dC pass of a
+      // wave are fixed (PT and NT divide the wave count): their operand
+      // fragments are read from LDS once per chunk, not once per pass.
+      // (kHoist)
+      static_assert(kWaves % PT == 0 && kWaves % NT == 0, "fixed tile per wave");
+      const int ptw = wave % PT, ntw = wave % NT;
+      bf16x8 fDYp[2], fGTp[NKB], fGn[PKB], fHn[PKB];
+      if constexpr (kHoist) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) fDYp[kb] = frag_col(sDY, PP, 16 * ptw, kb);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) fGTp[kb] = frag_row(sGT, PN, 16 * ptw, kb);
+#pragma unroll
+        for (int kb = 0; kb < PKB; ++kb) {
+          fGn[kb] = frag_col(sGT, PN, 16 * ntw, kb);
+          fHn[kb] = frag_col(sHT, PN, 16 * ntw, kb);
+        }
+      }
+      // (without kHoist: read in each pass, for that pass's tile pt / nt)
+      auto fDY = [&](int kb, int pt) __attribute__((always_inline)) {
+        if constexpr (kHoist) return fDYp[kb]; else return frag_col(sDY, PP, 16 * pt, kb);
+      };
+      auto fGTrow = [&](int kb, int pt) __attribute__((always_inline)) {
+        if constexpr (kHoist) return fGTp[kb]; else return frag_row(sGT, PN, 16 * pt, kb);
+      };
+      auto fGTcol = [&](int kb, int nt) __attribute__((always_inline)) {
+        if constexpr (kHoist) return fGn[kb]; else return frag_col(sGT, PN, 16 * nt, kb);
+      };
+      auto fHTcol = [&](int kb, int nt) __attribute__((always_inline)) {
+        if constexpr (kHoist) return fHn[kb]; else return frag_col(sHT, PN, 16 * nt, kb);
+      };
       // ---- dX^T tiles: [p][j] = (S1^T dY)^T + w_j (B G)^T
       // (compile-time trip counts, fully unrolled: the same stores in every wave)
 #pragma unroll
       for (int it = 0; it < (4 * PT + kWaves - 1) / kWaves; ++it) {
         const int k = wave + kWaves * it;
         if ((4 * PT) % kWaves != 0 && k >= 4 * PT) break;
-        const int jt = k / PT, pt = k % PT;
+        const int jt = k / PT, pt = k % PT;  // = ptw
         f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          if (32 * kb + 31 >= 16 * jt) a1 = mma(frag_col(sDY, PP, 16 * pt, kb), frag_row(sS1, PR, 16 * jt, kb), a1);
+          if (32 * kb + 31 >= 16 * jt) a1 = mma(fDY(kb, pt), frag_row(sS1, PR, 16 * jt, kb), a1);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a2 = mma(frag_row(sGT, PN, 16 * pt, kb), frag_row(sBr, PN, 16 * jt, kb), a2);
+        for (int kb = 0; kb < NKB; ++kb) a2 = mma(fGTrow(kb, pt), frag_row(sBr, PN, 16 * jt, kb), a2);
         const int j = 16 * jt + l16;
         const float wj = w[j >> lgR];
         const f32x4 dx = a1 + wj * a2;
@@ -779,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       for (int it = 0; it < (4 * NT + kWaves - 1) / kWaves; ++it) {
         const int k = wave + kWaves * it;
         if ((4 * NT) % kWaves != 0 && k >= 4 * NT) break;
-        const int t = k / NT, nt = k % NT;
+        const int t = k / NT, nt = k % NT;  // = ntw
         f32x4 b1 = {0.f, 0.f, 0.f, 0.f}, b2 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f},
               c2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -789,8 +830,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         }
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) {
-          b2 = mma(frag_col(sGT, PN, 16 * nt, kb), frag_row(sX, PP, 16 * t, kb), b2);
-          c2 = mma(frag_col(sHT, PN, 16 * nt, kb), frag_row(sDY, PP, 16 * t, kb), c2);
+          b2 = mma(fGTcol(kb, nt), frag_row(sX, PP, 16 * t, kb), b2);
+          c2 = mma(fHTcol(kb, nt), frag_row(sDY, PP, 16 * t, kb), c2);
         }
         const int r = 16 * t + l16, tl = r >> lgR;
         f32x4 db = b1 + w[tl] * b2;
@@ -834,9 +875,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (!tile_ok(m)) continue;
         f32x4 a = acc[m] * D;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          a = mma(frag_col(sCr, PN, 16 * tile_nt(m), kb),
-                  scale8(frag_col(sDY, PP, 16 * tile_pt(m), kb), krow4(E, kb, 0), krow4(E, kb, 1)), a);
+        for (int kb = 0; kb < 2; ++kb)  // tile_pt(m) = ptw
+          a = mma(frag_col(sCr, PN, 16 * tile_nt(m), kb), scale8(fDY(kb, tile_pt(m)), krow4(E, kb, 0), krow4(E, kb, 1)), a);
         acc[m] = a;
       }
     }
@@ -847,6 +887,11 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       for (int m = 0; m < STW; ++m)
         if (tile_ok(m)) turn_parts(m, acc[m], unpack4(hsave[m]));
     }
+
+    // the previous chunk's loads, issued after the products (their registers
+    // are free from the staging on) and in flight across the scalar phase and
+    // the next chunk's start (kLateLoads), else after the staging
+    if (kLateLoads && c > cA) load_rev(c - 1);
 
     // ---- per-token scalar gradients (wave 0, lane = token); every wave issues
     // the stores, with dropped offsets outside wave 0

@@ -63,6 +63,7 @@ struct DecodeParams {
 struct PrefillParams {
   int Bt, L, H, P, N, R;
   int log2R;
+  int chunk;  // tokens per chunk, 0: 64 / R (the fp32 kernel also takes a smaller power of two)
   bool bf16;
   const void* x;
   const void* B;

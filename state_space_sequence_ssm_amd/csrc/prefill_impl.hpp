@@ -22,7 +22,9 @@
 // MI355X design: one 512-thread workgroup (8 wave64) owns one (batch, head)
 // and walks its chunks in order with the N x P state resident in MFMA
 // accumulators (fp32); nothing per chunk is written to HBM except y.  A chunk
-// tile always holds 64 (token, rank) rows, so Q = 64 / R.  Per chunk:
+// tile holds 64 (token, rank) rows; a chunk is Q = 64 / R tokens, or fewer
+// when the caller asks (a power of two): the tile's rows past Q R are then
+// empty (zero operands, zero weights, never stored).  Per chunk:
 //   * the next chunk's x, B, C, theta, Delta, lambda are loaded into registers
 //     while the current chunk computes (software prefetch);
 //   * the Delta/lambda scan is one wave64 inclusive scan; the angle scan is a
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   const int b = bh / p.H;
   const int hh = bh % p.H;
   const int L = p.L, H = p.H, R = p.R, lgR = p.log2R;
-  const int Q = kRows >> lgR;  // tokens per chunk
+  const int Q = p.chunk > 0 ? p.chunk : (kRows >> lgR);  // tokens per chunk (Q R <= 64)
   const bool om = p.omega != nullptr;  // angles as rates: theta = Delta * omega
   const bool rope = p.theta != nullptr || om;
   const float Ah = p.A_tok != nullptr ? 0.f : p.A[hh];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           const int i = 4 * rb + k;
           const int t = s0 + (i >> lgR);
           u32x4 v = {0u, 0u, 0u, 0u};
-          if (t < L) {
+          if ((i >> lgR) < Q && t < L) {
             const T* src = base + (rowbase(t) + (i & (R - 1))) * D + cb * VE;
             v = *reinterpret_cast<const u32x4*>(src);
           }
@@ -233,14 +235,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const float lamEnd = __shfl(lamc, Q - 1, 64);
       const float gam = rlam * d;
       const float del = gam + (1.f - rlamn) * dn;
-      if (lane < Q) {
-        sLam[lane] = lamc;
-        sGam[lane] = gam;
-        sDel[lane] = del;
-        sW[lane] = __expf(lamEnd - lamc) * del;
-        sDec[lane] = __expf(lamc);
-        sDt[lane] = d;
-      }
+      // every lane: past the chunk's Q tokens Delta is 0, so the weights are 0
+      // and the decays finite (read for the tile's empty rows)
+      sLam[lane] = lamc;
+      sGam[lane] = gam;
+      sDel[lane] = del;
+      sW[lane] = __expf(lamEnd - lamc) * del;
+      sDec[lane] = __expf(lamc);
+      sDt[lane] = d;
       if (lane == 0) sChunkDec[0] = __expf(lamEnd);
     }
     if (rope) {
@@ -319,6 +321,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int tl = (4 * rb + k) >> lgR;
+            if (tl >= Q) continue;  // an empty row: no angle table entry
 #pragma unroll
             for (int q = 0; q < VE / 2; ++q) {
               const float2 csn = *reinterpret_cast<const float2*>(sCS + 2 * (tl * (N / 2) + c0 / 2 + q));
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int i = 4 * rb + k;
-            if (s0 + (i >> lgR) == L - 1) {
+            if ((i >> lgR) < Q && s0 + (i >> lgR) == L - 1) {
               const size_t o = (static_cast<size_t>(bh) * R + (i & (R - 1))) * D + c0;
               if (kind == 0 && p.Bprev_rot_out != nullptr) {
 #pragma unroll
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     // ---- store y rows of this chunk
     {
       const int t = c * Q + ti;
-      if (t < L) {
+      if (ti < Q && t < L) {
         T* yrow = yg + (rowbase(t) + (iRow & (R - 1))) * P;
 #pragma unroll
         for (int k = 0; k < Lt::YT; ++k) {

@@ -66,7 +66,12 @@ def test_prefill_validation():
         (lambda a: setattr(a, "N", 48), _lib.M3_ERR_UNSUPPORTED),
         (lambda a: setattr(a, "P", 8), _lib.M3_ERR_UNSUPPORTED),
         (lambda a: setattr(a, "in_dtype", 7), _lib.M3_ERR_UNSUPPORTED),
-        (lambda a: setattr(a, "chunk", 32), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "chunk", 32), _lib.M3_ERR_UNSUPPORTED),  # bf16: chunks of 64 / R only
+        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "chunk", 24)), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "chunk", 128)), _lib.M3_ERR_UNSUPPORTED),
+        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "R", 4), setattr(a, "chunk", 32)),
+         _lib.M3_ERR_UNSUPPORTED),  # 32 tokens x rank 4 > 64 rows
+        (lambda a: (setattr(a, "in_dtype", _lib.M3_F32), setattr(a, "chunk", -16)), _lib.M3_ERR_UNSUPPORTED),
         (lambda a: setattr(a, "x", 0x10000008), _lib.M3_ERR_INVALID_ARG),  # misaligned
         (lambda a: setattr(a, "Bprev_rot", 0x20000000), _lib.M3_ERR_INVALID_ARG),  # without xprev
         (lambda a: setattr(a, "phi0", 0x20000000), _lib.M3_ERR_INVALID_ARG),  # angle without theta

@@ -93,6 +93,48 @@ def test_prefill_small(ops, case):
         assert np.max(angle_diff(host(out["phi"]), ref["phi"])) <= 1e-4
 
 
+# ----------------------------------------------------------------- chunk length
+# Bt, L, H, P, N, R, rope, carry: the fp32 path at every chunk length it takes
+CHUNKS = [
+    (1, 256, 4, 16, 16, 1, False, False),
+    (2, 203, 3, 32, 32, 1, True, True),
+    (1, 150, 2, 64, 64, 2, True, True),
+    (1, 97, 2, 16, 32, 8, True, True),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKS, ids=lambda c: "-".join(map(str, c)))
+def test_prefill_chunk_length(ops, case):
+    """The chunked evaluation does not depend on the chunk length beyond
+    rounding: y, the final state and the carry at every power-of-two chunk of
+    Q tokens (Q R <= 64) against the oracle (token by token), and against the
+    run at Q = 64 / R."""
+    Bt, L, H, P, N, R, rope, carry = case
+    s = Shape(Bt, L, H, P, N, R, "f32", rope)
+    d = make_inputs(s, 2500 + L + N + R, h0=carry, carry=carry)
+    dd = to_device(d, s)
+    ref = oracle_prefill(d)
+    base = None
+    Q = 64 // R
+    while Q >= 1:
+        _say("prefill chunk", case, "Q", Q)
+        out = _run_prefill(ops, dd, s, carry=True, chunk=Q)
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in out.items() if v is not None}
+        ey, eh = orc.rel_l2(got["y"], ref["y"]), orc.rel_l2(got["h"], ref["h"])
+        _say(f"  rel_l2 y={ey:.2e} h={eh:.2e}")
+        assert ey <= TOL["f32"] and eh <= TOL["f32"]
+        assert orc.rel_l2(got["Bprev_rot"], ref["Bprev_rot"]) <= 1e-5
+        assert np.array_equal(got["xprev"], ref["xprev"])
+        if rope:
+            assert np.max(angle_diff(got["phi"], ref["phi"])) <= 1e-4
+        if base is None:
+            base = got
+        else:  # fp32 throughout: the chunk lengths agree far inside the oracle bar
+            assert orc.rel_l2(got["y"], base["y"]) <= 1e-4 and orc.rel_l2(got["h"], base["h"]) <= 1e-4
+        Q //= 4 if Q > 4 else 2
+
+
 # ----------------------------------------------------------------- angles from rates
 OMEGA = [
     # Bt, L, H, P, N, R, carry, dtype  (theta = dt * omega formed on chip)
