@@ -706,12 +706,22 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         // causal tiles numbered (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
         const int it = k < 1 ? 0 : (k < 3 ? 1 : (k < 6 ? 2 : 3));
         const int jt = k - it * (it + 1) / 2;
+        const int j = 16 * jt + l16, tj = j >> lgR;
+        // the mask's per-token scalars, read (unconditionally) before the
+        // products so that their latency overlaps them
+        const float lamJ = lam2[tj], delJ = del[tj];
+        float lamI[4], gamI[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int ti = (16 * it + 4 * g + jj) >> lgR;
+          lamI[jj] = lam2[ti];
+          gamI[jj] = gam[ti];
+        }
         f32x4 g1 = {0.f, 0.f, 0.f, 0.f}, g2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) g1 = mma(frag_row(sCr, PN, 16 * it, kb), frag_row(sBr, PN, 16 * jt, kb), g1);
 #pragma unroll
         for (int kb = 0; kb < PKB; ++kb) g2 = mma(frag_row(sDY, PP, 16 * it, kb), frag_row(sX, PP, 16 * jt, kb), g2);
-        const int j = 16 * jt + l16, tj = j >> lgR;
         f32x4 s1, s2;
         float colLo = 0.f, colDd = 0.f;
         float rowLo[4], rowDg[4];
@@ -719,9 +729,9 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         for (int jj = 0; jj < 4; ++jj) {
           const int i = 16 * it + 4 * g + jj, ti = i >> lgR;
           const bool lower = tj < ti, diag = tj == ti;
-          const float ex = __builtin_amdgcn_exp2f(lam2[ti] - lam2[tj]);
-          const float mlo = lower ? ex * del[tj] : 0.f;
-          const float mv = lower ? mlo : (diag ? gam[ti] : 0.f);
+          const float ex = __builtin_amdgcn_exp2f(lamI[jj] - lamJ);  // selected away above the diagonal
+          const float mlo = lower ? ex * delJ : 0.f;
+          const float mv = lower ? mlo : (diag ? gamI[jj] : 0.f);
           s1[jj] = mv * g1[jj];
           s2[jj] = mv * g2[jj];
           const float dm = g1[jj] * g2[jj];

@@ -157,6 +157,14 @@ __device__ __forceinline__ f32x4 unpack4(u32x2 u) {
 // columns c0 + 4q..+3 of row r_e of a row-major matrix, lane i receives column
 // c0 + i of rows r_0..r_3: four k values of an MFMA operand column.
 typedef short tr4_t __attribute__((ext_vector_type(4)));
+// A uniform LDS element offset the compiler cannot relate to other offsets.
+// Reads from two bases a constant distance apart are otherwise fused into one
+// ds_read2_b64, which the LDS serves at half the rate of two single 8-byte
+// reads (16 lanes per cycle on 32 banks instead of 32 lanes on 64 banks).
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
   typedef __attribute__((address_space(3))) tr4_t* lds_tr4_ptr;
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr4_ptr)(p)));

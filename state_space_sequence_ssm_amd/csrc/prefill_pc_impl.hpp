@@ -93,14 +93,6 @@ template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   return r * D + ((((c >> 2) ^ swz_unit<D>(r))) << 2);
 }
-// A uniform LDS element offset the compiler cannot relate to other offsets.
-// Reads from two bases a constant distance apart are otherwise fused into one
-// ds_read2_b64, which the LDS serves at half the rate of two single 8-byte
-// reads (16 lanes per cycle on 32 banks instead of 32 lanes on 64 banks).
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+s"(v));
-  return v;
-}
 // w-scaled copy of an MFMA operand: slots 0-3 by w0, slots 4-7 by w1 (one
 // rounding of the product to bf16)
 __device__ __forceinline__ bf16x8 scale8(bf16x8 x, f32x4 w0, f32x4 w1) {
