@@ -691,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) dd += acc[m][jj] * hv[jj];
       }
-      for (int off = 32; off > 0; off >>= 1) dd += __shfl_xor(dd, off);
+      dd = wave_sum(dd);
       if (lane == 0) sDp[wave] = dd;
     }
     if (!kLateLoads && c > cA) load_rev(c - 1);  // in flight during this chunk's products
@@ -933,8 +933,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       const float lamE = sc[kMisc * kSc + 1];
       const float D = sc[kMisc * kSc];
       const float Et = t < Q ? sc[kE * kSc + t] : 0.f, wt = t < Q ? sc[kW * kSc + t] : 0.f;
-      float sdw = dw * wt;
-      for (int off = 32; off > 0; off >>= 1) sdw += __shfl_xor(sdw, off);
+      const float sdw = wave_sum(dw * wt);
       float dLam = t < Q ? rlo - clo + dE * Et - dw * wt : 0.f;
       if (t == Q - 1) dLam += sdw + dD * D;
       const float ddl = t < Q ? cdd + dw * __builtin_amdgcn_exp2f(lamE - lam2) : 0.f;
@@ -945,7 +944,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       const float da = tot - incl + dLam;
       const float dtv = t < Q ? sc[kDt * kSc + t] : 0.f, lmv = t < Q ? sc[kLamb * kSc + t] : 0.f;
       const float At = t < Q ? sc[kA * kSc + t] : 0.f;
-      const float ddlPrev = __shfl_up(ddl, 1);
+      const float ddlPrev = dpp<0x138, 0xF, true>(ddl);  // lane t - 1 (wave_shr 1)
       float gdt = da * At + dgam * lmv;
       float glam = dgam * dtv;
       if (t >= 1) {  // delta_{t-1} = gamma_{t-1} + (1 - lambda_t) Delta_t
@@ -959,8 +958,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       stA = dA;
       if (v && t >= 1) offT = toff(c * Q + t);
       if (v) offA = toff(c * Q + t);
-      float sA = v ? dA : 0.f;
-      for (int off = 32; off > 0; off >>= 1) sA += __shfl_xor(sA, off);
+      const float sA = wave_sum(v ? dA : 0.f);
       // the later chunk's first token takes this chunk's last delta term
       const float ddlLast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ddl), Q - 1));
       if (t == 0) {
@@ -1040,7 +1038,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (p.dh0 != nullptr) p.dh0[static_cast<size_t>(bh) * N * P + static_cast<size_t>(n) * P + pc] = acc[m][jj];
       }
     }
-    for (int off = 32; off > 0; off >>= 1) dk += __shfl_xor(dk, off);
+    dk = wave_sum(dk);
     if (lane == 0) sDp[wave] = dk;
     // G in fp32 [N][P] over the (now free) bf16 tile area
     float* sG = reinterpret_cast<float*>(smem);

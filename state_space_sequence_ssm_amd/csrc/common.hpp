@@ -190,6 +190,11 @@ __device__ __forceinline__ float seg_scan(float v) {
   if constexpr (W >= 64) v += dpp<0x143, 0xC, false>(v);
   return v;
 }
+// Sum over the 64 lanes of a wave, in every lane: the DPP scan's last lane (no
+// LDS round trip, unlike a butterfly of lane shuffles).
+__device__ __forceinline__ float wave_sum(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, seg_scan<64>(v)), 63));
+}
 
 
 
