@@ -131,11 +131,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   // Register budget of the reverse walk: below the largest tiles with RoPE or
   // P = 128 the operand fragments of a wave's fixed tiles are held across a
   // chunk's products (at those tiles the extra live registers would spill).
-  // Without RoPE the next chunk's loads are then issued after the products,
-  // which frees their registers there; with RoPE that would queue the dtheta
-  // stores behind them, so they go out after the staging as otherwise.
   constexpr bool kHoist = !(ROPE && (N >= 128 || P >= 128)) && !(P >= 128 && N >= 64);
-  constexpr bool kLateLoads = kHoist && !ROPE;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* const sm16 = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const sCr = sm16 + Lt::oCr;
@@ -646,18 +642,28 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   u32x2 hsave[STW];                             // the shifted state entering the chunk (bf16)
   u32x2 hpre[STW];                              // the same (bf16), loaded a chunk ahead
   float phPre = 0.f;                            // the angle entering the chunk (tid < J), loaded a chunk ahead
-  auto load_rev = [&](int c) __attribute__((always_inline)) {
+  // The reverse walk's loads of chunk c, issued during chunk c + 1 in four
+  // parts spread over its phases (the scalars, angles and state at the Gram
+  // phase, C after it, B between the dX and dB / dC products, x and dy after
+  // the products): all at one point, every workgroup's requests arrive at once
+  // and the issuing waves stall on them.
+  auto load_rev_s = [&](int c) __attribute__((always_inline)) {
     load_scalars(c, S);
     load_theta(c, S);
-    load_tile(c, rCi, NC{}, S.c);
-    load_tile(c, rBi, NC{}, S.b);
-    load_tile(c, rXi, PC{}, S.x);
-    load_tile(c, rDYi, PC{}, S.dy);
     if constexpr (ROPE) phPre = bloadf(rPh, tid < J ? static_cast<uint32_t>(c * J + tid) * 4u : kBad);
 #pragma unroll
     for (int m = 0; m < STW; ++m) hpre[m] = bload8(rSt, st_off(c, m));
   };
-  load_rev(cB - 1);
+  auto load_rev_c = [&](int c) __attribute__((always_inline)) { load_tile(c, rCi, NC{}, S.c); };
+  auto load_rev_b = [&](int c) __attribute__((always_inline)) { load_tile(c, rBi, NC{}, S.b); };
+  auto load_rev_x = [&](int c) __attribute__((always_inline)) {
+    load_tile(c, rXi, PC{}, S.x);
+    load_tile(c, rDYi, PC{}, S.dy);
+  };
+  load_rev_s(cB - 1);
+  load_rev_c(cB - 1);
+  load_rev_b(cB - 1);
+  load_rev_x(cB - 1);
   for (int c = cB - 1; c >= cA; --c) {
     if constexpr (ROPE) {
       // dtheta at the start of chunk c + 1, from the parts its pass left in sAnc
@@ -694,8 +700,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       dd = wave_sum(dd);
       if (lane == 0) sDp[wave] = dd;
     }
-    if (!kLateLoads && c > cA) load_rev(c - 1);  // in flight during this chunk's products
     __syncthreads();
+    if (c > cA) load_rev_s(c - 1);
 
     // ---- Gram tiles (i tile it >= j tile jt): G1 = C B^T, G2 = dY X^T, masks
     {
@@ -763,6 +769,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
     }
     __syncthreads();
+    if (c > cA) load_rev_c(c - 1);
 
     {
       const float* w = sc + kW * kSc;
@@ -823,6 +830,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         s += __shfl_xor(s, 32);
         if (g == 0) sWp[pt * 64 + j] = s;
       }
+      if (c > cA) load_rev_b(c - 1);
       // ---- dB^T and dC^T tiles of the same rows (row tile t, n tile nt)
       // (rolled at N = 128, where unrolling spills)
       constexpr int kUnrollBC = NT >= 8 ? 1 : 4;
@@ -898,10 +906,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (tile_ok(m)) turn_parts(m, acc[m], unpack4(hsave[m]));
     }
 
-    // the previous chunk's loads, issued after the products (their registers
-    // are free from the staging on) and in flight across the scalar phase and
-    // the next chunk's start (kLateLoads), else after the staging
-    if (kLateLoads && c > cA) load_rev(c - 1);
+    if (c > cA) load_rev_x(c - 1);
 
     // ---- per-token scalar gradients (wave 0, lane = token); every wave issues
     // the stores, with dropped offsets outside wave 0
