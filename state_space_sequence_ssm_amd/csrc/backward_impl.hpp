@@ -992,25 +992,41 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     if constexpr (ROPE) {
       // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens
       // >= t: a segmented scan over the tokens in reverse order (lane tl holds
-      // token Q - 1 - tl), one segment of Q lanes per pair
-      // (a compile-time number of passes, R pairs per wave each: the same
-      // stores in every wave; passes past the last pair store nothing)
+      // token Q - 1 - tl), one segment of Q lanes per pair, R pairs per wave
+      // pass.  The result goes back into the table, in the token's rank-0 row
+      // (read above by this lane alone), and leaves as whole rows below.
       const int tl = lane & (Q - 1), tok = Q - 1 - tl;
 #pragma unroll
       for (int it = 0; it < (J + kWaves - 1) / kWaves; ++it) {
         const int q = (wave + kWaves * it) * R + (lane >> (6 - lgR));
-        const bool ok = q < J;
-        float v = 0.f;
-        if (ok)
+        if (q < J) {  // the same in every lane of the wave (R divides J)
+          float v = 0.f;
           for (int rr = 0; rr < R; ++rr) v += sDPhi[(tok * R + rr) * JP + q];
-        v = seg_scan_q(v);
-        const float d = (ok ? sThC[q] : 0.f) + v;
-        const int t = c * Q + tok;
-        bstoref(rDth, (ok && t < L) ? (static_cast<uint32_t>(t) * H * J + q) * 4u : kBad, d);
-        if (ok && t == cA * Q) sThC[q] = d;  // dtheta of the first token (dphi0), written after the walk
+          v = seg_scan_q(v);
+          const float d = sThC[q] + v;
+          sDPhi[tok * R * JP + q] = d;
+          if (c * Q + tok == cA * Q) sThC[q] = d;  // dtheta of the first token (dphi0), written after the walk
+        }
       }
     }
     __syncthreads();
+    if constexpr (ROPE) {
+      // the chunk's dtheta rows, 16 bytes (four pairs of one token) per lane
+      // and a compile-time number of stores per thread; the table is next
+      // rewritten in the next chunk's products
+      constexpr int kDU = (kRows * (J / 4) + kThreads - 1) / kThreads;
+#pragma unroll
+      for (int i = 0; i < kDU; ++i) {
+        const int u = tid + i * kThreads;
+        const bool ok = u < Q * (J / 4);
+        const int tok = ok ? u / (J / 4) : 0, q4 = u % (J / 4);
+        const float* src = sDPhi + tok * R * JP + 4 * q4;
+        const f32x4 v = {src[0], src[1], src[2], src[3]};
+        const int t = c * Q + tok;
+        bstore16(rDth, (ok && t < L) ? (static_cast<uint32_t>(t) * H * J + 4 * q4) * 4u : kBad,
+                 __builtin_bit_cast(u32x4, v));
+      }
+    }
   }
 
   if (MODE == 2 && seg == 1) {
