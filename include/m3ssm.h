@@ -302,7 +302,10 @@ int m3_ssm_decode_step(const m3_decode_args* args, void* stream);
  *   workspace: required, m3_ssm_prefill_backward_workspace_size bytes,
  *   256-byte aligned (the shifted state, in bf16, and the angle entering
  *   every chunk of every (batch, head), written by the kernel's forward
- *   state walk).
+ *   state walk; with at most half as many (batch, head) units as the
+ *   device has compute units and at least 8 chunks the sequence is split in
+ *   two walked at once, and the workspace also holds the values joined at
+ *   the split: so its size depends on the current device).
  * Sizes: bf16 only (M3_ERR_UNSUPPORTED for float32); N, P in {16, 32, 64,
  * 128} whose tiles fit the LDS of a CU (N = P = 128 does not:
  * M3_ERR_UNSUPPORTED); R a power of two <= 8; chunks of 64 / R tokens.
