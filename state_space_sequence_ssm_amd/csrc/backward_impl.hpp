@@ -233,6 +233,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   for (int e = tid; e < static_cast<int>(Lt::kBytes / 4); e += kThreads) reinterpret_cast<float*>(smem)[e] = 0.f;
   __syncthreads();
 
+  // (Tile loads, the state dump and its reread, and the dtheta rows move
+  // whole lines once: non-temporal cache policy.)
   // ---- staging of a chunk, split into its global loads (into registers,
   // issued a chunk ahead so that they overlap the previous chunk's products)
   // and the LDS stores that consume them.  Every load is unconditional: an
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     for (int i = 0; i < U; ++i) {
       const int e = tid + i * kThreads;
       const int r = e / (D / 8), k8 = e % (D / 8);
-      dst[i] = bload16(src, e < kRows * (D / 8) ? rrow(c, r) * (D * 2u) + 16u * k8 : kBad);
+      dst[i] = bload16_nt(src, e < kRows * (D / 8) ? rrow(c, r) * (D * 2u) + 16u * k8 : kBad);
     }
   };
   // per-token scalars of chunk c (wave 0, lane = token): the raw Delta, lambda,
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     if (c + 2 < cB) load_fwd(c + 2, S);  // in flight during the next two chunks
     // the shifted state entering chunk c, in the accumulator layout
 #pragma unroll
-    for (int m = 0; m < STW; ++m) bstore8(rSt, st_off(c, m), pack4(acc[m]));
+    for (int m = 0; m < STW; ++m) bstore8_nt(rSt, st_off(c, m), pack4(acc[m]));
     __syncthreads();
     // H <- D H + Btil^T (w X): k = the chunk's 64 rows
     const float D = sc[kMisc * kSc];
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     load_theta(c, S);
     if constexpr (ROPE) phPre = bloadf(rPh, tid < J ? static_cast<uint32_t>(c * J + tid) * 4u : kBad);
 #pragma unroll
-    for (int m = 0; m < STW; ++m) hpre[m] = bload8(rSt, st_off(c, m));
+    for (int m = 0; m < STW; ++m) hpre[m] = bload8_nt(rSt, st_off(c, m));
   };
   auto load_rev_c = [&](int c) __attribute__((always_inline)) { load_tile(c, rCi, NC{}, S.c); };
   auto load_rev_b = [&](int c) __attribute__((always_inline)) { load_tile(c, rBi, NC{}, S.b); };
@@ -1023,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         const float* src = sDPhi + tok * R * JP + 4 * q4;
         const f32x4 v = {src[0], src[1], src[2], src[3]};
         const int t = c * Q + tok;
-        bstore16(rDth, (ok && t < L) ? (static_cast<uint32_t>(t) * H * J + 4 * q4) * 4u : kBad,
+        bstore16_nt(rDth, (ok && t < L) ? (static_cast<uint32_t>(t) * H * J + 4 * q4) * 4u : kBad,
                  __builtin_bit_cast(u32x4, v));
       }
     }

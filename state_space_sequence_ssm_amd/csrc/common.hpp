@@ -212,6 +212,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// the same with the non-temporal cache policy (aux bit 1): data read or
+// written once, kept from displacing reused lines
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+__device__ __forceinline__ u32x2 bload8_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
+}
+__device__ __forceinline__ void bstore8_nt(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 2);
+}
+__device__ __forceinline__ void bstore16_nt(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
+}
 __device__ __forceinline__ u32x2 bload8(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }

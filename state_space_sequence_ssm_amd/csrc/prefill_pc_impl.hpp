@@ -403,7 +403,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     piece_rc(pc, row, col);
     const uint32_t grow = static_cast<uint32_t>((c * Q + (row >> LGR)) * tsR + (row & (R - 1)));
     const uint32_t off = col < D ? (grow * D + col) * 2u : kBad;
-    return bload16(pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB), off);
+    // whole-line loads stream with the non-temporal policy (7% off the SISO
+    // real workload); the half-line loads of the MFMA layout need the L2 to
+    // keep each line for its other half (with the policy: +25% at R = 4)
+    const rsrc_t rs = pc.kind == 2 ? rX : (pc.kind == 1 ? rC : rB);
+    if constexpr (kFL) return bload16_nt(rs, off); else return bload16(rs, off);
   };
   constexpr bool kLateRefill = LGR == 0;
   auto issue_bcx = [&](int c, u32x4 (&dst)[UPH], auto HALF) __attribute__((always_inline)) {
@@ -992,7 +996,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       const uint32_t off = (c >= 0 && e < kUnits)
                                ? (static_cast<uint32_t>((c * Q + (r >> LGR)) * tsR + (r & (R - 1))) * P + 8 * c8) * 2u
                                : kBad;
-      bstore16(rY, off, v);
+      bstore16_nt(rY, off, v);
     }
   };
 
