@@ -178,7 +178,7 @@ def backward_split(Bt, L, H, P, N, R, rope, cus=256):
     nch = (L + Q - 1) // Q
     if 2 * Bt * H > cus or nch < 8:
         return 0
-    return min(max((nch * 9 + 8) // 16, 4), nch - 4)
+    return min(max((nch * 11 + 10) // 20, 4), nch - 4)
 
 
 SPLIT_JOIN_KERNEL = "m3::bw::split_join_kernel"
