@@ -760,10 +760,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
             sRow[(jt * 64 + 16 * it + 4 * g + jj) * 2 + 1] = d;
           }
         }
-        colLo += __shfl_xor(colLo, 16);
-        colLo += __shfl_xor(colLo, 32);
-        colDd += __shfl_xor(colDd, 16);
-        colDd += __shfl_xor(colDd, 32);
+        colLo = add_x32(add_x16(colLo));
+        colDd = add_x32(add_x16(colDd));
         if (g == 0) {
           sCol[(it * 64 + j) * 2 + 0] = colLo;
           sCol[(it * 64 + j) * 2 + 1] = colDd;
@@ -828,8 +826,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         const u32x2 xv = *reinterpret_cast<const u32x2*>(sX + j * PP + 16 * pt + 4 * g);
         float s = a2[0] * __uint_as_float(xv[0] << 16) + a2[1] * __uint_as_float(xv[0] & 0xffff0000u) +
                   a2[2] * __uint_as_float(xv[1] << 16) + a2[3] * __uint_as_float(xv[1] & 0xffff0000u);
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
+        s = add_x32(add_x16(s));
         if (g == 0) sWp[pt * 64 + j] = s;
       }
       if (c > cA) load_rev_b(c - 1);
@@ -861,8 +858,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         const float cr[4] = {__uint_as_float(cv[0] << 16), __uint_as_float(cv[0] & 0xffff0000u),
                              __uint_as_float(cv[1] << 16), __uint_as_float(cv[1] & 0xffff0000u)};
         float s = c2[0] * cr[0] + c2[1] * cr[1] + c2[2] * cr[2] + c2[3] * cr[3];
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
+        s = add_x32(add_x16(s));
         if (g == 0) sEp[nt * 64 + r] = s;
         if constexpr (ROPE) {
           // the pair's angle gradient from the rotated tiles (dtheta adds at

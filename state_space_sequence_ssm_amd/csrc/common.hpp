@@ -190,6 +190,18 @@ __device__ __forceinline__ float seg_scan(float v) {
   if constexpr (W >= 64) v += dpp<0x143, 0xC, false>(v);
   return v;
 }
+// v plus the v of lane ^ 16 (add_x16) or lane ^ 32 (add_x32), in every lane:
+// gfx950's permlane swaps hand lanes l & ~16 and l | 16 (or 32) their values
+// on the vector ALU, where a lane shuffle is an LDS round trip.  Both lanes of
+// a pair add in the same order, so they hold the same bits.
+__device__ __forceinline__ float add_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // Sum over the 64 lanes of a wave, in every lane: the DPP scan's last lane (no
 // LDS round trip, unlike a butterfly of lane shuffles).
 __device__ __forceinline__ float wave_sum(float v) {

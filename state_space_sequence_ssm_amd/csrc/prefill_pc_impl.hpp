@@ -680,8 +680,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       row_scales(src, HALF, std::integral_constant<int, 1>{}, [](const Piece) { return 0; },
                  [&](int) { return 16 * quad + l16; },
                  [](float v) {
-                   v += __shfl_xor(v, 16);
-                   return v + __shfl_xor(v, 32);
+                   return add_x32(add_x16(v));
                  },
                  rsc);
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
