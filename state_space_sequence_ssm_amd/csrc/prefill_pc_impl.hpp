@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       const float lamEnd = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lamc), Q - 1));
       // next token's Delta, lambda: lane t + 1, or token 0 of chunk c + 1 (the
       // other register set; zeros past the end, i.e. Delta_L = 0) for t = Q - 1
-      const float dNext = __shfl_down(dl, 1), lNext = __shfl_down(rlam[set], 1);
+      const float dNext = dpp<0x130, 0xF, true>(dl), lNext = dpp<0x130, 0xF, true>(rlam[set]);  // lane t + 1 (wave_shl 1)
       const float d0 = delta_of(
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rdt[set ^ 1]), 0)), proDt, dtBias,
           (c + 1) * Q < L);
