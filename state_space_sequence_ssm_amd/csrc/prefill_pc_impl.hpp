@@ -30,7 +30,8 @@
 //     by the angle scan), rounded to bf16 and
 //     stored row-major with X, in tiles whose 8-byte units are XOR-swizzled by
 //     row.  Wave 0 scans the decays of chunk k+2 (log2 units, one DPP wave
-//     scan); the raw angles of chunk k+2 go to the angle table.  Every wave
+//     scan; with RoPE at R = 1 wave 3 does so in phase B instead); the raw
+//     angles of chunk k+2 go to the angle table.  Every wave
 //     then computes the readout partials C^T H'_prev of chunk k from the state
 //     it keeps.
 //   * phase B -- products of chunk k from slot k%2: the angle scan of chunk k+2
@@ -374,6 +375,15 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   // the memory latency; two sets kept ~1300 cache-line requests in flight per
   // CU and stalled the load issue of the later waves (measured 2-5% slower).
   constexpr int kSets = 1;
+  // Decay scan placement.  With RoPE at R = 1 it runs in phase B on wave 3,
+  // which computes one masked Gram tile there (waves 0 and 1 compute two) and
+  // refills nothing; the staging phase, where every wave waits for the
+  // slowest, then carries only the raw angles (and Delta, for angles given as
+  // rates).  Measured 3-5% faster on the RoPE SISO workloads; on the real and
+  // the R > 1 workloads phase B is the longer phase and the scan stays on
+  // wave 0 in phase A (moved, they ran 1-9% slower).
+  constexpr bool kDecayInB = ROPE && LGR == 0;
+  constexpr int kScanWave = kDecayInB ? 3 : 0;
   u32x4 raw[kSets][UPH];
   // theta of one chunk as whole token rows: float4 unit e = token e / NG, group e % NG
   constexpr int kThUnits = Q * NG;
@@ -419,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     // issue the same instructions with an out-of-range offset: no memory
     // request (one strided scalar per lane is one cache-line lookup per lane)
     // and identical wait counts everywhere.
-    const uint32_t off = (wave == 0 && lane < Q) ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
+    const uint32_t off = (wave == kScanWave && lane < Q) ? static_cast<uint32_t>((c * Q + lane) * H + hh) * 4u : kBad;
     rdt[set] = bloadf(rDt, off);
     rlam[set] = bloadf(rLam, off);
     rAt[set] = bloadf(rAtok, off);  // an empty range without A_tok: reads 0, no request
@@ -434,9 +444,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       }
     }
   };
-  // decay scalars (log2 units) of chunk c -> SC[c%3]; raw theta -> Phi[c%2]
-  auto stage_small = [&](int c, int set) __attribute__((always_inline)) {
-    if (wave == 0) {
+  // decay scalars (log2 units) of chunk c -> SC[c%3] (the scan wave)
+  auto stage_decay = [&](int c, int set) __attribute__((always_inline)) {
+    if (wave == kScanWave) {
       float* S = sc(c % 3);
       // Delta (softplus of raw + bias with the prologue; tokens past the end
       // have Delta = 0, which the zero-filled loads give without it)
@@ -458,8 +468,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       S[3 * 64 + lane] = __builtin_amdgcn_exp2f(lamEnd - lamc) * del;
       S[4 * 64 + lane] = __builtin_amdgcn_exp2f(lamc);
       if (lane == 0) S[5 * 64] = __builtin_amdgcn_exp2f(lamEnd);
-      S[6 * 64 + lane] = dl;  // Delta, for angles given as rates
+      if constexpr (!kDecayInB) S[6 * 64 + lane] = dl;  // Delta, for angles given as rates (else stage_dt)
     }
+  };
+  // Delta of chunk c alone -> SC[c%3] (for the angle scan of rates)
+  auto stage_dt = [&](int c, int set) __attribute__((always_inline)) {
+    if (wave == kScanWave)
+      sc(c % 3)[6 * 64 + lane] = delta_of(rdt[set], proDt, dtBias, lane < Q && c * Q + lane < L);
+  };
+  // raw theta of chunk c -> Phi[c%2] (every thread)
+  auto stage_theta = [&](int c, int set) __attribute__((always_inline)) {
     if constexpr (ROPE) {
       float* tab = phiTab(c & 1);
 #pragma unroll
@@ -468,6 +486,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         if (e < kThUnits) *reinterpret_cast<f32x4*>(tab + (e / NG) * PH + 4 * (e % NG)) = rawTh[set][s];
       }
     }
+  };
+  auto stage_small = [&](int c, int set) __attribute__((always_inline)) {
+    if constexpr (kDecayInB)
+      if (om) stage_dt(c, set);
+    stage_decay(c, set);
+    stage_theta(c, set);
   };
   // cumulative angles of chunk c in place in Phi[c%2] (after a barrier since
   // its raw theta was stored): lanes are tokens, a segment of Q lanes per
@@ -1075,8 +1099,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
   auto chunk = [&](int k, u32x4 (&bcx)[UPH], int sset, auto HALF) __attribute__((always_inline)) {
     if constexpr (kStageY) flush_y(k - 1);
     build_slot(k + 1, bcx, HALF);  // and issues chunk k+1+kSets into bcx
-    stage_small(k + 2, sset);
-    issue_small(k + 4, sset);
+    if constexpr (!kDecayInB)
+      stage_decay(k + 2, sset);
+    else if (om)
+      stage_dt(k + 2, sset);  // the angle scan of this chunk scales by Delta
+    stage_theta(k + 2, sset);
+    if constexpr (!kDecayInB) issue_small(k + 4, sset);  // after the reads of its register set
     if constexpr (!kEarly) gram_tiles(k);
     readout(k, HALF);
     __syncthreads();  // S(k), readout partials, slot k+1, raw theta(k+2) visible
@@ -1084,6 +1112,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     compute_rest(k, HALF);
     load_x(k + 1);  // slot k+1 is visible since the first barrier
     if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 1 + kSets, bcx, HALF);
+    if constexpr (kDecayInB) {
+      stage_decay(k + 2, sset);  // first read after the next barrier
+      issue_small(k + 4, sset);
+    }
     if constexpr (kEarly) gram_tiles(k + 1);  // overlaps the tail of chunk k
     __syncthreads();  // S(k+1), SC(k+2), Phi(k+2) visible; slot k free
   };
