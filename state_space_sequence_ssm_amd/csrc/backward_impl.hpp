@@ -102,7 +102,14 @@ struct Lay {
   static constexpr size_t fPhi = fPhiC + J;             // [64][JP] angles of the chunk's tokens
   static constexpr size_t fDPhi = fPhi + (ROPE ? 64 * JP : 0);  // [64 rows][JP] angle gradients
   static constexpr size_t fThC = fDPhi + (ROPE ? 64 * JP : 0);   // [J] dtheta at the next chunk start
-  static constexpr size_t fEnd = fThC + (ROPE ? J : 0);
+  // second buffers of the per-chunk scalars, Gram row / column sums and
+  // per-wave parts: a chunk's scalar gradients are formed during the next
+  // chunk's Gram phase, while that chunk fills the other buffer
+  static constexpr size_t fSc2 = fThC + (ROPE ? J : 0);
+  static constexpr size_t fRow2 = fSc2 + 10 * kSc;
+  static constexpr size_t fCol2 = fRow2 + 4 * 64 * 2;
+  static constexpr size_t fD2 = fCol2 + 4 * 64 * 2;
+  static constexpr size_t fEnd = fD2 + 16;
   static constexpr size_t kBytes = fBase + fEnd * 4;
 };
 // scalar rows of fSc
@@ -143,12 +150,13 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   uint16_t* const sS1 = sm16 + Lt::oS1;
   uint16_t* const sS2 = sm16 + Lt::oS2;
   float* const f32 = reinterpret_cast<float*>(smem + Lt::fBase);
-  float* const sc = f32 + Lt::fSc;
-  float* const sRow = f32 + Lt::fRow;
-  float* const sCol = f32 + Lt::fCol;
+  // per-chunk tables, one of two buffers by the chunk's parity
+  auto scb = [&](int c) { return f32 + ((c & 1) ? Lt::fSc2 : Lt::fSc); };
+  auto rowb = [&](int c) { return f32 + ((c & 1) ? Lt::fRow2 : Lt::fRow); };
+  auto colb = [&](int c) { return f32 + ((c & 1) ? Lt::fCol2 : Lt::fCol); };
+  auto dpb = [&](int c) { return f32 + ((c & 1) ? Lt::fD2 : Lt::fD); };
   float* const sEp = f32 + Lt::fE;
   float* const sWp = f32 + Lt::fW;
-  float* const sDp = f32 + Lt::fD;
   float* const phiC = f32 + Lt::fPhiC;
   float* const sPhi = f32 + Lt::fPhi;
   float* const sDPhi = f32 + Lt::fDPhi;
@@ -284,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   // Lam (log2 units), gamma, delta, E, w and the raw values into the scalar table
   auto store_scalars = [&](int c, const Stage& S) __attribute__((always_inline)) {
     if (wave != 0) return;
+    float* const sc = scb(c);
     const int t = lane;
     const bool v0 = t < Q && c * Q + t < L;
     const bool v1 = t < Q && c * Q + t + 1 < L;
@@ -484,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     for (int m = 0; m < STW; ++m) bstore8_nt(rSt, st_off(c, m), pack4(acc[m]));
     __syncthreads();
     // H <- D H + Btil^T (w X): k = the chunk's 64 rows
+    const float* const sc = scb(c);
     const float D = sc[kMisc * kSc];
     const float* w = sc + kW * kSc;
 #pragma unroll
@@ -544,6 +554,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       if (c + 2 < cB) load_gs(c + 2, S);
       __syncthreads();
       const float dc = __builtin_amdgcn_exp2f(lsum);
+      const float* const sc = scb(c);
       const float* E = sc + kE * kSc;
 #pragma unroll
       for (int m = 0; m < STW; ++m) {
@@ -637,9 +648,102 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     const int q = tid - 64;
     if (q >= 0 && q < J) Tq = turn_sum(q);
   }
-  float pendDt = 0.f, pendLam = 0.f;            // first token of the later chunk (wave 0, lane 0)
+  constexpr int kSW = kWaves - 1;               // the wave that forms the scalar gradients
+  float pendDt = 0.f, pendLam = 0.f;            // first token of the later chunk (wave kSW, lane 0)
   int pendTok = (MODE == 2 && seg == 0) ? cB * Q : -1;  // segment 0: token cm Q's part (to the workspace)
-  float dAsum = 0.f;                            // sum of dA over tokens (wave 0, lane 0)
+  float dAsum = 0.f;                            // sum of dA over tokens (wave kSW, lane 0)
+  // Per-token scalar gradients of chunk c (wave kSW, lane = token), formed
+  // during the Gram phase of the chunk before it in the walk (waves 0 and 1
+  // compute two Gram tiles there, kSW one), from the chunk's buffers of the
+  // scalars, the Gram row / column sums and the per-wave parts; every wave
+  // issues the stores, with dropped offsets outside wave kSW.  The pending
+  // Delta / lambda term of the later chunk's first token is carried in wave
+  // kSW's registers from one call to the next (chunks in reverse order).
+  auto scalar_grads = [&](int c) __attribute__((always_inline)) {
+    float stDt = 0.f, stLam = 0.f, stA = 0.f, stPdt = 0.f, stPlam = 0.f;
+    uint32_t offT = kBad, offA = kBad, offP = kBad;
+    if (wave == kSW) {
+      const int t = lane;
+      const float* const sc = scb(c);
+      const float* const sRow = rowb(c);
+      const float* const sCol = colb(c);
+      const float* const sDp = dpb(c);
+      float rlo = 0.f, rdg = 0.f, clo = 0.f, cdd = 0.f, dE = 0.f, dw = 0.f;
+      if (t < Q) {
+        for (int rr = 0; rr < R; ++rr) {
+          const int r = t * R + rr;
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) {
+            rlo += sRow[(k4 * 64 + r) * 2 + 0];
+            rdg += sRow[(k4 * 64 + r) * 2 + 1];
+            clo += sCol[(k4 * 64 + r) * 2 + 0];
+            cdd += sCol[(k4 * 64 + r) * 2 + 1];
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) dE += sEp[nt * 64 + r];
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt) dw += sWp[pt * 64 + r];
+        }
+      }
+      float dD = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < kWaves; ++w8) dD += sDp[w8];
+      const float lam2 = t < Q ? sc[kLam2 * kSc + t] : 0.f;
+      const float lamE = sc[kMisc * kSc + 1];
+      const float D = sc[kMisc * kSc];
+      const float Et = t < Q ? sc[kE * kSc + t] : 0.f, wt = t < Q ? sc[kW * kSc + t] : 0.f;
+      const float sdw = wave_sum(dw * wt);
+      float dLam = t < Q ? rlo - clo + dE * Et - dw * wt : 0.f;
+      if (t == Q - 1) dLam += sdw + dD * D;
+      const float ddl = t < Q ? cdd + dw * __builtin_amdgcn_exp2f(lamE - lam2) : 0.f;
+      const float dgam = t < Q ? rdg + ddl : 0.f;
+      // da_t = sum_{k >= t} dLam_k
+      const float incl = seg_scan<64>(dLam);
+      const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+      const float da = tot - incl + dLam;
+      const float dtv = t < Q ? sc[kDt * kSc + t] : 0.f, lmv = t < Q ? sc[kLamb * kSc + t] : 0.f;
+      const float At = t < Q ? sc[kA * kSc + t] : 0.f;
+      const float ddlPrev = dpp<0x138, 0xF, true>(ddl);  // lane t - 1 (wave_shr 1)
+      float gdt = da * At + dgam * lmv;
+      float glam = dgam * dtv;
+      if (t >= 1) {  // delta_{t-1} = gamma_{t-1} + (1 - lambda_t) Delta_t
+        gdt += ddlPrev * (1.f - lmv);
+        glam -= ddlPrev * dtv;
+      }
+      const float dA = da * dtv;
+      const bool v = t < Q && c * Q + t < L;
+      stDt = gdt;
+      stLam = glam;
+      stA = dA;
+      if (v && t >= 1) offT = toff(c * Q + t);
+      if (v) offA = toff(c * Q + t);
+      const float sA = wave_sum(v ? dA : 0.f);
+      // the later chunk's first token takes this chunk's last delta term
+      const float ddlLast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ddl), Q - 1));
+      if (t == 0) {
+        if (pendTok >= 0) {
+          const float dn = sc[kDt * kSc + Q], ln = sc[kLamb * kSc + Q];
+          stPdt = pendDt + ddlLast * (1.f - ln);
+          stPlam = pendLam - ddlLast * dn;
+          if (MODE == 2 && seg == 0 && c == cB - 1) {
+            p.sTok[bh * 2] = stPdt;  // token cm Q: joined with segment 1's part afterwards
+            p.sTok[bh * 2 + 1] = stPlam;
+          } else {
+            offP = toff(pendTok);
+          }
+        }
+        pendDt = gdt;
+        pendLam = glam;
+        pendTok = c * Q;
+        dAsum += sA;
+      }
+    }
+    bstoref(rDdt, offT, stDt);
+    bstoref(rDlam, offT, stLam);
+    bstoref(rDAt, offA, stA);
+    bstoref(rDdt, offP, stPdt);
+    bstoref(rDlam, offP, stPlam);
+  };
   Stage& S = S0;                                // the reverse walk's loads, one chunk ahead
   u32x2 hsave[STW];                             // the shifted state entering the chunk (bf16)
   u32x2 hpre[STW];                              // the same (bf16), loaded a chunk ahead
@@ -667,6 +771,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
   load_rev_b(cB - 1);
   load_rev_x(cB - 1);
   for (int c = cB - 1; c >= cA; --c) {
+    float* const sRow = rowb(c);
+    float* const sCol = colb(c);
+    float* const sDp = dpb(c);
+    const float* const sc = scb(c);
     if constexpr (ROPE) {
       // dtheta at the start of chunk c + 1, from the parts its pass left in sAnc
       const int q = tid - 64;
@@ -768,6 +876,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         }
       }
     }
+    if (c + 1 < cB) scalar_grads(c + 1);  // the later chunk's, from its buffers
     __syncthreads();
     if (c > cA) load_rev_c(c - 1);
 
@@ -906,87 +1015,6 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
 
     if (c > cA) load_rev_x(c - 1);
 
-    // ---- per-token scalar gradients (wave 0, lane = token); every wave issues
-    // the stores, with dropped offsets outside wave 0
-    float stDt = 0.f, stLam = 0.f, stA = 0.f, stPdt = 0.f, stPlam = 0.f;
-    uint32_t offT = kBad, offA = kBad, offP = kBad;
-    if (wave == 0) {
-      const int t = lane;
-      float rlo = 0.f, rdg = 0.f, clo = 0.f, cdd = 0.f, dE = 0.f, dw = 0.f;
-      if (t < Q) {
-        for (int rr = 0; rr < R; ++rr) {
-          const int r = t * R + rr;
-#pragma unroll
-          for (int k4 = 0; k4 < 4; ++k4) {
-            rlo += sRow[(k4 * 64 + r) * 2 + 0];
-            rdg += sRow[(k4 * 64 + r) * 2 + 1];
-            clo += sCol[(k4 * 64 + r) * 2 + 0];
-            cdd += sCol[(k4 * 64 + r) * 2 + 1];
-          }
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) dE += sEp[nt * 64 + r];
-#pragma unroll
-          for (int pt = 0; pt < PT; ++pt) dw += sWp[pt * 64 + r];
-        }
-      }
-      float dD = 0.f;
-#pragma unroll
-      for (int w8 = 0; w8 < kWaves; ++w8) dD += sDp[w8];
-      const float lam2 = t < Q ? sc[kLam2 * kSc + t] : 0.f;
-      const float lamE = sc[kMisc * kSc + 1];
-      const float D = sc[kMisc * kSc];
-      const float Et = t < Q ? sc[kE * kSc + t] : 0.f, wt = t < Q ? sc[kW * kSc + t] : 0.f;
-      const float sdw = wave_sum(dw * wt);
-      float dLam = t < Q ? rlo - clo + dE * Et - dw * wt : 0.f;
-      if (t == Q - 1) dLam += sdw + dD * D;
-      const float ddl = t < Q ? cdd + dw * __builtin_amdgcn_exp2f(lamE - lam2) : 0.f;
-      const float dgam = t < Q ? rdg + ddl : 0.f;
-      // da_t = sum_{k >= t} dLam_k
-      const float incl = seg_scan<64>(dLam);
-      const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
-      const float da = tot - incl + dLam;
-      const float dtv = t < Q ? sc[kDt * kSc + t] : 0.f, lmv = t < Q ? sc[kLamb * kSc + t] : 0.f;
-      const float At = t < Q ? sc[kA * kSc + t] : 0.f;
-      const float ddlPrev = dpp<0x138, 0xF, true>(ddl);  // lane t - 1 (wave_shr 1)
-      float gdt = da * At + dgam * lmv;
-      float glam = dgam * dtv;
-      if (t >= 1) {  // delta_{t-1} = gamma_{t-1} + (1 - lambda_t) Delta_t
-        gdt += ddlPrev * (1.f - lmv);
-        glam -= ddlPrev * dtv;
-      }
-      const float dA = da * dtv;
-      const bool v = t < Q && c * Q + t < L;
-      stDt = gdt;
-      stLam = glam;
-      stA = dA;
-      if (v && t >= 1) offT = toff(c * Q + t);
-      if (v) offA = toff(c * Q + t);
-      const float sA = wave_sum(v ? dA : 0.f);
-      // the later chunk's first token takes this chunk's last delta term
-      const float ddlLast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ddl), Q - 1));
-      if (t == 0) {
-        if (pendTok >= 0) {
-          const float dn = sc[kDt * kSc + Q], ln = sc[kLamb * kSc + Q];
-          stPdt = pendDt + ddlLast * (1.f - ln);
-          stPlam = pendLam - ddlLast * dn;
-          if (MODE == 2 && seg == 0 && c == cB - 1) {
-            p.sTok[bh * 2] = stPdt;  // token cm Q: joined with segment 1's part afterwards
-            p.sTok[bh * 2 + 1] = stPlam;
-          } else {
-            offP = toff(pendTok);
-          }
-        }
-        pendDt = gdt;
-        pendLam = glam;
-        pendTok = c * Q;
-        dAsum += sA;
-      }
-    }
-    bstoref(rDdt, offT, stDt);
-    bstoref(rDlam, offT, stLam);
-    bstoref(rDAt, offA, stA);
-    bstoref(rDdt, offP, stPdt);
-    bstoref(rDlam, offP, stPlam);
     if constexpr (ROPE) {
       // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens
       // >= t: a segmented scan over the tokens in reverse order (lane tl holds
@@ -1007,8 +1035,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         }
       }
     }
-    __syncthreads();
     if constexpr (ROPE) {
+      __syncthreads();
       // the chunk's dtheta rows, 16 bytes (four pairs of one token) per lane
       // and a compile-time number of stores per thread; the table is next
       // rewritten in the next chunk's products
@@ -1026,11 +1054,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
     }
   }
+  scalar_grads(cA);  // every table of chunk cA is complete since the walk's last barrier
 
   if (MODE == 2 && seg == 1) {
     // segment 1's part of token cm Q's Delta and lambda gradients, its dtheta
     // (the sum of dPhi over the segment) and its sum of dA
-    if (tid == 0) {
+    if (tid == kSW * 64) {
       p.sTok[(units + bh) * 2] = pendDt;
       p.sTok[(units + bh) * 2 + 1] = pendLam;
       if (p.dA_part != nullptr) p.dA_part[units + bh] = dAsum;
@@ -1058,7 +1087,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       }
     }
     dk = wave_sum(dk);
-    if (lane == 0) sDp[wave] = dk;
+    float* const sDk = dpb(cA + 1);  // not the buffer the last scalar gradients read
+    if (lane == 0) sDk[wave] = dk;
     // G in fp32 [N][P] over the (now free) bf16 tile area
     float* sG = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -1067,9 +1097,9 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) sG[(16 * tile_nt(m) + 4 * g + jj) * P + 16 * tile_pt(m) + l16] = acc[m][jj];
     __syncthreads();
-    if (tid == 0) {
+    if (tid == kSW * 64) {  // the lane that holds the pending terms and the sum of dA
       float dkap = 0.f;
-      for (int w8 = 0; w8 < kWaves; ++w8) dkap += sDp[w8];
+      for (int w8 = 0; w8 < kWaves; ++w8) dkap += sDk[w8];
       const float dn = p.dt[o0], ln = p.lam[o0];
       if (pendTok == 0) {
         p.ddt[o0] = pendDt + dkap * (1.f - ln);
