@@ -117,7 +117,8 @@ struct Piece {
 // MFMA-layout staging (used at R > 1): a load is 16 rows x 32 columns (k block
 // cb), lane (g, l16) reading row l16, 8 columns at 8 g.
 
-template <int N, int P>
+// BAL: the balanced whole-line ownership at N = 64 (kernels with the prologue)
+template <int N, int P, bool BAL = false>
 struct PcLayout {
   static constexpr int NK = N < 32 ? 32 : N;  // n contraction length (zero padded)
   static constexpr int PK = P < 32 ? 32 : P;  // X row length (columns past P unused)
@@ -134,15 +135,28 @@ struct PcLayout {
   static constexpr int ipu(int D) { return D >= 64 ? 2 : 1; }
   static constexpr int ncb(int D) { return D >= 64 ? D / 64 : 1; }
   static constexpr int NCBN = ncb(N), NCBP = ncb(P);
-  // unit ownership between the two waves of a row tile: B and C blocks by
-  // halves of n; X blocks alternate (all to the upper wave when B and C have a
-  // single block, all to the lower one when X has a single block)
-  static constexpr int bc_half(int cb) { return NCBN == 1 ? 0 : (2 * cb) / NCBN; }
-  static constexpr int x_half(int cb) { return NCBN == 1 ? 1 : (NCBP == 1 ? 0 : (cb & 1)); }
+  // Unit ownership between the two waves of a row tile (whole lines): B and C
+  // column blocks by halves of n; X blocks alternate (all to the upper wave
+  // when B and C have a single block, all to the lower one when X has a
+  // single block).  With the prologue at N = 64 (one column block of two
+  // loads) the two waves instead take one load (8 rows) of B, C and X each,
+  // so that both normalise and rotate: with B and C whole on the lower wave
+  // the RoPE SISO prefill with the prologue ran 7% longer (the plain one
+  // measured within noise either way and keeps whole blocks).  At N = 128 a
+  // single X block stays with the lower waves (split by rows too, the SISO
+  // real prefill ran 3% longer).
+  static constexpr bool kBcByI = BAL && NCBN == 1 && ipu(N) == 2;
+  static constexpr bool kXByI = kBcByI && NCBP == 1 && ipu(P) == 2;
+  static constexpr int bc_half(int cb, int i) { return NCBN == 1 ? (kBcByI ? i : 0) : (2 * cb) / NCBN; }
+  static constexpr int x_half(int cb, int i) {
+    return kXByI ? i : (NCBN == 1 ? 1 : (NCBP == 1 ? 0 : (cb & 1)));
+  }
   static constexpr int count(int h) {
     int n = 0;
-    for (int cb = 0; cb < NCBN; ++cb) n += bc_half(cb) == h ? 2 * ipu(N) : 0;
-    for (int cb = 0; cb < NCBP; ++cb) n += x_half(cb) == h ? ipu(P) : 0;
+    for (int cb = 0; cb < NCBN; ++cb)
+      for (int i = 0; i < ipu(N); ++i) n += bc_half(cb, i) == h ? 2 : 0;
+    for (int cb = 0; cb < NCBP; ++cb)
+      for (int i = 0; i < ipu(P); ++i) n += x_half(cb, i) == h ? 1 : 0;
     return n;
   }
   static constexpr int UPH_FL = count(0) > count(1) ? count(0) : count(1);  // loads per wave
@@ -150,15 +164,15 @@ struct PcLayout {
   static constexpr Piece piece_fl(int h, int s) {
     int n = 0;
     for (int cb = 0; cb < NCBN; ++cb)
-      if (bc_half(cb) == h)
-        for (int i = 0; i < ipu(N); ++i) {
+      for (int i = 0; i < ipu(N); ++i)
+        if (bc_half(cb, i) == h) {
           if (n == s) return Piece{0, cb, i};
           if (n + 1 == s) return Piece{1, cb, i};
           n += 2;
         }
     for (int cb = 0; cb < NCBP; ++cb)
-      if (x_half(cb) == h)
-        for (int i = 0; i < ipu(P); ++i) {
+      for (int i = 0; i < ipu(P); ++i)
+        if (x_half(cb, i) == h) {
           if (n == s) return Piece{2, cb, i};
           n += 1;
         }
@@ -274,7 +288,7 @@ struct PcLayout {
 // the step); without it the kernel compiles to the plain core.
 template <int N, int P, int LGR, bool ROPE, bool SO = false, bool PRO = false>
 __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
-  using Lt = PcLayout<N, P>;
+  using Lt = PcLayout<N, P, PRO>;
   constexpr int R = 1 << LGR;
   constexpr int Q = kRows >> LGR;  // tokens per chunk
   constexpr int NKB = Lt::NKB, NTH = Lt::NTH, NPT = Lt::NPT, UPT = Lt::UPT;
