@@ -142,34 +142,42 @@ struct PcLayout {
   // loads) the two waves instead take one load (8 rows) of B, C and X each,
   // so that both normalise and rotate: with B and C whole on the lower wave
   // the RoPE SISO prefill with the prologue ran 7% longer (the plain one
-  // measured within noise either way and keeps whole blocks).  At N = 128 a
-  // single X block stays with the lower waves (split by rows too, the SISO
-  // real prefill ran 3% longer).
+  // measured within noise either way and keeps whole blocks).  With the
+  // prologue at N = 128 the lower wave takes whole rows of B and the upper
+  // one whole rows of C (and one load of X each): every row's sum of squares
+  // is then in one wave, with no exchange through LDS behind a workgroup
+  // barrier (SISO real with the prologue 0.189 -> 0.181 ms).  Without the
+  // prologue a single X block stays with the lower waves at N = 128 (split by
+  // rows too, the SISO real prefill ran 3% longer).
   static constexpr bool kBcByI = BAL && NCBN == 1 && ipu(N) == 2;
-  static constexpr bool kXByI = kBcByI && NCBP == 1 && ipu(P) == 2;
+  static constexpr bool kByKind = BAL && NCBN == 2;
+  static constexpr bool kXByI = (kBcByI || kByKind) && NCBP == 1 && ipu(P) == 2;
   static constexpr int bc_half(int cb, int i) { return NCBN == 1 ? (kBcByI ? i : 0) : (2 * cb) / NCBN; }
+  // half of B (kind 0) or C (kind 1) piece (cb, i)
+  static constexpr int bck_half(int kind, int cb, int i) { return kByKind ? kind : bc_half(cb, i); }
   static constexpr int x_half(int cb, int i) {
     return kXByI ? i : (NCBN == 1 ? 1 : (NCBP == 1 ? 0 : (cb & 1)));
   }
   static constexpr int count(int h) {
     int n = 0;
     for (int cb = 0; cb < NCBN; ++cb)
-      for (int i = 0; i < ipu(N); ++i) n += bc_half(cb, i) == h ? 2 : 0;
+      for (int i = 0; i < ipu(N); ++i) n += (bck_half(0, cb, i) == h) + (bck_half(1, cb, i) == h);
     for (int cb = 0; cb < NCBP; ++cb)
       for (int i = 0; i < ipu(P); ++i) n += x_half(cb, i) == h ? 1 : 0;
     return n;
   }
   static constexpr int UPH_FL = count(0) > count(1) ? count(0) : count(1);  // loads per wave
-  // load s of half h; B(cb, i) directly precedes C(cb, i), which reuses its sin/cos
+  // load s of half h; B(cb, i) directly precedes C(cb, i) of the same half,
+  // which reuses its sin/cos
   static constexpr Piece piece_fl(int h, int s) {
     int n = 0;
     for (int cb = 0; cb < NCBN; ++cb)
       for (int i = 0; i < ipu(N); ++i)
-        if (bc_half(cb, i) == h) {
-          if (n == s) return Piece{0, cb, i};
-          if (n + 1 == s) return Piece{1, cb, i};
-          n += 2;
-        }
+        for (int kind = 0; kind < 2; ++kind)
+          if (bck_half(kind, cb, i) == h) {
+            if (n == s) return Piece{kind, cb, i};
+            n += 1;
+          }
     for (int cb = 0; cb < NCBP; ++cb)
       for (int i = 0; i < ipu(P); ++i)
         if (x_half(cb, i) == h) {
@@ -249,7 +257,7 @@ struct PcLayout {
   static constexpr size_t bytes(bool rope, bool pro) { return (rope ? kBytesRope : kBytesReal) + (pro ? kProBytes : 0); }
   // B and C columns of one row are staged by both waves of a row tile (whole
   // lines at R = 1: column blocks of 64; MFMA layout at R > 1: k blocks of 32)
-  static constexpr bool rows_split(bool fl) { return fl ? NCBN > 1 : NKB > 1; }
+  static constexpr bool rows_split(bool fl) { return fl ? NCBN > 1 && !kByKind : NKB > 1; }
   static constexpr bool has_bc(bool fl, int h) {
     for (int s = 0; s < uph(fl); ++s) {
       const Piece pc = piece(fl, h, s);
@@ -260,14 +268,14 @@ struct PcLayout {
   // column blocks of B / C staged by half h: the first one and how many
   static constexpr int bc_first(bool fl, int h) {
     for (int s = 0; s < uph(fl); ++s)
-      if (piece(fl, h, s).kind == 0) return piece(fl, h, s).cb;
+      if (piece(fl, h, s).kind == 0 || piece(fl, h, s).kind == 1) return piece(fl, h, s).cb;
     return 0;
   }
   static constexpr int bc_blocks(bool fl, int h) {
     int n = 0, last = -1;
     for (int s = 0; s < uph(fl); ++s) {
       const Piece pc = piece(fl, h, s);
-      if (pc.kind == 0 && pc.cb != last) {
+      if ((pc.kind == 0 || pc.kind == 1) && pc.cb != last) {
         ++n;
         last = pc.cb;
       }
@@ -686,7 +694,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         store_x(s2, row, col, v);
       } else {
         if constexpr (ROPE) {
-          if (pc.kind == 0) {  // B precedes C of the same rows and columns: C reuses sin/cos
+          // B precedes C of the same rows and columns: C reuses sin/cos (with
+          // B and C on different waves, each computes its own)
+          if (pc.kind == 0 || Lt::kByKind) {
             const int q = col < N ? (col >> 1) : 0;
             const f32x4 a = *reinterpret_cast<const f32x4*>(tab + (row >> LGR) * PH + q);
 #pragma unroll
@@ -697,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
           }
         }
         float f[8];
-        unpack_pro(v, pc.kind, 0, proNorm ? rsc[pc.kind][pc.i] : 1.f, f);
+        unpack_pro(v, pc.kind, pc.cb - Lt::bc_first(kFL, h), proNorm ? rsc[pc.kind][pc.i] : 1.f, f);
         // B and C feed the Gram tiles and the readout, B also the state
         *reinterpret_cast<u32x4*>((pc.kind == 1 ? sC : sB) + swz<NK>(row, col)) = rotate_pack(f, cs, sn);
       }
