@@ -188,10 +188,16 @@ struct PcLayout {
   }
   // MFMA-layout pieces: B/C k block kb -> half (2 kb / NKB); X k block -> alternate
   static constexpr int mf_bc_half(int kb) { return NKB == 1 ? 0 : (2 * kb) / NKB; }
+  // With the prologue (R > 1, rows of two or more k blocks): B whole on the
+  // lower wave and C whole on the upper one, so that each row's sum of squares
+  // stays in one wave (no exchange through LDS behind a workgroup barrier;
+  // MIMO with the prologue 0.774 -> 0.745 ms).
+  static constexpr bool kByKindMf = BAL && NKB >= 2;
+  static constexpr int mf_bck_half(int kind, int kb) { return kByKindMf ? kind : mf_bc_half(kb); }
   static constexpr int mf_x_half(int kb) { return PKB == 1 ? (NKB == 1 ? 1 : 0) : (kb & 1); }
   static constexpr int mf_count(int h) {
     int n = 0;
-    for (int kb = 0; kb < NKB; ++kb) n += mf_bc_half(kb) == h ? 2 : 0;
+    for (int kb = 0; kb < NKB; ++kb) n += (mf_bck_half(0, kb) == h) + (mf_bck_half(1, kb) == h);
     for (int kb = 0; kb < PKB; ++kb) n += mf_x_half(kb) == h ? 1 : 0;
     return n;
   }
@@ -199,11 +205,11 @@ struct PcLayout {
   static constexpr Piece piece_mf(int h, int s) {
     int n = 0;
     for (int kb = 0; kb < NKB; ++kb)
-      if (mf_bc_half(kb) == h) {
-        if (n == s) return Piece{0, kb, 0};
-        if (n + 1 == s) return Piece{1, kb, 0};
-        n += 2;
-      }
+      for (int kind = 0; kind < 2; ++kind)
+        if (mf_bck_half(kind, kb) == h) {
+          if (n == s) return Piece{kind, kb, 0};
+          n += 1;
+        }
     for (int kb = 0; kb < PKB; ++kb)
       if (mf_x_half(kb) == h) {
         if (n == s) return Piece{2, kb, 0};
@@ -257,7 +263,7 @@ struct PcLayout {
   static constexpr size_t bytes(bool rope, bool pro) { return (rope ? kBytesRope : kBytesReal) + (pro ? kProBytes : 0); }
   // B and C columns of one row are staged by both waves of a row tile (whole
   // lines at R = 1: column blocks of 64; MFMA layout at R > 1: k blocks of 32)
-  static constexpr bool rows_split(bool fl) { return fl ? NCBN > 1 && !kByKind : NKB > 1; }
+  static constexpr bool rows_split(bool fl) { return fl ? NCBN > 1 && !kByKind : NKB > 1 && !kByKindMf; }
   static constexpr bool has_bc(bool fl, int h) {
     for (int s = 0; s < uph(fl); ++s) {
       const Piece pc = piece(fl, h, s);
@@ -296,7 +302,7 @@ struct PcLayout {
 // the step); without it the kernel compiles to the plain core.
 template <int N, int P, int LGR, bool ROPE, bool SO = false, bool PRO = false>
 __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
-  using Lt = PcLayout<N, P, PRO>;
+  using Lt = PcLayout<N, P, PRO && !SO>;  // (the state-only walk stages no C)
   constexpr int R = 1 << LGR;
   constexpr int Q = kRows >> LGR;  // tokens per chunk
   constexpr int NKB = Lt::NKB, NTH = Lt::NTH, NPT = Lt::NPT, UPT = Lt::UPT;
@@ -751,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
         continue;
       }
       if constexpr (ROPE) {
-        if (pc.kind == 0) {  // B comes first for a k-block; C reuses its sin/cos
+        if (pc.kind == 0 || Lt::kByKindMf) {  // B comes first for a k-block; C reuses its sin/cos (same wave)
           const int q = (N >= 32 || 16 * pc.cb + 4 * g < N / 2) ? 16 * pc.cb + 4 * g : 0;
           const f32x4 a = *reinterpret_cast<const f32x4*>(tab + ((16 * quad + l16) >> LGR) * PH + q);
 #pragma unroll
