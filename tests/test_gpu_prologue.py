@@ -58,9 +58,13 @@ def _ref_inputs(d, q):
 CASES = [
     # name, Bt, L, H, P, N, R, dtype, rope, carry, options
     ("n64_r1_all", 2, 131, 3, 64, 64, 1, "bf16", True, True, {}),
-    ("n128_r1_real_rows_split", 1, 150, 2, 64, 128, 1, "bf16", False, True, {}),
+    ("n128_r1_real_rows_by_kind", 1, 150, 2, 64, 128, 1, "bf16", False, True, {}),
+    ("n128_r1_rope_gains", 1, 100, 2, 64, 128, 1, "bf16", True, False, {}),
+    ("n128_p128_r1_real", 1, 70, 2, 128, 128, 1, "bf16", False, True, {}),
+    ("n64_r1_real", 1, 130, 2, 64, 64, 1, "bf16", False, True, {}),
+    ("n64_p128_r1", 1, 100, 2, 128, 64, 1, "bf16", True, True, {}),
     ("n128_r1_rope", 1, 90, 2, 64, 128, 1, "bf16", True, True, dict(gains=False)),
-    ("n64_r4_rows_split", 1, 100, 2, 64, 64, 4, "bf16", True, True, {}),
+    ("n64_r4_by_kind", 1, 100, 2, 64, 64, 4, "bf16", True, True, {}),
     ("n32_r8", 1, 45, 2, 16, 32, 8, "bf16", True, False, dict(gains=False)),
     ("n16_r2_padded", 1, 77, 2, 32, 16, 2, "bf16", True, True, {}),
     ("n128_r4_real", 1, 90, 2, 64, 128, 4, "bf16", False, True, {}),
