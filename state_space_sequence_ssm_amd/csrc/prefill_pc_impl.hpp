@@ -529,10 +529,14 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
       const int tl = lane % Q, pg = lane / Q;
       float* tab = phiTab(c & 1);
       const float dsc = om ? sc(c % 3)[6 * 64 + tl] : 1.f;  // theta = Delta * omega (exact x 1 otherwise)
+      // Scan slots dealt from wave 2 on: with fewer angle groups than waves
+      // (R > 1) the work falls on waves 2, 3, ..., not on waves 0 and 1,
+      // which compute two masked Gram tiles in the same phase.
+      const int sw = (wave + kWaves - 2) & (kWaves - 1);
 #pragma unroll
       for (int s = 0; s < TSL; ++s) {
-        const int q4 = (s * kWaves + wave) * R + pg;  // uniform within a Q-lane segment
-        if ((s * kWaves + wave) * R < NG) {
+        const int q4 = (s * kWaves + sw) * R + pg;  // uniform within a Q-lane segment
+        if ((s * kWaves + sw) * R < NG) {
           constexpr f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
           f32x4 v = q4 < NG ? *reinterpret_cast<const f32x4*>(tab + tl * PH + 4 * q4) : zero4;
           v *= dsc;
