@@ -823,7 +823,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       const float* lam2 = sc + kLam2 * kSc;
       const float* del = sc + kDel * kSc;
       const float* gam = sc + kGam * kSc;
-      for (int k = wave; k < 10; k += kWaves) {
+      // Tiles 0..7 on waves 0..7, tile 8 on wave 3 and tile 9 on wave 1.  Waves
+      // w and w + 4 share a SIMD; with tile 8 on wave 0 the first SIMD ended
+      // this phase last (the third SIMD carries the scalar gradients).
+      for (int s = 0; s < 2; ++s) {
+        const int k = s == 0 ? wave : (wave == 3 ? 8 : (wave == 1 ? 9 : -1));
+        if (k < 0) break;
         // causal tiles numbered (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
         const int it = k < 1 ? 0 : (k < 3 ? 1 : (k < 6 ? 2 : 3));
         const int jt = k - it * (it + 1) / 2;
