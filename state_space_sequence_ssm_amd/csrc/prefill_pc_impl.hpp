@@ -1142,10 +1142,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pc_kernel(PrefillParams p) {
     if constexpr (!kEarly) gram_tiles(k);
     readout(k, HALF);
     __syncthreads();  // S(k), readout partials, slot k+1, raw theta(k+2) visible
+    // the upper waves' refill, first thing in phase B: issued after the
+    // products instead, its loads were still in flight when phase A staged
+    // them (the upper waves' staging took ~1,250 cycles against ~770)
+    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 1 + kSets, bcx, HALF);
     scan_angles(k + 2);
     compute_rest(k, HALF);
     load_x(k + 1);  // slot k+1 is visible since the first barrier
-    if constexpr (kLateRefill && decltype(HALF)::value == 1) issue_bcx(k + 1 + kSets, bcx, HALF);
     if constexpr (kDecayInB) {
       stage_decay(k + 2, sset);  // first read after the next barrier
       issue_small(k + 4, sset);
