@@ -492,7 +492,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     }
     store_bc(c, S.b, sBr);
     store_xp(c, S.x, sX);
-    if (c + 2 < cB) load_fwd(c + 2, S);  // in flight during the next two chunks
+    // in flight during the next two chunks; issued past the last chunk too
+    // (rows past the end read zeros), so that no branch makes the wait counts
+    // of the loop conservative
+    load_fwd(c + 2, S);
     // the shifted state entering chunk c, in the accumulator layout
 #pragma unroll
     for (int m = 0; m < STW; ++m) bstore8_nt(rSt, st_off(c, m), pack4(acc[m]));
