@@ -819,7 +819,10 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
       if (lane == 0) sDp[wave] = dd;
     }
     __syncthreads();
-    if (c > cA) load_rev_s(c - 1);
+    // the next chunk's loads are issued in every chunk, the last one too (its
+    // chunk c - 1 lies before the walk: the rows read zeros or are unused), so
+    // that no branch around them makes the loop's wait counts conservative
+    load_rev_s(c - 1);
 
     // ---- Gram tiles (i tile it >= j tile jt): G1 = C B^T, G2 = dY X^T, masks
     {
@@ -891,7 +894,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
     }
     if (c + 1 < cB) scalar_grads(c + 1);  // the later chunk's, from its buffers
     __syncthreads();
-    if (c > cA) load_rev_c(c - 1);
+    load_rev_c(c - 1);
 
     {
       const float* w = sc + kW * kSc;
@@ -951,7 +954,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         s = add_x32(add_x16(s));
         if (g == 0) sWp[pt * 64 + j] = s;
       }
-      if (c > cA) load_rev_b(c - 1);
+      load_rev_b(c - 1);
       // ---- dB^T and dC^T tiles of the same rows (row tile t, n tile nt)
       // (rolled at N = 128, where unrolling spills)
       constexpr int kUnrollBC = NT >= 8 ? 1 : 4;
@@ -1026,7 +1029,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(BackwardParams p) {
         if (tile_ok(m)) turn_parts(m, acc[m], unpack4(hsave[m]));
     }
 
-    if (c > cA) load_rev_x(c - 1);
+    load_rev_x(c - 1);
 
     if constexpr (ROPE) {
       // dtheta_t = dtheta at the next chunk start + dPhi of this chunk's tokens
